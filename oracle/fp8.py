@@ -1,0 +1,260 @@
+"""FP8 (e4m3) pieces of the method, in float64 (test infrastructure).
+
+Follows "FlashAttention-3" (lukebest.github.io), "Three techniques" §3 (FP8
+throughput and precision):
+
+* block quantisation: every tile gets its own scale, aligned with the
+  kernel's tiling;
+* incoherent processing: before quantisation, Q' = QM and K' = KM, where M
+  is an orthogonal Hadamard matrix times random +-1, so (QM)(KM)^T = QK^T;
+* compared with one scale per tensor, this lowers the error where some
+  feature channels are outliers.
+
+and "Flash Attention 3：让 GPU 跑满的注意力计算", §4.1.2: the forward pass uses
+E4M3 (4 exponent bits, 3 mantissa bits); the softmax statistics (max and
+sum) are kept in higher precision while the two products run in FP8.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes):
+
+* E4M3 is the OCP "fn" variant: exponent bias 7, no infinities, largest
+  finite 448, smallest normal 2^-6, subnormal step 2^-9; rounding is to
+  nearest, ties to even; magnitudes beyond 448 saturate to 448;
+* M = diag(s) H_d / sqrt(d) with H_d the Sylvester Hadamard matrix (d a
+  power of two) and s the random signs; the same M for Q and K and every
+  head, applied along the head dimension; V is not rotated;
+* one fp32 scale per (tensor, batch, head, 128-row tile): s = amax / 448
+  over the tile after rotation (amax = 0 gives s = 1), code = e4m3(x / s),
+  x ~= s * code.  Per-tensor mode uses one amax over the whole tensor;
+* the quantisation decisions are taken in fp32, as the device does: the
+  rotated values are rounded to fp32, s = fp32(amax / 448) and the code is
+  the e4m3 rounding of fp32(x / s);
+* in the PV product, P is rounded to e4m3 as P8 = e4m3(2^8 * 2^(t - M) * w)
+  with t = S log2(e) the scores in base 2, M = ceil(max_j t) the row's
+  integer reference max and w = s_v(tile of j) / max_tiles s_v the key
+  tile's V scale relative to the largest V scale of that head; l sums the
+  unrounded 2^(t - M); O = (max s_v) 2^-8 sum_j P8_j v8_j / l.  Because M is
+  an integer, any running reference max M' <= M gives the same codes up to
+  an exact power of two (outside the subnormal range), so a tiled kernel
+  can reach this result exactly.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .exact import _f64, causal_mask
+
+E4M3_MAX = 448.0
+E4M3_MIN_NORMAL_EXP = -6  # smallest normal 2^-6
+E4M3_MANT_BITS = 3
+LOG2E = 1.4426950408889634  # log2(e)
+
+
+# --------------------------------------------------------------------------
+# e4m3 from the format definition
+# --------------------------------------------------------------------------
+
+def e4m3_round(x) -> np.ndarray:
+    """Round to the nearest e4m3fn value (ties to even), saturating at +-448.
+
+    Binade of |x| = 2^e (e >= -6; below that the subnormal spacing of the
+    -6 binade applies); the spacing in the binade is 2^(e-3).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.maximum(e, E4M3_MIN_NORMAL_EXP)
+    # floor(log2) can be off by one next to a power of two; fix it exactly.
+    e = np.where(np.ldexp(1.0, e.astype(np.int64)) > ax, e - 1, e)
+    e = np.maximum(e, E4M3_MIN_NORMAL_EXP)
+    e = np.where(np.ldexp(1.0, (e + 1).astype(np.int64)) <= ax, e + 1, e)
+    quantum = np.ldexp(1.0, (e - E4M3_MANT_BITS).astype(np.int64))
+    r = np.rint(ax / quantum) * quantum  # np.rint: ties to even; ax/quantum is exact
+    r = np.minimum(r, E4M3_MAX)
+    r = np.where(ax == 0, 0.0, r)
+    out = np.copysign(r, x)
+    return np.where(np.isnan(x), np.nan, out)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Bit pattern (uint8) of values that are exactly representable in e4m3fn."""
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x)).astype(np.uint8)
+    ax = np.abs(x)
+    code = np.zeros(x.shape, dtype=np.uint8)
+    sub = ax < 2.0 ** E4M3_MIN_NORMAL_EXP
+    # subnormal: value = mant * 2^-9
+    code = np.where(sub, np.rint(ax * 2.0 ** 9).astype(np.int64), 0)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(sub, 1.0, ax))).astype(np.int64)
+    mant = np.rint((np.where(sub, 1.0, ax) / np.ldexp(1.0, e) - 1.0) * 8).astype(np.int64)
+    norm = ((e + 7) << 3) | mant
+    code = np.where(sub, code, norm).astype(np.uint8)
+    back = e4m3_decode(code | (sign << 7))
+    if not np.array_equal(back[~np.isnan(x)], x[~np.isnan(x)]):
+        raise ValueError("e4m3_encode: value not representable")
+    return (code | (sign << 7)).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of e4m3fn bit patterns (uint8) as float64; 0x7f/0xff are NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    ef = (c >> 3) & 0xF
+    mf = c & 0x7
+    val = np.where(ef == 0,
+                   mf * 2.0 ** -9,
+                   (1.0 + mf / 8.0) * np.ldexp(1.0, (ef - 7)))
+    val = np.where((ef == 0xF) & (mf == 0x7), np.nan, val)
+    return sign * val
+
+
+def e4m3_round_f32(x32) -> np.ndarray:
+    """e4m3 rounding of float32 values (the decision in fp32, as on device)."""
+    return e4m3_round(np.asarray(x32, dtype=np.float32).astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# Hadamard rotation
+# --------------------------------------------------------------------------
+
+def sylvester(d: int) -> np.ndarray:
+    """Sylvester Hadamard matrix H_d (int64): H_1 = [1], H_2n = [[H, H], [H, -H]]."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1), dtype=np.int64)
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def fwht(x) -> np.ndarray:
+    """Unnormalised fast Walsh-Hadamard transform along the last axis.
+
+    log2(d) butterfly stages (a, b) -> (a + b, a - b) with stride 1, 2, 4, ...;
+    the result equals x @ H_d (H_d symmetric).
+    """
+    y = np.array(x, dtype=np.float64, copy=True)
+    d = y.shape[-1]
+    if d & (d - 1):
+        raise ValueError("length must be a power of two")
+    h = 1
+    while h < d:
+        y = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
+        a = y[..., 0, :].copy()
+        b = y[..., 1, :].copy()
+        y[..., 0, :] = a + b
+        y[..., 1, :] = a - b
+        y = y.reshape(y.shape[:-3] + (d,))
+        h *= 2
+    return y
+
+
+def rotation_matrix(signs) -> np.ndarray:
+    """M = diag(s) H_d / sqrt(d) (float64), orthogonal for s in {-1, +1}^d."""
+    s = np.asarray(signs, dtype=np.float64)
+    d = s.shape[0]
+    return (s[:, None] * sylvester(d)) / np.sqrt(d)
+
+
+def rotate(x, signs) -> np.ndarray:
+    """x' = x M along the last axis (float64)."""
+    return _f64(x) @ rotation_matrix(signs)
+
+
+# --------------------------------------------------------------------------
+# Quantisation: block (per 128-row tile) and per tensor
+# --------------------------------------------------------------------------
+
+def quantize(x, signs=None, per_tensor: bool = False, tile: int = 128):
+    """Rotate (if signs is given) and quantise x [..., N, d] to e4m3.
+
+    Returns ``(codes uint8 [..., N, d], scales float32 [..., ceil(N/tile)])``
+    with x' ~= scales[..., n // tile] * decode(codes[..., n, :]).  Decisions
+    are taken in fp32: the rotated values are rounded to fp32, then
+    s = fp32(amax / 448) and code = e4m3(fp32(x' / s)).
+    """
+    xr = rotate(x, signs) if signs is not None else _f64(x)
+    x32 = xr.astype(np.float32)
+    n = x32.shape[-2]
+    nt = (n + tile - 1) // tile
+    lead = x32.shape[:-2]
+    scales = np.ones(lead + (nt,), dtype=np.float32)
+    if per_tensor:
+        amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
+        s = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+        scales[...] = s
+    else:
+        for t in range(nt):
+            blk = np.abs(x32[..., t * tile:(t + 1) * tile, :])
+            amax = blk.reshape(lead + (-1,)).max(axis=-1) if blk.size else np.zeros(lead, np.float32)
+            s = np.where(amax > 0, (amax / np.float32(E4M3_MAX)).astype(np.float32), np.float32(1.0))
+            scales[..., t] = s.astype(np.float32)
+    row_scale = np.repeat(scales, tile, axis=-1)[..., :n]
+    y32 = (x32 / row_scale[..., None]).astype(np.float32)
+    codes = e4m3_encode(e4m3_round_f32(y32))
+    return codes, scales
+
+
+def dequantize(codes, scales, tile: int = 128) -> np.ndarray:
+    """scales[..., n // tile] * decode(codes[..., n, :]) in float64."""
+    vals = e4m3_decode(codes)
+    n = vals.shape[-2]
+    row_scale = np.repeat(np.asarray(scales, np.float64), tile, axis=-1)[..., :n]
+    return vals * row_scale[..., None]
+
+
+# --------------------------------------------------------------------------
+# FP8 attention: what a tiled e4m3 kernel computes, emulated in float64
+# --------------------------------------------------------------------------
+
+P_SCALE_LOG2 = 8  # P is rounded as e4m3(2^8 * p), p <= 1, so codes stay <= 256
+
+
+def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
+                  tile: int = 128, quantize_p: bool = True):
+    """fp8 attention of one or more heads: codes [..., N, d], scales [..., nt].
+
+    S = scale * (sq q8)(sk k8)^T, softmax statistics in float64, and P
+    rounded to e4m3 as stated in the module docstring.  With
+    ``quantize_p=False`` P is kept exact (the method without P rounding).
+    Returns float64 ``(O [..., Nq, d], lse [..., Nq])``.
+    """
+    qd = dequantize(q8, sq, tile)
+    kd = dequantize(k8, sk, tile)
+    v_codes = e4m3_decode(v8)
+    sv = np.asarray(sv, dtype=np.float64)
+    nk = kd.shape[-2]
+    s = float(scale) * np.matmul(qd, np.swapaxes(kd, -1, -2))
+    if causal:
+        s = np.where(causal_mask(qd.shape[-2], nk), s, -np.inf)
+    t = s * LOG2E
+    tmax = t.max(axis=-1) if nk else np.full(t.shape[:-1], -np.inf)
+    live = np.isfinite(tmax)
+    M = np.where(live, np.ceil(np.where(live, tmax, 0.0)), 0.0)
+    p = np.where(live[..., None], np.exp2(t - M[..., None]), 0.0)  # <= 1
+    l = p.sum(axis=-1)
+    sv_max = sv.max(axis=-1) if sv.shape[-1] else np.ones(sv.shape[:-1])
+    w_tile = sv / sv_max[..., None]
+    w = np.repeat(w_tile, tile, axis=-1)[..., :nk]
+    pw = p * w[..., None, :]
+    if quantize_p:
+        p8 = e4m3_round_f32((pw * 2.0 ** P_SCALE_LOG2).astype(np.float32))
+    else:
+        p8 = pw * 2.0 ** P_SCALE_LOG2
+    o_acc = np.matmul(p8, v_codes)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o = np.where(live[..., None],
+                     o_acc * (sv_max[..., None, None] * 2.0 ** -P_SCALE_LOG2) / np.where(live, l, 1.0)[..., None],
+                     0.0)
+        lse = np.where(live, (M + np.log2(np.where(live, l, 1.0))) / LOG2E, -np.inf)
+    return o, lse
+
+
+def rmse(a, b) -> float:
+    """sqrt(mean((a - b)^2)) over all elements, in float64."""
+    a = _f64(a)
+    b = _f64(b)
+    return float(np.sqrt(np.mean((a - b) ** 2)))

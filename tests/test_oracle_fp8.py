@@ -1,0 +1,260 @@
+"""Pins of the fp8 oracle pieces (CPU only).
+
+* e4m3 rounding and codes against torch's float8_e4m3fn (a library routine),
+  bit for bit, plus the format's boundary values;
+* the Sylvester Hadamard matrix (H H^T = d I in integers), the fast
+  transform against the matrix, and (QM)(KM)^T = QK^T;
+* quantisation by its defining properties (amax element -> 448, round to
+  nearest code, per-tile independence);
+* fp8 attention: with P unrounded it reduces to plain attention on the
+  dequantised inputs; with P rounded it stays within the rounding bound;
+* the method-level claim of the wiki page ("Three techniques" §3): with
+  outlier channels, block scales plus incoherent processing give a lower
+  RMSE than one scale per tensor.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8 as F
+import workloads as W
+
+RNG = np.random.default_rng(7)
+
+
+# ------------------------------------------------------------------ e4m3
+
+def test_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = F.e4m3_decode(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+
+
+def test_encode_roundtrip_all_finite_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = F.e4m3_decode(codes)
+    fin = ~np.isnan(vals)
+    assert np.array_equal(F.e4m3_encode(vals[fin]), codes[fin])
+
+
+def test_round_matches_torch_cast_sweep():
+    mag = np.exp2(RNG.uniform(-14, np.log2(464), 400000))
+    x = (mag * RNG.choice([-1.0, 1.0], mag.shape)).astype(np.float32)
+    # every e4m3 value and every midpoint between neighbours, both signs
+    grid = np.unique(np.abs(F.e4m3_decode(np.arange(127, dtype=np.uint8))))
+    mids = (grid[:-1] + grid[1:]) / 2
+    x = np.concatenate([x, grid, -grid, mids, -mids]).astype(np.float32)
+    x = x[np.abs(x) <= 464]
+    ours = F.e4m3_round_f32(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(ours, ref.astype(np.float64))
+
+
+@pytest.mark.parametrize("x,expected", [
+    (448.0, 448.0), (464.0, 448.0),  # 464 is the tie between 448 and 480: even mantissa wins
+    (470.0, 448.0), (1e9, 448.0),  # saturation (the oracle's reading; torch gives NaN here)
+    (2.0 ** -9, 2.0 ** -9), (2.0 ** -10, 0.0), (3 * 2.0 ** -11, 2.0 ** -9),
+    (17.0, 16.0), (18.0, 18.0), (19.0, 20.0), (-0.0, -0.0), (2.0 ** -6, 2.0 ** -6),
+])
+def test_round_boundaries(x, expected):
+    r = float(F.e4m3_round(np.float64(x)))
+    assert r == expected and np.signbit(r) == np.signbit(expected)
+
+
+# ------------------------------------------------------------------ Hadamard
+
+@pytest.mark.parametrize("d", [1, 2, 4, 8, 64, 128, 256])
+def test_sylvester_orthogonal_integers(d):
+    h = F.sylvester(d)
+    assert h.dtype == np.int64 and set(np.unique(h)) <= {-1, 1}
+    assert np.array_equal(h @ h.T, d * np.eye(d, dtype=np.int64))
+    assert np.all(h[0] == 1) and np.all(h[:, 0] == 1)
+
+
+@pytest.mark.parametrize("d", [2, 64, 128, 256])
+def test_fwht_equals_matrix(d):
+    x = RNG.standard_normal((5, d))
+    np.testing.assert_allclose(F.fwht(x), x @ F.sylvester(d), rtol=0, atol=1e-12 * np.sqrt(d) * 8)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_rotation_preserves_scores(d):
+    s = RNG.choice([-1.0, 1.0], d)
+    m = F.rotation_matrix(s)
+    np.testing.assert_allclose(m @ m.T, np.eye(d), atol=1e-14)
+    q = RNG.standard_normal((33, d)) * np.where(np.arange(d) < 4, 50, 1)
+    k = RNG.standard_normal((40, d)) * np.where(np.arange(d) < 4, 50, 1)
+    qk = q @ k.T
+    rot = F.rotate(q, s) @ F.rotate(k, s).T
+    assert np.max(np.abs(rot - qk)) <= 1e-12 * np.max(np.abs(qk))
+
+
+# ------------------------------------------------------------------ quantisation
+
+def _check_quantized(x_rot, codes, scales, tile, per_tensor):
+    vals = F.e4m3_decode(codes)
+    n = x_rot.shape[-2]
+    rs = np.repeat(scales.astype(np.float64), tile, axis=-1)[..., :n][..., None]
+    y = (x_rot.astype(np.float32) / rs.astype(np.float32)).astype(np.float64)
+    # round to nearest: no other code is closer to y than the chosen one
+    grid = np.unique(F.e4m3_decode(np.arange(256, dtype=np.uint8)))
+    grid = grid[~np.isnan(grid)]
+    idx = np.clip(np.searchsorted(grid, y), 1, len(grid) - 1)
+    best = np.minimum(np.abs(grid[idx] - y), np.abs(grid[idx - 1] - y))
+    assert np.all(np.abs(vals - y) <= best)
+    # the largest magnitude of each tile (or of the tensor) lands on 448
+    if per_tensor:
+        assert np.max(np.abs(vals)) == 448.0
+        assert np.all(scales == scales.flat[0])
+    else:
+        for t in range(scales.shape[-1]):
+            blk = np.abs(vals[..., t * tile:(t + 1) * tile, :]).reshape(vals.shape[:-2] + (-1,))
+            xb = np.abs(x_rot[..., t * tile:(t + 1) * tile, :]).reshape(vals.shape[:-2] + (-1,))
+            nz = xb.max(axis=-1) > 0
+            assert np.all(blk.max(axis=-1)[nz] == 448.0)
+            assert np.all(scales[..., t][~nz] == 1.0)
+
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_quantize_properties(per_tensor, rotate):
+    d, n = 64, 300  # three 128-row tiles, the last one ragged
+    x = RNG.standard_normal((2, 3, n, d)).astype(np.float32) * np.exp(RNG.uniform(-3, 3, (2, 3, 1, 1))).astype(np.float32)
+    x[1, 2, 128:256] = 0.0  # an all-zero tile
+    s = RNG.choice([-1.0, 1.0], d).astype(np.float32) if rotate else None
+    codes, scales = F.quantize(x, s, per_tensor)
+    assert codes.dtype == np.uint8 and codes.shape == x.shape
+    assert scales.dtype == np.float32 and scales.shape == (2, 3, 3)
+    x_rot = F.rotate(x, s) if rotate else x.astype(np.float64)
+    _check_quantized(x_rot, codes, scales, 128, per_tensor)
+    # dequantisation error: half a spacing of the binade, relative 2^-4 (normals)
+    deq = F.dequantize(codes, scales)
+    rs = np.repeat(scales.astype(np.float64), 128, axis=-1)[..., :n][..., None]
+    assert np.all(np.abs(deq - x_rot) <= np.maximum(2.0 ** -4 * np.abs(x_rot), rs * 2.0 ** -10) * (1 + 1e-6))
+
+
+def test_quantize_tiles_independent():
+    x = RNG.standard_normal((1, 1, 256, 64)).astype(np.float32)
+    _, s1 = F.quantize(x)
+    x2 = x.copy()
+    x2[0, 0, 200, 5] = 1000.0
+    _, s2 = F.quantize(x2)
+    assert s1[0, 0, 0] == s2[0, 0, 0] and s2[0, 0, 1] > s1[0, 0, 1]
+
+
+# ------------------------------------------------------------------ fp8 attention
+
+def _codes_problem(nq, nk, d, seed):
+    q8 = W.random_e4m3_codes((2, nq, d), seed, max_exp_field=9)
+    k8 = W.random_e4m3_codes((2, nk, d), seed + 1, max_exp_field=9)
+    v8 = W.random_e4m3_codes((2, nk, d), seed + 2, max_exp_field=9)
+    nt = lambda n: (n + 127) // 128  # noqa: E731
+    sq = W.random_scales((2, nt(nq)), seed + 3)
+    sk = W.random_scales((2, nt(nk)), seed + 4)
+    sv = W.random_scales((2, nt(nk)), seed + 5)
+    return q8, k8, v8, sq, sk, sv
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_attention_reduces_to_plain(causal):
+    q8, k8, v8, sq, sk, sv = _codes_problem(200, 300, 32, 11)
+    o, lse = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, causal, quantize_p=False)
+    ref_o, ref_l = oracle.attention(F.dequantize(q8, sq), F.dequantize(k8, sk), F.dequantize(v8, sv), 0.3, causal)
+    np.testing.assert_allclose(o, ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_l, rtol=1e-13, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_attention_p_rounding_bound(causal):
+    q8, k8, v8, sq, sk, sv = _codes_problem(150, 260, 32, 21)
+    o, lse = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, causal)
+    o_exact, lse_exact = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, causal, quantize_p=False)
+    assert not np.allclose(o, o_exact, atol=1e-9)  # P really is rounded
+    np.testing.assert_allclose(lse, lse_exact, rtol=0, atol=1e-12)  # l uses unrounded p
+    # bound: each weight moves by <= 2^-4 relative, or <= 2^-10 * 2^-8 absolute (subnormal codes)
+    qd, kd, vd = F.dequantize(q8, sq), F.dequantize(k8, sk), F.dequantize(v8, sv)
+    p, _, _ = oracle.softmax_rows(oracle.scores(qd, kd, 0.3, causal))
+    bound = (2.0 ** -4 * p + 2.0 ** -18) @ np.abs(vd) * 1.000001
+    assert np.all(np.abs(o - o_exact) <= bound + 1e-12)
+
+
+def test_fp8_power_of_two_invariance():
+    """Doubling every V scale doubles O exactly; lse is untouched."""
+    q8, k8, v8, sq, sk, sv = _codes_problem(64, 200, 32, 31)
+    o1, l1 = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, False)
+    o2, l2 = F.attention_fp8(q8, k8, v8, sq, sk, sv * 2, 0.3, False)
+    assert np.array_equal(o2, 2 * o1) and np.array_equal(l1, l2)
+
+
+def test_fp8_causal_first_row():
+    q8, k8, v8, sq, sk, sv = _codes_problem(10, 10, 16, 41)
+    o, lse = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, True)
+    v0 = F.dequantize(v8, sv)[:, 0]
+    np.testing.assert_allclose(o[:, 0], v0, rtol=2.0 ** -4, atol=1e-12)
+    s00 = 0.3 * np.sum(F.dequantize(q8, sq)[:, 0] * F.dequantize(k8, sk)[:, 0], axis=-1)
+    np.testing.assert_allclose(lse[:, 0], s00, atol=1e-12)
+
+
+def test_fp8_empty_keys():
+    q8, k8, v8, sq, sk, sv = _codes_problem(5, 0, 16, 51)
+    o, lse = F.attention_fp8(q8, k8, v8, sq, sk[:, :0], sv[:, :0], 0.3, False)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+# ------------------------------------------------------------------ method-level claim
+
+def _fp8_rmse(w, q, k, v, signs, per_tensor, nq_sample):
+    qs, ks = (signs, signs) if not per_tensor else (None, None)
+    q8, sq = F.quantize(q, qs, per_tensor)
+    k8, sk = F.quantize(k, ks, per_tensor)
+    v8, sv = F.quantize(v, None, per_tensor)
+    o, _ = F.attention_fp8(q8[..., :nq_sample, :], k8, v8, sq[..., :(nq_sample + 127) // 128], sk, sv, w.scale)
+    truth, _ = oracle.attention(q[..., :nq_sample, :], k, v, w.scale)
+    return F.rmse(o, truth)
+
+
+@pytest.mark.slow
+def test_incoherent_block_beats_per_tensor_on_outliers():
+    """Same distribution as the fp8 outlier workload, one head, 256 queries x 8192 keys."""
+    w = W.Workload("fp8_outlier_sample", 1, 1, 8192, 8192, 128, "fp8", False, seed=0, outliers=4)
+    inp = W.make_inputs(w)
+    e_blk = _fp8_rmse(w, inp["q"], inp["k"], inp["v"], inp["signs"], False, 256)
+    e_pt = _fp8_rmse(w, inp["q"], inp["k"], inp["v"], inp["signs"], True, 256)
+    assert e_pt / e_blk >= 2.0, (e_pt, e_blk)
+
+
+@pytest.mark.slow
+def test_fp8_rmse_normal_inputs():
+    w = W.Workload("fp8_normal_sample", 1, 1, 8192, 8192, 128, "fp8", False, seed=0)
+    inp = W.make_inputs(w)
+    e_blk = _fp8_rmse(w, inp["q"], inp["k"], inp["v"], inp["signs"], False, 256)
+    assert e_blk <= 3e-2
+
+
+# ------------------------------------------------------------------ planted mistakes
+
+def test_mutation_unnormalised_rotation(monkeypatch):
+    monkeypatch.setattr(F, "rotation_matrix", lambda s: np.asarray(s)[:, None] * F.sylvester(len(s)))
+    with pytest.raises(AssertionError):
+        test_rotation_preserves_scores(64)
+
+
+def test_mutation_ties_away(monkeypatch):
+    orig = np.rint
+    monkeypatch.setattr(F.np, "rint", lambda a: np.floor(a + 0.5) if np.ndim(a) else orig(a))
+    try:
+        with pytest.raises(AssertionError):
+            test_round_matches_torch_cast_sweep()
+    finally:
+        monkeypatch.undo()
+
+
+def test_mutation_wrong_fp8_max(monkeypatch):
+    monkeypatch.setattr(F, "E4M3_MAX", 240.0)
+    with pytest.raises(AssertionError):
+        test_quantize_properties(False, True)
