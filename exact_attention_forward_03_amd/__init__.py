@@ -1,0 +1,182 @@
+"""Python binding of ``libattn.so`` (include/attn.h): exact attention forward
+on MI355X (gfx950).
+
+The C entry points are exposed under their own names with plain integer
+pointers (argument marshalling only): ``attn_fwd``, ``attn_fwd_stream``,
+``attn_fp8_quantize``, ``attn_strerror``.  ``forward`` and ``fp8_quantize``
+are the torch-facing conveniences: they allocate the outputs with torch on
+the inputs' device, pass ``data_ptr()``s and torch's current HIP stream, and
+raise ``RuntimeError`` on a non-zero return code.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = [
+    "ATTN_DT_F16", "ATTN_DT_BF16", "ATTN_DT_FP8_E4M3", "ATTN_DT_F32",
+    "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP",
+    "load", "lib_path", "attn_fwd", "attn_fwd_stream", "attn_fp8_quantize", "attn_strerror",
+    "forward", "fp8_quantize", "EXPORTS",
+]
+
+ATTN_DT_F16, ATTN_DT_BF16, ATTN_DT_FP8_E4M3, ATTN_DT_F32 = 0, 1, 2, 3
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
+
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fp8_quantize", "attn_strerror")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_FWD_ARGS = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _p, _i, _p, _p, _p]
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libattn.so")
+
+
+def load():
+    """Load libattn.so (built by ``__graft_entry__.build()``); raises if absent."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        lib.attn_fwd.argtypes = _FWD_ARGS
+        lib.attn_fwd.restype = _i
+        lib.attn_fwd_stream.argtypes = _FWD_ARGS + [_p]
+        lib.attn_fwd_stream.restype = _i
+        lib.attn_fp8_quantize.argtypes = [_p, _i, _p, _p, _i, _i, _i, _i, _p, _i, _p]
+        lib.attn_fp8_quantize.restype = _i
+        lib.attn_strerror.argtypes = [_i]
+        lib.attn_strerror.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+# ---------------------------------------------------------------- C names
+
+def attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q, cu_seqlens_k, dtype,
+             q_scale, k_scale, v_scale) -> int:
+    return load().attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q, cu_seqlens_k,
+                           dtype, q_scale, k_scale, v_scale)
+
+
+def attn_fwd_stream(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q, cu_seqlens_k, dtype,
+                    q_scale, k_scale, v_scale, hip_stream) -> int:
+    return load().attn_fwd_stream(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q,
+                                  cu_seqlens_k, dtype, q_scale, k_scale, v_scale, hip_stream)
+
+
+def attn_fp8_quantize(x, x_dtype, x_fp8, x_scale, B, H, N, d, signs, per_tensor, hip_stream) -> int:
+    return load().attn_fp8_quantize(x, x_dtype, x_fp8, x_scale, B, H, N, d, signs, per_tensor, hip_stream)
+
+
+def attn_strerror(code: int) -> str:
+    return load().attn_strerror(code).decode()
+
+
+# ---------------------------------------------------------------- torch front
+
+def _check(rc: int):
+    if rc != ATTN_OK:
+        raise RuntimeError(attn_strerror(rc))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float16:
+        return ATTN_DT_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_DT_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return ATTN_DT_FP8_E4M3
+    if t.dtype == torch.float32:
+        return ATTN_DT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(dev) -> int:
+    import torch
+
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def forward(q, k, v, *, causal: bool = False, scale: Optional[float] = None, cu_seqlens_q=None,
+            cu_seqlens_k=None, q_scale=None, k_scale=None, v_scale=None, out=None, lse=None):
+    """Exact attention forward through ``attn_fwd_stream``.
+
+    Dense: q [B, H, Nq, d], k/v [B, H, Nk, d] -> (o [B, H, Nq, d], lse [B, H, Nq]).
+    Varlen (cu_seqlens_q/k int32 [B+1] on the device): q [H, Tq, d],
+    k/v [H, Tk, d] -> (o [H, Tq, d], lse [H, Tq]).
+    fp8 (q, k, v uint8 e4m3 codes with fp32 scales [B, H, ceil(N/128)]):
+    o is bfloat16.  Tensors must be contiguous and on one GPU.
+    """
+    import torch
+
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt or dt == ATTN_DT_F32:
+        raise TypeError("q, k, v must share one of float16, bfloat16, uint8 (e4m3)")
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    varlen = cu_seqlens_q is not None
+    if varlen:
+        if q.dim() != 3:
+            raise ValueError("varlen q must be [H, T, d]")
+        H, Nq, _ = q.shape
+        Nk = k.shape[1]
+        B = cu_seqlens_q.numel() - 1
+        lse_shape = (H, Nq)
+    else:
+        if q.dim() != 4:
+            raise ValueError("dense q must be [B, H, N, d]")
+        B, H, Nq, _ = q.shape
+        Nk = k.shape[2]
+        lse_shape = (B, H, Nq)
+    o_dtype = torch.bfloat16 if dt == ATTN_DT_FP8_E4M3 else q.dtype
+    if out is None:
+        out = torch.empty(q.shape, dtype=o_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    rc = attn_fwd_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                         int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), dt,
+                         _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def fp8_quantize(x, signs=None, per_tensor: bool = False, out=None, scales=None):
+    """Incoherent processing (if ``signs``) and e4m3 block quantisation of x [B, H, N, d].
+
+    Returns ``(codes uint8 [B, H, N, d], scales float32 [B, H, ceil(N/128)])``.
+    """
+    import torch
+
+    if x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, N, d] tensor")
+    B, H, N, d = x.shape
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, (N + 127) // 128), dtype=torch.float32, device=x.device)
+    rc = attn_fp8_quantize(_ptr(x), _dtype_code(x), _ptr(out), _ptr(scales), B, H, N, d, _ptr(signs),
+                           int(bool(per_tensor)), _stream(x.device))
+    _check(rc)
+    return out, scales

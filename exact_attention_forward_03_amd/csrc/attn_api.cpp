@@ -1,0 +1,123 @@
+// The C ABI of include/attn.h: argument validation (pure host code, before
+// any HIP call), variant dispatch and launch geometry.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/attn.h"
+#include "attn_params.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
+
+// Validation shared by attn_fwd and attn_fwd_stream.  Returns ATTN_OK or an
+// error code; touches no device state.
+int validate_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                 int d, float scale, int causal, const int32_t* cu_q, const int32_t* cu_k, int dtype,
+                 const float* q_scale, const float* k_scale, const float* v_scale) {
+  if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return ATTN_ERR_INVALID_ARG;
+  // q, o, lse may be NULL only when there are no queries; k, v only when there are no keys
+  if (Nq > 0 && (!q || !o || !lse)) return ATTN_ERR_INVALID_ARG;
+  if (Nk > 0 && (!k || !v)) return ATTN_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if ((cu_q == nullptr) != (cu_k == nullptr)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16 && dtype != ATTN_DT_FP8_E4M3) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return ATTN_ERR_INVALID_ARG;
+  if (cu_q && (!aligned(cu_q, 4) || !aligned(cu_k, 4))) return ATTN_ERR_INVALID_ARG;
+  if (dtype == ATTN_DT_FP8_E4M3) {
+    if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4)) return ATTN_ERR_INVALID_ARG;
+  }
+  if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_DT_FP8_E4M3 && (d != 128 || cu_q)) return ATTN_ERR_UNSUPPORTED;
+  if (cu_q == nullptr && (int64_t)B * H > (int64_t)INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: unsupported configuration";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: HIP runtime error";
+    default: return "unknown attn error code";
+  }
+}
+
+int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                    int d, float scale, int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                    int dtype, const float* q_scale, const float* k_scale, const float* v_scale, void* hip_stream) {
+  const int rc = validate_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q, cu_seqlens_k, dtype,
+                              q_scale, k_scale, v_scale);
+  if (rc != ATTN_OK) return rc;
+  if (Nq == 0) return ATTN_OK;
+  const bool varlen = cu_seqlens_q != nullptr;
+  const int br = attn::fwd_block_rows(dtype, d);
+
+  attn::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk;
+  p.c = scale * 1.4426950408889634f;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.q_scale = q_scale; p.k_scale = k_scale; p.v_scale = v_scale;
+  int64_t heads, tiles;
+  if (varlen) {
+    // Sum over sequences of ceil(L_b / BR) <= ceil(Nq / BR) + B; surplus
+    // workgroups exit at once.
+    heads = H;
+    tiles = ((int64_t)Nq + br - 1) / br + B;
+  } else {
+    heads = (int64_t)B * H;
+    tiles = ((int64_t)Nq + br - 1) / br;
+  }
+  const int64_t n_work = heads * tiles;
+  if (n_work > INT32_MAX || tiles > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  p.tiles_per_head = (int)tiles;
+  p.n_work = (int)n_work;
+
+  hipStream_t st = (hipStream_t)hip_stream;
+  hipError_t e;
+  if (dtype == ATTN_DT_FP8_E4M3)
+    e = attn::launch_fwd_fp8(d, causal != 0, p, st);
+  else
+    e = attn::launch_fwd(dtype, d, causal != 0, varlen, p, st);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
+             float scale, int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
+             const float* q_scale, const float* k_scale, const float* v_scale) {
+  return attn_fwd_stream(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q, cu_seqlens_k, dtype,
+                         q_scale, k_scale, v_scale, nullptr);
+}
+
+int attn_fp8_quantize(const void* x, int x_dtype, void* x_fp8, float* x_scale, int B, int H, int N, int d,
+                      const float* signs, int per_tensor, void* hip_stream) {
+  if (!x || !x_fp8 || !x_scale) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || N < 0) return ATTN_ERR_INVALID_ARG;
+  if (x_dtype != ATTN_DT_F32 && x_dtype != ATTN_DT_BF16 && x_dtype != ATTN_DT_F16) return ATTN_ERR_INVALID_ARG;
+  if (per_tensor != 0 && per_tensor != 1) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(x_fp8, 16) || !aligned(x_scale, 4)) return ATTN_ERR_INVALID_ARG;
+  if (signs && !aligned(signs, 4)) return ATTN_ERR_INVALID_ARG;
+  if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
+  if (N == 0) return ATTN_OK;
+  attn::PrepParams p{};
+  p.x = x; p.x_dtype = x_dtype; p.x8 = (uint8_t*)x_fp8; p.scale = x_scale;
+  p.BH = B * H; p.N = N; p.d = d; p.signs = signs; p.mode = 0;
+  hipError_t e = attn::launch_fp8_prep(p, per_tensor != 0, (hipStream_t)hip_stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Host/device parameter blocks of the attention kernels and the internal
+// launch entry points the C ABI dispatches to.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Nq, Nk;
+  float c;               // scale * log2(e): scores are handled in base 2
+  const int32_t* cu_q;   // varlen only
+  const int32_t* cu_k;   // varlen only
+  int tiles_per_head;    // query tiles per (b, h) (varlen: upper bound per head)
+  int n_work;            // workgroups launched
+  const float* q_scale;  // fp8 only: [B, H, ceil(Nq/128)]
+  const float* k_scale;
+  const float* v_scale;
+};
+
+struct PrepParams {
+  const void* x;
+  int x_dtype;           // attn_dtype_t of x
+  uint8_t* x8;
+  float* scale;          // [B, H, ceil(N/128)]
+  int BH, N, d;
+  const float* signs;    // NULL: no rotation
+  int mode;              // 0: block scales; 1: tile amax only; 2: quantise with the tensor amax
+};
+
+// Query rows per workgroup and key rows per tile of each kernel variant.
+int fwd_block_rows(int dtype, int d);
+
+hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st);
+hipError_t launch_fwd_fp8(int d, bool causal, const FwdParams& p, hipStream_t st);
+hipError_t launch_fp8_prep(const PrepParams& p, bool per_tensor, hipStream_t st);
+
+}  // namespace attn

@@ -1,0 +1,133 @@
+/*
+ * attn.h — exact scaled-dot-product attention forward on AMD Instinct MI355X
+ * (gfx950), as a C ABI.
+ *
+ * The operation.  For every (batch, head), or every (sequence, head) of a
+ * variable-length batch:
+ *
+ *     S   = scale * Q K^T                      [Nq, Nk]
+ *     S_ij = -inf where causal and j > i       (top-left: key j is visible to
+ *                                               query i iff j <= i)
+ *     O   = softmax_rows(S) V                  [Nq, d]
+ *     lse_i = log sum_j exp(S_ij)              (natural log)
+ *
+ * Standard attention materialises S ("Flash Attention 3：让 GPU 跑满的注意力
+ * 计算", §1.2).  This library never does: each workgroup owns a block of
+ * queries, streams K and V through LDS tile by tile, and keeps the running
+ * row maximum, the running row sum and a rescaled fp32 output accumulator in
+ * registers (the online-softmax recurrence of the same page, §2.2, with the
+ * one-workgroup-per-query-block decomposition of §3.1).  The result is exact
+ * attention up to floating-point rounding ("FlashAttention-3", opening
+ * paragraph: exact attention).  lse is not on the pages; it is what a caller
+ * needs to merge partial results over key shards.
+ *
+ * Ownership and behaviour (all entry points):
+ *   - every array argument is a DEVICE pointer owned by the caller; the
+ *     library allocates nothing, keeps no pointer after it returns, and holds
+ *     no state between calls (thread-safe);
+ *   - work is enqueued on the given HIP stream (attn_fwd: the null stream) and
+ *     the host is never synchronised;
+ *   - the return value is the only error channel: ATTN_OK or a negative code.
+ *     Argument validation happens before any HIP call, so a bad call is
+ *     rejected without touching the device.  attn_strerror() names a code.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_DT_F16 = 0,      /* IEEE binary16 */
+  ATTN_DT_BF16 = 1,     /* bfloat16 */
+  ATTN_DT_FP8_E4M3 = 2, /* OCP e4m3fn codes (uint8), with fp32 block scales */
+  ATTN_DT_F32 = 3       /* float32: only as the input of attn_fp8_quantize */
+} attn_dtype_t;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad flag, bad scale */
+  ATTN_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d = 96) */
+  ATTN_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * attn_fwd — O = softmax(scale Q K^T [+causal]) V and lse, on the null stream.
+ *
+ * Layouts (row-major, contiguous, no strides):
+ *   dense   (cu_seqlens_q == cu_seqlens_k == NULL):
+ *           q [B, H, Nq, d]; k, v [B, H, Nk, d]; o [B, H, Nq, d]; lse [B, H, Nq]
+ *   varlen  (both cu_seqlens non-NULL; "Flash Attention 3：让 GPU 跑满的注意力
+ *           计算", §5.2): B sequences packed along the token axis with no
+ *           padding; cu_seqlens_q/k are int32 device arrays of B+1 cumulative
+ *           lengths [0, L0, L0+L1, ...]; Nq, Nk are the total packed tokens;
+ *           q [H, Nq, d]; k, v [H, Nk, d]; o [H, Nq, d]; lse [H, Nq].
+ *           Sequence b uses rows [cu_q[b], cu_q[b+1]) of q and
+ *           [cu_k[b], cu_k[b+1]) of k, v; causal uses indices local to the
+ *           sequence.  The kernel clamps cu_seqlens into [0, N] and never
+ *           faults on inconsistent values (the result is then unspecified).
+ *
+ * dtype: ATTN_DT_F16 / ATTN_DT_BF16: q, k, v, o all of that type; the two
+ *   products run on MFMA with fp32 accumulation, all softmax arithmetic is
+ *   fp32.  ATTN_DT_FP8_E4M3: q, k, v are e4m3 codes (uint8) as written by
+ *   attn_fp8_quantize, o is bfloat16, and q_scale, k_scale, v_scale are the
+ *   fp32 dequantisation multipliers [B, H, ceil(N/128)] (one per 128-row
+ *   tile; "FlashAttention-3", "Three techniques" §3: block quantisation).
+ *   For fp16/bf16 the three scale pointers are ignored (may be NULL).
+ *
+ * d ∈ {64, 128, 256} (else ATTN_ERR_UNSUPPORTED; fp8: d = 128 only).
+ * scale: finite and >= 0 (typically 1/sqrt(d)).  causal ∈ {0, 1}.
+ * B, H >= 1; Nq, Nk >= 0.  Nq = 0 is a no-op; Nk = 0 (or an empty key
+ * sequence) gives O = 0 and lse = -inf.  q, o, lse may be NULL only if
+ * Nq = 0, and k, v only if Nk = 0.  Pointers must be 16-byte aligned
+ * (cu_seqlens and the scales: 4-byte).  fp8 with cu_seqlens returns
+ * ATTN_ERR_UNSUPPORTED.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Nq, int Nk, int d, float scale, int causal,
+             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
+             const float* q_scale, const float* k_scale, const float* v_scale);
+
+/* attn_fwd_stream — attn_fwd on the HIP stream `hip_stream` (a hipStream_t;
+ * NULL = the null stream).  Same arguments, layouts and errors as attn_fwd. */
+int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
+                    const float* q_scale, const float* k_scale, const float* v_scale,
+                    void* hip_stream);
+
+/*
+ * attn_fp8_quantize — the fp8 pre-processing of one tensor
+ * ("FlashAttention-3", "Three techniques" §3 FP8 precision).
+ *
+ *   x [B, H, N, d] of x_dtype (ATTN_DT_F32, ATTN_DT_BF16 or ATTN_DT_F16).
+ *   If signs != NULL (fp32 [d], each +1 or -1): incoherent processing first,
+ *     x' = x diag(signs) H_d / sqrt(d), with H_d the Sylvester Hadamard
+ *     matrix applied along d by a fast Walsh-Hadamard transform (used for Q
+ *     and K; V is passed with signs == NULL).
+ *   Then block quantisation: for every (b, h, 128-row tile) t,
+ *     s_t = amax_t / 448 (s_t = 1 if the tile is all zero), with amax over
+ *     the tile's rotated values, and x_fp8 = e4m3(x' / s_t) rounded to
+ *     nearest-even in fp32; x' ~= s_t * x_fp8.
+ *   per_tensor = 1 replaces the per-tile amax by one amax over the whole
+ *     tensor (every entry of x_scale then holds the same s): the per-tensor
+ *     fp8 baseline the block scheme is compared with.
+ *   Outputs: x_fp8 uint8 [B, H, N, d]; x_scale fp32 [B, H, ceil(N/128)].
+ *   d ∈ {64, 128, 256}.  N = 0 is a no-op.  Same pointer, stream and error
+ *   rules as attn_fwd_stream.
+ */
+int attn_fp8_quantize(const void* x, int x_dtype, void* x_fp8, float* x_scale,
+                      int B, int H, int N, int d, const float* signs, int per_tensor,
+                      void* hip_stream);
+
+/* attn_strerror — a static, human-readable name for a return code. */
+const char* attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,142 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and rejects bad arguments before touching the device (CPU only).
+
+No call here reaches a kernel launch: every argument set is invalid, and
+validation returns before any HIP call, so these run without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_forward_03_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+FAKE = 0x10000  # a non-null, 64 KiB-aligned address; never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(attn.lib_path()):
+        pytest.fail("libattn.so is not built (run __graft_entry__.build())")
+    return attn.load()
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(attn.EXPORTS)
+
+
+def test_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(attn.lib_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_strerror(lib):
+    assert attn.attn_strerror(attn.ATTN_OK) == "ATTN_OK"
+    for code in (attn.ATTN_ERR_INVALID_ARG, attn.ATTN_ERR_UNSUPPORTED, attn.ATTN_ERR_HIP):
+        assert "ATTN_ERR" in attn.attn_strerror(code)
+    assert "unknown" in attn.attn_strerror(12345)
+
+
+def good_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=256, Nk=256, d=64, scale=0.125,
+             causal=0, cu_seqlens_q=None, cu_seqlens_k=None, dtype=attn.ATTN_DT_F16,
+             q_scale=None, k_scale=None, v_scale=None)
+    a.update(over)
+    return a
+
+
+def call_fwd(**over):
+    a = good_args(**over)
+    return attn.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                         a["scale"], a["causal"], a["cu_seqlens_q"], a["cu_seqlens_k"], a["dtype"],
+                         a["q_scale"], a["k_scale"], a["v_scale"])
+
+
+def call_fwd_stream(**over):
+    a = good_args(**over)
+    return attn.attn_fwd_stream(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"],
+                                a["d"], a["scale"], a["causal"], a["cu_seqlens_q"], a["cu_seqlens_k"],
+                                a["dtype"], a["q_scale"], a["k_scale"], a["v_scale"], None)
+
+
+INVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None),
+    dict(k=None, v=None, Nq=0), dict(q=None, Nk=0),
+    dict(B=0), dict(H=0), dict(B=-1), dict(Nq=-1), dict(Nk=-5),
+    dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=-0.5),
+    dict(causal=2), dict(causal=-1),
+    dict(cu_seqlens_q=FAKE), dict(cu_seqlens_k=FAKE),
+    dict(dtype=7), dict(dtype=-1), dict(dtype=attn.ATTN_DT_F32),
+    dict(dtype=attn.ATTN_DT_FP8_E4M3, d=128),  # fp8 without scales
+    dict(dtype=attn.ATTN_DT_FP8_E4M3, d=128, q_scale=FAKE, k_scale=FAKE),
+    dict(q=FAKE + 8), dict(o=FAKE + 2), dict(lse=FAKE + 2),
+    dict(cu_seqlens_q=FAKE + 2, cu_seqlens_k=FAKE),
+]
+
+
+@pytest.mark.parametrize("over", INVALID, ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+@pytest.mark.parametrize("entry", [call_fwd, call_fwd_stream], ids=["attn_fwd", "attn_fwd_stream"])
+def test_invalid_arguments(lib, entry, over):
+    assert entry(**over) == attn.ATTN_ERR_INVALID_ARG
+
+
+UNSUPPORTED = [
+    dict(d=96), dict(d=32), dict(d=512), dict(d=0),
+    dict(dtype=attn.ATTN_DT_FP8_E4M3, d=64, q_scale=FAKE, k_scale=FAKE, v_scale=FAKE),
+    dict(dtype=attn.ATTN_DT_FP8_E4M3, d=128, q_scale=FAKE, k_scale=FAKE, v_scale=FAKE,
+         cu_seqlens_q=FAKE, cu_seqlens_k=FAKE),
+]
+
+
+@pytest.mark.parametrize("over", UNSUPPORTED, ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_unsupported(lib, over):
+    assert call_fwd(**over) == attn.ATTN_ERR_UNSUPPORTED
+
+
+def test_empty_query_is_a_noop(lib):
+    # Nq = 0 returns before any HIP call
+    assert call_fwd(Nq=0) == attn.ATTN_OK
+    assert call_fwd(Nq=0, Nk=0) == attn.ATTN_OK
+    assert call_fwd(Nq=0, q=None, o=None, lse=None) == attn.ATTN_OK
+
+
+def quant(**over):
+    a = dict(x=FAKE, x_dtype=attn.ATTN_DT_F32, x_fp8=FAKE, x_scale=FAKE, B=1, H=1, N=128, d=128,
+             signs=None, per_tensor=0)
+    a.update(over)
+    return attn.attn_fp8_quantize(a["x"], a["x_dtype"], a["x_fp8"], a["x_scale"], a["B"], a["H"], a["N"],
+                                  a["d"], a["signs"], a["per_tensor"], None)
+
+
+@pytest.mark.parametrize("over", [dict(x=None), dict(x_fp8=None), dict(x_scale=None), dict(B=0), dict(H=0),
+                                  dict(N=-1), dict(x_dtype=attn.ATTN_DT_FP8_E4M3), dict(x_dtype=9),
+                                  dict(per_tensor=2), dict(x=FAKE + 4), dict(x_scale=FAKE + 1),
+                                  dict(signs=FAKE + 2)],
+                         ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_quantize_invalid(lib, over):
+    assert quant(**over) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_quantize_unsupported_and_noop(lib):
+    assert quant(d=96) == attn.ATTN_ERR_UNSUPPORTED
+    assert quant(N=0) == attn.ATTN_OK
+
+
+def test_binding_has_no_cpu_fallback():
+    """The torch front end goes through the library only: no oracle import."""
+    src = open(os.path.join(ROOT, "exact_attention_forward_03_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("no oracle", "")
+    for f in os.listdir(os.path.join(ROOT, "exact_attention_forward_03_amd", "csrc")):
+        assert "oracle" not in open(os.path.join(ROOT, "exact_attention_forward_03_amd", "csrc", f)).read()

@@ -1,0 +1,200 @@
+"""GPU parity of the fp16/bf16 attention kernels against the fp64 oracle.
+
+Inputs are seeded N(0,1) (workloads.py), rounded to fp16/bf16; the oracle
+sees the exact rounded values.  Bars: max |O - O_ref| <= 2e-3 (fp16) /
+8e-3 (bf16) on every element; |lse - lse_ref| <= 1e-3 max(1, |lse_ref|).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import exact as OX
+import workloads as W
+from gpu_util import check, run_dense, sample_rows, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_config(gpu_lib):
+    """1 x 2 heads, 256 x 256, d 64, fp16, non-causal, seed 0."""
+    w = W.WORKLOADS["tiny_f16"]
+    x = W.make_inputs(w)
+    o, lse, (q, k, v, s) = run_dense(gpu_lib, x["q"], x["k"], x["v"], "f16", False)
+    assert o.shape == (1, 2, 256, 64) and lse.shape == (1, 2, 256)
+    o_ref, l_ref = oracle.attention(q, k, v, s, False)
+    check(o, lse, o_ref, l_ref, "f16", "tiny")
+
+
+SHAPES = [(1, 1), (17, 17), (127, 127), (128, 128), (129, 129), (300, 1000), (1000, 300), (257, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", SHAPES)
+def test_dense_sweep(gpu_lib, dtype, d, causal, nq, nk):
+    q, k, v = W.random_problem(1, 2, nq, nk, d, seed=nq * 7 + nk + d)
+    k, v = k[:, :, :nk], v[:, :, :nk]
+    o, lse, (q64, k64, v64, s) = run_dense(gpu_lib, q, k, v, dtype, causal)
+    o_ref, l_ref = oracle.attention(q64, k64, v64, s, causal)
+    check(o, lse, o_ref, l_ref, dtype, f"{dtype} d{d} causal{causal} {nq}x{nk}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_batch_heads_and_scale(gpu_lib, dtype):
+    """B > 1, H > 1, a non-default scale: heads must not mix."""
+    q, k, v = W.random_problem(3, 5, 200, 333, 128, seed=5)
+    for causal in (False, True):
+        o, lse, (q64, k64, v64, s) = run_dense(gpu_lib, q, k, v, dtype, causal, scale=0.21)
+        o_ref, l_ref = oracle.attention(q64, k64, v64, s, causal)
+        check(o, lse, o_ref, l_ref, dtype, f"B3H5 causal{causal}")
+
+
+def test_empty_keys(gpu_lib):
+    """Nk = 0: O = 0 and lse = -inf, no NaN."""
+    q, _, _ = W.random_problem(1, 2, 70, 1, 64, seed=3)
+    qd, _ = to_device(q, "bf16")
+    kd = torch.zeros((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = gpu_lib.forward(qd, kd, kd, causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_zero_scale_uniform(gpu_lib):
+    """scale = 0: uniform weights over the visible keys (mean / prefix mean)."""
+    q, k, v = W.random_problem(1, 1, 150, 150, 64, seed=4)
+    for causal in (False, True):
+        o, lse, (q64, k64, v64, _) = run_dense(gpu_lib, q, k, v, "f16", causal, scale=0.0)
+        o_ref, l_ref = oracle.attention(q64, k64, v64, 0.0, causal)
+        check(o, lse, o_ref, l_ref, "f16", f"scale0 causal{causal}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_identical_keys_closed_form(gpu_lib, dtype):
+    """All keys equal: O = mean of V (causal: prefix mean), lse = s_i + ln(count)."""
+    nq = nk = 300
+    d = 128
+    q, _, v = W.random_problem(1, 1, nq, nk, d, seed=8)
+    k = np.repeat(W.random_problem(1, 1, 1, 1, d, seed=9)[1], nk, axis=2)
+    for causal in (False, True):
+        o, lse, (q64, k64, v64, s) = run_dense(gpu_lib, q, k, v, dtype, causal)
+        s_i = s * (q64[0, 0] @ k64[0, 0, 0])
+        if causal:
+            ref = np.cumsum(v64[0, 0], axis=0) / np.arange(1, nk + 1)[:, None]
+            lref = s_i + np.log(np.arange(1, nq + 1))
+        else:
+            ref = np.broadcast_to(v64[0, 0].mean(0), (nq, d))
+            lref = s_i + np.log(nk)
+        check(o[0, 0], lse[0, 0], ref, lref, dtype, f"identical keys causal{causal}")
+
+
+def test_causal_row0_exact(gpu_lib):
+    """Causal row 0 sees only key 0: O_0 = V_0 exactly (the weights are normalised by their own sum)."""
+    q, k, v = W.random_problem(2, 3, 129, 129, 128, seed=12)
+    v[..., 0, :] *= 3.0  # large |V_0|: a bf16 relative error would show
+    o, lse, (q64, k64, v64, s) = run_dense(gpu_lib, q, k, v, "bf16", True)
+    assert np.array_equal(o[:, :, 0], v64[:, :, 0])
+
+
+def test_determinism_and_canaries(gpu_lib):
+    """Two runs are bitwise equal; guard regions around O and lse stay untouched."""
+    q, k, v = W.random_problem(2, 4, 333, 517, 128, seed=21)
+    qd, _ = to_device(q, "bf16")
+    kd, _ = to_device(k, "bf16")
+    vd, _ = to_device(v, "bf16")
+    guard = 4096
+    n_o, n_l = qd.numel(), 2 * 4 * 333
+    for causal in (False, True):
+        outs = []
+        for _ in range(2):
+            ob = torch.full((n_o + 2 * guard,), 12345.0, dtype=torch.bfloat16, device="cuda")
+            lb = torch.full((n_l + 2 * guard,), -7.0, dtype=torch.float32, device="cuda")
+            o = ob[guard:guard + n_o].view(qd.shape)
+            lse = lb[guard:guard + n_l].view(2, 4, 333)
+            gpu_lib.forward(qd, kd, vd, causal=causal, out=o, lse=lse)
+            torch.cuda.synchronize()
+            assert torch.all(ob[:guard] == 12345.0) and torch.all(ob[guard + n_o:] == 12345.0)
+            assert torch.all(lb[:guard] == -7.0) and torch.all(lb[guard + n_l:] == -7.0)
+            outs.append((o.clone(), lse.clone()))
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+# ---------------------------------------------------------------- varlen
+
+def run_varlen(attn, lengths_q, lengths_k, H, d, dtype, causal, seed):
+    cq, ck = W.cu_seqlens(lengths_q), W.cu_seqlens(lengths_k)
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((H, int(cq[-1]), d), dtype=np.float32)
+    k = rng.standard_normal((H, int(ck[-1]), d), dtype=np.float32)
+    v = rng.standard_normal((H, int(ck[-1]), d), dtype=np.float32)
+    qd, q64 = to_device(q, dtype)
+    kd, k64 = to_device(k, dtype)
+    vd, v64 = to_device(v, dtype)
+    s = 1.0 / np.sqrt(d)
+    o, lse = attn.forward(qd, kd, vd, causal=causal, scale=s,
+                          cu_seqlens_q=torch.from_numpy(cq).cuda(), cu_seqlens_k=torch.from_numpy(ck).cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_varlen(q64, k64, v64, cq, ck, s, causal)
+    return o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_varlen(gpu_lib, dtype, causal, d):
+    lengths = [1, 0, 127, 129, 2048, 300]
+    o, lse, o_ref, l_ref = run_varlen(gpu_lib, lengths, lengths, 2, d, dtype, causal, seed=d)
+    check(o, lse, o_ref, l_ref, dtype, f"varlen {dtype} d{d} causal{causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_q_k_lengths_differ(gpu_lib, causal):
+    """Per-sequence Nq_b != Nk_b, including an empty key sequence (O = 0, lse = -inf)."""
+    lq = [5, 130, 64, 200, 33]
+    lk = [9, 100, 0, 260, 33]
+    o, lse, o_ref, l_ref = run_varlen(gpu_lib, lq, lk, 3, 128, "bf16", causal, seed=77)
+    check(o, lse, o_ref, l_ref, "bf16", f"varlen q!=k causal{causal}")
+
+
+# ---------------------------------------------------------------- full sizes (sampled rows)
+
+FULL = ["dense_bf16", "dense_bf16_causal", "hdim256_bf16", "n8k_bf16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(gpu_lib, name):
+    """The benchmark shapes in the benchmark's launch configuration; the oracle
+    checks sampled rows of sampled heads (it cannot materialise all of S)."""
+    w = W.WORKLOADS[name]
+    x = W.make_inputs(w)
+    o, lse, (q64, k64, v64, s) = run_dense(gpu_lib, x["q"], x["k"], x["v"], w.dtype, w.causal)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(1)
+    heads = [(0, 0), (w.B - 1, w.H - 1)] + [tuple(rng.integers(0, [w.B, w.H])) for _ in range(2)]
+    for (b, h) in heads:
+        rows = sample_rows(w.Nq, 48, seed=b * 100 + h)
+        o_ref, l_ref = OX.attention_rows(q64[b, h], k64[b, h], v64[b, h], rows, s, w.causal)
+        check(o[b, h][rows], lse[b, h][rows], o_ref, l_ref, w.dtype, f"{name} b{b} h{h}")
+
+
+def test_full_size_varlen_sampled(gpu_lib):
+    w = W.WORKLOADS["varlen_bf16_causal"]
+    x = W.make_inputs(w)
+    cu = x["cu_seqlens"]
+    qd, q64 = to_device(x["q"], "bf16")
+    kd, k64 = to_device(x["k"], "bf16")
+    vd, v64 = to_device(x["v"], "bf16")
+    cud = torch.from_numpy(cu).cuda()
+    o, lse = gpu_lib.forward(qd, kd, vd, causal=True, scale=w.scale, cu_seqlens_q=cud, cu_seqlens_k=cud)
+    torch.cuda.synchronize()
+    o = o.double().cpu().numpy()
+    lse = lse.double().cpu().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    for h in (0, w.H - 1, 13):
+        for b in range(w.B):
+            a, e = int(cu[b]), int(cu[b + 1])
+            rows = sample_rows(e - a, 8, seed=b + h)
+            o_ref, l_ref = OX.attention_rows(q64[h, a:e], k64[h, a:e], v64[h, a:e], rows, w.scale, True)
+            check(o[h, a:e][rows], lse[h, a:e][rows], o_ref, l_ref, "bf16", f"varlen full h{h} seq{b}")
