@@ -1,0 +1,288 @@
+"""Attention-forward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-detail]
+
+Workload (one "step"): the dense bf16 problem B=2, H=16, Nq=Nk=4096, d=128,
+scale 1/sqrt(128), seeded N(0,1) inputs already resident in HBM, run once
+non-causal and once causal (top-left) through the C ABI (attn_fwd_stream on
+torch's current stream).  value = (FLOPs of both runs) / (time per step),
+FLOPs = 4 B H Nq Nk d, halved for causal.
+
+Prints ONE JSON line with the roofline of the dominant kernel (the
+non-causal launch: algorithmic FLOPs / its mean duration from HIP events on
+its stream, against the dense bf16 MFMA peak of 2.5 PFLOP/s) and the CPU
+baseline (the fp64 oracle, timed on a bounded sample of the same workload).
+"detail" adds the other shapes (d=256, N=8192, variable length, fp8 when
+available), each with its own TFLOP/s and fraction of peak.
+
+--copy-calib runs only a plain device copy of known size (for scaling the
+HBM byte counters) and prints its byte count.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["exact_attention_forward_03_amd/csrc/attn_fwd.hip",
+                  "exact_attention_forward_03_amd/csrc/attn_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_d128_n4096_traffic.json")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(reps_heads: int = 8):
+    """The fp64 oracle on a bounded sample: B=1, `reps_heads` heads of the
+    dense bf16 workload, each run non-causal and causal (inputs on the host
+    in fp64, generation excluded)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import workloads as W
+
+    w = W.WORKLOADS["dense_bf16"]
+    rng = np.random.default_rng(0)
+    shape = (1, reps_heads, w.Nq, w.d)
+    q, k, v = (W.to_dtype(rng.standard_normal(shape, dtype=np.float32), "bf16").double().numpy() for _ in range(3))
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, w.scale, False)
+    oracle.attention(q, k, v, w.scale, True)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * reps_heads * w.Nq * w.Nk * w.d * 1.5
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"B=1 H={reps_heads} N=4096 d=128 bf16 inputs in fp64, non-causal + causal "
+                      f"({reps_heads}/32 of the heads of one step), {dt:.1f} s"}
+
+
+def timed_launches(fn, n, stream):
+    """Run fn() n times; return per-launch durations (ms) from events on `stream`."""
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def bench_detail(attn, steps, warmup):
+    """Per-shape throughput of the other workloads (mean over `steps` launches)."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name in ("n8k_bf16", "hdim256_bf16", "varlen_bf16_causal", "tiny_f16"):
+        w = W.WORKLOADS[name]
+        x = W.make_inputs(w)
+        q, k, v = (W.to_dtype(x[n], w.dtype).cuda() for n in ("q", "k", "v"))
+        kw = {}
+        if w.varlen:
+            cu = torch.from_numpy(x["cu_seqlens"]).cuda()
+            kw = dict(cu_seqlens_q=cu, cu_seqlens_k=cu)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+
+        def run():
+            attn.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, **kw)
+
+        for _ in range(warmup):
+            run()
+        ms = float(np.mean(timed_launches(run, steps, stream)))
+        tf = w.flops() / (ms / 1e3) / 1e12
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
+        del q, k, v, o, lse
+    fp8 = bench_fp8(attn, steps, warmup)
+    if fp8:
+        out.update(fp8)
+    return out
+
+
+def bench_fp8(attn, steps, warmup):
+    """fp8 workload (B=2 H=16 N=8192 d=128, outlier channels): the attention
+    kernel alone and the pre-processing of Q, K, V; None if not built."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+
+    w = W.WORKLOADS["fp8_outlier"]
+    x = W.make_inputs(w)
+    q32, k32, v32 = (torch.from_numpy(x[n]).cuda() for n in ("q", "k", "v"))
+    signs = torch.from_numpy(x["signs"]).cuda()
+    try:
+        q8, sq = attn.fp8_quantize(q32, signs)
+        k8, sk = attn.fp8_quantize(k32, signs)
+        v8, sv = attn.fp8_quantize(v32, None)
+        o, lse = attn.forward(q8, k8, v8, scale=w.scale, q_scale=sq, k_scale=sk, v_scale=sv)
+    except RuntimeError:
+        return None
+    stream = torch.cuda.current_stream()
+
+    def run_attn():
+        attn.forward(q8, k8, v8, scale=w.scale, q_scale=sq, k_scale=sk, v_scale=sv, out=o, lse=lse)
+
+    def run_prep():
+        attn.fp8_quantize(q32, signs, out=q8, scales=sq)
+        attn.fp8_quantize(k32, signs, out=k8, scales=sk)
+        attn.fp8_quantize(v32, None, out=v8, scales=sv)
+
+    for _ in range(warmup):
+        run_attn()
+        run_prep()
+    ms = float(np.mean(timed_launches(run_attn, steps, stream)))
+    ms_prep = float(np.mean(timed_launches(run_prep, steps, stream)))
+    tf = w.flops() / (ms / 1e3) / 1e12
+    prep_bytes = 3 * q32.numel() * (4 + 1) + 3 * sq.numel() * 4
+    return {"fp8_outlier": {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                            "shape": [w.B, w.H, w.Nq, w.Nk, w.d]},
+            "fp8_prep_qkv": {"ms": round(ms_prep, 4), "gbs": round(prep_bytes / (ms_prep / 1e3) / 1e9, 1),
+                             "frac_hbm": round(prep_bytes / (ms_prep / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
+def copy_calib():
+    """A plain copy of 1 GiB, to scale FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this library runs on one GPU; multi-GPU runs are not part of it "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calib:
+        copy_calib()
+        return
+
+    import exact_attention_forward_03_amd as attn
+    import workloads as W
+
+    attn.load()
+    w_nc = W.WORKLOADS["dense_bf16"]
+    w_c = W.WORKLOADS["dense_bf16_causal"]
+    x = W.make_inputs(w_nc)  # same seed and shape for both runs of the step
+    q, k, v = (W.to_dtype(x[n], "bf16").cuda() for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run_nc():
+        attn.forward(q, k, v, causal=False, scale=w_nc.scale, out=o, lse=lse)
+
+    def run_c():
+        attn.forward(q, k, v, causal=True, scale=w_c.scale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        run_nc()
+        run_c()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronised on both sides
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b, c in ev:
+        a.record(stream)
+        run_nc()
+        b.record(stream)
+        run_c()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nc_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    c_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    step_ms = float(np.mean(nc_ms + c_ms))
+    flops_step = w_nc.flops() + w_c.flops()
+    value = flops_step / (step_ms / 1e3) / 1e12
+    ach = w_nc.flops() / (float(np.mean(nc_ms)) / 1e3) / 1e12
+
+    result = {
+        "metric": "attention fwd TFLOP/s and % MFMA peak (bf16 + fp8), hdim 128/256, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dense bf16 attention fwd, B=2 H=16 Nq=Nk=4096 d=128, non-causal + causal",
+                   "B": 2, "H": 16, "seq_len": 4096, "head_dim": 128, "causal": [False, True],
+                   "wall_s_timed": round(wall, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(),
+                     "kernel": "attn_fwd_kernel<bf16, d128, non-causal>",
+                     "mean_launch_ms": round(float(np.mean(nc_ms)), 4),
+                     "causal_launch_ms": round(float(np.mean(c_ms)), 4)},
+    }
+    if not args.no_detail:
+        result["detail"] = bench_detail(attn, max(5, args.steps // 5), 2)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
