@@ -31,7 +31,8 @@ int validate_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     return ATTN_ERR_INVALID_ARG;
   if (cu_q && (!aligned(cu_q, 4) || !aligned(cu_k, 4))) return ATTN_ERR_INVALID_ARG;
   if (dtype == ATTN_DT_FP8_E4M3) {
-    if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_INVALID_ARG;
+    // scales may be NULL only for an empty tensor, like the tensor itself
+    if ((Nq > 0 && !q_scale) || (Nk > 0 && (!k_scale || !v_scale))) return ATTN_ERR_INVALID_ARG;
     if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4)) return ATTN_ERR_INVALID_ARG;
   }
   if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;

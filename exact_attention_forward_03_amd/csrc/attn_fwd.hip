@@ -410,7 +410,7 @@ hipError_t launch_t(int d, bool causal, bool varlen, const FwdParams& p, hipStre
 }  // namespace
 
 int fwd_block_rows(int dtype, int d) {
-  if (dtype == 2) return 128;  // the e4m3 kernel
+  if (dtype == 2) return fwd_fp8_block_rows();
   switch (d) {
     case 64: return 32 * FwdTile<64>::NW;
     case 128: return 32 * FwdTile<128>::NW;

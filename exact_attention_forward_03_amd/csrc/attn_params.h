@@ -34,8 +34,9 @@ struct PrepParams {
   int mode;              // 0: block scales; 1: tile amax only; 2: quantise with the tensor amax
 };
 
-// Query rows per workgroup and key rows per tile of each kernel variant.
+// Query rows per workgroup of each kernel variant (sizes the grid).
 int fwd_block_rows(int dtype, int d);
+int fwd_fp8_block_rows();
 
 hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st);
 hipError_t launch_fwd_fp8(int d, bool causal, const FwdParams& p, hipStream_t st);

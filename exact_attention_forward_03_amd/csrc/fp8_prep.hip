@@ -1,5 +1,211 @@
-// Placeholder: the fp8 pre-processing kernel is not built yet.
+// FP8 pre-processing of one tensor x [B*H, N, d]: incoherent processing
+// (random sign flip and Hadamard rotation along d) and block quantisation to
+// e4m3 with one fp32 scale per 128-row tile ("FlashAttention-3", "Three
+// techniques" §3: block quantisation; incoherent processing Q' = QM, K' = KM
+// with M a Hadamard matrix times random +-1, applied before quantising).
+//
+// One workgroup (256 threads) per (b*h, 128-row tile); the whole tile stays
+// in registers, so x is read once and the codes are written once.  A row of d
+// values is spread over d/8 lanes, 8 consecutive values per lane.  The
+// Hadamard transform H_d (Sylvester order) is a product of one butterfly
+// (a, b) -> (a + b, a - b) per bit of the column index: the three low bits are
+// done inside the lane, the others between lanes (lane ^ 1, ^ 2, ...).
+// Then the tile's amax, s = amax / 448 (1 if the tile is all zero), and
+// code = e4m3(x' / s), rounded to nearest even in fp32.
+//
+// Per-tensor mode runs three launches: the tile amaxes into the scale array,
+// one workgroup turning their maximum into s for every entry, and the
+// quantisation with that s.
+#include "attn_device.h"
 #include "attn_params.h"
+
 namespace attn {
-hipError_t launch_fp8_prep(const PrepParams&, bool, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kPrepThreads = 256;
+constexpr int kTileRows = 128;
+constexpr float kE4m3Max = 448.0f;
+
+__device__ __forceinline__ void load8(const float* src, float v[8]) {
+  const float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t* src, float v[8], bf16_t) {
+  const uint4 a = *(const uint4*)src;
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const uint16_t* src, float v[8], f16_t) {
+  const uint4 a = *(const uint4*)src;
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_t f = __builtin_convertvector(__builtin_bit_cast(f16x2_t, w[i]), f32x2_t);
+    v[2 * i] = f[0];
+    v[2 * i + 1] = f[1];
+  }
+}
+
+// Four fp32 values -> four e4m3 codes in one dword (round to nearest even).
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wv] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < kPrepThreads / 64; ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
+// MODE 0: block scales; 1: write the tile amax only; 2: quantise with the
+// scale already stored for the tile (per-tensor).
+template <int IN, int D, int MODE>
+__global__ void __launch_bounds__(kPrepThreads) fp8_prep_kernel(PrepParams p) {
+  constexpr int L = D / 8;                // lanes per row
+  constexpr int RPP = kPrepThreads / L;   // rows per pass
+  constexpr int PASSES = kTileRows / RPP;
+  __shared__ float red[kPrepThreads / 64];
+
+  const int nt = (p.N + kTileRows - 1) / kTileRows;
+  const int bh = blockIdx.x / nt;
+  const int tile = blockIdx.x - bh * nt;
+  const int tid = threadIdx.x;
+  const int rl = tid / L, cl = tid % L;
+  const int64_t base = (int64_t)bh * p.N;
+
+  float sg[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sg[j] = p.signs ? p.signs[cl * 8 + j] : 1.f;
+  const float norm = p.signs ? 1.0f / __builtin_sqrtf((float)D) : 1.0f;
+
+  float v[PASSES][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int row = tile * kTileRows + ps * RPP + rl;
+    if (row < p.N) {
+      const int64_t off = (base + row) * D + cl * 8;
+      if constexpr (IN == 3) load8((const float*)p.x + off, v[ps]);
+      else if constexpr (IN == 1) load8((const uint16_t*)p.x + off, v[ps], bf16_t{});
+      else load8((const uint16_t*)p.x + off, v[ps], f16_t{});
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[ps][j] = 0.f;
+    }
+    if (p.signs) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[ps][j] *= sg[j];
+      // butterflies on the three in-lane bits of the column index
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (!(j & h)) {
+            const float a = v[ps][j], b = v[ps][j + h];
+            v[ps][j] = a + b;
+            v[ps][j + h] = a - b;
+          }
+      // butterflies on the lane bits: the lower partner keeps a + b, the upper a - b
+#pragma unroll
+      for (int s = 1; s < L; s <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float o = __shfl_xor(v[ps][j], s);
+          v[ps][j] = (cl & s) ? (o - v[ps][j]) : (v[ps][j] + o);
+        }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[ps][j] *= norm;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[ps][j]));
+  }
+
+  const int sidx = bh * nt + tile;
+  float s;
+  if constexpr (MODE == 2) {
+    s = p.scale[sidx];
+  } else {
+    const float tmax = block_max(amax, red);
+    if constexpr (MODE == 1) {
+      if (tid == 0) p.scale[sidx] = tmax;
+      return;
+    }
+    s = tmax > 0.f ? tmax / kE4m3Max : 1.0f;
+    if (tid == 0) p.scale[sidx] = s;
+  }
+
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int row = tile * kTileRows + ps * RPP + rl;
+    if (row < p.N) {
+      uint2 w;
+      w.x = pack4_e4m3(v[ps][0] / s, v[ps][1] / s, v[ps][2] / s, v[ps][3] / s);
+      w.y = pack4_e4m3(v[ps][4] / s, v[ps][5] / s, v[ps][6] / s, v[ps][7] / s);
+      *(uint2*)(p.x8 + (base + row) * D + cl * 8) = w;
+    }
+  }
+}
+
+// Per-tensor: every entry of the scale array becomes max(entries) / 448.
+__global__ void __launch_bounds__(kPrepThreads) tensor_scale_kernel(float* scale, int n) {
+  __shared__ float red[kPrepThreads / 64];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < n; i += kPrepThreads) m = fmaxf(m, scale[i]);
+  m = block_max(m, red);
+  const float s = m > 0.f ? m / kE4m3Max : 1.0f;
+  for (int i = threadIdx.x; i < n; i += kPrepThreads) scale[i] = s;
+}
+
+template <int IN, int D>
+hipError_t launch_in_d(const PrepParams& p, bool per_tensor, hipStream_t st) {
+  const int nt = (p.N + kTileRows - 1) / kTileRows;
+  const int64_t grid = (int64_t)nt * p.BH;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (!per_tensor) {
+    hipLaunchKernelGGL((fp8_prep_kernel<IN, D, 0>), dim3((unsigned)grid), dim3(kPrepThreads), 0, st, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((fp8_prep_kernel<IN, D, 1>), dim3((unsigned)grid), dim3(kPrepThreads), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(kPrepThreads), 0, st, p.scale, (int)grid);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fp8_prep_kernel<IN, D, 2>), dim3((unsigned)grid), dim3(kPrepThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int IN>
+hipError_t launch_in(const PrepParams& p, bool per_tensor, hipStream_t st) {
+  switch (p.d) {
+    case 64: return launch_in_d<IN, 64>(p, per_tensor, st);
+    case 128: return launch_in_d<IN, 128>(p, per_tensor, st);
+    case 256: return launch_in_d<IN, 256>(p, per_tensor, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fp8_prep(const PrepParams& p, bool per_tensor, hipStream_t st) {
+  switch (p.x_dtype) {
+    case 3: return launch_in<3>(p, per_tensor, st);
+    case 1: return launch_in<1>(p, per_tensor, st);
+    case 0: return launch_in<0>(p, per_tensor, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace attn

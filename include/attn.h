@@ -76,7 +76,9 @@ enum {
  *   attn_fp8_quantize, o is bfloat16, and q_scale, k_scale, v_scale are the
  *   fp32 dequantisation multipliers [B, H, ceil(N/128)] (one per 128-row
  *   tile; "FlashAttention-3", "Three techniques" §3: block quantisation).
- *   For fp16/bf16 the three scale pointers are ignored (may be NULL).
+ *   For fp16/bf16 the three scale pointers are ignored (may be NULL); for
+ *   fp8 they may be NULL only where the tensor is empty (Nq or Nk = 0).
+ *   Scales must be >= 0 (attn_fp8_quantize writes positive ones).
  *
  * d ∈ {64, 128, 256} (else ATTN_ERR_UNSUPPORTED; fp8: d = 128 only).
  * scale: finite and >= 0 (typically 1/sqrt(d)).  causal ∈ {0, 1}.

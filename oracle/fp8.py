@@ -43,7 +43,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .exact import _f64, causal_mask
+from .exact import _f64
 
 E4M3_MAX = 448.0
 E4M3_MIN_NORMAL_EXP = -6  # smallest normal 2^-6
@@ -214,22 +214,39 @@ P_SCALE_LOG2 = 8  # P is rounded as e4m3(2^8 * p), p <= 1, so codes stay <= 256
 
 
 def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
-                  tile: int = 128, quantize_p: bool = True):
+                  tile: int = 128, quantize_p: bool = True, rows=None, ambiguity: float = 0.0,
+                  parts: bool = False):
     """fp8 attention of one or more heads: codes [..., N, d], scales [..., nt].
 
     S = scale * (sq q8)(sk k8)^T, softmax statistics in float64, and P
     rounded to e4m3 as stated in the module docstring.  With
     ``quantize_p=False`` P is kept exact (the method without P rounding).
+    ``rows`` (query indices) restricts the output to those query rows.
     Returns float64 ``(O [..., Nq, d], lse [..., Nq])``.
+
+    With ``ambiguity = delta > 0`` a third array [..., Nq, d] is returned:
+    the largest change of O that re-rounding, to the other neighbouring code,
+    every P element lying within relative distance delta of a rounding
+    midpoint could cause.  A computation whose pre-rounding values differ
+    from these by less than delta (relative) can land anywhere within it.
+
+    ``parts=True`` returns a dict instead, with the intermediate values:
+    "o", "lse", "flip" (if requested), "p8" (the rounded P, in code units,
+    [..., Nq, Nk]), "l" [..., Nq], "sv_max" [...] and "v_codes" (values of
+    the V codes).
     """
     qd = dequantize(q8, sq, tile)
+    qrow = np.arange(qd.shape[-2])
+    if rows is not None:
+        qrow = np.asarray(rows)
+        qd = qd[..., qrow, :]
     kd = dequantize(k8, sk, tile)
     v_codes = e4m3_decode(v8)
     sv = np.asarray(sv, dtype=np.float64)
     nk = kd.shape[-2]
     s = float(scale) * np.matmul(qd, np.swapaxes(kd, -1, -2))
     if causal:
-        s = np.where(causal_mask(qd.shape[-2], nk), s, -np.inf)
+        s = np.where(np.arange(nk)[None, :] <= qrow[:, None], s, -np.inf)
     t = s * LOG2E
     tmax = t.max(axis=-1) if nk else np.full(t.shape[:-1], -np.inf)
     live = np.isfinite(tmax)
@@ -245,11 +262,29 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     else:
         p8 = pw * 2.0 ** P_SCALE_LOG2
     o_acc = np.matmul(p8, v_codes)
+    flip = None
+    if ambiguity > 0:
+        x = pw * 2.0 ** P_SCALE_LOG2
+        with np.errstate(divide="ignore"):
+            e = np.maximum(np.floor(np.log2(np.where(x > 0, x, 1.0))), E4M3_MIN_NORMAL_EXP)
+        spacing = np.ldexp(1.0, (e - E4M3_MANT_BITS).astype(np.int64))
+        frac = x / spacing - np.floor(x / spacing)  # position between neighbouring codes
+        near_mid = np.abs(frac - 0.5) * spacing <= ambiguity * x
+        # a value just below a power of two can also round across the binade edge
+        flip = np.matmul(np.where(near_mid & (x > 0), spacing, 0.0), np.abs(v_codes))
     with np.errstate(invalid="ignore", divide="ignore"):
         o = np.where(live[..., None],
                      o_acc * (sv_max[..., None, None] * 2.0 ** -P_SCALE_LOG2) / np.where(live, l, 1.0)[..., None],
                      0.0)
         lse = np.where(live, (M + np.log2(np.where(live, l, 1.0))) / LOG2E, -np.inf)
+        if flip is not None:
+            flip = np.where(live[..., None],
+                            flip * (sv_max[..., None, None] * 2.0 ** -P_SCALE_LOG2) / np.where(live, l, 1.0)[..., None],
+                            0.0)
+    if parts:
+        return {"o": o, "lse": lse, "flip": flip, "p8": p8, "l": l, "sv_max": sv_max, "v_codes": v_codes}
+    if flip is not None:
+        return o, lse, flip
     return o, lse
 
 

@@ -1,0 +1,249 @@
+"""GPU parity of the fp8 path: pre-processing (rotation + block quantisation)
+and the e4m3 attention kernel, against the fp64 oracle.
+
+* Pre-processing without rotation takes every decision on the same fp32
+  values as the oracle (x, amax, s = amax/448 and x/s are all exact or
+  correctly rounded), so codes and scales must be bit-identical.  With the
+  rotation the device sums the Hadamard butterflies in fp32 while the oracle
+  rotates in fp64; scales then agree to a few ulps and a code may differ by
+  one step only where the oracle's value sits next to a rounding midpoint.
+* The attention kernel is fed e4m3 codes and scales drawn by the input
+  generator (no quantisation arithmetic), and compared with the oracle's
+  fp8 emulation (same P rounding).  The gfx950 e4m3 MFMA adds its products
+  in groups of 8, keeping 11 bits below the group's largest product (a
+  property of the instruction, measured with a probe), so it is not an
+  exact fp32 dot product.  The codes are drawn from {+-1, +-1.5, +-2, +-3,
+  +-4} with power-of-two scales, for which the S = K Q^T products are added
+  exactly; the PV product's truncation is bounded from the oracle's P codes.
+  Bar: max |O - O_emu| <= 4e-3 (the bf16 output rounding, half an ulp of
+  |O| < 0.5 <= 2^-10, plus fp32 accumulation) + that bound + the flips
+  below; lse within 1e-3 relative.  A P code is not unique where its
+  pre-rounding value lies within fp32 error (3e-5 relative: the fp32
+  score and the exp2) of an e4m3 midpoint: there either neighbour is valid,
+  so the bar of each element grows by the oracle's bound on what
+  re-rounding all such codes can change.
+* End to end at the full fp8 shape (B=2 H=16 N=8192 d=128): RMSE against
+  the fp64 truth <= 3e-2 on N(0,1) inputs; with outlier channels, the
+  per-tensor RMSE is >= 2x the block + Hadamard RMSE; and the device RMSE is
+  within 10 % of the emulation's (sampled rows of sampled heads).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import exact as OX
+from oracle import fp8 as F
+import workloads as W
+from gpu_util import sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+# ---------------------------------------------------------------- pre-processing
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_prep_no_rotation_bitwise(gpu_lib, in_dtype, d, per_tensor):
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((2, 3, 300, d), dtype=np.float32) * np.float32(3.0)
+    x[1, 1, 128:256] = 0.0  # an all-zero tile: scale 1, codes 0
+    xt = torch.from_numpy(x) if in_dtype == "f32" else W.to_dtype(x, in_dtype)
+    codes, scales = gpu_lib.fp8_quantize(xt.cuda(), None, per_tensor)
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = F.quantize(xt.double().numpy().astype(np.float32), None, per_tensor)
+    assert np.array_equal(scales.cpu().numpy(), ref_scales)
+    got = codes.cpu().numpy()
+    bad = np.argwhere(got != ref_codes)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("outliers", [0, 4])
+def test_prep_rotation(gpu_lib, d, outliers):
+    w = W.Workload("prep", 2, 3, 333, 333, d, "fp8", False, seed=d + outliers, outliers=outliers)
+    inp = W.make_inputs(w)
+    x, signs = inp["q"], inp["signs"]
+    codes, scales = gpu_lib.fp8_quantize(_dev(x), _dev(signs))
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = F.quantize(x, signs)
+    s_gpu = scales.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(s_gpu, ref_scales, rtol=4 * 2.0 ** -23, atol=0)
+    got = codes.cpu().numpy()
+    diff = got != ref_codes
+    assert diff.mean() <= 1e-3, f"{diff.sum()} of {diff.size} codes differ"
+    if diff.any():
+        # every difference is one step between neighbours, at a rounding midpoint
+        g = F.e4m3_decode(got[diff])
+        o = F.e4m3_decode(ref_codes[diff])
+        xr = F.rotate(x, signs)
+        n = x.shape[-2]
+        rs = np.repeat(ref_scales.astype(np.float64), 128, axis=-1)[..., :n][..., None]
+        y = (xr / rs)[diff]
+        mid = (g + o) / 2
+        # fp32 butterflies: each of the log2(d) stages and the final scaling
+        # rounds by at most 2^-24 of a partial sum bounded by sum_i |x_i|
+        row_l1 = np.broadcast_to(np.abs(x).sum(-1, keepdims=True) / np.sqrt(d), x.shape)[diff]
+        bound = (np.log2(d) + 3) * 2.0 ** -24 * row_l1 / np.broadcast_to(rs, x.shape)[diff]
+        assert np.all(np.abs(y - mid) <= bound + 1e-12), "a code differs away from a midpoint"
+        grid = np.unique(F.e4m3_decode(np.arange(256, dtype=np.uint8))[:127])
+        gi, oi = np.searchsorted(grid, np.abs(g)), np.searchsorted(grid, np.abs(o))
+        assert np.all(np.abs(gi - oi) == 1) and np.all(np.sign(g) == np.sign(o))
+
+
+# ---------------------------------------------------------------- attention kernel
+
+# +-1, +-1.5, +-2, +-3, +-4: products are multiples of 1/4 below 16, which the
+# 8-product groups of the e4m3 MFMA (kept to 11 bits below the group's
+# largest product) add exactly, so S has no hardware rounding.
+EXACT_CODES = [0x38, 0x3C, 0x40, 0x44, 0x48, 0xB8, 0xBC, 0xC0, 0xC4, 0xC8]
+
+
+def _exact_problem(B, H, nq, nk, seed):
+    d = 128
+    nt = lambda n: (n + 127) // 128  # noqa: E731
+    q8 = W.random_codes_from(EXACT_CODES, (B, H, nq, d), seed)
+    k8 = W.random_codes_from(EXACT_CODES, (B, H, nk, d), seed + 1)
+    v8 = W.random_codes_from(EXACT_CODES, (B, H, nk, d), seed + 2)
+    sq = W.random_pow2_scales((B, H, nt(nq)), seed + 3, -1, 0)
+    sk = W.random_pow2_scales((B, H, nt(nk)), seed + 4, -1, 0)
+    sv = W.random_pow2_scales((B, H, nt(nk)), seed + 5, -7, -4)
+    return q8, k8, v8, sq, sk, sv
+
+
+def _pv_bound(parts):
+    """Bound on the PV product's rounding inside the e4m3 MFMA, in O units.
+
+    Each 64-key MFMA step sums 8 groups of 8 products; a group keeps 11 bits
+    below the exponent e of its largest product, so each product loses less
+    than 2^(e - 11): at most 2^(e - 5) per step, with e taken from the
+    step's largest |P8 v8|.  Scaled like O: max s_v 2^-8 / l.
+    """
+    p8, vc, l, svm = parts["p8"], parts["v_codes"], parts["l"], parts["sv_max"]
+    vmax = np.abs(vc).max(-1)  # [..., Nk]
+    prod = p8 * vmax[..., None, :]  # [..., Nq, Nk]
+    nk = prod.shape[-1]
+    tot = np.zeros(prod.shape[:-1])
+    for j0 in range(0, nk, 64):
+        m = prod[..., j0:j0 + 64].max(-1)
+        with np.errstate(divide="ignore"):
+            e = np.floor(np.log2(np.where(m > 0, m, 1.0)))
+        tot += np.where(m > 0, np.exp2(e - 5), 0.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        out = np.where(l > 0, tot * svm[..., None] / 256.0 / np.where(l > 0, l, 1.0), 0.0)
+    return out[..., None]
+
+
+def _run_fp8(attn, q8, k8, v8, sq, sk, sv, scale, causal):
+    o, lse = attn.forward(_dev(q8), _dev(k8), _dev(v8), causal=causal, scale=scale,
+                          q_scale=_dev(sq), k_scale=_dev(sk), v_scale=_dev(sv))
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def _check(o, lse, o_ref, l_ref, what, tol=4e-3, allow=0.0):
+    assert not np.any(np.isnan(o)) and not np.any(np.isnan(lse)), what
+    err = np.abs(o - o_ref) - allow
+    i = np.unravel_index(np.argmax(err), err.shape) if err.size else None
+    assert err.size == 0 or err[i] <= tol, f"{what}: |O - O_emu| - allowance = {err[i]:.3e} at {i}"
+    assert np.array_equal(np.isneginf(lse), np.isneginf(l_ref)), what
+    fin = ~np.isneginf(l_ref)
+    rel = np.abs(lse[fin] - l_ref[fin]) / np.maximum(1.0, np.abs(l_ref[fin]))
+    assert rel.size == 0 or rel.max() <= 1e-3, f"{what}: lse rel err {rel.max():.3e}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(1, 1), (100, 100), (128, 128), (129, 300), (300, 129), (1000, 1000), (513, 2000)])
+def test_fp8_kernel_vs_emulation(gpu_lib, causal, nq, nk):
+    q8, k8, v8, sq, sk, sv = _exact_problem(2, 2, nq, nk, seed=nq + 3 * nk)
+    o, lse = _run_fp8(gpu_lib, q8, k8, v8, sq, sk, sv, 0.0884, causal)
+    ref = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.0884, causal, ambiguity=3e-5, parts=True)
+    allow = ref["flip"] + _pv_bound(ref)
+    _check(o, lse, ref["o"], ref["lse"], f"fp8 causal{causal} {nq}x{nk}", allow=allow)
+    # the allowances stay a small part of the signal
+    assert np.mean(allow) <= 0.25 * np.mean(np.abs(ref["o"])) + 1e-6
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_kernel_uniform_closed_form(gpu_lib, causal):
+    """scale = 0: every visible key weighs the same and P is exact (2^8 w with
+    w a power of two), so O is the mean (causal: prefix mean) of the
+    dequantised V rows, up to the bf16 rounding of O."""
+    nq = nk = 700
+    q8, k8, v8, sq, sk, sv = _exact_problem(2, 3, nq, nk, seed=33)
+    o, lse = _run_fp8(gpu_lib, q8, k8, v8, sq, sk, sv, 0.0, causal)
+    vd = F.dequantize(v8, sv)
+    if causal:
+        ref = np.cumsum(vd, axis=-2) / np.arange(1, nk + 1)[:, None]
+        lref = np.broadcast_to(np.log(np.arange(1, nq + 1)), lse.shape)
+    else:
+        ref = np.broadcast_to(vd.mean(-2, keepdims=True), o.shape)
+        lref = np.full(lse.shape, np.log(nk))
+    assert np.all(np.abs(o - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-7)
+    np.testing.assert_allclose(lse, lref, rtol=0, atol=1e-5)
+
+
+def test_fp8_kernel_empty_keys(gpu_lib):
+    q8, _, _, sq, _, _ = _exact_problem(1, 2, 50, 1, seed=5)
+    z8 = torch.zeros((1, 2, 0, 128), dtype=torch.uint8, device="cuda")
+    zs = torch.zeros((1, 2, 0), dtype=torch.float32, device="cuda")
+    o, lse = gpu_lib.forward(_dev(q8), z8, z8, scale=0.1, q_scale=_dev(sq), k_scale=zs, v_scale=zs)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+# ---------------------------------------------------------------- full size, end to end
+
+def _end_to_end(attn, w, per_tensor):
+    inp = W.make_inputs(w)
+    q, k, v, signs = inp["q"], inp["k"], inp["v"], inp["signs"]
+    sg = None if per_tensor else _dev(signs)
+    q8, sq = attn.fp8_quantize(_dev(q), sg, per_tensor)
+    k8, sk = attn.fp8_quantize(_dev(k), sg, per_tensor)
+    v8, sv = attn.fp8_quantize(_dev(v), None, per_tensor)
+    o, lse = attn.forward(q8, k8, v8, scale=w.scale, q_scale=sq, k_scale=sk, v_scale=sv)
+    torch.cuda.synchronize()
+    o = o.double().cpu().numpy()
+    assert np.all(np.isfinite(o)) and torch.all(torch.isfinite(lse))
+    # the oracle's own pipeline, on sampled heads and rows
+    so = None if per_tensor else signs
+    rq8, rsq = F.quantize(q, so, per_tensor)
+    rk8, rsk = F.quantize(k, so, per_tensor)
+    rv8, rsv = F.quantize(v, None, per_tensor)
+    heads = [(0, 0), (1, 7), (0, 15)]
+    gpu_err, emu_err = [], []
+    for b, h in heads:
+        rows = sample_rows(w.Nq, 64, seed=b * 16 + h)
+        truth, _ = OX.attention_rows(q[b, h], k[b, h], v[b, h], rows, w.scale)
+        emu, _ = F.attention_fp8(rq8[b, h], rk8[b, h], rv8[b, h], rsq[b, h], rsk[b, h], rsv[b, h], w.scale,
+                                 rows=rows)
+        gpu_err.append(o[b, h][rows] - truth)
+        emu_err.append(emu - truth)
+    g = float(np.sqrt(np.mean(np.concatenate(gpu_err) ** 2)))
+    e = float(np.sqrt(np.mean(np.concatenate(emu_err) ** 2)))
+    return g, e
+
+
+def test_fp8_full_normal_rmse(gpu_lib):
+    w = W.WORKLOADS["fp8_normal"]
+    g, e = _end_to_end(gpu_lib, w, False)
+    print(f"fp8 N(0,1): device RMSE {g:.3e}, emulation RMSE {e:.3e}")
+    assert g <= 3e-2
+    assert g <= 1.1 * e + 1e-5
+
+
+def test_fp8_full_outlier_gates(gpu_lib):
+    w = W.WORKLOADS["fp8_outlier"]
+    g_blk, e_blk = _end_to_end(gpu_lib, w, False)
+    g_pt, e_pt = _end_to_end(gpu_lib, w, True)
+    print(f"fp8 outliers: block+Hadamard RMSE {g_blk:.3e} (emulation {e_blk:.3e}); "
+          f"per-tensor {g_pt:.3e} (emulation {e_pt:.3e}); ratio {g_pt / g_blk:.2f}")
+    assert g_pt / g_blk >= 2.0
+    assert g_blk <= 1.1 * e_blk and g_pt <= 1.1 * e_pt

@@ -200,6 +200,37 @@ def test_fp8_causal_first_row():
     np.testing.assert_allclose(lse[:, 0], s00, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_rows_option(causal):
+    q8, k8, v8, sq, sk, sv = _codes_problem(300, 260, 32, 61)
+    o, lse = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, causal)
+    rows = [0, 5, 127, 128, 299]
+    o_r, lse_r = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, causal, rows=rows)
+    np.testing.assert_allclose(o_r, o[:, rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse_r, lse[:, rows], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_ambiguity_bound_covers_perturbation(causal):
+    """Nudging every score by ~1e-6 relative (as fp32 arithmetic does) moves O
+    by no more than the ambiguity bound plus the smooth change of the weights."""
+    q8, k8, v8, sq, sk, sv = _codes_problem(120, 333, 32, 71)
+    sq = sq * 100  # sharper softmax: larger weights, so flips matter
+    # a relative nudge eps of the scores moves each pre-rounding weight by
+    # ln(2) |t| eps relative; |t| < 14 here, so ambiguity 1e-3 covers eps = 1e-4
+    t = np.abs(F.dequantize(q8, sq) @ np.swapaxes(F.dequantize(k8, sk), -1, -2)) * 0.3 * F.LOG2E
+    assert 5 < t.max() < 14
+    o, lse, flip = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, causal, ambiguity=1e-3)
+    assert np.all(flip >= 0)
+    o2, _ = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3 * (1 + 1e-4), causal)
+    # besides flips, the nudge moves l (and the unrounded weights) by ~1e-3 relative
+    moved = np.abs(o2 - o) - 2e-3 * np.abs(o)
+    assert np.all(moved <= flip + 1e-12), moved.max()
+    assert np.any(np.abs(o2 - o) > 2e-3 * np.abs(o) + 1e-12)  # some code did flip
+    o0 = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, causal)
+    assert len(o0) == 2 and np.array_equal(o0[0], o)
+
+
 def test_fp8_empty_keys():
     q8, k8, v8, sq, sk, sv = _codes_problem(5, 0, 16, 51)
     o, lse = F.attention_fp8(q8, k8, v8, sq, sk[:, :0], sv[:, :0], 0.3, False)

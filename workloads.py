@@ -183,6 +183,18 @@ def random_e4m3_codes(shape, seed, max_exp_field=10) -> np.ndarray:
     return (sign << 7) | (expo << 3) | mant
 
 
+def random_codes_from(codes, shape, seed) -> np.ndarray:
+    """Uniform random choice (uint8) among the given e4m3 bit patterns."""
+    rng = np.random.default_rng(seed)
+    return rng.choice(np.asarray(codes, dtype=np.uint8), size=shape)
+
+
+def random_pow2_scales(shape, seed, lo_exp=-3, hi_exp=0) -> np.ndarray:
+    """Scales 2^e with e drawn uniformly from [lo_exp, hi_exp] (float32)."""
+    rng = np.random.default_rng(seed)
+    return np.ldexp(np.float32(1.0), rng.integers(lo_exp, hi_exp + 1, size=shape)).astype(np.float32)
+
+
 def random_scales(shape, seed, lo=0.01, hi=0.05) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return rng.uniform(lo, hi, size=shape).astype(np.float32)
