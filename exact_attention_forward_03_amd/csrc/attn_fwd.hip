@@ -1,103 +1,101 @@
 // Exact attention forward for fp16/bf16 on gfx950 (CDNA4).
 //
-// One workgroup owns a block of BR = 32*NW query rows of one (batch, head)
-// — or one (sequence, head) of a variable-length batch — and streams the
-// keys and values through LDS in tiles of BC rows, keeping the online-softmax
-// state in registers ("Flash Attention 3：让 GPU 跑满的注意力计算", §2.1 tiling,
-// §2.2 online softmax, §3.1 one independent query block per workgroup).
+// One workgroup owns a block of 32*NW query rows of one (batch, head) — or
+// one (sequence, head) of a variable-length batch — and streams the keys and
+// values through LDS in tiles of BC rows, keeping the online-softmax state in
+// registers ("Flash Attention 3：让 GPU 跑满的注意力计算", §2.1 tiling, §2.2
+// online softmax, §3.1 one independent query block per workgroup; the
+// asynchronous producer of "FlashAttention-3", "Three techniques" §1):
 //
-// Per wave (32 query rows, 64 lanes):
-//   * S^T = K Q^T on 32x32x16 MFMA: K rows are the A operand (read from LDS),
-//     the wave's Q rows are the B operand (held in registers for the whole
-//     kernel).  In the result every lane owns ONE query (lane % 32) and 16
-//     keys per 32-key block, so the row max/sum are in-register reductions
-//     plus one exchange between the two wave halves (v_permlane32_swap).
-//   * The probabilities P^T come out of the MFMA already in the B-operand
-//     layout of the second product, O^T = V^T P^T: they are converted to
-//     fp16/bf16 in registers and never touch LDS.
-//   * V is written into LDS transposed ([d][key]), with keys permuted inside
-//     each 16-key group so that one 16-byte LDS read gives a lane exactly
-//     the 8 keys its P^T fragment holds.
-//   * K/V tiles are double buffered: the global loads of tile j+1 are issued
-//     before tile j is computed and land in LDS after it, with one barrier
-//     per tile.
-//
-// Softmax in base 2 with an integer reference maximum.  For each row the
-// kernel keeps M = ceil(max of the scores seen so far, times scale*log2 e),
-// p = 2^(S*scale*log2e - M) <= 1, l = sum p (fp32, unrounded), and
-// O = sum p v.  M only moves when a tile raises the row max past the current
-// integer; then O and l are multiplied by 2^(M_old - M_new), an exact power
-// of two.  Skipping that rescale whenever no row of the wave moved is what
-// keeps the fp32 vector work per tile small.  The result O / l and
-// lse = (M + log2 l) ln 2 equal the page's recurrence (which rescales by
-// e^{m_old - m_new} at every tile) up to rounding; the reference point of
-// the exponentials does not change the sum they define.
-//
-// P enters the second product rounded to fp16/bf16.  While some row of the
-// wave has little weight accumulated (its mass sits on a few keys, so |O| can
-// be as large as |V|), the rounding residual p - round(p) is multiplied in by
-// a second MFMA pass, which makes the weights exact to ~16 more bits.
-
-// Causal masking is top-left (key j visible to query i iff j <= i).  Key
-// tiles entirely above a wave's diagonal are skipped by that wave; tiles
-// entirely above the workgroup's diagonal are never loaded.  Only tiles that
-// cross the diagonal or the end of the keys apply an element mask.
-//
-// Workgroup order: the hardware id is remapped so that consecutive work items
-// — the query tiles of one head — run on the same XCD and share its L2 copy
-// of that head's K and V; causal query tiles run heaviest first.
-
+// * NW waves per workgroup, each owning 32 query rows; with 8 waves two run
+//   on each SIMD, so one wave's softmax can overlap the other's MFMAs.
+// * K and V tiles go from HBM/L2 straight into LDS (global_load_lds_dwordx4:
+//   no staging registers, no VALU, no LDS write instructions), through a
+//   ring of NS buffers: the load of tile j+NS-1 is issued at step j, so a
+//   tile has NS-1 steps to arrive.  Rows are stored unpadded with the
+//   16-byte chunks of each row XOR-permuted by a function of the row, which
+//   keeps the fragment reads free of bank conflicts.
+// * S^T = K Q^T on 32x32x16 MFMA puts P in registers already in the
+//   B-operand layout of O^T = V^T P^T.  The V^T operand is read from the
+//   row-major V tile with the transposing LDS read (ds_read_b64_tr_b16):
+//   within a 16-lane group, lane i receives element i & 3 of the 8-byte
+//   pieces read by lanes 4j + i / 4, so 4 lanes reading 4 consecutive rows
+//   give every lane 4 consecutive keys of one column.
+// * Softmax in base 2 with an integer reference maximum.  For each row the
+//   kernel keeps M = ceil(max of the scores seen so far, times scale log2 e),
+//   p = 2^(S scale log2 e - M) <= 1, l = sum p (fp32, unrounded) and
+//   O = sum p v.  M only moves when a tile raises the row max past the
+//   current integer; then O and l are multiplied by 2^(M_old - M_new), an
+//   exact power of two, and only if some row of the wave moved.  O / l and
+//   lse = (M + log2 l) ln 2 equal the page's recurrence (which rescales by
+//   e^{m_old - m_new} at every tile) up to rounding: the reference point of
+//   the exponentials does not change the sum they define.
+// * P enters the second product rounded to fp16/bf16.  While some row of the
+//   wave has little weight accumulated (its mass sits on a few keys, so |O|
+//   can be as large as |V|), the rounding residual p - round(p) is multiplied
+//   in by a second MFMA pass on the same accumulators, which makes the
+//   weights exact to ~16 more bits.
+// * Causal masking is top-left (key j visible to query i iff j <= i).  Key
+//   tiles entirely above a wave's diagonal are skipped by that wave; tiles
+//   entirely above the workgroup's diagonal are never loaded.  Only tiles
+//   that cross the diagonal or the end of the keys apply an element mask.
+// * Workgroup order: the hardware id is remapped so that consecutive work
+//   items — the query tiles of one head — run on the same XCD and share its
+//   L2 copy of that head's K and V; causal query tiles run heaviest first.
 #include "attn_device.h"
 #include "attn_params.h"
 
 namespace attn {
 namespace {
 
-// Position of key k (within a tile) in a transposed V row: bits 2 and 3 of
-// the index inside its 16-key group are swapped, so that keys
-// {0-3, 8-11} (lanes 0..31) and {4-7, 12-15} (lanes 32..63) are contiguous.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3);
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr float kSplitBelowP = 8.0f;
+constexpr int kPreD = 4;  // LDS fragment reads in flight ahead of their MFMA
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {  // [a.lo, b.lo]
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {  // [a.hi, b.hi]
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
-// A lane's partial row sum below this (in units of the row's reference
-// maximum, i.e. fewer than ~16 effective keys for the whole row) switches on
-// the residual product for P.
-constexpr float kSplitBelow = 8.0f;
-
-template <int D, int BC, int NW>
-struct TileCfg {
-  static constexpr int BR = NW * 32;        // query rows per workgroup
-  static constexpr int NT = NW * 64;        // threads
-  static constexpr int KP = D + 8;          // K row pitch in LDS (elements)
-  static constexpr int VP = BC + 8;         // V^T row pitch in LDS (elements)
-  static constexpr int KS = D / 16;         // MFMA k-steps of S^T = K Q^T
-  static constexpr int MB = BC / 32;        // 32-key blocks per tile
-  static constexpr int DB = D / 32;         // 32-row blocks of O^T
-  static constexpr int KBUF = BC * KP;      // elements of one K buffer
-  static constexpr int VBUF = D * VP;       // elements of one V^T buffer
-  static constexpr int KCH = BC * D / 8 / NT;         // 16-byte K chunks per thread
-  static constexpr int VCH = (BC / 4) * (D / 4) / NT; // 4x4 V blocks per thread
-  static constexpr int LDS_BYTES = 2 * (KBUF + VBUF) * 2;
-  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert(KCH * NT * 8 == BC * D, "K tile must split evenly over the threads");
-  static_assert(VCH * NT * 16 == BC * D, "V tile must split evenly over the threads");
+template <int D, int NQB, int BC, int NW, int NS>
+struct PipeCfg {
+  static constexpr int QW = NQB * 32;        // query rows per wave
+  static constexpr int BR = NW * QW;         // query rows per workgroup
+  static constexpr int NT = NW * 64;
+  static constexpr int ROWB = D * 2;         // bytes per K/V row in LDS (unpadded)
+  static constexpr int CHUNKS = ROWB / 16;   // 16-byte chunks per row
+  static constexpr int TILEB = BC * ROWB;    // bytes per K or V tile
+  static constexpr int KS = D / 16;          // MFMA k-steps of S^T
+  static constexpr int MB = BC / 32;         // 32-key blocks per tile
+  static constexpr int DB = D / 32;          // 32-row blocks of O^T
+  static constexpr int LOADS = TILEB / 1024; // 1 KiB direct-to-LDS loads per tile
+  static constexpr int LDS_BYTES = 2 * NS * TILEB; // K and V rings of NS buffers
+  static constexpr int LPT = 2 * LOADS / NW;  // load instructions per wave per tile (K and V)
+  static_assert(LOADS % NW == 0, "each wave issues the same number of tile loads");
+  static_assert(CHUNKS >= 8, "row swizzle needs at least 8 chunks");
 };
 
-template <typename TT, int D, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
-attn_fwd_kernel(FwdParams p) {
-  using C = TileCfg<D, BC, NW>;
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+// Physical 16-byte chunk of logical chunk `ch` in K row `r`: all 16 rows of
+// an aligned group land on different chunks (K fragment reads: 16 lanes,
+// 16 rows, same logical chunk).
+template <int CHUNKS>
+__device__ __forceinline__ int k_chunk(int r, int ch) { return ch ^ (r & (CHUNKS >= 16 ? 15 : 7)); }
+// V rows: 4 consecutive rows x 2 neighbouring chunks (a transposing read of
+// 16 lanes) land on 8 different chunks.
+__device__ __forceinline__ int v_chunk(int r, int ch) { return ch ^ ((r & 3) << 1); }
 
-  // ---- work item -> (head, query tile) -------------------------------------
+template <typename TT, int D, int BC, int NW, int WPE, int NS, bool CAUSAL, bool VARLEN>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
+attn_fwd_dma_kernel(FwdParams p) {
+  constexpr int NQB = 1;
+  using C = PipeCfg<D, NQB, BC, NW, NS>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  // ---- work item -> (head, query tile) --------------------------------------
   const int work = xcd_remap(blockIdx.x, p.n_work);
   const int head = work / p.tiles_per_head;
   const int t = work - head * p.tiles_per_head;
@@ -121,7 +119,7 @@ attn_fwd_kernel(FwdParams p) {
       }
       acc += nt;
     }
-    if (seq < 0) return;  // surplus workgroup (the grid is an upper bound)
+    if (seq < 0) return;
     const int lt = t - acc;
     qt = CAUSAL ? (nts - 1 - lt) : lt;
     const int kb = min(max(p.cu_k[seq], 0), p.Nk);
@@ -132,279 +130,310 @@ attn_fwd_kernel(FwdParams p) {
     k_row0 = (int64_t)head * p.Nk + kb;
   }
   const int q0 = qt * C::BR;
-
   const uint16_t* __restrict__ Qp = (const uint16_t*)p.q + q_row0 * D;
-  const uint16_t* __restrict__ Kp = (const uint16_t*)p.k + k_row0 * D;
-  const uint16_t* __restrict__ Vp = (const uint16_t*)p.v + k_row0 * D;
+  const uint8_t* __restrict__ Kb = (const uint8_t*)p.k + k_row0 * D * 2;
+  const uint8_t* __restrict__ Vb = (const uint8_t*)p.v + k_row0 * D * 2;
 
   const int tid = threadIdx.x;
   const int wv = tid >> 6, lane = tid & 63, c = lane & 31, hh = lane >> 5;
-  const int qw0 = q0 + wv * 32;  // first query row of this wave
-  const int my_q = qw0 + c;      // this lane's query row
-  const bool q_ok = my_q < q_len;
+  const int qw0 = q0 + wv * C::QW;  // first query row of this wave
 
-  // ---- Q fragments: B operand of S^T = K Q^T, kept for the whole kernel ---
-  uint4 qf[C::KS];
-  {
-    const uint16_t* qrow = Qp + (int64_t)(q_ok ? my_q : 0) * D + 8 * hh;
+  // ---- Q fragments (B operands), one set per 32-row block ----------------
+  uint4 qf[NQB][C::KS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = q_ok ? *(const uint4*)(qrow + ks * 16) : zero4();
+  for (int nb = 0; nb < NQB; ++nb) {
+    const int q = qw0 + nb * 32 + c;
+    const bool ok = q < q_len;
+    const uint16_t* qrow = Qp + (int64_t)(ok ? q : 0) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qf[nb][ks] = ok ? *(const uint4*)(qrow + ks * 16) : zero4();
   }
 
-  // ---- key tiles this workgroup / wave needs ------------------------------
   int n_kt = (k_len + BC - 1) / BC;
-  if (CAUSAL) {
-    const int last_q = min(q0 + C::BR, q_len) - 1;
-    n_kt = min(n_kt, last_q / BC + 1);
-  }
+  if (CAUSAL) n_kt = min(n_kt, (min(q0 + C::BR, q_len) - 1) / BC + 1);
   int wave_kt = n_kt;
-  if (qw0 >= q_len) {
-    wave_kt = 0;
-  } else if (CAUSAL) {
-    const int wave_last_q = min(qw0 + 31, q_len - 1);
-    wave_kt = min(n_kt, wave_last_q / BC + 1);
-  }
+  if (qw0 >= q_len) wave_kt = 0;
+  else if (CAUSAL) wave_kt = min(n_kt, (min(qw0 + C::QW - 1, q_len - 1)) / BC + 1);
 
-  uint16_t* const ldsK = lds;
-  uint16_t* const ldsV = lds + 2 * C::KBUF;
+  uint8_t* const ldsK = lds;
+  uint8_t* const ldsV = lds + NS * C::TILEB;
 
-  uint4 kr[C::KCH];
-  uint2 vr[C::VCH][4];
-
-  auto load_tile = [&](int kt) {
+  // Direct-to-LDS load of one K (or V) tile into buffer `buf`: the wave's
+  // i-th instruction fills the 1 KiB block wv * LOADS/NW + i, i.e. rows
+  // RPB * block .. + RPB-1; lane l writes chunk l % CHUNKS of row
+  // RPB*block + l / CHUNKS and fetches the logical chunk stored there.  Rows
+  // past the end of the keys re-read the last key (finite values, masked).
+  constexpr int RPB = 1024 / C::ROWB;  // rows per 1 KiB block
+  auto load_k = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int ch = tid + i * C::NT;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      const int key = kt * BC + row;
-      kr[i] = key < k_len ? *(const uint4*)(Kp + (int64_t)key * D + col) : zero4();
-    }
-#pragma unroll
-    for (int i = 0; i < C::VCH; ++i) {
-      const int ch = tid + i * C::NT;
-      const int kg = ch / (D / 4), dg = ch % (D / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kt * BC + 4 * kg + r;
-        vr[i][r] = key < k_len ? *(const uint2*)(Vp + (int64_t)key * D + 4 * dg) : make_uint2(0u, 0u);
-      }
+    for (int i = 0; i < C::LOADS / NW; ++i) {
+      const int blk = wv * (C::LOADS / NW) + i;
+      const int r = blk * RPB + lane / C::CHUNKS;
+      const int key = min(kt * BC + r, k_len - 1);
+      const uint8_t* src = Kb + (int64_t)key * C::ROWB + k_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsK + buf * C::TILEB + blk * 1024), 16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* kb = ldsK + buf * C::KBUF;
-    uint16_t* vb = ldsV + buf * C::VBUF;
+  auto load_v = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int ch = tid + i * C::NT;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *(uint4*)(kb + row * C::KP + col) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::VCH; ++i) {
-      const int ch = tid + i * C::NT;
-      const int kg = ch / (D / 4), dg = ch % (D / 4);
-      uint16_t* dst = vb + (4 * dg) * C::VP + vt_pos(4 * kg);
-      // 4 keys x 4 channels -> for each channel, the 4 keys as one 8-byte word
-      *(uint2*)(dst + 0 * C::VP) = make_uint2(lo_halves(vr[i][0].x, vr[i][1].x), lo_halves(vr[i][2].x, vr[i][3].x));
-      *(uint2*)(dst + 1 * C::VP) = make_uint2(hi_halves(vr[i][0].x, vr[i][1].x), hi_halves(vr[i][2].x, vr[i][3].x));
-      *(uint2*)(dst + 2 * C::VP) = make_uint2(lo_halves(vr[i][0].y, vr[i][1].y), lo_halves(vr[i][2].y, vr[i][3].y));
-      *(uint2*)(dst + 3 * C::VP) = make_uint2(hi_halves(vr[i][0].y, vr[i][1].y), hi_halves(vr[i][2].y, vr[i][3].y));
+    for (int i = 0; i < C::LOADS / NW; ++i) {
+      const int blk = wv * (C::LOADS / NW) + i;
+      const int r = blk * RPB + lane / C::CHUNKS;
+      const int key = min(kt * BC + r, k_len - 1);
+      const uint8_t* src = Vb + (int64_t)key * C::ROWB + v_chunk(r, lane % C::CHUNKS) * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsV + buf * C::TILEB + blk * 1024), 16, 0, 0);
     }
   };
-
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
 
   const float cs = p.c;
-  float M = -INFINITY;  // integer reference max (base 2) of this lane's row
-  float l = 0.f;        // this lane's partial row sum (its half of the keys)
-  f32x16_t oacc[C::DB];
+  float M[NQB], l[NQB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) oacc[db] = f32x16_t{};
+  for (int nb = 0; nb < NQB; ++nb) { M[nb] = -INFINITY; l[nb] = 0.f; }
+  f32x16_t oacc[NQB][C::DB];
+#pragma unroll
+  for (int nb = 0; nb < NQB; ++nb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) oacc[nb][db] = f32x16_t{};
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+  // S^T for the key tile in K buffer kbuf; fragments read kPreD MFMAs ahead
+  auto compute_s = [&](int kbuf, f32x16_t (&s)[NQB][C::MB]) {
+    const uint8_t* kb = ldsK + kbuf * C::TILEB;
+    constexpr int N = C::MB * C::KS;
+    auto frag = [&](int i) {
+      const int r = (i / C::KS) * 32 + c;
+      return *(const uint4*)(kb + r * C::ROWB + k_chunk<C::CHUNKS>(r, 2 * (i % C::KS) + hh) * 16);
+    };
+    uint4 fr[kPreD];
+#pragma unroll
+    for (int i = 0; i < kPreD; ++i) fr[i] = frag(i);
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) s[0][mb] = f32x16_t{};
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint4 a = fr[i % kPreD];
+      if (i + kPreD < N) fr[i % kPreD] = frag(i + kPreD);
+      s[0][i / C::KS] = mfma32(TT{}, a, qf[0][i % C::KS], s[0][i / C::KS]);
+    }
+  };
 
-    if (kt < wave_kt) {
-      const uint16_t* kb = ldsK + buf * C::KBUF;
-      const uint16_t* vb = ldsV + buf * C::VBUF;
-
-      // S^T = K Q^T for the tile
-      f32x16_t s[C::MB];
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
-        s[mb] = f32x16_t{};
-        const uint16_t* krow = kb + (mb * 32 + c) * C::KP + 8 * hh;
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) s[mb] = mfma32(TT{}, *(const uint4*)(krow + ks * 16), qf[ks], s[mb]);
-      }
-
-      const int key0 = kt * BC;
-      const bool need_mask = (key0 + BC > k_len) || (CAUSAL && key0 + BC - 1 > qw0);
-      float tmax = -INFINITY;
-      if (need_mask) {
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            const bool ok = key < k_len && (!CAUSAL || key <= my_q);
-            s[mb][i] = ok ? s[mb][i] * cs : -INFINITY;
-            tmax = fmaxf(tmax, s[mb][i]);
-          }
-      } else {
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
-        tmax *= cs;
-      }
-      tmax = max_halves(tmax);
-      const float m_new = fmaxf(M, __builtin_ceilf(tmax));
-      if (__any(m_new > M)) {
-        const float alpha = (m_new == M) ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
-      M = m_new;
-      const float m_use = (M == -INFINITY) ? 0.f : M;
-
-      float rs = 0.f;
-      if (need_mask) {
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            s[mb][i] = __builtin_amdgcn_exp2f(s[mb][i] - m_use);
-            rs += s[mb][i];
-          }
-      } else {
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            s[mb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][i], cs, -m_use));
-            rs += s[mb][i];
-          }
-      }
-      l += rs;
-
-      // P^T as the B operand of O^T += V^T P^T (keys of register i of block mb:
-      // 8*(i/4) + 4*hh + i%4, which is the order vt_pos lays V^T out in).
-      //
-      // Rows whose weight so far sits on few keys (small l) have large |O|,
-      // where the 16-bit rounding of P would show.  For them the residual
-      // p - round16(p) goes through a second product, so the weights carry
-      // about 16 more bits; diffuse rows average the rounding out and skip it.
-      uint4 pf[C::MB][2];
+  // Masks, row max, M update (with the rare rescale of O and l).
+  auto prepare = [&](int kt, f32x16_t (&s)[NQB][C::MB], float (&m_use)[NQB], bool& masked) {
+    const int key0 = kt * BC;
+    masked = (key0 + BC > k_len) || (CAUSAL && key0 + BC - 1 > qw0);
+    float tmax = -INFINITY;
+    const int my_q = qw0 + c;
+    if (masked) {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int b = 8 * h2;
-          pf[mb][h2] = make_uint4(pack2(TT{}, s[mb][b + 0], s[mb][b + 1]), pack2(TT{}, s[mb][b + 2], s[mb][b + 3]),
-                                  pack2(TT{}, s[mb][b + 4], s[mb][b + 5]), pack2(TT{}, s[mb][b + 6], s[mb][b + 7]));
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const bool ok = key < k_len && (!CAUSAL || key <= my_q);
+          s[0][mb][i] = ok ? s[0][mb][i] * cs : -INFINITY;
+          tmax = fmaxf(tmax, s[0][mb][i]);
         }
-      if (__any(l < kSplitBelow)) {
-        uint4 pl[C::MB][2];
+    } else {
 #pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
+      for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int b = 8 * h2;
-            pl[mb][h2] = make_uint4(residual2(TT{}, pf[mb][h2].x, s[mb][b + 0], s[mb][b + 1]),
-                                    residual2(TT{}, pf[mb][h2].y, s[mb][b + 2], s[mb][b + 3]),
-                                    residual2(TT{}, pf[mb][h2].z, s[mb][b + 4], s[mb][b + 5]),
-                                    residual2(TT{}, pf[mb][h2].w, s[mb][b + 6], s[mb][b + 7]));
-          }
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[0][mb][i]);
+      tmax *= cs;
+    }
+    tmax = max_halves(tmax);
+    const float m_new = fmaxf(M[0], __builtin_ceilf(tmax));
+    if (__any(m_new > M[0])) {
+      const float alpha = (m_new == M[0]) ? 1.f : __builtin_amdgcn_exp2f(M[0] - m_new);
+      l[0] *= alpha;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const uint16_t* vrow = vb + (db * 32 + c) * C::VP + 8 * hh;
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-          for (int mb = 0; mb < C::MB; ++mb)
+        for (int i = 0; i < 16; ++i) oacc[0][db][i] *= alpha;
+    }
+    M[0] = m_new;
+    m_use[0] = (M[0] == -INFINITY) ? 0.f : M[0];
+  };
+
+  // exponentials, exact row sum and P^T packing of one tile
+  auto exps = [&](f32x16_t (&s)[NQB][C::MB], const float (&m_use)[NQB], bool masked, uint4 (&pf)[NQB][C::MB][2]) {
+    float rs = 0.f;
+    if (masked) {
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const uint4 va = *(const uint4*)(vrow + mb * 32 + 16 * h2);
-              oacc[db] = mfma32(TT{}, va, pf[mb][h2], oacc[db]);
-              oacc[db] = mfma32(TT{}, va, pl[mb][h2], oacc[db]);
-            }
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[0][mb][i] = __builtin_amdgcn_exp2f(s[0][mb][i] - m_use[0]);
+          rs += s[0][mb][i];
         }
-      } else {
+    } else {
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const uint16_t* vrow = vb + (db * 32 + c) * C::VP + 8 * hh;
+      for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-          for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-              oacc[db] = mfma32(TT{}, *(const uint4*)(vrow + mb * 32 + 16 * h2), pf[mb][h2], oacc[db]);
+        for (int i = 0; i < 16; ++i) {
+          s[0][mb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][mb][i], cs, -m_use[0]));
+          rs += s[0][mb][i];
         }
+    }
+    l[0] += rs;
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int b = 8 * h2;
+        const f32x16_t& v = s[0][mb];
+        pf[0][mb][h2] = make_uint4(pack2(TT{}, v[b + 0], v[b + 1]), pack2(TT{}, v[b + 2], v[b + 3]),
+                                   pack2(TT{}, v[b + 4], v[b + 5]), pack2(TT{}, v[b + 6], v[b + 7]));
       }
+  };
+
+  // O^T += V^T P^T for the tile in V buffer vbuf; the V^T fragment of
+  // (db, 16-key step) comes from two transposing reads (keys 4h.. and
+  // 8+4h..), read kPreD MFMAs ahead.
+  auto pv_pass = [&](int vbuf, const uint4 (&pp)[NQB][C::MB][2]) {
+    const uint8_t* vb = ldsV + vbuf * C::TILEB;
+    const int g = (lane >> 4) & 1, s4 = lane & 15;
+    constexpr int N = C::DB * 2 * C::MB;
+    auto frag = [&](int i) {
+      const int db = i / (2 * C::MB), k16 = i % (2 * C::MB);
+      const int col = db * 32 + 16 * g + 4 * (s4 & 3);  // element column read by this lane
+      const int ch = col >> 3, half = (col >> 2) & 1;
+      const int r0 = k16 * 16 + 4 * hh + (s4 >> 2);
+      const int r1 = r0 + 8;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(vb + r0 * C::ROWB + v_chunk(r0, ch) * 16 + half * 8));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(vb + r1 * C::ROWB + v_chunk(r1, ch) * 16 + half * 8));
+      const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+      return make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+    };
+    uint4 fr[kPreD];
+#pragma unroll
+    for (int i = 0; i < kPreD; ++i) fr[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint4 a = fr[i % kPreD];
+      if (i + kPreD < N) fr[i % kPreD] = frag(i + kPreD);
+      const int db = i / (2 * C::MB), k16 = i % (2 * C::MB);
+      oacc[0][db] = mfma32(TT{}, a, pp[0][k16 >> 1][k16 & 1], oacc[0][db]);
+    }
+  };
+
+  auto residual = [&](f32x16_t (&s)[NQB][C::MB], const uint4 (&pf)[NQB][C::MB][2], uint4 (&pl)[NQB][C::MB][2]) {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int b = 8 * h2;
+        const f32x16_t& v = s[0][mb];
+        pl[0][mb][h2] = make_uint4(residual2(TT{}, pf[0][mb][h2].x, v[b + 0], v[b + 1]),
+                                   residual2(TT{}, pf[0][mb][h2].y, v[b + 2], v[b + 3]),
+                                   residual2(TT{}, pf[0][mb][h2].z, v[b + 4], v[b + 5]),
+                                   residual2(TT{}, pf[0][mb][h2].w, v[b + 6], v[b + 7]));
+      }
+  };
+
+  // prologue: tiles 0 .. NS-2 in flight
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_kt) {
+      load_k(j, j);
+      load_v(j, j);
     }
 
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+  int buf = 0;  // ring slot of tile kt
+  for (int kt = 0; kt < n_kt; ++kt) {
+    // tile kt must have landed (its loads are the oldest in flight); later
+    // tiles may still be on their way
+    if (kt + NS - 2 < n_kt) wait_vm<(NS - 2) * C::LPT>();
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // refill the slot that tile kt-1 used (every wave is past it now)
+    if (kt + NS - 1 < n_kt) {
+      const int fb = (buf == 0) ? NS - 1 : buf - 1;
+      load_k(kt + NS - 1, fb);
+      load_v(kt + NS - 1, fb);
+    }
+    if (kt < wave_kt) {
+      f32x16_t s[NQB][C::MB];
+      float m_use[NQB];
+      bool masked = false;
+      uint4 pf[NQB][C::MB][2];
+      compute_s(buf, s);
+      prepare(kt, s, m_use, masked);
+      exps(s, m_use, masked, pf);
+      const bool split = __any(l[0] < kSplitBelowP);
+      pv_pass(buf, pf);
+      if (split) {
+        uint4 pl[NQB][C::MB][2];
+        residual(s, pf, pl);
+        pv_pass(buf, pl);
+      }
+    }
+    buf = (buf + 1 == NS) ? 0 : buf + 1;
   }
 
-  // ---- epilogue: O = O / l, lse = (M + log2 l) ln 2 -----------------------
-  const float l_tot = sum_halves(l);
-  if (q_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = (uint16_t*)p.o + (q_row0 + my_q) * D;
+  // ---- epilogue -----------------------------------------------------------
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+  for (int nb = 0; nb < NQB; ++nb) {
+    const int my_q = qw0 + nb * 32 + c;
+    const float l_tot = sum_halves(l[nb]);
+    if (my_q < q_len) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* orow = (uint16_t*)p.o + (q_row0 + my_q) * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dcol = db * 32 + 8 * g + 4 * hh;
-        *(uint2*)(orow + dcol) = make_uint2(pack2(TT{}, oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
-                                            pack2(TT{}, oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv));
-      }
-    if (hh == 0) p.lse[q_row0 + my_q] = l_tot > 0.f ? (M + __log2f(l_tot)) * kLn2 : -INFINITY;
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dcol = db * 32 + 8 * g + 4 * hh;
+          *(uint2*)(orow + dcol) =
+              make_uint2(pack2(TT{}, oacc[nb][db][4 * g + 0] * inv, oacc[nb][db][4 * g + 1] * inv),
+                         pack2(TT{}, oacc[nb][db][4 * g + 2] * inv, oacc[nb][db][4 * g + 3] * inv));
+        }
+      if (hh == 0) p.lse[q_row0 + my_q] = l_tot > 0.f ? (M[nb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
   }
 }
 
-template <typename TT, int D, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN>
-hipError_t launch_one(const FwdParams& p, hipStream_t st) {
-  using C = TileCfg<D, BC, NW>;
-  auto kern = attn_fwd_kernel<TT, D, BC, NW, WPE, CAUSAL, VARLEN>;
+template <typename TT, int D, int BC, int NW, int WPE, int NS, bool CAUSAL, bool VARLEN>
+hipError_t launch_dma_one(const FwdParams& p, hipStream_t st) {
+  using C = PipeCfg<D, 1, BC, NW, NS>;
+  auto kern = attn_fwd_dma_kernel<TT, D, BC, NW, WPE, NS, CAUSAL, VARLEN>;
   static bool attr_set = false;  // idempotent; a benign race between threads
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(p.n_work), dim3(C::NT), C::LDS_BYTES, st, p);
+  hipLaunchKernelGGL(kern, dim3(p.n_work), dim3(NW * 64), C::LDS_BYTES, st, p);
   return hipGetLastError();
 }
 
-// Tile configuration per head dimension: key rows per tile BC, waves per
-// workgroup NW (query rows BR = 32 NW), waves per SIMD the registers allow.
-template <int D> struct FwdTile;
-template <> struct FwdTile<64> { static constexpr int BC = 64, NW = 4, WPE = 2; };
-template <> struct FwdTile<128> { static constexpr int BC = 64, NW = 8, WPE = 2; };
-template <> struct FwdTile<256> { static constexpr int BC = 32, NW = 4, WPE = 1; };
+// Tile configuration per head dimension: key rows per tile, waves per
+// workgroup (query rows = 32 x waves), waves per SIMD, LDS ring depth.
+template <int D> struct DmaTile;
+template <> struct DmaTile<64> { static constexpr int BC = 64, NW = 8, WPE = 2, NS = 3; };
+template <> struct DmaTile<128> { static constexpr int BC = 64, NW = 8, WPE = 2, NS = 3; };
+template <> struct DmaTile<256> { static constexpr int BC = 32, NW = 4, WPE = 1, NS = 3; };
+
+template <typename TT, int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_dma_d(const FwdParams& p, hipStream_t st) {
+  using T = DmaTile<D>;
+  return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, CAUSAL, VARLEN>(p, st);
+}
 
 template <typename TT, bool CAUSAL, bool VARLEN>
-hipError_t launch_d(int d, const FwdParams& p, hipStream_t st) {
+hipError_t launch_dma_cv(int d, const FwdParams& p, hipStream_t st) {
   switch (d) {
-    case 64: return launch_one<TT, 64, FwdTile<64>::BC, FwdTile<64>::NW, FwdTile<64>::WPE, CAUSAL, VARLEN>(p, st);
-    case 128: return launch_one<TT, 128, FwdTile<128>::BC, FwdTile<128>::NW, FwdTile<128>::WPE, CAUSAL, VARLEN>(p, st);
-    case 256: return launch_one<TT, 256, FwdTile<256>::BC, FwdTile<256>::NW, FwdTile<256>::WPE, CAUSAL, VARLEN>(p, st);
+    case 64: return launch_dma_d<TT, 64, CAUSAL, VARLEN>(p, st);
+    case 128: return launch_dma_d<TT, 128, CAUSAL, VARLEN>(p, st);
+    case 256: return launch_dma_d<TT, 256, CAUSAL, VARLEN>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename TT>
-hipError_t launch_t(int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
-  if (causal) return varlen ? launch_d<TT, true, true>(d, p, st) : launch_d<TT, true, false>(d, p, st);
-  return varlen ? launch_d<TT, false, true>(d, p, st) : launch_d<TT, false, false>(d, p, st);
+hipError_t launch_dma_t(int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
+  if (causal) return varlen ? launch_dma_cv<TT, true, true>(d, p, st) : launch_dma_cv<TT, true, false>(d, p, st);
+  return varlen ? launch_dma_cv<TT, false, true>(d, p, st) : launch_dma_cv<TT, false, false>(d, p, st);
 }
 
 }  // namespace
@@ -412,15 +441,15 @@ hipError_t launch_t(int d, bool causal, bool varlen, const FwdParams& p, hipStre
 int fwd_block_rows(int dtype, int d) {
   if (dtype == 2) return fwd_fp8_block_rows();
   switch (d) {
-    case 64: return 32 * FwdTile<64>::NW;
-    case 128: return 32 * FwdTile<128>::NW;
-    default: return 32 * FwdTile<256>::NW;
+    case 64: return 32 * DmaTile<64>::NW;
+    case 128: return 32 * DmaTile<128>::NW;
+    default: return 32 * DmaTile<256>::NW;
   }
 }
 
 hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
-  if (dtype == 0) return launch_t<f16_t>(d, causal, varlen, p, st);
-  return launch_t<bf16_t>(d, causal, varlen, p, st);
+  if (dtype == 0) return launch_dma_t<f16_t>(d, causal, varlen, p, st);
+  return launch_dma_t<bf16_t>(d, causal, varlen, p, st);
 }
 
 }  // namespace attn
