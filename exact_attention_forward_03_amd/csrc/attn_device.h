@@ -70,11 +70,26 @@ __device__ __forceinline__ uint32_t residual2(TT t, uint32_t pk, float a, float 
 }
 
 // Reductions across the two halves of the wave (lane l and lane l ^ 32, the
-// two halves of a 32x32 MFMA column), through ds_bpermute.  (The compiler
-// folds the two results of v_permlane32_swap into one register when both
-// operands are the same value, so that instruction is not used here.)
-__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 32); }
+// two halves of a 32x32 MFMA column) with v_permlane32_swap, which exchanges
+// the upper 32 lanes of its first register with the lower 32 lanes of its
+// second: with both holding x, the first ends up with the lower half of x in
+// all 64 lanes and the second with the upper half.  The instruction is
+// written as inline asm because the compiler builtin loses its second result
+// (it returns the first one twice).  The s_nop pairs keep two wait states
+// between the swap and the VALU writes of its operands on either side.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
+}
 
 // Workgroups are dealt to the 8 XCDs round-robin (id % 8).  Remap the
 // hardware id so that consecutive work items land on the same XCD and share

@@ -7,8 +7,11 @@
 // online softmax, §3.1 one independent query block per workgroup; the
 // asynchronous producer of "FlashAttention-3", "Three techniques" §1):
 //
-// * NW waves per workgroup, each owning 32 query rows; with 8 waves two run
-//   on each SIMD, so one wave's softmax can overlap the other's MFMAs.
+// * NW waves per workgroup, each owning 32 query rows; two waves run on each
+//   SIMD (one 8-wave workgroup or two 4-wave workgroups per CU), so one
+//   wave's softmax can overlap the other's MFMAs.  The LDS fragment reads
+//   of each MFMA chain are issued a fixed number of MFMAs ahead, and a wave
+//   raises its issue priority while it runs an MFMA chain.
 // * K and V tiles go from HBM/L2 straight into LDS (global_load_lds_dwordx4:
 //   no staging registers, no VALU, no LDS write instructions), through a
 //   ring of NS buffers: the load of tile j+NS-1 is issued at step j, so a
@@ -42,6 +45,8 @@
 // * Workgroup order: the hardware id is remapped so that consecutive work
 //   items — the query tiles of one head — run on the same XCD and share its
 //   L2 copy of that head's K and V; causal query tiles run heaviest first.
+#include <stdlib.h>
+
 #include "attn_device.h"
 #include "attn_params.h"
 
@@ -52,7 +57,6 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr float kSplitBelowP = 8.0f;
-constexpr int kPreD = 4;  // LDS fragment reads in flight ahead of their MFMA
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maximum).
 template <int N>
@@ -73,7 +77,7 @@ struct PipeCfg {
   static constexpr int MB = BC / 32;         // 32-key blocks per tile
   static constexpr int DB = D / 32;          // 32-row blocks of O^T
   static constexpr int LOADS = TILEB / 1024; // 1 KiB direct-to-LDS loads per tile
-  static constexpr int LDS_BYTES = 2 * NS * TILEB; // K and V rings of NS buffers
+  static constexpr int LDS_BYTES = 2 * NS * TILEB;  // K and V rings of NS slots
   static constexpr int LPT = 2 * LOADS / NW;  // load instructions per wave per tile (K and V)
   static_assert(LOADS % NW == 0, "each wave issues the same number of tile loads");
   static_assert(CHUNKS >= 8, "row swizzle needs at least 8 chunks");
@@ -84,13 +88,26 @@ struct PipeCfg {
 // 16 rows, same logical chunk).
 template <int CHUNKS>
 __device__ __forceinline__ int k_chunk(int r, int ch) { return ch ^ (r & (CHUNKS >= 16 ? 15 : 7)); }
-// V rows: 4 consecutive rows x 2 neighbouring chunks (a transposing read of
-// 16 lanes) land on 8 different chunks.
-__device__ __forceinline__ int v_chunk(int r, int ch) { return ch ^ ((r & 3) << 1); }
+// V rows: a transposing read of 32 lanes covers 4 consecutive rows x 4
+// neighbouring chunks (two 16-lane groups, 2 chunks each); XOR-ing with
+// (row & 3) << 2 puts them on 16 different chunks.  Rows of 8 chunks (d = 64)
+// use (row & 3) << 1.
+template <int CHUNKS>
+__device__ __forceinline__ int v_chunk(int r, int ch) { return ch ^ ((r & 3) << (CHUNKS >= 16 ? 2 : 1)); }
 
-template <typename TT, int D, int BC, int NW, int WPE, int NS, bool CAUSAL, bool VARLEN>
+// Loop options (bit flags).  kOptPin: the LDS fragment reads are pinned
+// kPreD MFMAs ahead of their use by scheduling barriers (left alone, the
+// compiler keeps only two in flight and the MFMAs wait on LDS latency).
+// kOptPrio: a wave raises its issue priority while it runs an MFMA chain, so
+// the chain is not starved by the softmax VALU work of the other wave on the
+// SIMD.
+constexpr int kOptPin = 1, kOptPrio = 2;
+
+template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_dma_kernel(FwdParams p) {
+  constexpr bool PIN = OPT & kOptPin, PRIO = OPT & kOptPrio;
+  constexpr int kPreD = 4;  // LDS fragment reads in flight ahead of their MFMA
   constexpr int NQB = 1;
   using C = PipeCfg<D, NQB, BC, NW, NS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -135,7 +152,8 @@ attn_fwd_dma_kernel(FwdParams p) {
   const uint8_t* __restrict__ Vb = (const uint8_t*)p.v + k_row0 * D * 2;
 
   const int tid = threadIdx.x;
-  const int wv = tid >> 6, lane = tid & 63, c = lane & 31, hh = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
   const int qw0 = q0 + wv * C::QW;  // first query row of this wave
 
   // ---- Q fragments (B operands), one set per 32-row block ----------------
@@ -180,7 +198,7 @@ attn_fwd_dma_kernel(FwdParams p) {
       const int blk = wv * (C::LOADS / NW) + i;
       const int r = blk * RPB + lane / C::CHUNKS;
       const int key = min(kt * BC + r, k_len - 1);
-      const uint8_t* src = Vb + (int64_t)key * C::ROWB + v_chunk(r, lane % C::CHUNKS) * 16;
+      const uint8_t* src = Vb + (int64_t)key * C::ROWB + v_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
       __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsV + buf * C::TILEB + blk * 1024), 16, 0, 0);
     }
   };
@@ -199,28 +217,34 @@ attn_fwd_dma_kernel(FwdParams p) {
   auto compute_s = [&](int kbuf, f32x16_t (&s)[NQB][C::MB]) {
     const uint8_t* kb = ldsK + kbuf * C::TILEB;
     constexpr int N = C::MB * C::KS;
+    // step i: key block i % MB (alternating accumulators), k-step i / MB
     auto frag = [&](int i) {
-      const int r = (i / C::KS) * 32 + c;
-      return *(const uint4*)(kb + r * C::ROWB + k_chunk<C::CHUNKS>(r, 2 * (i % C::KS) + hh) * 16);
+      const int r = (i % C::MB) * 32 + c;
+      return *(const uint4*)(kb + r * C::ROWB + k_chunk<C::CHUNKS>(r, 2 * (i / C::MB) + hh) * 16);
     };
     uint4 fr[kPreD];
 #pragma unroll
     for (int i = 0; i < kPreD; ++i) fr[i] = frag(i);
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) s[0][mb] = f32x16_t{};
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
+    if (PIN) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const uint4 a = fr[i % kPreD];
+      s[0][i % C::MB] = mfma32(TT{}, a, qf[0][i / C::MB], s[0][i % C::MB]);
       if (i + kPreD < N) fr[i % kPreD] = frag(i + kPreD);
-      s[0][i / C::KS] = mfma32(TT{}, a, qf[0][i % C::KS], s[0][i / C::KS]);
+      if (PIN) __builtin_amdgcn_sched_barrier(0);
     }
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   // Masks, row max, M update (with the rare rescale of O and l).
   auto prepare = [&](int kt, f32x16_t (&s)[NQB][C::MB], float (&m_use)[NQB], bool& masked) {
     const int key0 = kt * BC;
     masked = (key0 + BC > k_len) || (CAUSAL && key0 + BC - 1 > qw0);
-    float tmax = -INFINITY;
+    // four independent max chains (short dependency chains)
+    float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     const int my_q = qw0 + c;
     if (masked) {
 #pragma unroll
@@ -230,15 +254,16 @@ attn_fwd_dma_kernel(FwdParams p) {
           const int key = key0 + mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
           const bool ok = key < k_len && (!CAUSAL || key <= my_q);
           s[0][mb][i] = ok ? s[0][mb][i] * cs : -INFINITY;
-          tmax = fmaxf(tmax, s[0][mb][i]);
+          t4[i & 3] = fmaxf(t4[i & 3], s[0][mb][i]);
         }
     } else {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[0][mb][i]);
-      tmax *= cs;
+        for (int i = 0; i < 16; ++i) t4[i & 3] = fmaxf(t4[i & 3], s[0][mb][i]);
     }
+    float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+    if (!masked) tmax *= cs;
     tmax = max_halves(tmax);
     const float m_new = fmaxf(M[0], __builtin_ceilf(tmax));
     if (__any(m_new > M[0])) {
@@ -255,14 +280,14 @@ attn_fwd_dma_kernel(FwdParams p) {
 
   // exponentials, exact row sum and P^T packing of one tile
   auto exps = [&](f32x16_t (&s)[NQB][C::MB], const float (&m_use)[NQB], bool masked, uint4 (&pf)[NQB][C::MB][2]) {
-    float rs = 0.f;
+    float r4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
     if (masked) {
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           s[0][mb][i] = __builtin_amdgcn_exp2f(s[0][mb][i] - m_use[0]);
-          rs += s[0][mb][i];
+          r4[i & 3] += s[0][mb][i];
         }
     } else {
 #pragma unroll
@@ -270,10 +295,10 @@ attn_fwd_dma_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           s[0][mb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][mb][i], cs, -m_use[0]));
-          rs += s[0][mb][i];
+          r4[i & 3] += s[0][mb][i];
         }
     }
-    l[0] += rs;
+    l[0] += (r4[0] + r4[1]) + (r4[2] + r4[3]);
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -292,29 +317,35 @@ attn_fwd_dma_kernel(FwdParams p) {
     const uint8_t* vb = ldsV + vbuf * C::TILEB;
     const int g = (lane >> 4) & 1, s4 = lane & 15;
     constexpr int N = C::DB * 2 * C::MB;
+    // step i: output block i % DB (alternating accumulators), 16-key step i / DB
     auto frag = [&](int i) {
-      const int db = i / (2 * C::MB), k16 = i % (2 * C::MB);
+      const int db = i % C::DB, k16 = i / C::DB;
       const int col = db * 32 + 16 * g + 4 * (s4 & 3);  // element column read by this lane
       const int ch = col >> 3, half = (col >> 2) & 1;
       const int r0 = k16 * 16 + 4 * hh + (s4 >> 2);
       const int r1 = r0 + 8;
       const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4_t*)(vb + r0 * C::ROWB + v_chunk(r0, ch) * 16 + half * 8));
+          (__attribute__((address_space(3))) s16x4_t*)(vb + r0 * C::ROWB + v_chunk<C::CHUNKS>(r0, ch) * 16 + half * 8));
       const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4_t*)(vb + r1 * C::ROWB + v_chunk(r1, ch) * 16 + half * 8));
+          (__attribute__((address_space(3))) s16x4_t*)(vb + r1 * C::ROWB + v_chunk<C::CHUNKS>(r1, ch) * 16 + half * 8));
       const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
       return make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
     };
-    uint4 fr[kPreD];
+    constexpr int PV_PRE = kPreD;  // two LDS reads each
+    uint4 fr[PV_PRE];
 #pragma unroll
-    for (int i = 0; i < kPreD; ++i) fr[i] = frag(i);
+    for (int i = 0; i < PV_PRE; ++i) fr[i] = frag(i);
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
+    if (PIN) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const uint4 a = fr[i % kPreD];
-      if (i + kPreD < N) fr[i % kPreD] = frag(i + kPreD);
-      const int db = i / (2 * C::MB), k16 = i % (2 * C::MB);
+      const uint4 a = fr[i % PV_PRE];
+      const int db = i % C::DB, k16 = i / C::DB;
       oacc[0][db] = mfma32(TT{}, a, pp[0][k16 >> 1][k16 & 1], oacc[0][db]);
+      if (i + PV_PRE < N) fr[i % PV_PRE] = frag(i + PV_PRE);
+      if (PIN) __builtin_amdgcn_sched_barrier(0);
     }
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   auto residual = [&](f32x16_t (&s)[NQB][C::MB], const uint4 (&pf)[NQB][C::MB][2], uint4 (&pl)[NQB][C::MB][2]) {
@@ -331,44 +362,48 @@ attn_fwd_dma_kernel(FwdParams p) {
       }
   };
 
-  // prologue: tiles 0 .. NS-2 in flight
+  // Softmax and second product of tile kt held in s (its K/V ring slot `slot`).
+  auto softmax_pv = [&](int kt, int slot, f32x16_t (&s)[NQB][C::MB]) {
+    float m_use[NQB];
+    bool masked = false;
+    uint4 pf[NQB][C::MB][2];
+    prepare(kt, s, m_use, masked);
+    exps(s, m_use, masked, pf);
+    const bool split = __any(l[0] < kSplitBelowP);
+    pv_pass(slot, pf);
+    if (split) {
+      uint4 pl[NQB][C::MB][2];
+      residual(s, pf, pl);
+      pv_pass(slot, pl);
+    }
+  };
+
+  // prologue: tiles 0 .. NS-2 in flight (tile j in ring slot j % NS)
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
     if (j < n_kt) {
       load_k(j, j);
       load_v(j, j);
     }
-
-  int buf = 0;  // ring slot of tile kt
+  int slot = 0;  // ring slot of tile kt
   for (int kt = 0; kt < n_kt; ++kt) {
     // tile kt must have landed (its loads are the oldest in flight); later
     // tiles may still be on their way
     if (kt + NS - 2 < n_kt) wait_vm<(NS - 2) * C::LPT>();
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // refill the slot that tile kt-1 used (every wave is past it now)
+    // refill the slot tile kt-1 used (every wave is past it now)
     if (kt + NS - 1 < n_kt) {
-      const int fb = (buf == 0) ? NS - 1 : buf - 1;
-      load_k(kt + NS - 1, fb);
-      load_v(kt + NS - 1, fb);
+      const int fs = (slot == 0) ? NS - 1 : slot - 1;
+      load_k(kt + NS - 1, fs);
+      load_v(kt + NS - 1, fs);
     }
     if (kt < wave_kt) {
       f32x16_t s[NQB][C::MB];
-      float m_use[NQB];
-      bool masked = false;
-      uint4 pf[NQB][C::MB][2];
-      compute_s(buf, s);
-      prepare(kt, s, m_use, masked);
-      exps(s, m_use, masked, pf);
-      const bool split = __any(l[0] < kSplitBelowP);
-      pv_pass(buf, pf);
-      if (split) {
-        uint4 pl[NQB][C::MB][2];
-        residual(s, pf, pl);
-        pv_pass(buf, pl);
-      }
+      compute_s(slot, s);
+      softmax_pv(kt, slot, s);
     }
-    buf = (buf + 1 == NS) ? 0 : buf + 1;
+    slot = (slot + 1 == NS) ? 0 : slot + 1;
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -393,10 +428,10 @@ attn_fwd_dma_kernel(FwdParams p) {
   }
 }
 
-template <typename TT, int D, int BC, int NW, int WPE, int NS, bool CAUSAL, bool VARLEN>
+template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN>
 hipError_t launch_dma_one(const FwdParams& p, hipStream_t st) {
   using C = PipeCfg<D, 1, BC, NW, NS>;
-  auto kern = attn_fwd_dma_kernel<TT, D, BC, NW, WPE, NS, CAUSAL, VARLEN>;
+  auto kern = attn_fwd_dma_kernel<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN>;
   static bool attr_set = false;  // idempotent; a benign race between threads
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
@@ -407,17 +442,50 @@ hipError_t launch_dma_one(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile configuration per head dimension: key rows per tile, waves per
-// workgroup (query rows = 32 x waves), waves per SIMD, LDS ring depth.
-template <int D> struct DmaTile;
-template <> struct DmaTile<64> { static constexpr int BC = 64, NW = 8, WPE = 2, NS = 3; };
-template <> struct DmaTile<128> { static constexpr int BC = 64, NW = 8, WPE = 2, NS = 3; };
-template <> struct DmaTile<256> { static constexpr int BC = 32, NW = 4, WPE = 1, NS = 3; };
+// Tile configuration per head dimension and masking: key rows per tile,
+// waves per workgroup (query rows = 32 x waves), waves per SIMD, LDS ring
+// depth and loop options.  Causal attention at d = 128 runs 4-wave
+// workgroups, two per CU: their diagonal tiles and early exits then do not
+// hold a whole 8-wave workgroup at its barriers.
+template <int D, bool CAUSAL> struct DmaTile;
+template <bool CAUSAL> struct DmaTile<64, CAUSAL> {
+  static constexpr int BC = 64, NW = 8, WPE = 2, NS = 3, OPT = kOptPin | kOptPrio;
+};
+template <> struct DmaTile<128, false> { static constexpr int BC = 64, NW = 8, WPE = 2, NS = 3, OPT = kOptPin | kOptPrio; };
+template <> struct DmaTile<128, true> { static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
+template <bool CAUSAL> struct DmaTile<256, CAUSAL> {
+  static constexpr int BC = 32, NW = 4, WPE = 1, NS = 3, OPT = kOptPin;
+};
+
+// Measurement switch read once from the environment: ATTN_TUNE_CFG selects
+// alternative loop options for d = 256 and non-causal d = 128 (same
+// workgroup shape, so the grid does not change); 0 or unset is the default.
+int tune_cfg() {
+  static const int v = [] {
+    const char* e = getenv("ATTN_TUNE_CFG");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
 
 template <typename TT, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_dma_d(const FwdParams& p, hipStream_t st) {
-  using T = DmaTile<D>;
-  return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, CAUSAL, VARLEN>(p, st);
+  using T = DmaTile<D, CAUSAL>;
+  if constexpr (D == 128 && !CAUSAL) {
+    switch (tune_cfg()) {
+      case 1: return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, 0, CAUSAL, VARLEN>(p, st);
+      case 2: return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, kOptPin, CAUSAL, VARLEN>(p, st);
+      default: break;
+    }
+  }
+  if constexpr (D == 256) {
+    switch (tune_cfg()) {
+      case 1: return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, kOptPin | kOptPrio, CAUSAL, VARLEN>(p, st);
+      case 2: return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, 0, CAUSAL, VARLEN>(p, st);
+      default: break;
+    }
+  }
+  return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, T::OPT, CAUSAL, VARLEN>(p, st);
 }
 
 template <typename TT, bool CAUSAL, bool VARLEN>
@@ -438,12 +506,12 @@ hipError_t launch_dma_t(int d, bool causal, bool varlen, const FwdParams& p, hip
 
 }  // namespace
 
-int fwd_block_rows(int dtype, int d) {
+int fwd_block_rows(int dtype, int d, bool causal) {
   if (dtype == 2) return fwd_fp8_block_rows();
   switch (d) {
-    case 64: return 32 * DmaTile<64>::NW;
-    case 128: return 32 * DmaTile<128>::NW;
-    default: return 32 * DmaTile<256>::NW;
+    case 64: return 32 * DmaTile<64, false>::NW;
+    case 128: return causal ? 32 * DmaTile<128, true>::NW : 32 * DmaTile<128, false>::NW;
+    default: return 32 * DmaTile<256, false>::NW;
   }
 }
 

@@ -35,7 +35,7 @@ struct PrepParams {
 };
 
 // Query rows per workgroup of each kernel variant (sizes the grid).
-int fwd_block_rows(int dtype, int d);
+int fwd_block_rows(int dtype, int d, bool causal);
 int fwd_fp8_block_rows();
 
 hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st);
