@@ -271,7 +271,7 @@ def main():
                    "wall_s_timed": round(wall, 4)},
         "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(),
-                     "kernel": "attn_fwd_kernel<bf16, d128, non-causal>",
+                     "kernel": "attn_fwd_dma_kernel<bf16, d=128, non-causal>",
                      "mean_launch_ms": round(float(np.mean(nc_ms)), 4),
                      "causal_launch_ms": round(float(np.mean(c_ms)), 4)},
     }
