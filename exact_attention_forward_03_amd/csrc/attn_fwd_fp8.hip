@@ -8,8 +8,8 @@
 // Output O is bfloat16, lse fp32.
 //
 // The kernel has the shape of the fp16/bf16 one (one workgroup per 32*NW
-// query rows, K/V tiles double buffered in LDS, S^T = K Q^T so P stays in
-// registers), with these differences:
+// query rows, K/V tiles streamed from global memory straight into a ring of
+// LDS slots, S^T = K Q^T so P stays in registers), with these differences:
 //   * 32x32x64 e4m3 MFMA, fp32 accumulation; key tiles of 128 rows, so each
 //     tile has exactly one K scale and one V scale;
 //   * scores t = acc * (scale log2 e * s_q * s_k) in base 2; M = ceil(max t)
@@ -18,39 +18,47 @@
 //     max_tiles s_v: the V tile's scale is folded into the exponent, so the
 //     PV product needs no per-tile correction of O and the codes stay <= 256;
 //     l sums the unrounded 2^(t - M) and O = (max s_v) 2^-8 sum P8 v8 / l;
-//   * V is transposed byte-wise into LDS in the key order of P's registers.
+//   * V stays row-major in LDS; the V^T operand comes from the 8-bit
+//     transposing LDS read (ds_read_b64_tr_b8: within a 16-lane group, lane
+//     i receives byte i % 8 of the 8-byte pieces read by lanes 2j + i / 8),
+//     so each lane reads the 8 keys of one V column that its P bytes need.
 #include "attn_device.h"
 #include "attn_params.h"
 
 namespace attn {
 namespace {
 
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 constexpr int kFp8D = 128;
-constexpr int kFp8BC = 128;
+constexpr int kFp8BC = 128;   // key rows per tile (= rows per scale)
 constexpr int kFp8NW = 8;
-constexpr int kScaleRows = 128;
+constexpr int kFp8NS = 3;     // LDS ring slots
+constexpr int kFp8Pre = 4;    // K fragments (two reads each) in flight ahead of their MFMA
+constexpr int kFp8PvPre = 3;  // V^T fragments (four reads each): at most 12 LDS reads in flight,
+                              // within what the 4-bit lgkmcnt counter can track
+constexpr int kRowB = kFp8D;                  // bytes per K/V row
+constexpr int kTileB = kFp8BC * kRowB;        // bytes per K or V tile
+constexpr int kLoads = kTileB / 1024;         // 1 KiB direct-to-LDS loads per tile
+constexpr int kLds = 2 * kFp8NS * kTileB;
 
-// Byte position of key k (0..127) inside a transposed V row: the PV MFMA
-// takes 64 keys per step; lane half h, slot j of step g holds key
-// 64 g + 32 (j / 16) + 8 ((j % 16) / 4) + 4 h + j % 4.
-__device__ __forceinline__ int vt8_pos(int k) {
-  const int g = k >> 6, kk = k & 63, blk = kk >> 5, k32 = kk & 31;
-  const int h = (k32 >> 2) & 1;
-  const int j = 16 * blk + 4 * (k32 >> 3) + (k32 & 3);
-  return 64 * g + 32 * h + j;
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maximum).
+template <int N>
+__device__ __forceinline__ void fp8_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// 4 rows x 4 bytes -> 4 columns x 4 bytes (byte transpose of a 4x4 block).
-__device__ __forceinline__ void transpose4x4(const uint32_t r[4], uint32_t out[4]) {
-  const uint32_t t01l = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
-  const uint32_t t23l = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
-  const uint32_t t01h = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
-  const uint32_t t23h = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
-  out[1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
-  out[2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
-}
+// Physical 16-byte chunk (of 8 per row) of logical chunk ch in row r.
+// K fragment reads: 16 lanes read 16 consecutive rows at one logical chunk;
+// with 128-byte rows, rows r and r+1 share a bank line, so the chunk is
+// XOR-ed with bits 1..3 of the row: the 16 reads hit 16 different 16-byte
+// bank slots.  V transposing reads: 32 lanes read 8 rows {0..3, 8..11} + 4h
+// (plus a multiple of 16) at two neighbouring chunks; XOR-ing with
+// 2 * bit1 + 4 * bit3 of the row spreads them over 16 slots.
+__device__ __forceinline__ int k8_chunk(int r, int ch) { return ch ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int v8_chunk(int r, int ch) { return ch ^ (((r >> 1) & 1) << 1) ^ (((r >> 3) & 1) << 2); }
 
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -58,21 +66,18 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return (uint32_t)w;
 }
 
-template <int NW, bool CAUSAL>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
+template <bool CAUSAL>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kFp8NW * 64, kFp8NW * 64), amdgpu_waves_per_eu(2, 2)))
 attn_fwd_fp8_kernel(FwdParams p) {
-  constexpr int D = kFp8D, BC = kFp8BC;
-  constexpr int BR = NW * 32, NT = NW * 64;
-  constexpr int KP = D + 16;    // K row pitch in LDS (bytes)
-  constexpr int VP = BC + 16;   // V^T row pitch in LDS (bytes)
-  constexpr int KBUF = BC * KP, VBUF = D * VP;
+  constexpr int D = kFp8D, BC = kFp8BC, NW = kFp8NW, NS = kFp8NS;
+  constexpr int BR = NW * 32;
   constexpr int KS = D / 64;    // MFMA k-steps of S^T
   constexpr int MB = BC / 32;   // 32-key blocks per tile
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int PG = BC / 64;   // MFMA k-steps of O^T (64 keys each)
-  constexpr int KCH = BC * D / 16 / NT;          // 16-byte K chunks per thread
-  constexpr int VCH = (BC / 4) * (D / 4) / NT;   // 4x4-byte V blocks per thread
-  static_assert(KCH * NT * 16 == BC * D && VCH * NT * 16 == BC * D, "tile split");
+  constexpr int LPW = kLoads / NW;  // loads per wave per K (or V) tile
+  constexpr int LPT = 2 * LPW;      // per tile, K and V
+  static_assert(kLoads % NW == 0, "each wave issues the same number of tile loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
 
   const int work = xcd_remap(blockIdx.x, p.n_work);
@@ -82,8 +87,8 @@ attn_fwd_fp8_kernel(FwdParams p) {
   const int q_len = p.Nq, k_len = p.Nk;
   const int q0 = qt * BR;
   const int64_t q_row0 = (int64_t)head * p.Nq, k_row0 = (int64_t)head * p.Nk;
-  const int nqs = (q_len + kScaleRows - 1) / kScaleRows;
-  const int nks = (k_len + kScaleRows - 1) / kScaleRows;
+  const int nqs = (q_len + BC - 1) / BC;
+  const int nks = (k_len + BC - 1) / BC;
   const float* __restrict__ sk = p.k_scale + (int64_t)head * nks;
   const float* __restrict__ sv = p.v_scale + (int64_t)head * nks;
 
@@ -92,7 +97,8 @@ attn_fwd_fp8_kernel(FwdParams p) {
   const uint8_t* __restrict__ Vp = (const uint8_t*)p.v + k_row0 * D;
 
   const int tid = threadIdx.x;
-  const int wv = tid >> 6, lane = tid & 63, c = lane & 31, hh = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
   const int qw0 = q0 + wv * 32;
   const int my_q = qw0 + c;
   const bool q_ok = my_q < q_len;
@@ -104,7 +110,7 @@ attn_fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) sv_max = fmaxf(sv_max, __shfl_xor(sv_max, s));
   const float lsv_max = sv_max > 0.f ? __log2f(sv_max) : 0.f;
-  const float sq = wave_live ? p.q_scale[(int64_t)head * nqs + qw0 / kScaleRows] : 0.f;
+  const float sq = wave_live ? p.q_scale[(int64_t)head * nqs + qw0 / BC] : 0.f;
 
   // Q fragments (B operand of S^T): row my_q, bytes [64 ks + 32 hh, +32)
   uint4 qf[KS][2];
@@ -124,87 +130,130 @@ attn_fwd_fp8_kernel(FwdParams p) {
   else if (CAUSAL) wave_kt = min(n_kt, (min(qw0 + 31, q_len - 1)) / BC + 1);
 
   uint8_t* const ldsK = lds8;
-  uint8_t* const ldsV = lds8 + 2 * KBUF;
-  uint4 kr[KCH];
-  uint32_t vr[VCH][4];
-
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + i * NT;
-      const int row = ch / (D / 16), col = (ch % (D / 16)) * 16;
-      const int key = kt * BC + row;
-      kr[i] = key < k_len ? *(const uint4*)(Kp + (int64_t)key * D + col) : zero4();
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int ch = tid + i * NT;
-      const int kg = ch / (D / 4), dg = ch % (D / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kt * BC + 4 * kg + r;
-        vr[i][r] = key < k_len ? *(const uint32_t*)(Vp + (int64_t)key * D + 4 * dg) : 0u;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint8_t* kb = ldsK + buf * KBUF;
-    uint8_t* vb = ldsV + buf * VBUF;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = tid + i * NT;
-      const int row = ch / (D / 16), col = (ch % (D / 16)) * 16;
-      *(uint4*)(kb + row * KP + col) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int ch = tid + i * NT;
-      const int kg = ch / (D / 4), dg = ch % (D / 4);
-      uint32_t cols[4];
-      transpose4x4(vr[i], cols);
-      uint8_t* dst = vb + (4 * dg) * VP + vt8_pos(4 * kg);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *(uint32_t*)(dst + j * VP) = cols[j];
-    }
-  };
-
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  uint8_t* const ldsV = lds8 + NS * kTileB;
 
   float M = -INFINITY, l = 0.f;
   f32x16_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
 
+  // Direct-to-LDS load of one tile into ring slot `buf`: the wave's i-th
+  // instruction fills 1 KiB block wv * LPW + i (8 rows); lane l writes
+  // physical chunk l % 8 of row 8 * block + l / 8 and fetches the logical
+  // chunk stored there.  Rows past the end of the keys re-read the last key
+  // (finite codes, masked).
+  auto load_tile = [&](int kt, int buf) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = wv * LPW + i;
+      const int r = blk * 8 + (lane >> 3);
+      const int key = min(kt * BC + r, k_len - 1);
+      const uint8_t* srck = Kp + (int64_t)key * kRowB + k8_chunk(r, lane & 7) * 16;
+      __builtin_amdgcn_global_load_lds(srck, (lds_void_t*)(ldsK + buf * kTileB + blk * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = wv * LPW + i;
+      const int r = blk * 8 + (lane >> 3);
+      const int key = min(kt * BC + r, k_len - 1);
+      const uint8_t* srcv = Vp + (int64_t)key * kRowB + v8_chunk(r, lane & 7) * 16;
+      __builtin_amdgcn_global_load_lds(srcv, (lds_void_t*)(ldsV + buf * kTileB + blk * 1024), 16, 0, 0);
+    }
+  };
+
+  // S^T of the tile in slot kbuf: step i = (32-key block i % MB, k-step i / MB)
+  auto compute_s = [&](int kbuf, f32x16_t (&s)[MB]) {
+    const uint8_t* kb = ldsK + kbuf * kTileB;
+    constexpr int N = MB * KS;
+    auto frag = [&](int i, uint4 (&f)[2]) {
+      const int r = (i % MB) * 32 + c;
+      const int ch = 4 * (i / MB) + 2 * hh;
+      f[0] = *(const uint4*)(kb + r * kRowB + k8_chunk(r, ch) * 16);
+      f[1] = *(const uint4*)(kb + r * kRowB + k8_chunk(r, ch + 1) * 16);
+    };
+    uint4 fr[kFp8Pre][2];
+#pragma unroll
+    for (int i = 0; i < kFp8Pre; ++i) frag(i, fr[i]);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) s[mb] = f32x16_t{};
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint4 a0 = fr[i % kFp8Pre][0], a1 = fr[i % kFp8Pre][1];
+      s[i % MB] = mfma32_fp8(a0, a1, qf[i / MB][0], qf[i / MB][1], s[i % MB]);
+      if (i + kFp8Pre < N) frag(i + kFp8Pre, fr[i % kFp8Pre]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // O^T += V^T P^T for the tile in slot vbuf.  Step i = (output block
+  // i % DB, 64-key step i / DB).  MFMA k-index 32 h + j of lane half h holds
+  // key 64 g + 32 (j / 16) + 8 ((j % 16) / 4) + 4 h + j % 4 (the order of P's
+  // registers); the four transposing reads m = 0..3 of a fragment deliver
+  // k-indices 8m .. 8m+7.  In 16-lane group G (h = G / 2), source lane s
+  // reads row key(8m + s / 2) at columns 32 db + 16 (G % 2) + 8 (s % 2) ..+8.
+  auto pv_pass = [&](int vbuf, const uint4 (&pp)[PG][2]) {
+    const uint8_t* vb = ldsV + vbuf * kTileB;
+    const int G = lane >> 4, s16 = lane & 15, b = s16 >> 1;
+    constexpr int N = DB * PG;
+    auto frag = [&](int i, uint4 (&f)[2]) {
+      const int db = i % DB, g = i / DB;
+      const int ch = 2 * db + (G & 1);
+      uint32_t w[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int r = 64 * g + 32 * (m >> 1) + 16 * (m & 1) + 8 * (b >> 2) + 4 * hh + (b & 3);
+        const i32x2_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t*)(vb + r * kRowB + v8_chunk(r, ch) * 16 + 8 * (s16 & 1)));
+        w[2 * m] = (uint32_t)x[0];
+        w[2 * m + 1] = (uint32_t)x[1];
+      }
+      f[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      f[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    };
+    uint4 fr[kFp8PvPre][2];
+#pragma unroll
+    for (int i = 0; i < kFp8PvPre; ++i) frag(i, fr[i]);
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int db = i % DB, g = i / DB;
+      const uint4 a0 = fr[i % kFp8PvPre][0], a1 = fr[i % kFp8PvPre][1];
+      oacc[db] = mfma32_fp8(a0, a1, pp[g][0], pp[g][1], oacc[db]);
+      if (i + kFp8PvPre < N) frag(i + kFp8PvPre, fr[i % kFp8PvPre]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // prologue: tiles 0 .. NS-2 in flight (tile j in ring slot j % NS)
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_kt) load_tile(j, j);
+
+  int slot = 0;  // ring slot of tile kt
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (kt + NS - 2 < n_kt) fp8_wait_vm<(NS - 2) * LPT>();
+    else __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // refill the slot tile kt-1 used (every wave is past it now)
+    if (kt + NS - 1 < n_kt) load_tile(kt + NS - 1, slot == 0 ? NS - 1 : slot - 1);
 
     if (kt < wave_kt) {
-      const uint8_t* kb = ldsK + buf * KBUF;
-      const uint8_t* vb = ldsV + buf * VBUF;
       const float cs = p.c * sq * sk[kt];
       const float svt = sv[kt];
       // log2 of 2^8 w: P codes are e4m3(2^(t - M) * 2^8 * s_v / max s_v)
       const float bias = 8.f + (svt > 0.f ? __log2f(svt) - lsv_max : -INFINITY);
 
       f32x16_t s[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        s[mb] = f32x16_t{};
-        const uint8_t* krow = kb + (mb * 32 + c) * KP + 32 * hh;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[mb] = mfma32_fp8(*(const uint4*)(krow + 64 * ks), *(const uint4*)(krow + 64 * ks + 16), qf[ks][0],
-                             qf[ks][1], s[mb]);
-      }
+      compute_s(slot, s);
 
       const int key0 = kt * BC;
       const bool need_mask = (key0 + BC > k_len) || (CAUSAL && key0 + BC - 1 > qw0);
-      float tmax = -INFINITY;
+      float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       if (need_mask) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -213,15 +262,16 @@ attn_fwd_fp8_kernel(FwdParams p) {
             const int key = key0 + mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
             const bool ok = key < k_len && (!CAUSAL || key <= my_q);
             s[mb][i] = ok ? s[mb][i] * cs : -INFINITY;
-            tmax = fmaxf(tmax, s[mb][i]);
+            t4[i & 3] = fmaxf(t4[i & 3], s[mb][i]);
           }
       } else {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
-        tmax *= cs;  // scales are >= 0
+          for (int i = 0; i < 16; ++i) t4[i & 3] = fmaxf(t4[i & 3], s[mb][i]);
       }
+      float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+      if (!need_mask) tmax *= cs;  // scales are >= 0
       tmax = max_halves(tmax);
       const float m_new = fmaxf(M, __builtin_ceilf(tmax));
       if (__any(m_new > M)) {
@@ -236,14 +286,14 @@ attn_fwd_fp8_kernel(FwdParams p) {
       const float m_use = (M == -INFINITY) ? 0.f : M;
       const float off = bias - m_use;
 
-      float rs = 0.f;
+      float r4[4] = {0.f, 0.f, 0.f, 0.f};
       if (need_mask) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             s[mb][i] = __builtin_amdgcn_exp2f(s[mb][i] + off);
-            rs += s[mb][i];
+            r4[i & 3] += s[mb][i];
           }
       } else {
 #pragma unroll
@@ -251,31 +301,27 @@ attn_fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             s[mb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][i], cs, off));
-            rs += s[mb][i];
+            r4[i & 3] += s[mb][i];
           }
       }
+      const float rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
       // rs sums 2^(t - M) * 2^bias; l keeps the unweighted sum
       l += bias == -INFINITY ? 0.f : rs * __builtin_amdgcn_exp2f(-bias);
 
-      // P codes: step g takes key blocks 2g (slots 0..15) and 2g+1 (slots 16..31)
+      // P codes: step g takes key blocks 2g (bytes 0..15) and 2g+1 (16..31)
+      uint4 pp[PG][2];
 #pragma unroll
       for (int g = 0; g < PG; ++g) {
         const f32x16_t& a = s[2 * g];
-        const f32x16_t& b = s[2 * g + 1];
-        const uint4 p0 = make_uint4(pack4_e4m3(a[0], a[1], a[2], a[3]), pack4_e4m3(a[4], a[5], a[6], a[7]),
-                                    pack4_e4m3(a[8], a[9], a[10], a[11]), pack4_e4m3(a[12], a[13], a[14], a[15]));
-        const uint4 p1 = make_uint4(pack4_e4m3(b[0], b[1], b[2], b[3]), pack4_e4m3(b[4], b[5], b[6], b[7]),
-                                    pack4_e4m3(b[8], b[9], b[10], b[11]), pack4_e4m3(b[12], b[13], b[14], b[15]));
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint8_t* vrow = vb + (db * 32 + c) * VP + 64 * g + 32 * hh;
-          oacc[db] = mfma32_fp8(*(const uint4*)vrow, *(const uint4*)(vrow + 16), p0, p1, oacc[db]);
-        }
+        const f32x16_t& bb = s[2 * g + 1];
+        pp[g][0] = make_uint4(pack4_e4m3(a[0], a[1], a[2], a[3]), pack4_e4m3(a[4], a[5], a[6], a[7]),
+                              pack4_e4m3(a[8], a[9], a[10], a[11]), pack4_e4m3(a[12], a[13], a[14], a[15]));
+        pp[g][1] = make_uint4(pack4_e4m3(bb[0], bb[1], bb[2], bb[3]), pack4_e4m3(bb[4], bb[5], bb[6], bb[7]),
+                              pack4_e4m3(bb[8], bb[9], bb[10], bb[11]), pack4_e4m3(bb[12], bb[13], bb[14], bb[15]));
       }
+      pv_pass(slot, pp);
     }
-
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
-    __syncthreads();
+    slot = (slot + 1 == NS) ? 0 : slot + 1;
   }
 
   const float l_tot = sum_halves(l);
@@ -294,17 +340,16 @@ attn_fwd_fp8_kernel(FwdParams p) {
   }
 }
 
-template <int NW, bool CAUSAL>
+template <bool CAUSAL>
 hipError_t launch_fp8(const FwdParams& p, hipStream_t st) {
-  constexpr int lds = 2 * (kFp8BC * (kFp8D + 16) + kFp8D * (kFp8BC + 16));
-  auto kern = attn_fwd_fp8_kernel<NW, CAUSAL>;
-  static bool attr_set = false;
+  auto kern = attn_fwd_fp8_kernel<CAUSAL>;
+  static bool attr_set = false;  // idempotent; a benign race between threads
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(p.n_work), dim3(NW * 64), lds, st, p);
+  hipLaunchKernelGGL(kern, dim3(p.n_work), dim3(kFp8NW * 64), kLds, st, p);
   return hipGetLastError();
 }
 
@@ -314,7 +359,7 @@ int fwd_fp8_block_rows() { return 32 * kFp8NW; }
 
 hipError_t launch_fwd_fp8(int d, bool causal, const FwdParams& p, hipStream_t st) {
   if (d != kFp8D) return hipErrorInvalidValue;
-  return causal ? launch_fp8<kFp8NW, true>(p, st) : launch_fp8<kFp8NW, false>(p, st);
+  return causal ? launch_fp8<true>(p, st) : launch_fp8<false>(p, st);
 }
 
 }  // namespace attn
