@@ -11,7 +11,8 @@
 // (a, b) -> (a + b, a - b) per bit of the column index: the three low bits are
 // done inside the lane, the others between lanes (lane ^ 1, ^ 2, ...).
 // Then the tile's amax, s = amax / 448 (1 if the tile is all zero), and
-// code = e4m3(x' / s), rounded to nearest even in fp32.
+// code = e4m3(x' / s): x' / s correctly rounded to fp32, then rounded to
+// nearest even e4m3.
 //
 // Per-tensor mode runs three launches: the tile amaxes into the scale array,
 // one workgroup turning their maximum into s for every entry, and the
@@ -50,11 +51,44 @@ __device__ __forceinline__ void load8(const uint16_t* src, float v[8], f16_t) {
   }
 }
 
+// v from lane (lane ^ S) with S < 16, by DPP lane permutes inside 16-lane
+// rows (VALU only): XOR 1 and XOR 2 are quad permutations; the half-row
+// mirror maps lane i to i ^ 7 and the row mirror to i ^ 15, so XOR 4 =
+// mirror-half then XOR 3, and XOR 8 = mirror then mirror-half.  Larger
+// strides go through ds_bpermute.
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppQuadXor3 = 0x1B;
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+template <int S>
+__device__ __forceinline__ float xor_lanes(float v) {
+  if constexpr (S == 1) return dpp<kDppQuadXor1>(v);
+  else if constexpr (S == 2) return dpp<kDppQuadXor2>(v);
+  else if constexpr (S == 4) return dpp<kDppQuadXor3>(dpp<kDppRowHalfMirror>(v));
+  else if constexpr (S == 8) return dpp<kDppRowHalfMirror>(dpp<kDppRowMirror>(v));
+  else return __shfl_xor(v, S);
+}
+
 // Four fp32 values -> four e4m3 codes in one dword (round to nearest even).
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
+}
+
+// One butterfly stage between lanes cl and cl ^ S (no-op when S >= L).
+template <int S, int L>
+__device__ __forceinline__ void lane_stage(float (&v)[8], int cl) {
+  if constexpr (S < L) {
+    const float sg = (cl & S) ? -1.f : 1.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float o = xor_lanes<S>(v[j]);
+      v[j] = __builtin_fmaf(sg, v[j], o);  // lower: o + v, upper: o - v (exact: a sign flip)
+    }
+  }
 }
 
 __device__ __forceinline__ float block_max(float v, float* red) {
@@ -118,13 +152,11 @@ __global__ void __launch_bounds__(kPrepThreads) fp8_prep_kernel(PrepParams p) {
             v[ps][j + h] = a - b;
           }
       // butterflies on the lane bits: the lower partner keeps a + b, the upper a - b
-#pragma unroll
-      for (int s = 1; s < L; s <<= 1)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float o = __shfl_xor(v[ps][j], s);
-          v[ps][j] = (cl & s) ? (o - v[ps][j]) : (v[ps][j] + o);
-        }
+      lane_stage<1, L>(v[ps], cl);
+      lane_stage<2, L>(v[ps], cl);
+      lane_stage<4, L>(v[ps], cl);
+      lane_stage<8, L>(v[ps], cl);
+      lane_stage<16, L>(v[ps], cl);
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[ps][j] *= norm;
     }
@@ -146,13 +178,29 @@ __global__ void __launch_bounds__(kPrepThreads) fp8_prep_kernel(PrepParams p) {
     if (tid == 0) p.scale[sidx] = s;
   }
 
+  // x / s correctly rounded, by Markstein's division: with y = RN(1/s) (one
+  // IEEE division per thread), q = RN(x y), r = x - q s (exact with an fma)
+  // and RN(q + r y) = RN(x / s).  Tiles with a tiny scale, where r could
+  // underflow, use the IEEE division itself.
+  const float y = 1.0f / s;
+  const bool markstein = s >= 0x1p-80f;
+  auto quot = [&](float x) {
+    const float q = x * y;
+    return __builtin_fmaf(__builtin_fmaf(-q, s, x), y, q);
+  };
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
     const int row = tile * kTileRows + ps * RPP + rl;
     if (row < p.N) {
-      uint2 w;
-      w.x = pack4_e4m3(v[ps][0] / s, v[ps][1] / s, v[ps][2] / s, v[ps][3] / s);
-      w.y = pack4_e4m3(v[ps][4] / s, v[ps][5] / s, v[ps][6] / s, v[ps][7] / s);
+      float z[8];
+      if (markstein) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[j] = quot(v[ps][j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z[j] = v[ps][j] / s;
+      }
+      const uint2 w = make_uint2(pack4_e4m3(z[0], z[1], z[2], z[3]), pack4_e4m3(z[4], z[5], z[6], z[7]));
       *(uint2*)(p.x8 + (base + row) * D + cl * 8) = w;
     }
   }

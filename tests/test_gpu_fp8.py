@@ -64,6 +64,22 @@ def test_prep_no_rotation_bitwise(gpu_lib, in_dtype, d, per_tensor):
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
 
 
+@pytest.mark.parametrize("magnitude", [1e-32, 1e-20, 3e4])
+def test_prep_scale_range_bitwise(gpu_lib, magnitude):
+    """Tiles whose scale is tiny (the kernel then divides with the IEEE
+    quotient instead of the reciprocal-and-correction form) or large: codes
+    and scales still equal the oracle's fp32 decisions bit for bit."""
+    rng = np.random.default_rng(int(-np.log10(magnitude) * 10) + 7)
+    x = (rng.standard_normal((1, 2, 256, 128), dtype=np.float32) * np.float32(magnitude)).astype(np.float32)
+    x[0, 1, 128:] *= np.float32(1e-3)  # a second, smaller tile scale
+    codes, scales = gpu_lib.fp8_quantize(_dev(x), None)
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = F.quantize(x, None)
+    assert np.array_equal(scales.cpu().numpy(), ref_scales)
+    bad = np.argwhere(codes.cpu().numpy() != ref_codes)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("outliers", [0, 4])
 def test_prep_rotation(gpu_lib, d, outliers):
