@@ -348,6 +348,7 @@ attn_fwd_dma_kernel(FwdParams p) {
     if (PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
+  // pl <- the rounding residual p - round16(p) of the packed P in pf
   auto residual = [&](f32x16_t (&s)[NQB][C::MB], const uint4 (&pf)[NQB][C::MB][2], uint4 (&pl)[NQB][C::MB][2]) {
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
@@ -355,10 +356,9 @@ attn_fwd_dma_kernel(FwdParams p) {
       for (int h2 = 0; h2 < 2; ++h2) {
         const int b = 8 * h2;
         const f32x16_t& v = s[0][mb];
-        pl[0][mb][h2] = make_uint4(residual2(TT{}, pf[0][mb][h2].x, v[b + 0], v[b + 1]),
-                                   residual2(TT{}, pf[0][mb][h2].y, v[b + 2], v[b + 3]),
-                                   residual2(TT{}, pf[0][mb][h2].z, v[b + 4], v[b + 5]),
-                                   residual2(TT{}, pf[0][mb][h2].w, v[b + 6], v[b + 7]));
+        const uint4 r = pf[0][mb][h2];
+        pl[0][mb][h2] = make_uint4(residual2(TT{}, r.x, v[b + 0], v[b + 1]), residual2(TT{}, r.y, v[b + 2], v[b + 3]),
+                                   residual2(TT{}, r.z, v[b + 4], v[b + 5]), residual2(TT{}, r.w, v[b + 6], v[b + 7]));
       }
   };
 
@@ -370,12 +370,12 @@ attn_fwd_dma_kernel(FwdParams p) {
     prepare(kt, s, m_use, masked);
     exps(s, m_use, masked, pf);
     const bool split = __any(l[0] < kSplitBelowP);
+    // the residual is formed before the first product, so the fp32 P dies
+    // there and only the two packed copies stay live through the MFMAs
+    uint4 pl[NQB][C::MB][2];
+    if (split) residual(s, pf, pl);
     pv_pass(slot, pf);
-    if (split) {
-      uint4 pl[NQB][C::MB][2];
-      residual(s, pf, pl);
-      pv_pass(slot, pl);
-    }
+    if (split) pv_pass(slot, pl);
   };
 
   // prologue: tiles 0 .. NS-2 in flight (tile j in ring slot j % NS)
@@ -451,7 +451,7 @@ template <int D, bool CAUSAL> struct DmaTile;
 template <bool CAUSAL> struct DmaTile<64, CAUSAL> {
   static constexpr int BC = 64, NW = 8, WPE = 2, NS = 3, OPT = kOptPin | kOptPrio;
 };
-template <> struct DmaTile<128, false> { static constexpr int BC = 64, NW = 8, WPE = 2, NS = 3, OPT = kOptPin | kOptPrio; };
+template <> struct DmaTile<128, false> { static constexpr int BC = 128, NW = 8, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
 template <> struct DmaTile<128, true> { static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
 template <bool CAUSAL> struct DmaTile<256, CAUSAL> {
   static constexpr int BC = 32, NW = 4, WPE = 1, NS = 3, OPT = kOptPin;
@@ -473,8 +473,8 @@ hipError_t launch_dma_d(const FwdParams& p, hipStream_t st) {
   using T = DmaTile<D, CAUSAL>;
   if constexpr (D == 128 && !CAUSAL) {
     switch (tune_cfg()) {
-      case 1: return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, 0, CAUSAL, VARLEN>(p, st);
-      case 2: return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, kOptPin, CAUSAL, VARLEN>(p, st);
+      case 1: return launch_dma_one<TT, D, 64, T::NW, T::WPE, 3, kOptPin | kOptPrio, CAUSAL, VARLEN>(p, st);
+      case 2: return launch_dma_one<TT, D, 96, T::NW, T::WPE, 2, kOptPin | kOptPrio, CAUSAL, VARLEN>(p, st);
       default: break;
     }
   }
