@@ -454,7 +454,7 @@ template <bool CAUSAL> struct DmaTile<64, CAUSAL> {
 template <> struct DmaTile<128, false> { static constexpr int BC = 128, NW = 8, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
 template <> struct DmaTile<128, true> { static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
 template <bool CAUSAL> struct DmaTile<256, CAUSAL> {
-  static constexpr int BC = 32, NW = 4, WPE = 1, NS = 3, OPT = kOptPin;
+  static constexpr int BC = 64, NW = 4, WPE = 1, NS = 2, OPT = kOptPin;
 };
 
 // Measurement switch read once from the environment: ATTN_TUNE_CFG selects
@@ -481,7 +481,7 @@ hipError_t launch_dma_d(const FwdParams& p, hipStream_t st) {
   if constexpr (D == 256) {
     switch (tune_cfg()) {
       case 1: return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, kOptPin | kOptPrio, CAUSAL, VARLEN>(p, st);
-      case 2: return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, 0, CAUSAL, VARLEN>(p, st);
+      case 2: return launch_dma_one<TT, D, 32, T::NW, T::WPE, 3, kOptPin, CAUSAL, VARLEN>(p, st);
       default: break;
     }
   }
