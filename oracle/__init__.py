@@ -24,7 +24,9 @@ Modules:
   normalised form the blog prints and the deferred-normalisation form;
 * ``fp8``: e4m3 rounding from the format definition, the Sylvester Hadamard
   and its fast transform, the rotation, block/per-tensor quantisation, and
-  an fp64 emulation of fp8 attention.
+  an fp64 emulation of fp8 attention;
+* ``splitkv``: attention over key chunks and the (O, lse) merge of the
+  partial results.
 
 Pins (the independent checks each function is held to) live in
 ``tests/test_oracle_*.py``; every function here is pinned, none is "parity
@@ -34,3 +36,4 @@ unpinned".
 from .exact import attention, attention_varlen, softmax_rows, scores  # noqa: F401
 from .tiled import attention_tiled  # noqa: F401
 from . import fp8  # noqa: F401
+from . import splitkv  # noqa: F401
