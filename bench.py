@@ -12,8 +12,9 @@ Prints ONE JSON line with the roofline of the dominant kernel (the
 non-causal launch: algorithmic FLOPs / its mean duration from HIP events on
 its stream, against the dense bf16 MFMA peak of 2.5 PFLOP/s) and the CPU
 baseline (the fp64 oracle, timed on a bounded sample of the same workload).
-"detail" adds the other shapes (d=256, N=8192, variable length, fp8 when
-available), each with its own TFLOP/s and fraction of peak.
+"detail" adds the other shapes (d=256, N=8192, variable length, decoding
+over key chunks, fp8 when available), each with its own TFLOP/s (or GB/s)
+and fraction of peak.
 
 --copy-calib runs only a plain device copy of known size (for scaling the
 HBM byte counters) and prints its byte count.
@@ -126,10 +127,50 @@ def bench_detail(attn, steps, warmup):
         out[name] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                      "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
         del q, k, v, o, lse
+    out.update(bench_decode(attn, steps, warmup))
     fp8 = bench_fp8(attn, steps, warmup)
     if fp8:
         out.update(fp8)
     return out
+
+
+def bench_decode(attn, steps, warmup):
+    """Decoding (B=2 H=32, one query per head, Nk=32768, d=128, bf16): attention
+    over key chunks plus the merge, against HBM bandwidth (the K and V bytes
+    are the algorithmic traffic); the single-pass kernel on the same shape
+    for comparison."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+
+    w = W.WORKLOADS["decode_bf16"]
+    x = W.make_inputs(w)
+    q, k, v = (W.to_dtype(x[n], w.dtype).cuda() for n in ("q", "k", "v"))
+    splits = attn.default_splits(w.B, w.H, w.Nq, w.Nk,
+                                 target_workgroups=torch.cuda.get_device_properties(0).multi_processor_count)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    op = torch.empty((splits,) + tuple(q.shape), dtype=torch.float32, device="cuda")
+    lp = torch.empty((splits,) + tuple(q.shape[:-1]), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run_split():
+        attn.forward_splitkv(q, k, v, scale=w.scale, num_splits=splits, out=o, lse=lse, o_part=op, lse_part=lp)
+
+    def run_single():
+        attn.forward(q, k, v, scale=w.scale, out=o, lse=lse)
+
+    for _ in range(warmup):
+        run_split()
+        run_single()
+    ms = float(np.mean(timed_launches(run_split, steps, stream)))
+    ms1 = float(np.mean(timed_launches(run_single, steps, stream)))
+    kv_bytes = 2 * k.numel() * 2
+    gbs = kv_bytes / (ms / 1e3) / 1e9
+    return {"decode_bf16_splitkv": {"ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                    "num_splits": splits, "single_pass_ms": round(ms1, 4),
+                                    "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}}
 
 
 def bench_fp8(attn, steps, warmup):

@@ -3,10 +3,12 @@ on MI355X (gfx950).
 
 The C entry points are exposed under their own names with plain integer
 pointers (argument marshalling only): ``attn_fwd``, ``attn_fwd_stream``,
-``attn_fp8_quantize``, ``attn_strerror``.  ``forward`` and ``fp8_quantize``
-are the torch-facing conveniences: they allocate the outputs with torch on
-the inputs' device, pass ``data_ptr()``s and torch's current HIP stream, and
-raise ``RuntimeError`` on a non-zero return code.  Every step of the
+``attn_fwd_splitkv``, ``attn_merge``, ``attn_fp8_quantize``,
+``attn_strerror``.  ``forward``, ``forward_splitkv``, ``merge`` and
+``fp8_quantize`` are the torch-facing conveniences: they allocate the outputs
+(and the split-KV workspace) with torch on the inputs' device, pass
+``data_ptr()``s and torch's current HIP stream, and raise ``RuntimeError`` on
+a non-zero return code.  Every step of the
 computation runs in the library's HIP kernels; there is no fallback.
 """
 
@@ -20,14 +22,14 @@ from typing import Optional
 __all__ = [
     "ATTN_DT_F16", "ATTN_DT_BF16", "ATTN_DT_FP8_E4M3", "ATTN_DT_F32",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP",
-    "load", "lib_path", "attn_fwd", "attn_fwd_stream", "attn_fp8_quantize", "attn_strerror",
-    "forward", "fp8_quantize", "EXPORTS",
+    "load", "lib_path", "attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_fp8_quantize",
+    "attn_strerror", "forward", "forward_splitkv", "merge", "fp8_quantize", "default_splits", "EXPORTS",
 ]
 
 ATTN_DT_F16, ATTN_DT_BF16, ATTN_DT_FP8_E4M3, ATTN_DT_F32 = 0, 1, 2, 3
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
 
-EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fp8_quantize", "attn_strerror")
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_fp8_quantize", "attn_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -54,6 +56,10 @@ def load():
         lib.attn_fwd.restype = _i
         lib.attn_fwd_stream.argtypes = _FWD_ARGS + [_p]
         lib.attn_fwd_stream.restype = _i
+        lib.attn_fwd_splitkv.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p, _p, _p]
+        lib.attn_fwd_splitkv.restype = _i
+        lib.attn_merge.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]
+        lib.attn_merge.restype = _i
         lib.attn_fp8_quantize.argtypes = [_p, _i, _p, _p, _i, _i, _i, _i, _p, _i, _p]
         lib.attn_fp8_quantize.restype = _i
         lib.attn_strerror.argtypes = [_i]
@@ -74,6 +80,16 @@ def attn_fwd_stream(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, cu_seqlens_
                     q_scale, k_scale, v_scale, hip_stream) -> int:
     return load().attn_fwd_stream(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q,
                                   cu_seqlens_k, dtype, q_scale, k_scale, v_scale, hip_stream)
+
+
+def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num_splits, o_part, lse_part,
+                     hip_stream) -> int:
+    return load().attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num_splits, o_part,
+                                   lse_part, hip_stream)
+
+
+def attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, o_dtype, hip_stream) -> int:
+    return load().attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, o_dtype, hip_stream)
 
 
 def attn_fp8_quantize(x, x_dtype, x_fp8, x_scale, B, H, N, d, signs, per_tensor, hip_stream) -> int:
@@ -158,6 +174,78 @@ def forward(q, k, v, *, causal: bool = False, scale: Optional[float] = None, cu_
     rc = attn_fwd_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
                          int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), dt,
                          _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def default_splits(B: int, H: int, Nq: int, Nk: int, rows_per_workgroup: int = 256,
+                   target_workgroups: int = 256, min_keys: int = 512) -> int:
+    """Key chunks for ``forward_splitkv``: about one work item per compute
+    unit (``target_workgroups``; more chunks only add partial traffic and
+    per-item overhead, measured), without chunks shorter than ``min_keys``."""
+    items = B * H * max(1, -(-Nq // rows_per_workgroup))
+    want = max(1, -(-target_workgroups // items))
+    return int(max(1, min(want, Nk // min_keys if Nk >= min_keys else 1, 1024)))
+
+
+def forward_splitkv(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
+                    num_splits: Optional[int] = None, out=None, lse=None, o_part=None, lse_part=None):
+    """Attention over key chunks plus the merge, through ``attn_fwd_splitkv``.
+
+    Dense fp16/bf16 only: q [B, H, Nq, d], k/v [B, H, Nk, d] -> (o, lse).
+    ``o_part`` float32 [S, B, H, Nq, d] and ``lse_part`` float32 [S, B, H, Nq]
+    are the workspace (allocated here if not given; they hold the per-chunk
+    results afterwards).
+    """
+    import torch
+
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        num_splits = default_splits(B, H, Nq, Nk, target_workgroups=cus)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if o_part is None:
+        o_part = torch.empty((num_splits, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((num_splits, B, H, Nq), dtype=torch.float32, device=q.device)
+    if o_part.numel() < num_splits * B * H * Nq * d or lse_part.numel() < num_splits * B * H * Nq:
+        raise ValueError("o_part / lse_part are smaller than num_splits chunks")
+    rc = attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                          int(bool(causal)), dt, int(num_splits), _ptr(o_part), _ptr(lse_part),
+                          _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def merge(o_part, lse_part, *, out_dtype=None, out=None, lse=None):
+    """Combine per-chunk results: o_part float32 [S, B, H, Nq, d], lse_part
+    float32 [S, B, H, Nq] -> (o [B, H, Nq, d] of ``out_dtype``, lse [B, H, Nq])."""
+    import torch
+
+    if o_part.dim() != 5 or lse_part.dim() != 4 or not o_part.is_contiguous() or not lse_part.is_contiguous():
+        raise ValueError("o_part must be a contiguous [S, B, H, Nq, d] and lse_part [S, B, H, Nq] tensor")
+    S, B, H, Nq, d = o_part.shape
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=o_part.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=o_part.device)
+    rc = attn_merge(_ptr(o_part), _ptr(lse_part), S, B, H, Nq, d, _ptr(out), _ptr(lse), _dtype_code(out),
+                    _stream(o_part.device))
     _check(rc)
     return out, lse
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_fp8.hip", "fp8_prep.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_fp8.hip", "fp8_prep.hip", "attn_merge.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.
 COMMON_FLAGS = [

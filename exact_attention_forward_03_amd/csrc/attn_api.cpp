@@ -14,6 +14,8 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
 
+constexpr int kMaxSplits = 1024;  // key chunks per split-KV call
+
 // Validation shared by attn_fwd and attn_fwd_stream.  Returns ATTN_OK or an
 // error code; touches no device state.
 int validate_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
@@ -92,7 +94,7 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   if (dtype == ATTN_DT_FP8_E4M3)
     e = attn::launch_fwd_fp8(d, causal != 0, p, st);
   else
-    e = attn::launch_fwd(dtype, d, causal != 0, varlen, p, st);
+    e = attn::launch_fwd(dtype, d, causal != 0, varlen, false, p, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -101,6 +103,57 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              const float* q_scale, const float* k_scale, const float* v_scale) {
   return attn_fwd_stream(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q, cu_seqlens_k, dtype,
                          q_scale, k_scale, v_scale, nullptr);
+}
+
+int attn_merge(const float* o_part, const float* lse_part, int num_splits, int B, int H, int Nq, int d, void* o,
+               float* lse, int o_dtype, void* hip_stream) {
+  if (B < 1 || H < 1 || Nq < 0) return ATTN_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
+  if (o_dtype != ATTN_DT_F16 && o_dtype != ATTN_DT_BF16) return ATTN_ERR_INVALID_ARG;
+  if (Nq > 0 && (!o_part || !lse_part || !o || !lse)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(o_part, 16) || !aligned(lse_part, 4) || !aligned(o, 16) || !aligned(lse, 4))
+    return ATTN_ERR_INVALID_ARG;
+  if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > (int64_t)INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
+  if (Nq == 0) return ATTN_OK;
+  attn::MergeParams mp{};
+  mp.o_part = o_part; mp.lse_part = lse_part; mp.S = num_splits;
+  mp.rows = (int64_t)B * H * Nq; mp.d = d; mp.o = o; mp.o_dtype = o_dtype; mp.lse = lse;
+  const hipError_t e = attn::launch_merge(mp, (hipStream_t)hip_stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                     int d, float scale, int causal, int dtype, int num_splits, float* o_part, float* lse_part,
+                     void* hip_stream) {
+  // fp8 is not offered here: validate the rest as for bf16, then refuse it
+  const int vdt = dtype == ATTN_DT_FP8_E4M3 ? ATTN_DT_BF16 : dtype;
+  const int rc = validate_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, nullptr, nullptr, vdt, nullptr,
+                              nullptr, nullptr);
+  if (rc != ATTN_OK) return rc;
+  if (num_splits < 1 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
+  if (Nq > 0 && (!o_part || !lse_part)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(o_part, 16) || !aligned(lse_part, 4)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (Nq == 0) return ATTN_OK;
+  const int br = attn::fwd_block_rows(dtype, d, causal != 0);
+  const int64_t tiles = ((int64_t)Nq + br - 1) / br;
+  const int64_t n_work = (int64_t)B * H * num_splits * tiles;
+  if (n_work > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  attn::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk;
+  p.c = scale * 1.4426950408889634f;
+  p.tiles_per_head = (int)tiles;
+  p.n_work = (int)n_work;
+  p.n_split = num_splits;
+  p.split_len = (int)(((int64_t)Nk + num_splits - 1) / num_splits);
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  hipStream_t st = (hipStream_t)hip_stream;
+  hipError_t e = attn::launch_fwd(dtype, d, causal != 0, false, true, p, st);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  return attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, dtype, hip_stream);
 }
 
 int attn_fp8_quantize(const void* x, int x_dtype, void* x_fp8, float* x_scale, int B, int H, int N, int d,

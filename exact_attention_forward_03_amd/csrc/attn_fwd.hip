@@ -103,26 +103,41 @@ __device__ __forceinline__ int v_chunk(int r, int ch) { return ch ^ ((r & 3) << 
 // SIMD.
 constexpr int kOptPin = 1, kOptPrio = 2;
 
-template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN>
+// SPLIT: the keys of each head are cut into p.n_split chunks of p.split_len
+// rows; a work item is (head, chunk, query tile) and writes the chunk's
+// normalised O and its lse in fp32 to p.o_part / p.lse_part, for the merge
+// kernel.  Causal masks use absolute key indices (chunk offset + local).
+template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_dma_kernel(FwdParams p) {
+  static_assert(!(SPLIT && VARLEN), "key chunks are for dense batches");
   constexpr bool PIN = OPT & kOptPin, PRIO = OPT & kOptPrio;
   constexpr int kPreD = 4;  // LDS fragment reads in flight ahead of their MFMA
   constexpr int NQB = 1;
   using C = PipeCfg<D, NQB, BC, NW, NS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  // ---- work item -> (head, query tile) --------------------------------------
+  // ---- work item -> (head[, key chunk], query tile) --------------------------
   const int work = xcd_remap(blockIdx.x, p.n_work);
-  const int head = work / p.tiles_per_head;
-  const int t = work - head * p.tiles_per_head;
+  const int hs = work / p.tiles_per_head;  // head, or head * n_split + chunk
+  const int t = work - hs * p.tiles_per_head;
+  const int head = SPLIT ? hs / p.n_split : hs;
+  const int split = SPLIT ? hs - head * p.n_split : 0;
   int64_t q_row0, k_row0;
   int q_len, k_len, qt;
+  int k_off = 0;  // absolute index of the first key of the range this item sees
   if constexpr (!VARLEN) {
     q_len = p.Nq;
-    k_len = p.Nk;
     q_row0 = (int64_t)head * p.Nq;
-    k_row0 = (int64_t)head * p.Nk;
+    if constexpr (SPLIT) {
+      const int64_t kb = min((int64_t)split * p.split_len, (int64_t)p.Nk);
+      const int64_t ke = min(kb + p.split_len, (int64_t)p.Nk);
+      k_off = (int)kb;
+      k_len = (int)(ke - kb);
+    } else {
+      k_len = p.Nk;
+    }
+    k_row0 = (int64_t)head * p.Nk + k_off;
     qt = CAUSAL ? (p.tiles_per_head - 1 - t) : t;
   } else {
     int acc = 0, seq = -1, qb = 0, qe = 0, nts = 0;
@@ -168,10 +183,18 @@ attn_fwd_dma_kernel(FwdParams p) {
   }
 
   int n_kt = (k_len + BC - 1) / BC;
-  if (CAUSAL) n_kt = min(n_kt, (min(q0 + C::BR, q_len) - 1) / BC + 1);
+  if (CAUSAL) {
+    // last key (local index) that some row of the workgroup sees
+    const int last = min(q0 + C::BR, q_len) - 1 - k_off;
+    n_kt = last < 0 ? 0 : min(n_kt, last / BC + 1);
+  }
   int wave_kt = n_kt;
-  if (qw0 >= q_len) wave_kt = 0;
-  else if (CAUSAL) wave_kt = min(n_kt, (min(qw0 + C::QW - 1, q_len - 1)) / BC + 1);
+  if (qw0 >= q_len) {
+    wave_kt = 0;
+  } else if (CAUSAL) {
+    const int last = min(qw0 + C::QW - 1, q_len - 1) - k_off;
+    wave_kt = last < 0 ? 0 : min(n_kt, last / BC + 1);
+  }
 
   uint8_t* const ldsK = lds;
   uint8_t* const ldsV = lds + NS * C::TILEB;
@@ -242,7 +265,7 @@ attn_fwd_dma_kernel(FwdParams p) {
   // Masks, row max, M update (with the rare rescale of O and l).
   auto prepare = [&](int kt, f32x16_t (&s)[NQB][C::MB], float (&m_use)[NQB], bool& masked) {
     const int key0 = kt * BC;
-    masked = (key0 + BC > k_len) || (CAUSAL && key0 + BC - 1 > qw0);
+    masked = (key0 + BC > k_len) || (CAUSAL && k_off + key0 + BC - 1 > qw0);
     // four independent max chains (short dependency chains)
     float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     const int my_q = qw0 + c;
@@ -252,7 +275,7 @@ attn_fwd_dma_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          const bool ok = key < k_len && (!CAUSAL || key <= my_q);
+          const bool ok = key < k_len && (!CAUSAL || k_off + key <= my_q);
           s[0][mb][i] = ok ? s[0][mb][i] * cs : -INFINITY;
           t4[i & 3] = fmaxf(t4[i & 3], s[0][mb][i]);
         }
@@ -413,25 +436,39 @@ attn_fwd_dma_kernel(FwdParams p) {
     const float l_tot = sum_halves(l[nb]);
     if (my_q < q_len) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      uint16_t* orow = (uint16_t*)p.o + (q_row0 + my_q) * D;
+      const float lse_v = l_tot > 0.f ? (M[nb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+      if constexpr (SPLIT) {
+        const int64_t prow = (int64_t)split * p.B * p.H * p.Nq + q_row0 + my_q;
+        float* orow = p.o_part + prow * D;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int dcol = db * 32 + 8 * g + 4 * hh;
-          *(uint2*)(orow + dcol) =
-              make_uint2(pack2(TT{}, oacc[nb][db][4 * g + 0] * inv, oacc[nb][db][4 * g + 1] * inv),
-                         pack2(TT{}, oacc[nb][db][4 * g + 2] * inv, oacc[nb][db][4 * g + 3] * inv));
-        }
-      if (hh == 0) p.lse[q_row0 + my_q] = l_tot > 0.f ? (M[nb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+          for (int g = 0; g < 4; ++g)
+            *(float4*)(orow + db * 32 + 8 * g + 4 * hh) =
+                make_float4(oacc[nb][db][4 * g + 0] * inv, oacc[nb][db][4 * g + 1] * inv,
+                            oacc[nb][db][4 * g + 2] * inv, oacc[nb][db][4 * g + 3] * inv);
+        if (hh == 0) p.lse_part[prow] = lse_v;
+      } else {
+        uint16_t* orow = (uint16_t*)p.o + (q_row0 + my_q) * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int dcol = db * 32 + 8 * g + 4 * hh;
+            *(uint2*)(orow + dcol) =
+                make_uint2(pack2(TT{}, oacc[nb][db][4 * g + 0] * inv, oacc[nb][db][4 * g + 1] * inv),
+                           pack2(TT{}, oacc[nb][db][4 * g + 2] * inv, oacc[nb][db][4 * g + 3] * inv));
+          }
+        if (hh == 0) p.lse[q_row0 + my_q] = lse_v;
+      }
     }
   }
 }
 
-template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN>
+template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT>
 hipError_t launch_dma_one(const FwdParams& p, hipStream_t st) {
   using C = PipeCfg<D, 1, BC, NW, NS>;
-  auto kern = attn_fwd_dma_kernel<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN>;
+  auto kern = attn_fwd_dma_kernel<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT>;
   static bool attr_set = false;  // idempotent; a benign race between threads
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
@@ -468,40 +505,45 @@ int tune_cfg() {
   return v;
 }
 
-template <typename TT, int D, bool CAUSAL, bool VARLEN>
+template <typename TT, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
 hipError_t launch_dma_d(const FwdParams& p, hipStream_t st) {
   using T = DmaTile<D, CAUSAL>;
   if constexpr (D == 128 && !CAUSAL) {
     switch (tune_cfg()) {
-      case 1: return launch_dma_one<TT, D, 64, T::NW, T::WPE, 3, kOptPin | kOptPrio, CAUSAL, VARLEN>(p, st);
-      case 2: return launch_dma_one<TT, D, 96, T::NW, T::WPE, 2, kOptPin | kOptPrio, CAUSAL, VARLEN>(p, st);
+      case 1: return launch_dma_one<TT, D, 64, T::NW, T::WPE, 3, kOptPin | kOptPrio, CAUSAL, VARLEN, SPLIT>(p, st);
+      case 2: return launch_dma_one<TT, D, 96, T::NW, T::WPE, 2, kOptPin | kOptPrio, CAUSAL, VARLEN, SPLIT>(p, st);
       default: break;
     }
   }
   if constexpr (D == 256) {
     switch (tune_cfg()) {
-      case 1: return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, kOptPin | kOptPrio, CAUSAL, VARLEN>(p, st);
-      case 2: return launch_dma_one<TT, D, 32, T::NW, T::WPE, 3, kOptPin, CAUSAL, VARLEN>(p, st);
+      case 1: return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, kOptPin | kOptPrio, CAUSAL, VARLEN, SPLIT>(p, st);
+      case 2: return launch_dma_one<TT, D, 32, T::NW, T::WPE, 3, kOptPin, CAUSAL, VARLEN, SPLIT>(p, st);
       default: break;
     }
   }
-  return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, T::OPT, CAUSAL, VARLEN>(p, st);
+  return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, T::OPT, CAUSAL, VARLEN, SPLIT>(p, st);
 }
 
-template <typename TT, bool CAUSAL, bool VARLEN>
+template <typename TT, bool CAUSAL, bool VARLEN, bool SPLIT>
 hipError_t launch_dma_cv(int d, const FwdParams& p, hipStream_t st) {
   switch (d) {
-    case 64: return launch_dma_d<TT, 64, CAUSAL, VARLEN>(p, st);
-    case 128: return launch_dma_d<TT, 128, CAUSAL, VARLEN>(p, st);
-    case 256: return launch_dma_d<TT, 256, CAUSAL, VARLEN>(p, st);
+    case 64: return launch_dma_d<TT, 64, CAUSAL, VARLEN, SPLIT>(p, st);
+    case 128: return launch_dma_d<TT, 128, CAUSAL, VARLEN, SPLIT>(p, st);
+    case 256: return launch_dma_d<TT, 256, CAUSAL, VARLEN, SPLIT>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename TT>
-hipError_t launch_dma_t(int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
-  if (causal) return varlen ? launch_dma_cv<TT, true, true>(d, p, st) : launch_dma_cv<TT, true, false>(d, p, st);
-  return varlen ? launch_dma_cv<TT, false, true>(d, p, st) : launch_dma_cv<TT, false, false>(d, p, st);
+hipError_t launch_dma_t(int d, bool causal, bool varlen, bool split, const FwdParams& p, hipStream_t st) {
+  if (split) {
+    if (varlen) return hipErrorInvalidValue;
+    return causal ? launch_dma_cv<TT, true, false, true>(d, p, st) : launch_dma_cv<TT, false, false, true>(d, p, st);
+  }
+  if (causal)
+    return varlen ? launch_dma_cv<TT, true, true, false>(d, p, st) : launch_dma_cv<TT, true, false, false>(d, p, st);
+  return varlen ? launch_dma_cv<TT, false, true, false>(d, p, st) : launch_dma_cv<TT, false, false, false>(d, p, st);
 }
 
 }  // namespace
@@ -515,9 +557,9 @@ int fwd_block_rows(int dtype, int d, bool causal) {
   }
 }
 
-hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
-  if (dtype == 0) return launch_dma_t<f16_t>(d, causal, varlen, p, st);
-  return launch_dma_t<bf16_t>(d, causal, varlen, p, st);
+hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, const FwdParams& p, hipStream_t st) {
+  if (dtype == 0) return launch_dma_t<f16_t>(d, causal, varlen, split, p, st);
+  return launch_dma_t<bf16_t>(d, causal, varlen, split, p, st);
 }
 
 }  // namespace attn

@@ -22,6 +22,21 @@ struct FwdParams {
   const float* q_scale;  // fp8 only: [B, H, ceil(Nq/128)]
   const float* k_scale;
   const float* v_scale;
+  int n_split;           // key chunks (split launches only)
+  int split_len;         // keys per chunk
+  float* o_part;         // [n_split, B, H, Nq, d] fp32 normalised partial outputs
+  float* lse_part;       // [n_split, B, H, Nq]
+};
+
+struct MergeParams {
+  const float* o_part;   // [S, rows, d]
+  const float* lse_part; // [S, rows]
+  int S;
+  int64_t rows;          // B * H * Nq
+  int d;
+  void* o;               // [rows, d] in o_dtype (fp16 or bf16)
+  int o_dtype;
+  float* lse;            // [rows]
 };
 
 struct PrepParams {
@@ -38,7 +53,8 @@ struct PrepParams {
 int fwd_block_rows(int dtype, int d, bool causal);
 int fwd_fp8_block_rows();
 
-hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st);
+hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, const FwdParams& p, hipStream_t st);
+hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_fwd_fp8(int d, bool causal, const FwdParams& p, hipStream_t st);
 hipError_t launch_fp8_prep(const PrepParams& p, bool per_tensor, hipStream_t st);
 

@@ -125,6 +125,48 @@ int attn_fp8_quantize(const void* x, int x_dtype, void* x_fp8, float* x_scale,
                       int B, int H, int N, int d, const float* signs, int per_tensor,
                       void* hip_stream);
 
+/*
+ * attn_fwd_splitkv — attn_fwd (dense layout only) computed over key chunks
+ * and merged: the keys of every (b, h) are cut into num_splits chunks of
+ * ceil(Nk / num_splits) rows; each (b, h, chunk, query tile) is an
+ * independent work item, which writes the chunk's normalised output and its
+ * lse in fp32 to the workspace; attn_merge then combines them into o, lse.
+ * This is FlashDecoding ("FlashAttention-3" wiki page, related work): with
+ * few queries (decoding: Nq = 1 per head) the key length, not the query
+ * count, supplies the parallelism.  Causal masks use absolute key indices
+ * (same top-left convention as attn_fwd); a chunk that a query cannot see
+ * contributes nothing.  The result equals attn_fwd's up to rounding.
+ *
+ *   dtype ATTN_DT_F16 or ATTN_DT_BF16 (fp8: ATTN_ERR_UNSUPPORTED);
+ *   1 <= num_splits <= 1024 (more chunks than keys is allowed: the extra
+ *     chunks are empty);
+ *   o_part: fp32 workspace [num_splits, B, H, Nq, d], lse_part: fp32
+ *     [num_splits, B, H, Nq], both caller-owned, 16- and 4-byte aligned; on
+ *     return they hold the per-chunk results (O_s normalised, lse_s = -inf
+ *     for a chunk with no visible key).  NULL only if Nq = 0.
+ * Other arguments, layouts and errors as attn_fwd_stream (no cu_seqlens).
+ */
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                     int num_splits, float* o_part, float* lse_part, void* hip_stream);
+
+/*
+ * attn_merge — combine results over disjoint key chunks (the online-softmax
+ * combination of "Flash Attention 3：让 GPU 跑满的注意力计算", §2.2, for any
+ * number of blocks):
+ *     lse = ln sum_s e^{lse_s},    O = sum_s e^{lse_s - lse} O_s,
+ * with lse_s = -inf parts ignored; a row whose parts are all -inf gives
+ * O = 0 and lse = -inf.  This is also the merge of results computed on
+ * different devices over key shards.
+ *   o_part fp32 [num_splits, B, H, Nq, d] (normalised rows), lse_part fp32
+ *   [num_splits, B, H, Nq]; o [B, H, Nq, d] of o_dtype (ATTN_DT_F16 or
+ *   ATTN_DT_BF16); lse fp32 [B, H, Nq].  1 <= num_splits <= 1024,
+ *   d ∈ {64, 128, 256}; 16-byte aligned arrays (lse arrays: 4-byte).
+ *   Nq = 0 is a no-op.  Same stream and error rules as attn_fwd_stream.
+ */
+int attn_merge(const float* o_part, const float* lse_part, int num_splits, int B, int H, int Nq, int d,
+               void* o, float* lse, int o_dtype, void* hip_stream);
+
 /* attn_strerror — a static, human-readable name for a return code. */
 const char* attn_strerror(int code);
 

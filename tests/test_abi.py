@@ -140,3 +140,58 @@ def test_binding_has_no_cpu_fallback():
     assert "oracle" not in src.replace("no oracle", "")
     for f in os.listdir(os.path.join(ROOT, "exact_attention_forward_03_amd", "csrc")):
         assert "oracle" not in open(os.path.join(ROOT, "exact_attention_forward_03_amd", "csrc", f)).read()
+
+
+def split_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=1, Nk=4096, d=128, scale=0.125, causal=0,
+             dtype=attn.ATTN_DT_BF16, num_splits=8, o_part=FAKE, lse_part=FAKE)
+    a.update(over)
+    return attn.attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"],
+                                 a["d"], a["scale"], a["causal"], a["dtype"], a["num_splits"], a["o_part"],
+                                 a["lse_part"], None)
+
+
+SPLIT_INVALID = [
+    dict(q=None), dict(o=None), dict(lse=None), dict(k=None), dict(B=0), dict(Nq=-1), dict(Nk=-1),
+    dict(scale=float("nan")), dict(causal=3), dict(dtype=5), dict(num_splits=0), dict(num_splits=-2),
+    dict(num_splits=1025), dict(o_part=None), dict(lse_part=None), dict(o_part=FAKE + 4),
+    dict(lse_part=FAKE + 2), dict(q=FAKE + 8),
+]
+
+
+@pytest.mark.parametrize("over", SPLIT_INVALID, ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_splitkv_invalid(lib, over):
+    assert split_call(**over) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_splitkv_unsupported_and_empty(lib):
+    assert split_call(d=96) == attn.ATTN_ERR_UNSUPPORTED
+    assert split_call(dtype=attn.ATTN_DT_FP8_E4M3) == attn.ATTN_ERR_UNSUPPORTED
+    assert split_call(Nq=0) == attn.ATTN_OK
+    assert split_call(Nq=0, q=None, o=None, lse=None, o_part=None, lse_part=None) == attn.ATTN_OK
+
+
+def merge_call(**over):
+    a = dict(o_part=FAKE, lse_part=FAKE, num_splits=4, B=1, H=2, Nq=16, d=128, o=FAKE, lse=FAKE,
+             o_dtype=attn.ATTN_DT_BF16)
+    a.update(over)
+    return attn.attn_merge(a["o_part"], a["lse_part"], a["num_splits"], a["B"], a["H"], a["Nq"], a["d"], a["o"],
+                           a["lse"], a["o_dtype"], None)
+
+
+MERGE_INVALID = [
+    dict(o_part=None), dict(lse_part=None), dict(o=None), dict(lse=None), dict(num_splits=0),
+    dict(num_splits=2000), dict(B=0), dict(H=-1), dict(Nq=-3), dict(o_dtype=attn.ATTN_DT_F32),
+    dict(o_dtype=attn.ATTN_DT_FP8_E4M3), dict(o_part=FAKE + 8), dict(o=FAKE + 2), dict(lse=FAKE + 1),
+]
+
+
+@pytest.mark.parametrize("over", MERGE_INVALID, ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_merge_invalid(lib, over):
+    assert merge_call(**over) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_merge_unsupported_and_empty(lib):
+    assert merge_call(d=80) == attn.ATTN_ERR_UNSUPPORTED
+    assert merge_call(Nq=0) == attn.ATTN_OK
+    assert merge_call(Nq=0, o_part=None, lse_part=None, o=None, lse=None) == attn.ATTN_OK

@@ -94,6 +94,8 @@ WORKLOADS = {
     "fp8_outlier": Workload("fp8_outlier", 2, 16, 8192, 8192, 128, "fp8", False, outliers=4),
     "fp8_normal": Workload("fp8_normal", 2, 16, 8192, 8192, 128, "fp8", False),
     "n8k_bf16": Workload("n8k_bf16", 2, 16, 8192, 8192, 128, "bf16", False),
+    # decoding: one query per (batch, head) against a long key cache
+    "decode_bf16": Workload("decode_bf16", 2, 32, 1, 32768, 128, "bf16", False),
 }
 
 
