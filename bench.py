@@ -10,7 +10,8 @@ FLOPs = 4 B H Nq Nk d, halved for causal.
 
 Prints ONE JSON line with the roofline of the dominant kernel (the
 non-causal launch: algorithmic FLOPs / its mean duration from HIP events on
-its stream, against the dense bf16 MFMA peak of 2.5 PFLOP/s) and the CPU
+its stream, against the dense bf16 MFMA peak of 2.5 PFLOP/s; also against
+the MFMA rate a register-only probe kernel sustains on this GPU) and the CPU
 baseline (the fp64 oracle, timed on a bounded sample of the same workload).
 "detail" adds the other shapes (d=256, N=8192, variable length, decoding
 over key chunks, fp8 when available), each with its own TFLOP/s (or GB/s)
@@ -82,6 +83,25 @@ def cpu_baseline(reps_heads: int = 8):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"B=1 H={reps_heads} N=4096 d=128 bf16 inputs in fp64, non-causal + causal "
                       f"({reps_heads}/32 of the heads of one step), {dt:.1f} s"}
+
+
+def measured_mfma_tflops():
+    """Dense MFMA rate measured by the probe library on this GPU: (bf16, fp8)
+    TFLOP/s, or (None, None) if the probe is not built."""
+    import ctypes
+
+    path = os.path.join(ROOT, "exact_attention_forward_03_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        return None, None
+    lib = ctypes.CDLL(path)
+    lib.attn_probe_mfma_tflops.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    lib.attn_probe_mfma_tflops.restype = ctypes.c_int
+    out = []
+    for kind in (0, 1):
+        v = ctypes.c_double(0.0)
+        rc = lib.attn_probe_mfma_tflops(kind, ctypes.byref(v), None)
+        out.append(round(v.value, 1) if rc == 0 else None)
+    return tuple(out)
 
 
 def timed_launches(fn, n, stream):
@@ -316,8 +336,15 @@ def main():
                      "mean_launch_ms": round(float(np.mean(nc_ms)), 4),
                      "causal_launch_ms": round(float(np.mean(c_ms)), 4)},
     }
+    mb16, mf8 = measured_mfma_tflops()
+    result["roofline"]["measured_mfma_peak"] = mb16
+    result["roofline"]["frac_of_measured_peak"] = round(ach / mb16, 4) if mb16 else None
     if not args.no_detail:
         result["detail"] = bench_detail(attn, max(5, args.steps // 5), 2)
+        if mf8 and "fp8_outlier" in result["detail"]:
+            fp8 = result["detail"]["fp8_outlier"]
+            fp8["measured_mfma_peak"] = mf8
+            fp8["frac_of_measured_peak"] = round(fp8["tflops"] / mf8, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     else:

@@ -1,7 +1,10 @@
-"""Build ``libattn.so`` (the C ABI of include/attn.h) for gfx950 with hipcc.
+"""Build ``libattn.so`` (the C ABI of include/attn.h) for gfx950 with hipcc,
+and ``libattn_probe.so`` (the MFMA throughput probe that bench.py reports
+next to the spec peak; not part of the attention ABI).
 
 Every source is compiled to an object in ``_build/`` in parallel, then
-linked into ``exact_attention_forward_03_amd/libattn.so``.  Always rebuilds.
+linked into ``exact_attention_forward_03_amd/libattn.so`` and
+``libattn_probe.so``.  Always rebuilds.
 
     python -m exact_attention_forward_03_amd.build
 """
@@ -18,8 +21,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
+PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_fp8.hip", "fp8_prep.hip", "attn_merge.hip"]
+PROBE_SOURCES = ["mfma_peak.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.
 COMMON_FLAGS = [
@@ -43,7 +48,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     flags = COMMON_FLAGS + list(extra_flags or [])
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"]
@@ -61,14 +66,16 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     if failed:
         msg = "\n".join(f"--- {s}\n{o}" for s, o in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB + ".tmp"
-    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{res.stdout}")
-    os.replace(tmp, LIB)
+    n = len(SOURCES)
+    for lib, lib_objs in ((LIB, objs[:n]), (PROBE_LIB, objs[n:])):
+        tmp = lib + ".tmp"
+        cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + lib_objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed:\n{res.stdout}")
+        os.replace(tmp, lib)
     return LIB
 
 
