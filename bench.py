@@ -168,7 +168,7 @@ def bench_decode(attn, steps, warmup):
     x = W.make_inputs(w)
     q, k, v = (W.to_dtype(x[n], w.dtype).cuda() for n in ("q", "k", "v"))
     splits = attn.default_splits(w.B, w.H, w.Nq, w.Nk,
-                                 target_workgroups=torch.cuda.get_device_properties(0).multi_processor_count)
+                                 target_workgroups=2 * torch.cuda.get_device_properties(0).multi_processor_count)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
     op = torch.empty((splits,) + tuple(q.shape), dtype=torch.float32, device="cuda")

@@ -178,11 +178,12 @@ def forward(q, k, v, *, causal: bool = False, scale: Optional[float] = None, cu_
     return out, lse
 
 
-def default_splits(B: int, H: int, Nq: int, Nk: int, rows_per_workgroup: int = 256,
-                   target_workgroups: int = 256, min_keys: int = 512) -> int:
-    """Key chunks for ``forward_splitkv``: about one work item per compute
-    unit (``target_workgroups``; more chunks only add partial traffic and
-    per-item overhead, measured), without chunks shorter than ``min_keys``."""
+def default_splits(B: int, H: int, Nq: int, Nk: int, rows_per_workgroup: int = 128,
+                   target_workgroups: int = 512, min_keys: int = 512) -> int:
+    """Key chunks for ``forward_splitkv``: about ``target_workgroups`` work
+    items (two per compute unit: the key-chunk launches run two workgroups
+    per CU; more chunks only add partial traffic and per-item overhead,
+    measured), without chunks shorter than ``min_keys``."""
     items = B * H * max(1, -(-Nq // rows_per_workgroup))
     want = max(1, -(-target_workgroups // items))
     return int(max(1, min(want, Nk // min_keys if Nk >= min_keys else 1, 1024)))
@@ -213,7 +214,7 @@ def forward_splitkv(q, k, v, *, causal: bool = False, scale: Optional[float] = N
         scale = 1.0 / math.sqrt(d)
     if num_splits is None:
         cus = torch.cuda.get_device_properties(q.device).multi_processor_count
-        num_splits = default_splits(B, H, Nq, Nk, target_workgroups=cus)
+        num_splits = default_splits(B, H, Nq, Nk, target_workgroups=2 * cus)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is None:

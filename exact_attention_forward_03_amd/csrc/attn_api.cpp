@@ -136,7 +136,7 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   if (!aligned(o_part, 16) || !aligned(lse_part, 4)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16) return ATTN_ERR_UNSUPPORTED;
   if (Nq == 0) return ATTN_OK;
-  const int br = attn::fwd_block_rows(dtype, d, causal != 0);
+  const int br = attn::fwd_split_block_rows(dtype, d, causal != 0);
   const int64_t tiles = ((int64_t)Nq + br - 1) / br;
   const int64_t n_work = (int64_t)B * H * num_splits * tiles;
   if (n_work > INT32_MAX) return ATTN_ERR_INVALID_ARG;

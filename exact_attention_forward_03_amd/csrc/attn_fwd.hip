@@ -505,9 +505,17 @@ int tune_cfg() {
   return v;
 }
 
+// Key-chunk launches at d = 128 (decoding and long keys with few queries):
+// 4-wave workgroups with a 64 KiB ring, so two run on each CU.
+struct SplitTile128 { static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
+
 template <typename TT, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
 hipError_t launch_dma_d(const FwdParams& p, hipStream_t st) {
   using T = DmaTile<D, CAUSAL>;
+  if constexpr (SPLIT && D == 128) {
+    using S = SplitTile128;
+    return launch_dma_one<TT, D, S::BC, S::NW, S::WPE, S::NS, S::OPT, CAUSAL, VARLEN, SPLIT>(p, st);
+  }
   if constexpr (D == 128 && !CAUSAL) {
     switch (tune_cfg()) {
       case 1: return launch_dma_one<TT, D, 64, T::NW, T::WPE, 3, kOptPin | kOptPrio, CAUSAL, VARLEN, SPLIT>(p, st);
@@ -547,6 +555,11 @@ hipError_t launch_dma_t(int d, bool causal, bool varlen, bool split, const FwdPa
 }
 
 }  // namespace
+
+int fwd_split_block_rows(int dtype, int d, bool causal) {
+  if (d == 128) return 32 * SplitTile128::NW;
+  return fwd_block_rows(dtype, d, causal);
+}
 
 int fwd_block_rows(int dtype, int d, bool causal) {
   if (dtype == 2) return fwd_fp8_block_rows();

@@ -51,6 +51,7 @@ struct PrepParams {
 
 // Query rows per workgroup of each kernel variant (sizes the grid).
 int fwd_block_rows(int dtype, int d, bool causal);
+int fwd_split_block_rows(int dtype, int d, bool causal);  // key-chunk launches
 int fwd_fp8_block_rows();
 
 hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, const FwdParams& p, hipStream_t st);
