@@ -494,17 +494,6 @@ template <bool CAUSAL> struct DmaTile<256, CAUSAL> {
   static constexpr int BC = 64, NW = 4, WPE = 1, NS = 2, OPT = kOptPin;
 };
 
-// Measurement switch read once from the environment: ATTN_TUNE_CFG selects
-// alternative loop options for d = 256 and non-causal d = 128 (same
-// workgroup shape, so the grid does not change); 0 or unset is the default.
-int tune_cfg() {
-  static const int v = [] {
-    const char* e = getenv("ATTN_TUNE_CFG");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
-}
-
 // Key-chunk launches at d = 128 (decoding and long keys with few queries):
 // 4-wave workgroups with a 64 KiB ring, so two run on each CU.
 struct SplitTile128 { static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
@@ -556,13 +545,24 @@ hipError_t launch_dma_t(int d, bool causal, bool varlen, bool split, const FwdPa
 
 }  // namespace
 
+// Measurement switch read once from the environment: ATTN_TUNE_CFG selects
+// alternative tile configurations of the same workgroup shape (so the grid
+// does not change) for comparisons in one process; 0 or unset is the default.
+int tune_cfg() {
+  static const int v = [] {
+    const char* e = getenv("ATTN_TUNE_CFG");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 int fwd_split_block_rows(int dtype, int d, bool causal) {
   if (d == 128) return 32 * SplitTile128::NW;
   return fwd_block_rows(dtype, d, causal);
 }
 
 int fwd_block_rows(int dtype, int d, bool causal) {
-  if (dtype == 2) return fwd_fp8_block_rows();
+  if (dtype == 2) return fwd_fp8_block_rows(causal);
   switch (d) {
     case 64: return 32 * DmaTile<64, false>::NW;
     case 128: return causal ? 32 * DmaTile<128, true>::NW : 32 * DmaTile<128, false>::NW;

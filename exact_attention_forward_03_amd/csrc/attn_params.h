@@ -49,10 +49,13 @@ struct PrepParams {
   int mode;              // 0: block scales; 1: tile amax only; 2: quantise with the tensor amax
 };
 
+// Alternative tile configurations for measurement (ATTN_TUNE_CFG, 0 = default).
+int tune_cfg();
+
 // Query rows per workgroup of each kernel variant (sizes the grid).
 int fwd_block_rows(int dtype, int d, bool causal);
 int fwd_split_block_rows(int dtype, int d, bool causal);  // key-chunk launches
-int fwd_fp8_block_rows();
+int fwd_fp8_block_rows(bool causal);
 
 hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, const FwdParams& p, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
