@@ -45,8 +45,6 @@
 // * Workgroup order: the hardware id is remapped so that consecutive work
 //   items — the query tiles of one head — run on the same XCD and share its
 //   L2 copy of that head's K and V; causal query tiles run heaviest first.
-#include <stdlib.h>
-
 #include "attn_device.h"
 #include "attn_params.h"
 
@@ -505,20 +503,6 @@ hipError_t launch_dma_d(const FwdParams& p, hipStream_t st) {
     using S = SplitTile128;
     return launch_dma_one<TT, D, S::BC, S::NW, S::WPE, S::NS, S::OPT, CAUSAL, VARLEN, SPLIT>(p, st);
   }
-  if constexpr (D == 128 && !CAUSAL) {
-    switch (tune_cfg()) {
-      case 1: return launch_dma_one<TT, D, 64, T::NW, T::WPE, 3, kOptPin | kOptPrio, CAUSAL, VARLEN, SPLIT>(p, st);
-      case 2: return launch_dma_one<TT, D, 96, T::NW, T::WPE, 2, kOptPin | kOptPrio, CAUSAL, VARLEN, SPLIT>(p, st);
-      default: break;
-    }
-  }
-  if constexpr (D == 256) {
-    switch (tune_cfg()) {
-      case 1: return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, kOptPin | kOptPrio, CAUSAL, VARLEN, SPLIT>(p, st);
-      case 2: return launch_dma_one<TT, D, 32, T::NW, T::WPE, 3, kOptPin, CAUSAL, VARLEN, SPLIT>(p, st);
-      default: break;
-    }
-  }
   return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, T::OPT, CAUSAL, VARLEN, SPLIT>(p, st);
 }
 
@@ -544,17 +528,6 @@ hipError_t launch_dma_t(int d, bool causal, bool varlen, bool split, const FwdPa
 }
 
 }  // namespace
-
-// Measurement switch read once from the environment: ATTN_TUNE_CFG selects
-// alternative tile configurations of the same workgroup shape (so the grid
-// does not change) for comparisons in one process; 0 or unset is the default.
-int tune_cfg() {
-  static const int v = [] {
-    const char* e = getenv("ATTN_TUNE_CFG");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
-}
 
 int fwd_split_block_rows(int dtype, int d, bool causal) {
   if (d == 128) return 32 * SplitTile128::NW;

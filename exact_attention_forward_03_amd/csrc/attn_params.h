@@ -49,9 +49,6 @@ struct PrepParams {
   int mode;              // 0: block scales; 1: tile amax only; 2: quantise with the tensor amax
 };
 
-// Alternative tile configurations for measurement (ATTN_TUNE_CFG, 0 = default).
-int tune_cfg();
-
 // Query rows per workgroup of each kernel variant (sizes the grid).
 int fwd_block_rows(int dtype, int d, bool causal);
 int fwd_split_block_rows(int dtype, int d, bool causal);  // key-chunk launches
