@@ -26,7 +26,10 @@ Modules:
   and its fast transform, the rotation, block/per-tensor quantisation, and
   an fp64 emulation of fp8 attention;
 * ``splitkv``: attention over key chunks and the (O, lse) merge of the
-  partial results.
+  partial results;
+* ``backward``: the gradients dQ, dK, dV of the attention definition (the
+  chain rule written out; the pages measure a backward pass but print no
+  algorithm for it).
 
 Pins (the independent checks each function is held to) live in
 ``tests/test_oracle_*.py``; every function here is pinned, none is "parity
@@ -37,3 +40,4 @@ from .exact import attention, attention_varlen, softmax_rows, scores  # noqa: F4
 from .tiled import attention_tiled  # noqa: F401
 from . import fp8  # noqa: F401
 from . import splitkv  # noqa: F401
+from . import backward  # noqa: F401
