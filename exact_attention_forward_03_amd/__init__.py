@@ -1,12 +1,12 @@
 """Python binding of ``libattn.so`` (include/attn.h): exact attention forward
-on MI355X (gfx950).
+(and its gradients) on MI355X (gfx950).
 
 The C entry points are exposed under their own names with plain integer
 pointers (argument marshalling only): ``attn_fwd``, ``attn_fwd_stream``,
-``attn_fwd_splitkv``, ``attn_merge``, ``attn_fp8_quantize``,
-``attn_strerror``.  ``forward``, ``forward_splitkv``, ``merge`` and
-``fp8_quantize`` are the torch-facing conveniences: they allocate the outputs
-(and the split-KV workspace) with torch on the inputs' device, pass
+``attn_fwd_splitkv``, ``attn_merge``, ``attn_bwd``, ``attn_fp8_quantize``,
+``attn_strerror``.  ``forward``, ``forward_splitkv``, ``merge``, ``backward``
+and ``fp8_quantize`` are the torch-facing conveniences: they allocate the
+outputs (and workspaces) with torch on the inputs' device, pass
 ``data_ptr()``s and torch's current HIP stream, and raise ``RuntimeError`` on
 a non-zero return code.  Every step of the
 computation runs in the library's HIP kernels; there is no fallback.
@@ -23,13 +23,15 @@ __all__ = [
     "ATTN_DT_F16", "ATTN_DT_BF16", "ATTN_DT_FP8_E4M3", "ATTN_DT_F32",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP",
     "load", "lib_path", "attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_fp8_quantize",
-    "attn_strerror", "forward", "forward_splitkv", "merge", "fp8_quantize", "default_splits", "EXPORTS",
+    "attn_bwd", "attn_strerror", "forward", "forward_splitkv", "merge", "backward", "fp8_quantize",
+    "default_splits", "EXPORTS",
 ]
 
 ATTN_DT_F16, ATTN_DT_BF16, ATTN_DT_FP8_E4M3, ATTN_DT_F32 = 0, 1, 2, 3
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
 
-EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_fp8_quantize", "attn_strerror")
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_bwd", "attn_fp8_quantize",
+           "attn_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -60,6 +62,8 @@ def load():
         lib.attn_fwd_splitkv.restype = _i
         lib.attn_merge.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]
         lib.attn_merge.restype = _i
+        lib.attn_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p]
+        lib.attn_bwd.restype = _i
         lib.attn_fp8_quantize.argtypes = [_p, _i, _p, _p, _i, _i, _i, _i, _p, _i, _p]
         lib.attn_fp8_quantize.restype = _i
         lib.attn_strerror.argtypes = [_i]
@@ -90,6 +94,11 @@ def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num
 
 def attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, o_dtype, hip_stream) -> int:
     return load().attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, o_dtype, hip_stream)
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, dtype, hip_stream) -> int:
+    return load().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, dtype,
+                           hip_stream)
 
 
 def attn_fp8_quantize(x, x_dtype, x_fp8, x_scale, B, H, N, d, signs, per_tensor, hip_stream) -> int:
@@ -249,6 +258,40 @@ def merge(o_part, lse_part, *, out_dtype=None, out=None, lse=None):
                     _stream(o_part.device))
     _check(rc)
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None, dq=None, dk=None,
+             dv=None, delta=None):
+    """Gradients (dq, dk, dv) of ``forward(q, k, v)`` for the output gradient
+    ``dout``, through ``attn_bwd``.  Dense fp16/bf16, d = 64 or 128:
+    q, o, dout [B, H, Nq, d]; k, v [B, H, Nk, d]; lse float32 [B, H, Nq] from
+    the forward.  ``delta`` float32 [B, H, Nq] is the workspace (allocated
+    here if not given; it holds rowsum(dout * o) afterwards)."""
+    import torch
+
+    for t in (q, k, v, o, dout, lse):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v, o, dout, lse must be contiguous")
+    dt = _dtype_code(q)
+    if any(_dtype_code(t) != dt for t in (k, v, o, dout)):
+        raise TypeError("q, k, v, o, dout must share one dtype")
+    if q.dim() != 4 or k.shape != v.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, o, dout must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be float32 [B, H, Nq]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    rc = attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                  _ptr(delta), B, H, Nq, Nk, d, float(scale), int(bool(causal)), dt, _stream(q.device))
+    _check(rc)
+    return dq, dk, dv
 
 
 def fp8_quantize(x, signs=None, per_tensor: bool = False, out=None, scales=None):

@@ -156,6 +156,36 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   return attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, dtype, hip_stream);
 }
 
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq, int Nk, int d, float scale,
+             int causal, int dtype, void* hip_stream) {
+  if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return ATTN_ERR_INVALID_ARG;
+  // query-side arrays may be NULL only without queries, key-side ones only without keys
+  if (Nq > 0 && (!q || !o || !lse || !dout || !dq || !delta)) return ATTN_ERR_INVALID_ARG;
+  if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16 && dtype != ATTN_DT_FP8_E4M3) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+    return ATTN_ERR_INVALID_ARG;
+  if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_DT_FP8_E4M3 || d == 256) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > (int64_t)INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
+  const int64_t kt = ((int64_t)Nk + attn::bwd_key_block(d) - 1) / attn::bwd_key_block(d);
+  const int64_t qt = ((int64_t)Nq + attn::bwd_query_block(d) - 1) / attn::bwd_query_block(d);
+  if ((int64_t)B * H * kt > INT32_MAX || (int64_t)B * H * qt > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  if (Nq == 0 && Nk == 0) return ATTN_OK;
+  attn::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.delta = delta;
+  p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  const hipError_t e = attn::launch_bwd(dtype, d, causal != 0, p, (hipStream_t)hip_stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 int attn_fp8_quantize(const void* x, int x_dtype, void* x_fp8, float* x_scale, int B, int H, int N, int d,
                       const float* signs, int per_tensor, void* hip_stream) {
   if (!x || !x_fp8 || !x_scale) return ATTN_ERR_INVALID_ARG;

@@ -1,0 +1,458 @@
+// Backward pass of exact attention for fp16/bf16 on gfx950 (CDNA4).
+//
+// The pages measure a backward pass ("FlashAttention-3" wiki page, the
+// "Measured (H100 80GB SXM5)" table) without printing it; what it computes
+// is the derivative of the forward definition ("Flash Attention 3：让 GPU
+// 跑满的注意力计算", §1.2 and §2.2).  With P = softmax(scale Q K^T [+causal])
+// and dO the gradient of the output:
+//
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - delta),   delta_i = dO_i . O_i,
+//   dQ = scale dS K,   dK = scale dS^T Q.
+//
+// Like the forward it never forms an N x N matrix in HBM: P is recomputed
+// tile by tile from Q, K and the forward's lse (P = 2^(S scale log2 e -
+// lse log2 e)), the same tiling as the forward (§2.1).  Three kernels:
+//
+// * delta: delta_i = sum_c dO_ic O_ic in fp32 (memory-bound; one read of O
+//   and dO), written to a caller-provided fp32 buffer.
+// * dK/dV: a workgroup owns 32*NW keys of one head, each wave 32 keys whose
+//   K and V rows stay in registers as MFMA B operands.  Blocks of 32 query
+//   rows (Q, dO, lse, delta) stream through an LDS ring (direct-to-LDS
+//   loads).  Per block and wave: S = Q K^T and dP = dO V^T (A operands read
+//   from LDS), the 32x32 P and dS in registers, then dV^T += dO^T P^T and
+//   dK^T += Q^T dS^T, whose A operands dO^T and Q^T come from the row-major
+//   tiles by the transposing LDS read (ds_read_b64_tr_b16) and whose B
+//   operands are P and dS exactly as the S accumulator holds them.
+// * dQ: a workgroup owns 32*NW query rows, each wave 32 rows with Q and dO
+//   in registers; K and V tiles stream through the ring as in the forward.
+//   Per tile: S^T = K Q^T and dP^T = V dO^T, dS^T in registers, then
+//   dQ^T += K^T dS^T (K^T by the transposing read).
+//
+// dQ is computed by its own pass over the keys rather than accumulated
+// across dK/dV workgroups with atomics: the result is deterministic and no
+// fp32 scratch is needed, at the cost of recomputing S and dP once more.
+// Causal masking is top-left (key j visible to query i iff j <= i); blocks
+// entirely outside the mask are skipped, diagonal blocks are masked per
+// element.
+#include "attn_device.h"
+#include "attn_params.h"
+
+namespace attn {
+namespace {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int N>
+__device__ __forceinline__ void bwd_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Row-major tiles of D 16-bit values per row, rows unpadded, the 16-byte
+// chunks of row r XOR-permuted by r mod (chunks per row, at most 16).
+template <int D>
+struct Tile {
+  static constexpr int ROWB = D * 2;
+  static constexpr int CH = ROWB / 16;
+  static constexpr int RPK = 1024 / ROWB;  // rows per 1 KiB direct-to-LDS load
+  __device__ static int pos(int r, int ch) { return ch ^ (r & (CH >= 16 ? 15 : CH - 1)); }
+  // MFMA operand with rows along the tile rows: lane l gets row `row`, the
+  // 8 values of k-step ks of its half.
+  __device__ static uint4 rows_frag(const uint8_t* t, int row, int ks, int hh) {
+    return *(const uint4*)(t + row * ROWB + pos(row, 2 * ks + hh) * 16);
+  }
+  // MFMA operand with rows along the tile columns (the transpose of 32
+  // columns x 16 rows): two transposing reads give lane l column
+  // 32 db + l % 32 at rows 16 k16 + 8 (t / 4) + 4 (l / 32) + t % 4, t = 0..7,
+  // the order in which a 32x32 accumulator holds its rows.
+  __device__ static uint4 cols_frag(const uint8_t* t, int db, int k16, int lane) {
+    const int hh = lane >> 5, g = (lane >> 4) & 1, s4 = lane & 15;
+    const int col = db * 32 + 16 * g + 4 * (s4 & 3);
+    const int ch = col >> 3, half = (col >> 2) & 1;
+    const int r0 = k16 * 16 + 4 * hh + (s4 >> 2), r1 = r0 + 8;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(t + r0 * ROWB + pos(r0, ch) * 16 + half * 8));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(t + r1 * ROWB + pos(r1, ch) * 16 + half * 8));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return make_uint4(a.x, a.y, b.x, b.y);
+  }
+  // Direct-to-LDS load of 1 KiB block `blk` of a tile whose first row is
+  // `row0` of `src` (rows past `n_rows` re-read the last row).
+  __device__ static void load_block(const uint8_t* src, int64_t row0, int n_rows, int r_base, uint8_t* dst, int blk,
+                                    int lane) {
+    const int r = blk * RPK + lane / CH;
+    const int row = min(r_base + r, n_rows - 1);
+    __builtin_amdgcn_global_load_lds(src + (row0 + row) * ROWB + pos(r, lane % CH) * 16,
+                                     (lds_void_t*)(dst + blk * 1024), 16, 0, 0);
+  }
+};
+
+__device__ __forceinline__ uint4 pack8(f16_t t, const f32x16_t& v, int b) {
+  return make_uint4(pack2(t, v[b + 0], v[b + 1]), pack2(t, v[b + 2], v[b + 3]), pack2(t, v[b + 4], v[b + 5]),
+                    pack2(t, v[b + 6], v[b + 7]));
+}
+__device__ __forceinline__ uint4 pack8(bf16_t t, const f32x16_t& v, int b) {
+  return make_uint4(pack2(t, v[b + 0], v[b + 1]), pack2(t, v[b + 2], v[b + 3]), pack2(t, v[b + 4], v[b + 5]),
+                    pack2(t, v[b + 6], v[b + 7]));
+}
+
+// Store a 32-row block of a transposed accumulator: lane l owns output row
+// `row` (a key or a query) and columns 32 db + 8 g + 4 (l / 32) + (0..3).
+template <typename TT, int DB>
+__device__ __forceinline__ void store_rows(uint16_t* dst_row, const f32x16_t (&acc)[DB], float mul, int hh) {
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(uint2*)(dst_row + db * 32 + 8 * g + 4 * hh) =
+          make_uint2(pack2(TT{}, acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul),
+                     pack2(TT{}, acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul));
+}
+
+// ---------------------------------------------------------------------------
+// delta_i = sum_c dO_ic O_ic: D/8 threads per row, 8 values each.
+// ---------------------------------------------------------------------------
+constexpr int kDeltaThreads = 256;
+
+template <typename TT, int D>
+__global__ void __launch_bounds__(kDeltaThreads) attn_bwd_delta_kernel(BwdParams p, int64_t rows) {
+  constexpr int TPR = D / 8;
+  const int64_t row = (int64_t)blockIdx.x * (kDeltaThreads / TPR) + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 a = *(const uint4*)((const uint16_t*)p.o + row * D + part * 8);
+    const uint4 b = *(const uint4*)((const uint16_t*)p.dout + row * D + part * 8);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2_t x = unpack2(TT{}, aw[i]), y = unpack2(TT{}, bw[i]);
+      acc = __builtin_fmaf(x[0], y[0], acc);
+      acc = __builtin_fmaf(x[1], y[1], acc);
+    }
+  }
+#pragma unroll
+  for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, TPR);
+  if (row < rows && part == 0) p.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.
+// ---------------------------------------------------------------------------
+template <typename TT, int D, int NW, int WPE, int NS, bool CAUSAL>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
+attn_bwd_dkdv_kernel(BwdParams p) {
+  using T = Tile<D>;
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int TILEB = 32 * T::ROWB;            // one 32-row tile of Q or dO
+  constexpr int BLK = TILEB / 1024;              // 1 KiB loads per tile
+  constexpr int STAGE = 2 * TILEB + 256;         // Q, dO, then lse[32] and delta[32]
+  constexpr int LPT = 2 * BLK / NW + 1;          // load instructions per wave per stage
+  static_assert((2 * BLK) % NW == 0, "each wave issues the same number of loads");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  const int work = xcd_remap(blockIdx.x, p.n_work);
+  const int head = work / p.tiles_per_head;
+  const int kt = work - head * p.tiles_per_head;
+  const int64_t q_row0 = (int64_t)head * p.Nq, k_row0 = (int64_t)head * p.Nk;
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
+  const int k0 = kt * 32 * NW, kw0 = k0 + 32 * wv;
+  const int my_key = kw0 + c;
+  const float cs = p.c;
+
+  // this wave's 32 keys as B operands: column = key, k-slice of d
+  uint4 kf[KS], vf[KS];
+  {
+    const int key = min(my_key, p.Nk - 1);
+    const uint16_t* kr = (const uint16_t*)p.k + (k_row0 + key) * D + 8 * hh;
+    const uint16_t* vr = (const uint16_t*)p.v + (k_row0 + key) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = *(const uint4*)(kr + ks * 16);
+      vf[ks] = *(const uint4*)(vr + ks * 16);
+    }
+  }
+  f32x16_t dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = f32x16_t{};
+    dv[db] = f32x16_t{};
+  }
+
+  // query blocks of 32 rows: causal starts at the block of the first key
+  const int n_qb = (p.Nq + 31) / 32;
+  const int qb0 = CAUSAL ? min(k0 / 32, n_qb) : 0;
+  const int wave_qb0 = CAUSAL ? min(kw0 / 32, n_qb) : 0;
+  const int n_steps = n_qb - qb0;
+
+  auto load_stage = [&](int qb, int slot) {
+    uint8_t* st = lds + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < 2 * BLK / NW; ++i) {
+      const int blk = wv * (2 * BLK / NW) + i;  // blocks 0..BLK-1: Q, BLK..: dO
+      if (blk < BLK) T::load_block((const uint8_t*)p.q, q_row0, p.Nq, qb * 32, st, blk, lane);
+      else T::load_block((const uint8_t*)p.dout, q_row0, p.Nq, qb * 32, st + TILEB, blk - BLK, lane);
+    }
+    // lse and delta: 64 floats, 16 per wave (4-byte direct-to-LDS loads)
+    const int idx = 16 * (wv & 3) + (lane & 15);
+    const int q = min(qb * 32 + (idx & 31), p.Nq - 1);
+    const float* src = (idx < 32 ? p.lse : p.delta) + q_row0 + q;
+    if (wv < 4 && lane < 16)
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(st + 2 * TILEB + 64 * (wv & 3)), 4, 0, 0);
+  };
+  static_assert(NW == 4, "the four waves load 16 of the 64 lse and delta values each");
+
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_steps) load_stage(qb0 + j, j);
+  int slot = 0;
+  for (int it = 0; it < n_steps; ++it) {
+    const int qb = qb0 + it;
+    if (it + NS - 2 < n_steps) bwd_wait_vm<(NS - 2) * LPT>();
+    else __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + NS - 1 < n_steps) load_stage(qb + NS - 1, slot == 0 ? NS - 1 : slot - 1);
+    if (qb >= wave_qb0) {
+      const uint8_t* tq = lds + slot * STAGE;
+      const uint8_t* tdo = tq + TILEB;
+      const float* tl = (const float*)(tq + 2 * TILEB);
+      // S = Q K^T and dP = dO V^T: column = this lane's key, rows = queries
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(TT{}, T::rows_frag(tq, c, ks, hh), kf[ks], s);
+        dp = mfma32(TT{}, T::rows_frag(tdo, c, ks, hh), vf[ks], dp);
+      }
+      const bool masked = (CAUSAL && qb * 32 < kw0 + 31) || qb * 32 + 32 > p.Nq;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = *(const float4*)(tl + 8 * g + 4 * hh);
+        const float4 d4 = *(const float4*)(tl + 32 + 8 * g + 4 * hh);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * g + j;
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cs, -lv[j] * kLog2e));
+          if (masked) {
+            const int q = qb * 32 + 8 * g + 4 * hh + j;
+            if (q >= p.Nq || (CAUSAL && my_key > q)) pv = 0.f;
+          }
+          s[i] = pv;
+          dp[i] = pv * (dp[i] - dl[j]);
+        }
+      }
+      uint4 pp[2], dsp[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        pp[h2] = pack8(TT{}, s, 8 * h2);
+        dsp[h2] = pack8(TT{}, dp, 8 * h2);
+      }
+      // dV^T += dO^T P^T, dK^T += Q^T dS^T over the block's 32 queries
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = mfma32(TT{}, T::cols_frag(tdo, db, h2, lane), pp[h2], dv[db]);
+          dk[db] = mfma32(TT{}, T::cols_frag(tq, db, h2, lane), dsp[h2], dk[db]);
+        }
+    }
+    slot = (slot + 1 == NS) ? 0 : slot + 1;
+  }
+
+  if (my_key < p.Nk) {
+    store_rows<TT, DB>((uint16_t*)p.dk + (k_row0 + my_key) * D, dk, p.scale, hh);
+    store_rows<TT, DB>((uint16_t*)p.dv + (k_row0 + my_key) * D, dv, 1.f, hh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.
+// ---------------------------------------------------------------------------
+template <typename TT, int D, int BC, int NW, int WPE, int NS, bool CAUSAL>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
+attn_bwd_dq_kernel(BwdParams p) {
+  using T = Tile<D>;
+  constexpr int KS = D / 16, DB = D / 32, MB = BC / 32;
+  constexpr int TILEB = BC * T::ROWB;
+  constexpr int BLK = TILEB / 1024;
+  constexpr int STAGE = 2 * TILEB;               // K then V
+  constexpr int LPT = 2 * BLK / NW;
+  static_assert((2 * BLK) % NW == 0, "each wave issues the same number of loads");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  const int work = xcd_remap(blockIdx.x, p.n_work);
+  const int head = work / p.tiles_per_head;
+  int qt = work - head * p.tiles_per_head;
+  if (CAUSAL) qt = p.tiles_per_head - 1 - qt;  // heaviest query tiles first
+  const int64_t q_row0 = (int64_t)head * p.Nq, k_row0 = (int64_t)head * p.Nk;
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
+  const int q0 = qt * 32 * NW, qw0 = q0 + 32 * wv;
+  const int my_q = qw0 + c;
+  const float cs = p.c;
+
+  uint4 qf[KS], df[KS];
+  float lse2 = 0.f, dl = 0.f;
+  {
+    const int q = min(my_q, p.Nq - 1);
+    const uint16_t* qr = (const uint16_t*)p.q + (q_row0 + q) * D + 8 * hh;
+    const uint16_t* dr = (const uint16_t*)p.dout + (q_row0 + q) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = *(const uint4*)(qr + ks * 16);
+      df[ks] = *(const uint4*)(dr + ks * 16);
+    }
+    lse2 = p.lse[q_row0 + q] * kLog2e;
+    dl = p.delta[q_row0 + q];
+  }
+  f32x16_t acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
+
+  int n_kt = (p.Nk + BC - 1) / BC, wave_kt = n_kt;
+  if (CAUSAL) {
+    const int last_wg = min(q0 + 32 * NW, p.Nq) - 1;  // the workgroup's last query
+    n_kt = last_wg < 0 ? 0 : min(n_kt, last_wg / BC + 1);
+    const int last_w = min(qw0 + 31, p.Nq - 1);
+    wave_kt = last_w < 0 ? 0 : min(n_kt, last_w / BC + 1);
+  }
+  if (qw0 >= p.Nq) wave_kt = 0;
+
+  auto load_stage = [&](int kt, int slot) {
+    uint8_t* st = lds + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int blk = wv * LPT + i;
+      if (blk < BLK) T::load_block((const uint8_t*)p.k, k_row0, p.Nk, kt * BC, st, blk, lane);
+      else T::load_block((const uint8_t*)p.v, k_row0, p.Nk, kt * BC, st + TILEB, blk - BLK, lane);
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_kt) load_stage(j, j);
+  int slot = 0;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    if (kt + NS - 2 < n_kt) bwd_wait_vm<(NS - 2) * LPT>();
+    else __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + NS - 1 < n_kt) load_stage(kt + NS - 1, slot == 0 ? NS - 1 : slot - 1);
+    if (kt < wave_kt) {
+      const uint8_t* tk = lds + slot * STAGE;
+      const uint8_t* tv = tk + TILEB;
+      // S^T = K Q^T, dP^T = V dO^T: column = this lane's query, rows = keys
+      f32x16_t s[MB], dp[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        s[mb] = f32x16_t{};
+        dp[mb] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s[mb] = mfma32(TT{}, T::rows_frag(tk, mb * 32 + c, ks, hh), qf[ks], s[mb]);
+          dp[mb] = mfma32(TT{}, T::rows_frag(tv, mb * 32 + c, ks, hh), df[ks], dp[mb]);
+        }
+      }
+      const bool masked = (CAUSAL && kt * BC + BC - 1 > qw0) || kt * BC + BC > p.Nk;
+      uint4 dsp[MB][2];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][i], cs, -lse2));
+          if (masked) {
+            const int key = kt * BC + mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if (key >= p.Nk || (CAUSAL && key > my_q)) pv = 0.f;
+          }
+          dp[mb][i] = pv * (dp[mb][i] - dl);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) dsp[mb][h2] = pack8(TT{}, dp[mb], 8 * h2);
+      }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int k16 = 0; k16 < 2 * MB; ++k16)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc[db] = mfma32(TT{}, T::cols_frag(tk, db, k16, lane), dsp[k16 >> 1][k16 & 1], acc[db]);
+    }
+    slot = (slot + 1 == NS) ? 0 : slot + 1;
+  }
+  if (my_q < p.Nq) store_rows<TT, DB>((uint16_t*)p.dq + (q_row0 + my_q) * D, acc, p.scale, hh);
+}
+
+// ---------------------------------------------------------------------------
+// Launch configurations.
+// ---------------------------------------------------------------------------
+// dK/dV: NW waves of 32 keys, WPE waves per SIMD, an NS-slot ring of
+// 32-query blocks.  At d = 128 a wave holds K, V (64 registers) and the dK,
+// dV accumulators (128) and runs alone on its SIMD.  dQ: 64-key tiles in a
+// 2-slot ring, two waves per SIMD.
+template <int D>
+struct BwdCfg {
+  static constexpr int NW = 4, WPE = D >= 128 ? 1 : 2, NS = 3;
+  static constexpr int DQ_BC = 64, DQ_NW = 4, DQ_WPE = 2, DQ_NS = 2;
+};
+
+template <typename TT, int D, bool CAUSAL>
+hipError_t launch_bwd_t(BwdParams p, hipStream_t st) {
+  const int64_t rows = (int64_t)p.B * p.H * p.Nq;
+  if (rows > 0) {
+    constexpr int RPB = kDeltaThreads / (D / 8);
+    hipLaunchKernelGGL((attn_bwd_delta_kernel<TT, D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+                       dim3(kDeltaThreads), 0, st, p, rows);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  if (p.Nk > 0) {
+    using C = BwdCfg<D>;
+    constexpr int STAGE = 2 * 32 * D * 2 + 256;
+    constexpr int lds = C::NS * STAGE;
+    auto kern = attn_bwd_dkdv_kernel<TT, D, C::NW, C::WPE, C::NS, CAUSAL>;
+    if (hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        e != hipSuccess)
+      return e;
+    BwdParams pk = p;
+    pk.tiles_per_head = (p.Nk + 32 * C::NW - 1) / (32 * C::NW);
+    pk.n_work = p.B * p.H * pk.tiles_per_head;
+    hipLaunchKernelGGL(kern, dim3(pk.n_work), dim3(C::NW * 64), lds, st, pk);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  if (p.Nq > 0) {
+    using C = BwdCfg<D>;
+    constexpr int lds = C::DQ_NS * 2 * C::DQ_BC * D * 2;
+    auto kern = attn_bwd_dq_kernel<TT, D, C::DQ_BC, C::DQ_NW, C::DQ_WPE, C::DQ_NS, CAUSAL>;
+    if (hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        e != hipSuccess)
+      return e;
+    BwdParams pq = p;
+    pq.tiles_per_head = (p.Nq + 32 * C::DQ_NW - 1) / (32 * C::DQ_NW);
+    pq.n_work = p.B * p.H * pq.tiles_per_head;
+    hipLaunchKernelGGL(kern, dim3(pq.n_work), dim3(C::DQ_NW * 64), lds, st, pq);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename TT>
+hipError_t launch_bwd_d(int d, bool causal, const BwdParams& p, hipStream_t st) {
+  switch (d) {
+    case 64: return causal ? launch_bwd_t<TT, 64, true>(p, st) : launch_bwd_t<TT, 64, false>(p, st);
+    case 128: return causal ? launch_bwd_t<TT, 128, true>(p, st) : launch_bwd_t<TT, 128, false>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int bwd_key_block(int d) { return 32 * (d == 64 ? BwdCfg<64>::NW : BwdCfg<128>::NW); }
+int bwd_query_block(int d) { return 32 * (d == 64 ? BwdCfg<64>::DQ_NW : BwdCfg<128>::DQ_NW); }
+
+hipError_t launch_bwd(int dtype, int d, bool causal, BwdParams p, hipStream_t st) {
+  return dtype == 0 ? launch_bwd_d<f16_t>(d, causal, p, st) : launch_bwd_d<bf16_t>(d, causal, p, st);
+}
+
+}  // namespace attn

@@ -50,6 +50,29 @@ struct PrepParams {
 };
 
 // Query rows per workgroup of each kernel variant (sizes the grid).
+// Backward pass (fp16/bf16, dense [B, H, N, d]).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;          // [B, H, Nq] fp32: rowsum(dO * O), written by the first kernel
+  int B, H, Nq, Nk;
+  float scale;           // softmax scale (multiplies dS in dQ and dK)
+  float c;               // scale * log2(e)
+  int tiles_per_head;    // set per launch: key tiles (dK/dV) or query tiles (dQ) per head
+  int n_work;
+};
+
+int bwd_key_block(int d);    // keys per dK/dV workgroup
+int bwd_query_block(int d);  // queries per dQ workgroup
+hipError_t launch_bwd(int dtype, int d, bool causal, BwdParams p, hipStream_t st);
+
 int fwd_block_rows(int dtype, int d, bool causal);
 int fwd_split_block_rows(int dtype, int d, bool causal);  // key-chunk launches
 int fwd_fp8_block_rows(bool causal);

@@ -167,6 +167,32 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
 int attn_merge(const float* o_part, const float* lse_part, int num_splits, int B, int H, int Nq, int d,
                void* o, float* lse, int o_dtype, void* hip_stream);
 
+/*
+ * attn_bwd — gradients of the attention computed by attn_fwd: given dO =
+ * dL/dO, writes dQ, dK, dV (the derivative of the forward definition of
+ * "Flash Attention 3：让 GPU 跑满的注意力计算", §1.2 and §2.2; the
+ * "FlashAttention-3" wiki page measures such a backward pass in its
+ * "Measured (H100 80GB SXM5)" table):
+ *     dV = P^T dO,  dS = P * (dO V^T - delta),  delta_i = dO_i . O_i,
+ *     dQ = scale dS K,  dK = scale dS^T Q.
+ * P is recomputed from Q, K and the forward's lse; no N x N matrix is
+ * stored.
+ *   q, o, dout, dq [B, H, Nq, d]; k, v, dk, dv [B, H, Nk, d]; all of dtype
+ *     ATTN_DT_F16 or ATTN_DT_BF16, contiguous, 16-byte aligned;
+ *   o, lse: the forward's outputs for the same q, k, v, scale, causal;
+ *   delta: fp32 workspace [B, H, Nq], caller-owned, 4-byte aligned; on
+ *     return it holds delta_i = sum_c dO_ic O_ic;
+ *   d ∈ {64, 128} (256 and fp8: ATTN_ERR_UNSUPPORTED); dense batches only.
+ *   Query-side arrays may be NULL only if Nq = 0, key-side arrays only if
+ *   Nk = 0.  Nk = 0 gives dQ = 0; Nq = 0 gives dK = dV = 0.  dQ is
+ *   accumulated per query row in one workgroup (no atomics): results are
+ *   deterministic.  Same stream, ownership and error rules as
+ *   attn_fwd_stream.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq, int Nk, int d, float scale,
+             int causal, int dtype, void* hip_stream);
+
 /* attn_strerror — a static, human-readable name for a return code. */
 const char* attn_strerror(int code);
 

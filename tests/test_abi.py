@@ -195,3 +195,34 @@ def test_merge_unsupported_and_empty(lib):
     assert merge_call(d=80) == attn.ATTN_ERR_UNSUPPORTED
     assert merge_call(Nq=0) == attn.ATTN_OK
     assert merge_call(Nq=0, o_part=None, lse_part=None, o=None, lse=None) == attn.ATTN_OK
+
+
+def bwd_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE, B=1, H=2,
+             Nq=256, Nk=256, d=128, scale=0.125, causal=0, dtype=attn.ATTN_DT_BF16)
+    a.update(over)
+    return attn.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"], a["delta"],
+                         a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+
+
+BWD_INVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None), dict(dout=None), dict(dq=None),
+    dict(dk=None), dict(dv=None), dict(delta=None), dict(B=0), dict(H=0), dict(Nq=-1), dict(Nk=-5),
+    dict(scale=float("inf")), dict(scale=-1.0), dict(causal=2), dict(dtype=7), dict(q=FAKE + 8),
+    dict(dout=FAKE + 4), dict(dq=FAKE + 2), dict(dk=FAKE + 8), dict(dv=FAKE + 8), dict(o=FAKE + 8),
+    dict(lse=FAKE + 2), dict(delta=FAKE + 1),
+]
+
+
+@pytest.mark.parametrize("over", BWD_INVALID, ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_bwd_invalid(lib, over):
+    assert bwd_call(**over) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_bwd_unsupported_and_empty(lib):
+    assert bwd_call(d=256) == attn.ATTN_ERR_UNSUPPORTED
+    assert bwd_call(d=80) == attn.ATTN_ERR_UNSUPPORTED
+    assert bwd_call(dtype=attn.ATTN_DT_FP8_E4M3) == attn.ATTN_ERR_UNSUPPORTED
+    # no queries and no keys: nothing to write, no launch
+    none = dict(q=None, k=None, v=None, o=None, lse=None, dout=None, dq=None, dk=None, dv=None, delta=None)
+    assert bwd_call(Nq=0, Nk=0, **none) == attn.ATTN_OK
