@@ -14,8 +14,8 @@ its stream, against the dense bf16 MFMA peak of 2.5 PFLOP/s; also against
 the MFMA rate a register-only probe kernel sustains on this GPU) and the CPU
 baseline (the fp64 oracle, timed on a bounded sample of the same workload).
 "detail" adds the other shapes (d=256, N=8192, variable length, decoding
-over key chunks, fp8 when available), each with its own TFLOP/s (or GB/s)
-and fraction of peak.
+over key chunks, the backward pass, fp8 when available), each with its own
+TFLOP/s (or GB/s) and fraction of peak.
 
 --copy-calib runs only a plain device copy of known size (for scaling the
 HBM byte counters) and prints its byte count.
@@ -148,6 +148,7 @@ def bench_detail(attn, steps, warmup):
                      "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
         del q, k, v, o, lse
     out.update(bench_decode(attn, steps, warmup))
+    out.update(bench_backward(attn, steps, warmup))
     fp8 = bench_fp8(attn, steps, warmup)
     if fp8:
         out.update(fp8)
@@ -191,6 +192,41 @@ def bench_decode(attn, steps, warmup):
     return {"decode_bf16_splitkv": {"ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                                     "num_splits": splits, "single_pass_ms": round(ms1, 4),
                                     "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}}
+
+
+def bench_backward(attn, steps, warmup):
+    """Backward pass (attn_bwd: delta, dK/dV and dQ kernels) on the dense
+    bf16 shape B=2 H=16 N=4096 d=128, non-causal and causal.  FLOPs are those
+    of the five products of the gradient (S, dP, dV, dK, dQ: 10 B H N^2 d,
+    halved for causal); the kernels recompute S and dP once more for dQ."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name in ("dense_bf16", "dense_bf16_causal"):
+        w = W.WORKLOADS[name]
+        rng = np.random.default_rng(5)
+        shape = (w.B, w.H, w.Nq, w.d)
+        q, k, v, do = (W.to_dtype(rng.standard_normal(shape, dtype=np.float32), "bf16").cuda() for _ in range(4))
+        o, lse = attn.forward(q, k, v, causal=w.causal, scale=w.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+
+        def run():
+            attn.backward(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+
+        for _ in range(warmup):
+            run()
+        ms = float(np.mean(timed_launches(run, steps, stream)))
+        flops = 10.0 * w.B * w.H * w.Nq * w.Nk * w.d * (0.5 if w.causal else 1.0)
+        tf = flops / (ms / 1e3) / 1e12
+        out["bwd_" + name] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                              "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
+        del q, k, v, do, o, lse, dq, dk, dv, delta
+    return out
 
 
 def bench_fp8(attn, steps, warmup):

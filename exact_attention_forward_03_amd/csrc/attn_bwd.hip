@@ -16,10 +16,11 @@
 // * delta: delta_i = sum_c dO_ic O_ic in fp32 (memory-bound; one read of O
 //   and dO), written to a caller-provided fp32 buffer.
 // * dK/dV: a workgroup owns 32*NW keys of one head, each wave 32 keys whose
-//   K and V rows stay in registers as MFMA B operands.  Blocks of 32 query
-//   rows (Q, dO, lse, delta) stream through an LDS ring (direct-to-LDS
-//   loads).  Per block and wave: S = Q K^T and dP = dO V^T (A operands read
-//   from LDS), the 32x32 P and dS in registers, then dV^T += dO^T P^T and
+//   K rows stay in registers as MFMA B operands (the workgroup's V rows are
+//   loaded once into LDS).  Blocks of 32 query rows (Q, dO, lse, delta)
+//   stream through an LDS ring (direct-to-LDS loads).  Per block and wave:
+//   S = Q K^T and dP = dO V^T (operands read from LDS but K), the 32x32 P
+//   and dS in registers, then dV^T += dO^T P^T and
 //   dK^T += Q^T dS^T, whose A operands dO^T and Q^T come from the row-major
 //   tiles by the transposing LDS read (ds_read_b64_tr_b16) and whose B
 //   operands are P and dS exactly as the S accumulator holds them.
@@ -153,9 +154,20 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   static_assert((2 * BLK) % NW == 0, "each wave issues the same number of loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const int work = xcd_remap(blockIdx.x, p.n_work);
-  const int head = work / p.tiles_per_head;
-  const int kt = work - head * p.tiles_per_head;
+  // Non-causal: the key tiles of one head run on one XCD (shared L2 copy of
+  // the head's Q and dO).  Causal: tile kt sees the queries from kt*32*NW
+  // on, so the work falls with kt; all heads' tile 0 go first, then tile 1,
+  // ..., dealt round-robin over the XCDs.
+  int head, kt;
+  if constexpr (CAUSAL) {
+    const int heads = p.B * p.H;
+    kt = blockIdx.x / heads;
+    head = blockIdx.x - kt * heads;
+  } else {
+    const int work = xcd_remap(blockIdx.x, p.n_work);
+    head = work / p.tiles_per_head;
+    kt = work - head * p.tiles_per_head;
+  }
   const int64_t q_row0 = (int64_t)head * p.Nq, k_row0 = (int64_t)head * p.Nk;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -164,17 +176,22 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   const int my_key = kw0 + c;
   const float cs = p.c;
 
-  // this wave's 32 keys as B operands: column = key, k-slice of d
-  uint4 kf[KS], vf[KS];
+  // this wave's 32 keys of K as B operands in registers (column = key,
+  // k-slice of d); the workgroup's V rows in LDS after the ring, read as B
+  // operands of dP (registers are the limit at two waves per SIMD)
+  uint8_t* const ldsV = lds + NS * STAGE;
+  {
+    constexpr int VBLK = 32 * NW * T::ROWB / 1024;
+#pragma unroll
+    for (int i = 0; i < VBLK / NW; ++i)
+      T::load_block((const uint8_t*)p.v, k_row0, p.Nk, k0, ldsV, wv * (VBLK / NW) + i, lane);
+  }
+  uint4 kf[KS];
   {
     const int key = min(my_key, p.Nk - 1);
     const uint16_t* kr = (const uint16_t*)p.k + (k_row0 + key) * D + 8 * hh;
-    const uint16_t* vr = (const uint16_t*)p.v + (k_row0 + key) * D + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = *(const uint4*)(kr + ks * 16);
-      vf[ks] = *(const uint4*)(vr + ks * 16);
-    }
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const uint4*)(kr + ks * 16);
   }
   f32x16_t dk[DB], dv[DB];
 #pragma unroll
@@ -183,10 +200,12 @@ attn_bwd_dkdv_kernel(BwdParams p) {
     dv[db] = f32x16_t{};
   }
 
-  // query blocks of 32 rows: causal starts at the block of the first key
+  // query blocks of 32 rows: causal starts at the block of the workgroup's
+  // first key (for the later waves the first blocks are fully masked: they
+  // run them rather than branch around them, which costs the compiler
+  // dozens of registers)
   const int n_qb = (p.Nq + 31) / 32;
   const int qb0 = CAUSAL ? min(k0 / 32, n_qb) : 0;
-  const int wave_qb0 = CAUSAL ? min(kw0 / 32, n_qb) : 0;
   const int n_steps = n_qb - qb0;
 
   auto load_stage = [&](int qb, int slot) {
@@ -216,7 +235,7 @@ attn_bwd_dkdv_kernel(BwdParams p) {
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (it + NS - 1 < n_steps) load_stage(qb + NS - 1, slot == 0 ? NS - 1 : slot - 1);
-    if (qb >= wave_qb0) {
+    {
       const uint8_t* tq = lds + slot * STAGE;
       const uint8_t* tdo = tq + TILEB;
       const float* tl = (const float*)(tq + 2 * TILEB);
@@ -225,9 +244,14 @@ attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s = mfma32(TT{}, T::rows_frag(tq, c, ks, hh), kf[ks], s);
-        dp = mfma32(TT{}, T::rows_frag(tdo, c, ks, hh), vf[ks], dp);
+        dp = mfma32(TT{}, T::rows_frag(tdo, c, ks, hh), T::rows_frag(ldsV, 32 * wv + c, ks, hh), dp);
       }
       const bool masked = (CAUSAL && qb * 32 < kw0 + 31) || qb * 32 + 32 > p.Nq;
+      // element (g, j) is query q = qb*32 + 4 hh + 8 g + j: it exists iff
+      // 8 g + j < q_lim and sees this lane's key iff 8 g + j >= key_rel
+      // (comparisons against constants, nothing kept live across blocks)
+      const int q_lim = p.Nq - qb * 32 - 4 * hh;
+      const int key_rel = my_key - qb * 32 - 4 * hh;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float4 l4 = *(const float4*)(tl + 8 * g + 4 * hh);
@@ -237,10 +261,7 @@ attn_bwd_dkdv_kernel(BwdParams p) {
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * g + j;
           float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cs, -lv[j] * kLog2e));
-          if (masked) {
-            const int q = qb * 32 + 8 * g + 4 * hh + j;
-            if (q >= p.Nq || (CAUSAL && my_key > q)) pv = 0.f;
-          }
+          if (masked && (8 * g + j >= q_lim || (CAUSAL && 8 * g + j < key_rel))) pv = 0.f;
           s[i] = pv;
           dp[i] = pv * (dp[i] - dl[j]);
         }
@@ -358,16 +379,18 @@ attn_bwd_dq_kernel(BwdParams p) {
         }
       }
       const bool masked = (CAUSAL && kt * BC + BC - 1 > qw0) || kt * BC + BC > p.Nk;
+      // element (mb, i) is key kt*BC + 4 hh + e with e = 32 mb + 8 (i/4) + i%4:
+      // it exists iff e < k_lim and is visible to this lane's query iff e <= q_rel
+      const int k_lim = p.Nk - kt * BC - 4 * hh;
+      const int q_rel = my_q - kt * BC - 4 * hh;
       uint4 dsp[MB][2];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][i], cs, -lse2));
-          if (masked) {
-            const int key = kt * BC + mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if (key >= p.Nk || (CAUSAL && key > my_q)) pv = 0.f;
-          }
+          const int e = 32 * mb + 8 * (i >> 2) + (i & 3);
+          if (masked && (e >= k_lim || (CAUSAL && e > q_rel))) pv = 0.f;
           dp[mb][i] = pv * (dp[mb][i] - dl);
         }
 #pragma unroll
@@ -389,12 +412,15 @@ attn_bwd_dq_kernel(BwdParams p) {
 // Launch configurations.
 // ---------------------------------------------------------------------------
 // dK/dV: NW waves of 32 keys, WPE waves per SIMD, an NS-slot ring of
-// 32-query blocks.  At d = 128 a wave holds K, V (64 registers) and the dK,
-// dV accumulators (128) and runs alone on its SIMD.  dQ: 64-key tiles in a
+// 32-query blocks.  At d = 128 a wave holds K (32 registers) and the dK, dV
+// accumulators (128); V sits in LDS.  Measured at d = 128: with V in
+// registers too, two waves per SIMD spill ~20 values (still 14 % faster
+// than one wave per SIMD), and V in LDS removes the spills (+14 %); the
+// 2-slot ring keeps two workgroups within a CU's LDS.  dQ: 64-key tiles in a
 // 2-slot ring, two waves per SIMD.
 template <int D>
 struct BwdCfg {
-  static constexpr int NW = 4, WPE = D >= 128 ? 1 : 2, NS = 3;
+  static constexpr int NW = 4, WPE = 2, NS = 2;
   static constexpr int DQ_BC = 64, DQ_NW = 4, DQ_WPE = 2, DQ_NS = 2;
 };
 
@@ -410,7 +436,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t st) {
   if (p.Nk > 0) {
     using C = BwdCfg<D>;
     constexpr int STAGE = 2 * 32 * D * 2 + 256;
-    constexpr int lds = C::NS * STAGE;
+    constexpr int lds = C::NS * STAGE + 32 * C::NW * D * 2;
     auto kern = attn_bwd_dkdv_kernel<TT, D, C::NW, C::WPE, C::NS, CAUSAL>;
     if (hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         e != hipSuccess)
