@@ -29,7 +29,9 @@ Modules:
   partial results;
 * ``backward``: the gradients dQ, dK, dV of the attention definition (the
   chain rule written out; the pages measure a backward pass but print no
-  algorithm for it).
+  algorithm for it);
+* ``paged``: attention over a paged key/value cache (pages gathered through
+  a page table, then the definition).
 
 Pins (the independent checks each function is held to) live in
 ``tests/test_oracle_*.py``; every function here is pinned, none is "parity
@@ -41,3 +43,4 @@ from .tiled import attention_tiled  # noqa: F401
 from . import fp8  # noqa: F401
 from . import splitkv  # noqa: F401
 from . import backward  # noqa: F401
+from . import paged  # noqa: F401
