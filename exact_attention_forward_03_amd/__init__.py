@@ -3,9 +3,10 @@
 
 The C entry points are exposed under their own names with plain integer
 pointers (argument marshalling only): ``attn_fwd``, ``attn_fwd_stream``,
-``attn_fwd_splitkv``, ``attn_merge``, ``attn_bwd``, ``attn_fp8_quantize``,
-``attn_strerror``.  ``forward``, ``forward_splitkv``, ``merge``, ``backward``
-and ``fp8_quantize`` are the torch-facing conveniences: they allocate the
+``attn_fwd_splitkv``, ``attn_fwd_paged``, ``attn_merge``, ``attn_bwd``,
+``attn_fp8_quantize``, ``attn_strerror``.  ``forward``, ``forward_splitkv``,
+``forward_paged``, ``merge``, ``backward`` and ``fp8_quantize`` are the
+torch-facing conveniences: they allocate the
 outputs (and workspaces) with torch on the inputs' device, pass
 ``data_ptr()``s and torch's current HIP stream, and raise ``RuntimeError`` on
 a non-zero return code.  Every step of the
@@ -23,15 +24,16 @@ __all__ = [
     "ATTN_DT_F16", "ATTN_DT_BF16", "ATTN_DT_FP8_E4M3", "ATTN_DT_F32",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP",
     "load", "lib_path", "attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_fp8_quantize",
-    "attn_bwd", "attn_strerror", "forward", "forward_splitkv", "merge", "backward", "fp8_quantize",
+    "attn_fwd_paged", "attn_bwd", "attn_strerror", "forward", "forward_splitkv", "forward_paged", "merge",
+    "backward", "fp8_quantize",
     "default_splits", "EXPORTS",
 ]
 
 ATTN_DT_F16, ATTN_DT_BF16, ATTN_DT_FP8_E4M3, ATTN_DT_F32 = 0, 1, 2, 3
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
 
-EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_bwd", "attn_fp8_quantize",
-           "attn_strerror")
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_fwd_paged", "attn_merge", "attn_bwd",
+           "attn_fp8_quantize", "attn_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -62,6 +64,9 @@ def load():
         lib.attn_fwd_splitkv.restype = _i
         lib.attn_merge.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]
         lib.attn_merge.restype = _i
+        lib.attn_fwd_paged.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _p, _p,
+                                        _p]
+        lib.attn_fwd_paged.restype = _i
         lib.attn_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p]
         lib.attn_bwd.restype = _i
         lib.attn_fp8_quantize.argtypes = [_p, _i, _p, _p, _i, _i, _i, _i, _p, _i, _p]
@@ -94,6 +99,12 @@ def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num
 
 def attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, o_dtype, hip_stream) -> int:
     return load().attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, o_dtype, hip_stream)
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, o, lse, B, H, Nq, d, num_pages, page_size,
+                   max_pages, scale, dtype, num_splits, o_part, lse_part, hip_stream) -> int:
+    return load().attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, o, lse, B, H, Nq, d, num_pages,
+                                 page_size, max_pages, scale, dtype, num_splits, o_part, lse_part, hip_stream)
 
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, dtype, hip_stream) -> int:
@@ -237,6 +248,53 @@ def forward_splitkv(q, k, v, *, causal: bool = False, scale: Optional[float] = N
     rc = attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
                           int(bool(causal)), dt, int(num_splits), _ptr(o_part), _ptr(lse_part),
                           _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def forward_paged(q, k_cache, v_cache, block_table, seqlens_k, *, scale: Optional[float] = None,
+                  num_splits: Optional[int] = None, out=None, lse=None, o_part=None, lse_part=None):
+    """Non-causal attention of q [B, H, Nq, d] over a paged cache through
+    ``attn_fwd_paged``: k_cache, v_cache [num_pages, page_size, H, d] (same
+    dtype as q), block_table int32 [B, max_pages], seqlens_k int32 [B] (all
+    on the GPU) -> (o, lse).  ``num_splits`` defaults to ``default_splits``
+    for the longest possible sequence."""
+    import torch
+
+    for t in (q, k_cache, v_cache, block_table, seqlens_k):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    dt = _dtype_code(q)
+    if _dtype_code(k_cache) != dt or _dtype_code(v_cache) != dt:
+        raise TypeError("q and the caches must share one dtype")
+    if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
+        raise TypeError("block_table and seqlens_k must be int32")
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, H, Nq, d] and the caches [num_pages, page_size, H, d]")
+    B, H, Nq, d = q.shape
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    if tuple(k_cache.shape[2:]) != (H, d) or block_table.dim() != 2 or block_table.shape[0] != B or \
+            tuple(seqlens_k.shape) != (B,):
+        raise ValueError("cache / block_table / seqlens_k shapes do not match q")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        num_splits = default_splits(B, H, Nq, max_pages * page_size, target_workgroups=2 * cus)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if o_part is None:
+        o_part = torch.empty((num_splits, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((num_splits, B, H, Nq), dtype=torch.float32, device=q.device)
+    if o_part.numel() < num_splits * B * H * Nq * d or lse_part.numel() < num_splits * B * H * Nq:
+        raise ValueError("o_part / lse_part are smaller than num_splits chunks")
+    rc = attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seqlens_k), _ptr(out),
+                        _ptr(lse), B, H, Nq, d, num_pages, page_size, max_pages, float(scale), dt,
+                        int(num_splits), _ptr(o_part), _ptr(lse_part), _stream(q.device))
     _check(rc)
     return out, lse
 

@@ -94,7 +94,7 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   if (dtype == ATTN_DT_FP8_E4M3)
     e = attn::launch_fwd_fp8(d, causal != 0, p, st);
   else
-    e = attn::launch_fwd(dtype, d, causal != 0, varlen, false, p, st);
+    e = attn::launch_fwd(dtype, d, causal != 0, varlen, false, false, p, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -151,7 +151,57 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   p.o_part = o_part;
   p.lse_part = lse_part;
   hipStream_t st = (hipStream_t)hip_stream;
-  hipError_t e = attn::launch_fwd(dtype, d, causal != 0, false, true, p, st);
+  hipError_t e = attn::launch_fwd(dtype, d, causal != 0, false, true, false, p, st);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  return attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, dtype, hip_stream);
+}
+
+int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                   const int32_t* seqlens_k, void* o, float* lse, int B, int H, int Nq, int d, int num_pages,
+                   int page_size, int max_pages, float scale, int dtype, int num_splits, float* o_part,
+                   float* lse_part, void* hip_stream) {
+  if (B < 1 || H < 1 || Nq < 0) return ATTN_ERR_INVALID_ARG;
+  if (num_pages < 1 || max_pages < 1 || page_size < 1) return ATTN_ERR_INVALID_ARG;
+  if (Nq > 0 && (!q || !k_cache || !v_cache || !block_table || !seqlens_k || !o || !lse || !o_part || !lse_part))
+    return ATTN_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16 && dtype != ATTN_DT_FP8_E4M3) return ATTN_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(block_table, 4) || !aligned(seqlens_k, 4) || !aligned(o_part, 16) || !aligned(lse_part, 4))
+    return ATTN_ERR_INVALID_ARG;
+  if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_DT_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+  const int tile = attn::fwd_split_tile_keys(d);
+  if (page_size % tile != 0) return ATTN_ERR_UNSUPPORTED;
+  const int64_t max_keys = (int64_t)max_pages * page_size;
+  if (max_keys > INT32_MAX / 2 || (int64_t)B * max_pages > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H > (int64_t)INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
+  if (Nq == 0) return ATTN_OK;
+  const int br = attn::fwd_split_block_rows(dtype, d, false);
+  const int64_t tiles = ((int64_t)Nq + br - 1) / br;
+  const int64_t n_work = (int64_t)B * H * num_splits * tiles;
+  if (n_work > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  // chunks of whole tiles, so that no tile crosses a page
+  int64_t split_len = (max_keys + num_splits - 1) / num_splits;
+  split_len = (split_len + tile - 1) / tile * tile;
+  attn::FwdParams p{};
+  p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.lse = lse;
+  p.B = B; p.H = H; p.Nq = Nq; p.Nk = (int)max_keys;
+  p.c = scale * 1.4426950408889634f;
+  p.tiles_per_head = (int)tiles;
+  p.n_work = (int)n_work;
+  p.n_split = num_splits;
+  p.split_len = (int)split_len;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.block_table = block_table;
+  p.seqlens_k = seqlens_k;
+  p.page_size = page_size;
+  p.max_pages = max_pages;
+  p.num_pages = num_pages;
+  hipStream_t st = (hipStream_t)hip_stream;
+  hipError_t e = attn::launch_fwd(dtype, d, false, false, true, true, p, st);
   if (e != hipSuccess) return ATTN_ERR_HIP;
   return attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, dtype, hip_stream);
 }

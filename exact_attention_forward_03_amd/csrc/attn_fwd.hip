@@ -101,14 +101,32 @@ __device__ __forceinline__ int v_chunk(int r, int ch) { return ch ^ ((r & 3) << 
 // SIMD.
 constexpr int kOptPin = 1, kOptPrio = 2;
 
+// A wave-uniform int32 read through the scalar data cache (s_load): it does
+// not count against the vector-memory counter that paces the tile loads.
+__device__ __forceinline__ int load_uniform(const int32_t* ptr, int64_t idx) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(idx & 0xffffffff));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(idx >> 32));
+  const int64_t i = ((int64_t)hi << 32) | (uint32_t)lo;
+  return ((const __attribute__((address_space(4))) int32_t*)ptr)[i];
+}
+
 // SPLIT: the keys of each head are cut into p.n_split chunks of p.split_len
 // rows; a work item is (head, chunk, query tile) and writes the chunk's
 // normalised O and its lse in fp32 to p.o_part / p.lse_part, for the merge
 // kernel.  Causal masks use absolute key indices (chunk offset + local).
-template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT>
+// PAGED (with SPLIT, non-causal): K and V come from a paged cache through
+// the page table ("Flash Attention 3：让 GPU 跑满的注意力计算", §5.3 pairs
+// the method with PagedAttention by first copying the pages into a
+// contiguous buffer; here each tile's rows are loaded from their page
+// directly, no copy).  Sequence b has p.seqlens_k[b] keys; chunk lengths and
+// the page size are multiples of BC, so one tile lies within one page and
+// needs one table read.
+template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT,
+          bool PAGED>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_dma_kernel(FwdParams p) {
   static_assert(!(SPLIT && VARLEN), "key chunks are for dense batches");
+  static_assert(!PAGED || (SPLIT && !CAUSAL), "paged caches are read by non-causal key-chunk launches");
   constexpr bool PIN = OPT & kOptPin, PRIO = OPT & kOptPrio;
   constexpr int kPreD = 4;  // LDS fragment reads in flight ahead of their MFMA
   constexpr int NQB = 1;
@@ -128,14 +146,17 @@ attn_fwd_dma_kernel(FwdParams p) {
     q_len = p.Nq;
     q_row0 = (int64_t)head * p.Nq;
     if constexpr (SPLIT) {
-      const int64_t kb = min((int64_t)split * p.split_len, (int64_t)p.Nk);
-      const int64_t ke = min(kb + p.split_len, (int64_t)p.Nk);
+      int64_t nk = p.Nk;
+      if constexpr (PAGED)
+        nk = min(max(load_uniform(p.seqlens_k, head / p.H), 0), p.max_pages * p.page_size);
+      const int64_t kb = min((int64_t)split * p.split_len, nk);
+      const int64_t ke = min(kb + p.split_len, nk);
       k_off = (int)kb;
       k_len = (int)(ke - kb);
     } else {
       k_len = p.Nk;
     }
-    k_row0 = (int64_t)head * p.Nk + k_off;
+    k_row0 = PAGED ? 0 : (int64_t)head * p.Nk + k_off;
     qt = CAUSAL ? (p.tiles_per_head - 1 - t) : t;
   } else {
     int acc = 0, seq = -1, qb = 0, qe = 0, nts = 0;
@@ -203,24 +224,59 @@ attn_fwd_dma_kernel(FwdParams p) {
   // RPB*block + l / CHUNKS and fetches the logical chunk stored there.  Rows
   // past the end of the keys re-read the last key (finite values, masked).
   constexpr int RPB = 1024 / C::ROWB;  // rows per 1 KiB block
+  // Paged: tile kt's first row is row `ka0 mod page_size` of page
+  // block_table[b][ka0 / page_size] (ka0 = absolute key of the tile's first
+  // row; page indices clamped into the cache), and rows are H * ROWB bytes
+  // apart.  Returns the byte offset of that row in the cache.
+  auto paged_base = [&](int kt) -> int64_t {
+    const int b = head / p.H, h = head - b * p.H;
+    const int ka0 = k_off + kt * BC;
+    const int j = ka0 / p.page_size;
+    const int pg = min(max(load_uniform(p.block_table, (int64_t)b * p.max_pages + j), 0), p.num_pages - 1);
+    return (((int64_t)pg * p.page_size + (ka0 - j * p.page_size)) * p.H + h) * C::ROWB;
+  };
   auto load_k = [&](int kt, int buf) {
+    if constexpr (PAGED) {
+      const uint8_t* base = (const uint8_t*)p.k + paged_base(kt);
 #pragma unroll
-    for (int i = 0; i < C::LOADS / NW; ++i) {
-      const int blk = wv * (C::LOADS / NW) + i;
-      const int r = blk * RPB + lane / C::CHUNKS;
-      const int key = min(kt * BC + r, k_len - 1);
-      const uint8_t* src = Kb + (int64_t)key * C::ROWB + k_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsK + buf * C::TILEB + blk * 1024), 16, 0, 0);
+      for (int i = 0; i < C::LOADS / NW; ++i) {
+        const int blk = wv * (C::LOADS / NW) + i;
+        const int r = blk * RPB + lane / C::CHUNKS;
+        const int rr = min(r, k_len - 1 - kt * BC);
+        const uint8_t* src = base + (int64_t)rr * p.H * C::ROWB + k_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsK + buf * C::TILEB + blk * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::LOADS / NW; ++i) {
+        const int blk = wv * (C::LOADS / NW) + i;
+        const int r = blk * RPB + lane / C::CHUNKS;
+        const int key = min(kt * BC + r, k_len - 1);
+        const uint8_t* src = Kb + (int64_t)key * C::ROWB + k_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsK + buf * C::TILEB + blk * 1024), 16, 0, 0);
+      }
     }
   };
   auto load_v = [&](int kt, int buf) {
+    if constexpr (PAGED) {
+      const uint8_t* base = (const uint8_t*)p.v + paged_base(kt);
 #pragma unroll
-    for (int i = 0; i < C::LOADS / NW; ++i) {
-      const int blk = wv * (C::LOADS / NW) + i;
-      const int r = blk * RPB + lane / C::CHUNKS;
-      const int key = min(kt * BC + r, k_len - 1);
-      const uint8_t* src = Vb + (int64_t)key * C::ROWB + v_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsV + buf * C::TILEB + blk * 1024), 16, 0, 0);
+      for (int i = 0; i < C::LOADS / NW; ++i) {
+        const int blk = wv * (C::LOADS / NW) + i;
+        const int r = blk * RPB + lane / C::CHUNKS;
+        const int rr = min(r, k_len - 1 - kt * BC);
+        const uint8_t* src = base + (int64_t)rr * p.H * C::ROWB + v_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsV + buf * C::TILEB + blk * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::LOADS / NW; ++i) {
+        const int blk = wv * (C::LOADS / NW) + i;
+        const int r = blk * RPB + lane / C::CHUNKS;
+        const int key = min(kt * BC + r, k_len - 1);
+        const uint8_t* src = Vb + (int64_t)key * C::ROWB + v_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsV + buf * C::TILEB + blk * 1024), 16, 0, 0);
+      }
     }
   };
 
@@ -463,10 +519,11 @@ attn_fwd_dma_kernel(FwdParams p) {
   }
 }
 
-template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT>
+template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT,
+          bool PAGED>
 hipError_t launch_dma_one(const FwdParams& p, hipStream_t st) {
   using C = PipeCfg<D, 1, BC, NW, NS>;
-  auto kern = attn_fwd_dma_kernel<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT>;
+  auto kern = attn_fwd_dma_kernel<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, PAGED>;
   static bool attr_set = false;  // idempotent; a benign race between threads
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
@@ -496,28 +553,34 @@ template <bool CAUSAL> struct DmaTile<256, CAUSAL> {
 // 4-wave workgroups with a 64 KiB ring, so two run on each CU.
 struct SplitTile128 { static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
 
-template <typename TT, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
+template <typename TT, int D, bool CAUSAL, bool VARLEN, bool SPLIT, bool PAGED = false>
 hipError_t launch_dma_d(const FwdParams& p, hipStream_t st) {
   using T = DmaTile<D, CAUSAL>;
   if constexpr (SPLIT && D == 128) {
     using S = SplitTile128;
-    return launch_dma_one<TT, D, S::BC, S::NW, S::WPE, S::NS, S::OPT, CAUSAL, VARLEN, SPLIT>(p, st);
+    return launch_dma_one<TT, D, S::BC, S::NW, S::WPE, S::NS, S::OPT, CAUSAL, VARLEN, SPLIT, PAGED>(p, st);
+  } else {
+    return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, T::OPT, CAUSAL, VARLEN, SPLIT, PAGED>(p, st);
   }
-  return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, T::OPT, CAUSAL, VARLEN, SPLIT>(p, st);
 }
 
-template <typename TT, bool CAUSAL, bool VARLEN, bool SPLIT>
+template <typename TT, bool CAUSAL, bool VARLEN, bool SPLIT, bool PAGED = false>
 hipError_t launch_dma_cv(int d, const FwdParams& p, hipStream_t st) {
   switch (d) {
-    case 64: return launch_dma_d<TT, 64, CAUSAL, VARLEN, SPLIT>(p, st);
-    case 128: return launch_dma_d<TT, 128, CAUSAL, VARLEN, SPLIT>(p, st);
-    case 256: return launch_dma_d<TT, 256, CAUSAL, VARLEN, SPLIT>(p, st);
+    case 64: return launch_dma_d<TT, 64, CAUSAL, VARLEN, SPLIT, PAGED>(p, st);
+    case 128: return launch_dma_d<TT, 128, CAUSAL, VARLEN, SPLIT, PAGED>(p, st);
+    case 256: return launch_dma_d<TT, 256, CAUSAL, VARLEN, SPLIT, PAGED>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename TT>
-hipError_t launch_dma_t(int d, bool causal, bool varlen, bool split, const FwdParams& p, hipStream_t st) {
+hipError_t launch_dma_t(int d, bool causal, bool varlen, bool split, bool paged, const FwdParams& p,
+                        hipStream_t st) {
+  if (paged) {
+    if (!split || varlen || causal) return hipErrorInvalidValue;
+    return launch_dma_cv<TT, false, false, true, true>(d, p, st);
+  }
   if (split) {
     if (varlen) return hipErrorInvalidValue;
     return causal ? launch_dma_cv<TT, true, false, true>(d, p, st) : launch_dma_cv<TT, false, false, true>(d, p, st);
@@ -543,9 +606,18 @@ int fwd_block_rows(int dtype, int d, bool causal) {
   }
 }
 
-hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, const FwdParams& p, hipStream_t st) {
-  if (dtype == 0) return launch_dma_t<f16_t>(d, causal, varlen, split, p, st);
-  return launch_dma_t<bf16_t>(d, causal, varlen, split, p, st);
+int fwd_split_tile_keys(int d) {
+  switch (d) {
+    case 64: return DmaTile<64, false>::BC;
+    case 128: return SplitTile128::BC;
+    default: return DmaTile<256, false>::BC;
+  }
+}
+
+hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, bool paged, const FwdParams& p,
+                      hipStream_t st) {
+  if (dtype == 0) return launch_dma_t<f16_t>(d, causal, varlen, split, paged, p, st);
+  return launch_dma_t<bf16_t>(d, causal, varlen, split, paged, p, st);
 }
 
 }  // namespace attn

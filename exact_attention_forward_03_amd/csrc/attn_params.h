@@ -26,6 +26,14 @@ struct FwdParams {
   int split_len;         // keys per chunk
   float* o_part;         // [n_split, B, H, Nq, d] fp32 normalised partial outputs
   float* lse_part;       // [n_split, B, H, Nq]
+  // paged key/value cache (split launches only): K and V rows of token t of
+  // sequence b, head h at cache[block_table[b * max_pages + t / page_size],
+  // t % page_size, h] of a [num_pages, page_size, H, d] array
+  const int32_t* block_table;  // [B, max_pages]
+  const int32_t* seqlens_k;    // [B]
+  int page_size;
+  int max_pages;
+  int num_pages;
 };
 
 struct MergeParams {
@@ -75,9 +83,11 @@ hipError_t launch_bwd(int dtype, int d, bool causal, BwdParams p, hipStream_t st
 
 int fwd_block_rows(int dtype, int d, bool causal);
 int fwd_split_block_rows(int dtype, int d, bool causal);  // key-chunk launches
+int fwd_split_tile_keys(int d);  // key rows per tile of key-chunk launches (chunk lengths are multiples)
 int fwd_fp8_block_rows(bool causal);
 
-hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, const FwdParams& p, hipStream_t st);
+hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, bool paged, const FwdParams& p,
+                      hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_fwd_fp8(int d, bool causal, const FwdParams& p, hipStream_t st);
 hipError_t launch_fp8_prep(const PrepParams& p, bool per_tensor, hipStream_t st);

@@ -168,6 +168,37 @@ int attn_merge(const float* o_part, const float* lse_part, int num_splits, int B
                void* o, float* lse, int o_dtype, void* hip_stream);
 
 /*
+ * attn_fwd_paged — attention of dense queries over a paged key/value cache
+ * ("Flash Attention 3：让 GPU 跑满的注意力计算", §5.3: the method run on the
+ * pages of a PagedAttention cache; here the kernel reads each tile from its
+ * page through the table, no contiguous copy is made), computed over
+ * `num_splits` key chunks and merged as attn_fwd_splitkv.  Non-causal: every
+ * query of sequence b attends to all its seqlens_k[b] cached keys (the
+ * decoding setting).
+ *   q [B, H, Nq, d]; o [B, H, Nq, d] (same dtype, ATTN_DT_F16/BF16);
+ *   lse fp32 [B, H, Nq];
+ *   k_cache, v_cache [num_pages, page_size, H, d] of the same dtype: row
+ *     (page, i, h) holds head h of one token;
+ *   block_table int32 [B, max_pages]: token t of sequence b is row
+ *     t % page_size of page block_table[b][t / page_size];
+ *   seqlens_k int32 [B]: keys of each sequence (clamped to
+ *     [0, max_pages * page_size]; 0 gives O = 0, lse = -inf);
+ *   page indices outside [0, num_pages) are clamped (never read out of
+ *     bounds; the result is then unspecified);
+ *   page_size a multiple of 64 (else ATTN_ERR_UNSUPPORTED);
+ *   o_part fp32 [num_splits, B, H, Nq, d], lse_part fp32 [num_splits, B, H,
+ *     Nq]: caller-owned workspace, as attn_fwd_splitkv (chunks of
+ *     ceil(max_pages * page_size / num_splits) keys rounded up to 64).
+ *   All device pointers; tensors 16-byte aligned, int32 and lse arrays
+ *   4-byte aligned; NULL allowed only when Nq = 0.  fp8: UNSUPPORTED.  Same
+ *   stream and error rules as attn_fwd_stream.
+ */
+int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                   const int32_t* seqlens_k, void* o, float* lse, int B, int H, int Nq, int d, int num_pages,
+                   int page_size, int max_pages, float scale, int dtype, int num_splits, float* o_part,
+                   float* lse_part, void* hip_stream);
+
+/*
  * attn_bwd — gradients of the attention computed by attn_fwd: given dO =
  * dL/dO, writes dQ, dK, dV (the derivative of the forward definition of
  * "Flash Attention 3：让 GPU 跑满的注意力计算", §1.2 and §2.2; the

@@ -226,3 +226,37 @@ def test_bwd_unsupported_and_empty(lib):
     # no queries and no keys: nothing to write, no launch
     none = dict(q=None, k=None, v=None, o=None, lse=None, dout=None, dq=None, dk=None, dv=None, delta=None)
     assert bwd_call(Nq=0, Nk=0, **none) == attn.ATTN_OK
+
+
+def paged_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, o=FAKE, lse=FAKE, B=2, H=4, Nq=1, d=128, num_pages=64,
+             page_size=128, max_pages=16, scale=0.125, dtype=attn.ATTN_DT_BF16, num_splits=4, o_part=FAKE,
+             lse_part=FAKE)
+    a.update(over)
+    return attn.attn_fwd_paged(a["q"], a["k"], a["v"], a["table"], a["lens"], a["o"], a["lse"], a["B"], a["H"],
+                               a["Nq"], a["d"], a["num_pages"], a["page_size"], a["max_pages"], a["scale"],
+                               a["dtype"], a["num_splits"], a["o_part"], a["lse_part"], None)
+
+
+PAGED_INVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(table=None), dict(lens=None), dict(o=None), dict(lse=None),
+    dict(o_part=None), dict(lse_part=None), dict(B=0), dict(H=0), dict(Nq=-1), dict(num_pages=0),
+    dict(page_size=0), dict(max_pages=0), dict(scale=float("nan")), dict(dtype=9), dict(num_splits=0),
+    dict(num_splits=1025), dict(q=FAKE + 8), dict(k=FAKE + 8), dict(table=FAKE + 2), dict(lens=FAKE + 1),
+    dict(o_part=FAKE + 4), dict(max_pages=1 << 24, page_size=1 << 10),
+]
+
+
+@pytest.mark.parametrize("over", PAGED_INVALID, ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_paged_invalid(lib, over):
+    assert paged_call(**over) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_paged_unsupported_and_empty(lib):
+    assert paged_call(d=96) == attn.ATTN_ERR_UNSUPPORTED
+    assert paged_call(page_size=96) == attn.ATTN_ERR_UNSUPPORTED
+    assert paged_call(page_size=16) == attn.ATTN_ERR_UNSUPPORTED
+    assert paged_call(dtype=attn.ATTN_DT_FP8_E4M3) == attn.ATTN_ERR_UNSUPPORTED
+    assert paged_call(Nq=0) == attn.ATTN_OK
+    none = dict(q=None, k=None, v=None, table=None, lens=None, o=None, lse=None, o_part=None, lse_part=None)
+    assert paged_call(Nq=0, **none) == attn.ATTN_OK
