@@ -159,7 +159,7 @@ def bench_decode(attn, steps, warmup):
     """Decoding (B=2 H=32, one query per head, Nk=32768, d=128, bf16): attention
     over key chunks plus the merge, against HBM bandwidth (the K and V bytes
     are the algorithmic traffic); the single-pass kernel on the same shape
-    for comparison."""
+    for comparison; the same keys and values read from a paged cache."""
     import numpy as np
     import torch
 
@@ -189,9 +189,34 @@ def bench_decode(attn, steps, warmup):
     ms1 = float(np.mean(timed_launches(run_single, steps, stream)))
     kv_bytes = 2 * k.numel() * 2
     gbs = kv_bytes / (ms / 1e3) / 1e9
-    return {"decode_bf16_splitkv": {"ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                                    "num_splits": splits, "single_pass_ms": round(ms1, 4),
-                                    "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}}
+    out = {"decode_bf16_splitkv": {"ms": round(ms, 4), "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                   "num_splits": splits, "single_pass_ms": round(ms1, 4),
+                                   "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}}
+
+    # the same keys and values in a paged cache: 256-token pages stored in a
+    # shuffled order, read through the page table
+    P = 256
+    n_pages = w.B * w.Nk // P
+    perm = torch.from_numpy(np.random.default_rng(1).permutation(n_pages)).cuda()
+    kc = torch.empty((n_pages, P, w.H, w.d), dtype=k.dtype, device="cuda")
+    vc = torch.empty_like(kc)
+    kc[perm] = k.transpose(1, 2).reshape(n_pages, P, w.H, w.d)
+    vc[perm] = v.transpose(1, 2).reshape(n_pages, P, w.H, w.d)
+    table = perm.to(torch.int32).reshape(w.B, w.Nk // P).contiguous()
+    lens = torch.full((w.B,), w.Nk, dtype=torch.int32, device="cuda")
+
+    def run_paged():
+        attn.forward_paged(q, kc, vc, table, lens, scale=w.scale, num_splits=splits, out=o, lse=lse, o_part=op,
+                           lse_part=lp)
+
+    for _ in range(warmup):
+        run_paged()
+    msp = float(np.mean(timed_launches(run_paged, steps, stream)))
+    gbp = kv_bytes / (msp / 1e3) / 1e9
+    out["decode_bf16_paged"] = {"ms": round(msp, 4), "gbs": round(gbp, 1), "frac_hbm": round(gbp / HBM_PEAK_GBS, 4),
+                                "page_size": P, "num_splits": splits, "vs_contiguous": round(msp / ms, 4),
+                                "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
+    return out
 
 
 def bench_backward(attn, steps, warmup):
