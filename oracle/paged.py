@@ -15,6 +15,12 @@ it.  This module is that definition written out:
   queries are the newest tokens, as in decoding), ``oracle.attention``.
 
 A sequence with no valid token gives O = 0 and lse = -inf.
+
+Low-precision caches (§4.1.3 of the same post: INT8 and FP8 KV caches) hold
+8-bit codes and one fp32 scale per (token, head); the cached key is
+scale * decode(code), with decode the e4m3 format definition (``oracle.fp8``)
+or the signed 8-bit integer.  ``dequantize`` writes that out; attention then
+runs on the dequantized cache.
 """
 
 from __future__ import annotations
@@ -22,6 +28,7 @@ from __future__ import annotations
 import numpy as np
 
 from .exact import _f64, attention
+from .fp8 import e4m3_decode
 
 
 def gather(cache, block_table, seqlens, b: int) -> np.ndarray:
@@ -49,3 +56,22 @@ def attention_paged(q, k_cache, v_cache, block_table, seqlens, scale: float):
         v = gather(v_cache, block_table, seqlens, b)
         o[b], lse[b] = attention(q[b], k, v, scale, False)
     return o, lse
+
+
+def dequantize(codes, scales, kind: str) -> np.ndarray:
+    """codes uint8 [num_pages, page_size, H, d], scales [num_pages, page_size, H]
+    -> float64 cache scale * decode(code); kind "e4m3" or "int8"."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    if kind == "e4m3":
+        vals = e4m3_decode(codes)
+    elif kind == "int8":
+        vals = codes.view(np.int8).astype(np.float64)
+    else:
+        raise ValueError(kind)
+    return np.asarray(scales, dtype=np.float64)[..., None] * vals
+
+
+def attention_paged_quant(q, k_codes, v_codes, k_scales, v_scales, block_table, seqlens, scale: float, kind: str):
+    """Attention over an 8-bit paged cache: the definition on the dequantized cache."""
+    return attention_paged(q, dequantize(k_codes, k_scales, kind), dequantize(v_codes, v_scales, kind),
+                           block_table, seqlens, scale)

@@ -137,3 +137,44 @@ def test_mutations(name, fn):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught > 0, f"no pin catches: {name}"
+
+
+# ---------------------------------------------------------------- 8-bit caches
+
+def test_dequantize_int8_and_e4m3():
+    codes = np.array([[[[0x00, 0x01, 0x7f, 0x80, 0x81, 0xff, 0x38, 0xb8]]]], dtype=np.uint8)
+    sc = np.array([[[0.5]]])
+    # int8: two's complement
+    np.testing.assert_array_equal(PG.dequantize(codes, sc, "int8")[0, 0, 0],
+                                  0.5 * np.array([0, 1, 127, -128, -127, -1, 56, -72]))
+    # e4m3: 0x38 = 1.0, 0xb8 = -1.0, 0x01 = 2^-9 (smallest subnormal), 0x7f is NaN in e4m3fn
+    e = PG.dequantize(codes, sc, "e4m3")[0, 0, 0]
+    assert e[0] == 0.0 and e[1] == 0.5 * 2.0 ** -9 and e[6] == 0.5 and e[7] == -0.5
+    assert np.isnan(e[2])
+
+
+def test_quantized_cache_per_token_scales():
+    """A per-(token, head) scale multiplies that key row (or value row); with
+    codes and scales built from a dense cache the result is the dense one."""
+    rng = np.random.default_rng(8)
+    B, H, L, d, P = 2, 2, 20, 4, 8
+    q = rng.standard_normal((B, H, 3, d))
+    kint = rng.integers(-100, 100, size=(B, H, L, d))
+    vint = rng.integers(-100, 100, size=(B, H, L, d))
+    ks = rng.uniform(0.01, 0.03, size=(B, H, L))
+    vs = rng.uniform(0.01, 0.03, size=(B, H, L))
+    kc, table = _cut(kint.astype(np.float64), P, np.random.default_rng(4))
+    vc, _ = _cut(vint.astype(np.float64), P, np.random.default_rng(4))
+    ksc, _ = _cut(ks[..., None], P, np.random.default_rng(4))
+    vsc, _ = _cut(vs[..., None], P, np.random.default_rng(4))
+    codes_k = kc.astype(np.int64).astype(np.int8).view(np.uint8)
+    codes_v = vc.astype(np.int64).astype(np.int8).view(np.uint8)
+    seqlens = np.array([20, 11])
+    o, lse = PG.attention_paged_quant(q, codes_k, codes_v, ksc[..., 0], vsc[..., 0], table, seqlens, 0.7, "int8")
+    for b in range(B):
+        n = seqlens[b]
+        kd = ks[b, :, :n, None] * kint[b, :, :n]
+        vd = vs[b, :, :n, None] * vint[b, :, :n]
+        ro, rl = oracle.attention(q[b], kd, vd, 0.7, False)
+        np.testing.assert_allclose(o[b], ro, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[b], rl, rtol=0, atol=1e-13)
