@@ -21,7 +21,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "ATTN_DT_F16", "ATTN_DT_BF16", "ATTN_DT_FP8_E4M3", "ATTN_DT_F32",
+    "ATTN_DT_F16", "ATTN_DT_BF16", "ATTN_DT_FP8_E4M3", "ATTN_DT_F32", "ATTN_DT_INT8",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP",
     "load", "lib_path", "attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_fp8_quantize",
     "attn_fwd_paged", "attn_bwd", "attn_strerror", "forward", "forward_splitkv", "forward_paged", "merge",
@@ -29,7 +29,7 @@ __all__ = [
     "default_splits", "EXPORTS",
 ]
 
-ATTN_DT_F16, ATTN_DT_BF16, ATTN_DT_FP8_E4M3, ATTN_DT_F32 = 0, 1, 2, 3
+ATTN_DT_F16, ATTN_DT_BF16, ATTN_DT_FP8_E4M3, ATTN_DT_F32, ATTN_DT_INT8 = 0, 1, 2, 3, 4
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
 
 EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_fwd_paged", "attn_merge", "attn_bwd",
@@ -64,8 +64,8 @@ def load():
         lib.attn_fwd_splitkv.restype = _i
         lib.attn_merge.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]
         lib.attn_merge.restype = _i
-        lib.attn_fwd_paged.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _p, _p,
-                                        _p]
+        lib.attn_fwd_paged.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i,
+                                        _i, _p, _p, _p]
         lib.attn_fwd_paged.restype = _i
         lib.attn_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p]
         lib.attn_bwd.restype = _i
@@ -101,10 +101,11 @@ def attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, o_dtype, hip_s
     return load().attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, o_dtype, hip_stream)
 
 
-def attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, o, lse, B, H, Nq, d, num_pages, page_size,
-                   max_pages, scale, dtype, num_splits, o_part, lse_part, hip_stream) -> int:
-    return load().attn_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, o, lse, B, H, Nq, d, num_pages,
-                                 page_size, max_pages, scale, dtype, num_splits, o_part, lse_part, hip_stream)
+def attn_fwd_paged(q, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k, o, lse, B, H, Nq, d, num_pages,
+                   page_size, max_pages, scale, dtype, kv_dtype, num_splits, o_part, lse_part, hip_stream) -> int:
+    return load().attn_fwd_paged(q, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k, o, lse, B, H, Nq, d,
+                                 num_pages, page_size, max_pages, scale, dtype, kv_dtype, num_splits, o_part,
+                                 lse_part, hip_stream)
 
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, dtype, hip_stream) -> int:
@@ -253,20 +254,32 @@ def forward_splitkv(q, k, v, *, causal: bool = False, scale: Optional[float] = N
 
 
 def forward_paged(q, k_cache, v_cache, block_table, seqlens_k, *, scale: Optional[float] = None,
-                  num_splits: Optional[int] = None, out=None, lse=None, o_part=None, lse_part=None):
+                  k_scale=None, v_scale=None, kv_dtype: Optional[str] = None, num_splits: Optional[int] = None,
+                  out=None, lse=None, o_part=None, lse_part=None):
     """Non-causal attention of q [B, H, Nq, d] over a paged cache through
-    ``attn_fwd_paged``: k_cache, v_cache [num_pages, page_size, H, d] (same
-    dtype as q), block_table int32 [B, max_pages], seqlens_k int32 [B] (all
-    on the GPU) -> (o, lse).  ``num_splits`` defaults to ``default_splits``
-    for the longest possible sequence."""
+    ``attn_fwd_paged``: k_cache, v_cache [num_pages, page_size, H, d],
+    block_table int32 [B, max_pages], seqlens_k int32 [B] (all on the GPU)
+    -> (o, lse).  The caches have q's dtype, or hold 8-bit codes (uint8;
+    ``kv_dtype`` "e4m3" or "int8") with float32 ``k_scale`` / ``v_scale``
+    [num_pages, page_size, H].  ``num_splits`` defaults to
+    ``default_splits`` for the longest possible sequence."""
     import torch
 
     for t in (q, k_cache, v_cache, block_table, seqlens_k):
         if not t.is_contiguous():
             raise ValueError("inputs must be contiguous")
     dt = _dtype_code(q)
-    if _dtype_code(k_cache) != dt or _dtype_code(v_cache) != dt:
-        raise TypeError("q and the caches must share one dtype")
+    if kv_dtype is None:
+        if _dtype_code(k_cache) != dt or _dtype_code(v_cache) != dt:
+            raise TypeError("q and the caches must share one dtype")
+        kvd = dt
+    else:
+        kvd = {"e4m3": ATTN_DT_FP8_E4M3, "int8": ATTN_DT_INT8}[kv_dtype]
+        if k_cache.element_size() != 1 or v_cache.element_size() != 1 or k_scale is None or v_scale is None:
+            raise TypeError("8-bit caches need 1-byte codes and k_scale / v_scale")
+        for t in (k_scale, v_scale):
+            if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(k_cache.shape[:3]):
+                raise ValueError("k_scale / v_scale must be contiguous float32 [num_pages, page_size, H]")
     if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise TypeError("block_table and seqlens_k must be int32")
     if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
@@ -292,9 +305,9 @@ def forward_paged(q, k_cache, v_cache, block_table, seqlens_k, *, scale: Optiona
         lse_part = torch.empty((num_splits, B, H, Nq), dtype=torch.float32, device=q.device)
     if o_part.numel() < num_splits * B * H * Nq * d or lse_part.numel() < num_splits * B * H * Nq:
         raise ValueError("o_part / lse_part are smaller than num_splits chunks")
-    rc = attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seqlens_k), _ptr(out),
-                        _ptr(lse), B, H, Nq, d, num_pages, page_size, max_pages, float(scale), dt,
-                        int(num_splits), _ptr(o_part), _ptr(lse_part), _stream(q.device))
+    rc = attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                        _ptr(seqlens_k), _ptr(out), _ptr(lse), B, H, Nq, d, num_pages, page_size, max_pages,
+                        float(scale), dt, kvd, int(num_splits), _ptr(o_part), _ptr(lse_part), _stream(q.device))
     _check(rc)
     return out, lse
 

@@ -94,7 +94,7 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   if (dtype == ATTN_DT_FP8_E4M3)
     e = attn::launch_fwd_fp8(d, causal != 0, p, st);
   else
-    e = attn::launch_fwd(dtype, d, causal != 0, varlen, false, false, p, st);
+    e = attn::launch_fwd(dtype, d, causal != 0, varlen, false, 0, p, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -151,24 +151,28 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   p.o_part = o_part;
   p.lse_part = lse_part;
   hipStream_t st = (hipStream_t)hip_stream;
-  hipError_t e = attn::launch_fwd(dtype, d, causal != 0, false, true, false, p, st);
+  hipError_t e = attn::launch_fwd(dtype, d, causal != 0, false, true, 0, p, st);
   if (e != hipSuccess) return ATTN_ERR_HIP;
   return attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, dtype, hip_stream);
 }
 
-int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
-                   const int32_t* seqlens_k, void* o, float* lse, int B, int H, int Nq, int d, int num_pages,
-                   int page_size, int max_pages, float scale, int dtype, int num_splits, float* o_part,
-                   float* lse_part, void* hip_stream) {
+int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                   const float* v_scale, const int32_t* block_table, const int32_t* seqlens_k, void* o, float* lse,
+                   int B, int H, int Nq, int d, int num_pages, int page_size, int max_pages, float scale, int dtype,
+                   int kv_dtype, int num_splits, float* o_part, float* lse_part, void* hip_stream) {
   if (B < 1 || H < 1 || Nq < 0) return ATTN_ERR_INVALID_ARG;
   if (num_pages < 1 || max_pages < 1 || page_size < 1) return ATTN_ERR_INVALID_ARG;
   if (Nq > 0 && (!q || !k_cache || !v_cache || !block_table || !seqlens_k || !o || !lse || !o_part || !lse_part))
     return ATTN_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16 && dtype != ATTN_DT_FP8_E4M3) return ATTN_ERR_INVALID_ARG;
+  const bool quant = kv_dtype == ATTN_DT_FP8_E4M3 || kv_dtype == ATTN_DT_INT8;
+  if (kv_dtype != dtype && !quant) return ATTN_ERR_INVALID_ARG;
+  if (quant && Nq > 0 && (!k_scale || !v_scale)) return ATTN_ERR_INVALID_ARG;
   if (num_splits < 1 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
-      !aligned(block_table, 4) || !aligned(seqlens_k, 4) || !aligned(o_part, 16) || !aligned(lse_part, 4))
+      !aligned(block_table, 4) || !aligned(seqlens_k, 4) || !aligned(o_part, 16) || !aligned(lse_part, 4) ||
+      !aligned(k_scale, 4) || !aligned(v_scale, 4))
     return ATTN_ERR_INVALID_ARG;
   if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
   if (dtype == ATTN_DT_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
@@ -200,8 +204,11 @@ int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, cons
   p.page_size = page_size;
   p.max_pages = max_pages;
   p.num_pages = num_pages;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  const int kv = kv_dtype == ATTN_DT_FP8_E4M3 ? 2 : kv_dtype == ATTN_DT_INT8 ? 3 : 1;
   hipStream_t st = (hipStream_t)hip_stream;
-  hipError_t e = attn::launch_fwd(dtype, d, false, false, true, true, p, st);
+  hipError_t e = attn::launch_fwd(dtype, d, false, false, true, kv, p, st);
   if (e != hipSuccess) return ATTN_ERR_HIP;
   return attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, dtype, hip_stream);
 }

@@ -114,17 +114,49 @@ __device__ __forceinline__ int load_uniform(const int32_t* ptr, int64_t idx) {
 // rows; a work item is (head, chunk, query tile) and writes the chunk's
 // normalised O and its lse in fp32 to p.o_part / p.lse_part, for the merge
 // kernel.  Causal masks use absolute key indices (chunk offset + local).
-// PAGED (with SPLIT, non-causal): K and V come from a paged cache through
-// the page table ("Flash Attention 3：让 GPU 跑满的注意力计算", §5.3 pairs
-// the method with PagedAttention by first copying the pages into a
+// KV (with SPLIT, non-causal): kKvPaged* read K and V from a paged cache
+// through the page table ("Flash Attention 3：让 GPU 跑满的注意力计算", §5.3
+// pairs the method with PagedAttention by first copying the pages into a
 // contiguous buffer; here each tile's rows are loaded from their page
 // directly, no copy).  Sequence b has p.seqlens_k[b] keys; chunk lengths and
 // the page size are multiples of BC, so one tile lies within one page and
-// needs one table read.
+// needs one table read.  kKvPagedE4m3 / kKvPagedInt8: the cache holds 8-bit
+// codes with one fp32 scale per (token, head) in p.k_scale / p.v_scale (the
+// INT8 and FP8 KV caches of §4.1.3 of the same post).  Their tiles are
+// loaded into registers, converted exactly to the 16-bit type (every e4m3
+// and int8 value is representable) and written to the same LDS tiles; the K
+// scale multiplies the scores of its key, the V scale the probability of its
+// key as it enters the PV product (l sums the unscaled probabilities).
+constexpr int kKvDense = 0, kKvPaged = 1, kKvPagedE4m3 = 2, kKvPagedInt8 = 3;
+
+// 16 8-bit codes (one uint4) -> 16 values of the 16-bit type (two uint4), exactly.
+template <int KVQ, typename TT>
+__device__ __forceinline__ void decode16(TT t, const uint4& w, uint4& lo, uint4& hi) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (KVQ == kKvPagedE4m3) {
+      const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], false);
+      const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[i], true);
+      out[2 * i] = pack2(t, a[0], a[1]);
+      out[2 * i + 1] = pack2(t, b[0], b[1]);
+    } else {
+      const uint32_t v = ws[i];
+      out[2 * i] = pack2(t, (float)(int8_t)(v & 0xff), (float)(int8_t)((v >> 8) & 0xff));
+      out[2 * i + 1] = pack2(t, (float)(int8_t)((v >> 16) & 0xff), (float)(int8_t)(v >> 24));
+    }
+  }
+  lo = make_uint4(out[0], out[1], out[2], out[3]);
+  hi = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
 template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT,
-          bool PAGED>
+          int KV>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_dma_kernel(FwdParams p) {
+  constexpr bool PAGED = KV != kKvDense;
+  constexpr int KVQ = KV >= kKvPagedE4m3 ? KV : 0;  // 8-bit cache kind, 0 for 16-bit
   static_assert(!(SPLIT && VARLEN), "key chunks are for dense batches");
   static_assert(!PAGED || (SPLIT && !CAUSAL), "paged caches are read by non-causal key-chunk launches");
   constexpr bool PIN = OPT & kOptPin, PRIO = OPT & kOptPrio;
@@ -226,18 +258,18 @@ attn_fwd_dma_kernel(FwdParams p) {
   constexpr int RPB = 1024 / C::ROWB;  // rows per 1 KiB block
   // Paged: tile kt's first row is row `ka0 mod page_size` of page
   // block_table[b][ka0 / page_size] (ka0 = absolute key of the tile's first
-  // row; page indices clamped into the cache), and rows are H * ROWB bytes
-  // apart.  Returns the byte offset of that row in the cache.
-  auto paged_base = [&](int kt) -> int64_t {
+  // row; page indices clamped into the cache); the rows of a tile are H
+  // cache rows apart.  Returns the index of that (token, head) row.
+  auto paged_row = [&](int kt) -> int64_t {
     const int b = head / p.H, h = head - b * p.H;
     const int ka0 = k_off + kt * BC;
     const int j = ka0 / p.page_size;
     const int pg = min(max(load_uniform(p.block_table, (int64_t)b * p.max_pages + j), 0), p.num_pages - 1);
-    return (((int64_t)pg * p.page_size + (ka0 - j * p.page_size)) * p.H + h) * C::ROWB;
+    return ((int64_t)pg * p.page_size + (ka0 - j * p.page_size)) * p.H + h;
   };
   auto load_k = [&](int kt, int buf) {
     if constexpr (PAGED) {
-      const uint8_t* base = (const uint8_t*)p.k + paged_base(kt);
+      const uint8_t* base = (const uint8_t*)p.k + paged_row(kt) * C::ROWB;
 #pragma unroll
       for (int i = 0; i < C::LOADS / NW; ++i) {
         const int blk = wv * (C::LOADS / NW) + i;
@@ -259,7 +291,7 @@ attn_fwd_dma_kernel(FwdParams p) {
   };
   auto load_v = [&](int kt, int buf) {
     if constexpr (PAGED) {
-      const uint8_t* base = (const uint8_t*)p.v + paged_base(kt);
+      const uint8_t* base = (const uint8_t*)p.v + paged_row(kt) * C::ROWB;
 #pragma unroll
       for (int i = 0; i < C::LOADS / NW; ++i) {
         const int blk = wv * (C::LOADS / NW) + i;
@@ -278,6 +310,67 @@ attn_fwd_dma_kernel(FwdParams p) {
         __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsV + buf * C::TILEB + blk * 1024), 16, 0, 0);
       }
     }
+  };
+
+  // 8-bit caches: tile kt's K and V codes go to registers (gload), then are
+  // converted and written to the LDS tiles of a ring slot (cvt_store).  A
+  // 16-code piece covers 16 values of one row; lane `tid` takes pieces tid,
+  // tid + 64 NW, ... of the K tile followed by the V tile, and threads
+  // 0 .. 2 BC-1 the K and V scales of the tile's rows.
+  constexpr int PIECES = 2 * BC * D / 16;
+  constexpr int PPL = KVQ ? PIECES / (NW * 64) : 1;
+  static_assert(!KVQ || PIECES % (NW * 64) == 0, "whole pieces per lane");
+  static_assert(!KVQ || 2 * BC <= NW * 64, "one scale per thread");
+  uint4 raw[PPL];
+  float raw_scale = 0.f;
+  float* const ldsS = (float*)(lds + 2 * NS * C::TILEB);  // per slot: BC K scales, BC V scales
+  auto gload = [&](int kt) {
+    const int64_t row0 = paged_row(kt);
+    const int last = k_len - 1 - kt * BC;  // last row of the tile that holds a key
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int g = tid + i * NW * 64;
+      const bool isv = g >= PIECES / 2;
+      const int gg = isv ? g - PIECES / 2 : g;
+      const int r = gg / (D / 16), pc = gg % (D / 16);
+      const uint8_t* src = (const uint8_t*)(isv ? p.v : p.k) + (row0 + (int64_t)min(r, last) * p.H) * D + pc * 16;
+      raw[i] = *(const uint4*)src;
+    }
+    if (tid < 2 * BC) {
+      const int r = tid % BC;
+      raw_scale = (tid < BC ? p.k_scale : p.v_scale)[row0 + (int64_t)min(r, last) * p.H];
+    }
+  };
+  auto cvt_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int g = tid + i * NW * 64;
+      const bool isv = g >= PIECES / 2;
+      const int gg = isv ? g - PIECES / 2 : g;
+      const int r = gg / (D / 16), pc = gg % (D / 16);
+      uint4 lo, hi;
+      decode16<KVQ>(TT{}, raw[i], lo, hi);
+      uint8_t* row = (isv ? ldsV : ldsK) + buf * C::TILEB + r * C::ROWB;
+      const int c0 = isv ? v_chunk<C::CHUNKS>(r, 2 * pc) : k_chunk<C::CHUNKS>(r, 2 * pc);
+      const int c1 = isv ? v_chunk<C::CHUNKS>(r, 2 * pc + 1) : k_chunk<C::CHUNKS>(r, 2 * pc + 1);
+      *(uint4*)(row + c0 * 16) = lo;
+      *(uint4*)(row + c1 * 16) = hi;
+    }
+    if (tid < 2 * BC) ldsS[buf * 2 * BC + tid] = raw_scale;
+  };
+  // scores times the K scale of their key: lane (c, hh) holds keys
+  // mb*32 + 8 g + 4 hh + j at s[mb][4 g + j]
+  auto scale_by = [&](const float* sc, f32x16_t (&s)[NQB][C::MB]) {
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 f = *(const float4*)(sc + mb * 32 + 8 * g + 4 * hh);
+        s[0][mb][4 * g + 0] *= f.x;
+        s[0][mb][4 * g + 1] *= f.y;
+        s[0][mb][4 * g + 2] *= f.z;
+        s[0][mb][4 * g + 3] *= f.w;
+      }
   };
 
   const float cs = p.c;
@@ -356,7 +449,8 @@ attn_fwd_dma_kernel(FwdParams p) {
   };
 
   // exponentials, exact row sum and P^T packing of one tile
-  auto exps = [&](f32x16_t (&s)[NQB][C::MB], const float (&m_use)[NQB], bool masked, uint4 (&pf)[NQB][C::MB][2]) {
+  auto exps = [&](int slot, f32x16_t (&s)[NQB][C::MB], const float (&m_use)[NQB], bool masked,
+                  uint4 (&pf)[NQB][C::MB][2]) {
     float r4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
     if (masked) {
 #pragma unroll
@@ -376,6 +470,7 @@ attn_fwd_dma_kernel(FwdParams p) {
         }
     }
     l[0] += (r4[0] + r4[1]) + (r4[2] + r4[3]);
+    if constexpr (KVQ) scale_by(ldsS + slot * 2 * BC + BC, s);  // V scales enter with P
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -445,7 +540,7 @@ attn_fwd_dma_kernel(FwdParams p) {
     bool masked = false;
     uint4 pf[NQB][C::MB][2];
     prepare(kt, s, m_use, masked);
-    exps(s, m_use, masked, pf);
+    exps(slot, s, m_use, masked, pf);
     const bool split = __any(l[0] < kSplitBelowP);
     // the residual is formed before the first product, so the fp32 P dies
     // there and only the two packed copies stay live through the MFMAs
@@ -455,15 +550,40 @@ attn_fwd_dma_kernel(FwdParams p) {
     if (split) pv_pass(slot, pl);
   };
 
+  if constexpr (KVQ) {
+    // tile kt+1 is converted into its slot right after the barrier that
+    // frees it, while the codes of tile kt+2 are loaded into registers
+    if (n_kt > 0) {
+      gload(0);
+      cvt_store(0);
+    }
+    if (n_kt > 1) gload(1);
+    int slot = 0;
+    for (int kt = 0; kt < n_kt; ++kt) {
+      __syncthreads();
+      const int nxt = (slot + 1 == NS) ? 0 : slot + 1;
+      if (kt + 1 < n_kt) {
+        cvt_store(nxt);
+        if (kt + 2 < n_kt) gload(kt + 2);
+      }
+      if (kt < wave_kt) {
+        f32x16_t s[NQB][C::MB];
+        compute_s(slot, s);
+        scale_by(ldsS + slot * 2 * BC, s);
+        softmax_pv(kt, slot, s);
+      }
+      slot = nxt;
+    }
+  }
   // prologue: tiles 0 .. NS-2 in flight (tile j in ring slot j % NS)
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < n_kt) {
+    if (!KVQ && j < n_kt) {
       load_k(j, j);
       load_v(j, j);
     }
   int slot = 0;  // ring slot of tile kt
-  for (int kt = 0; kt < n_kt; ++kt) {
+  for (int kt = 0; kt < (KVQ ? 0 : n_kt); ++kt) {
     // tile kt must have landed (its loads are the oldest in flight); later
     // tiles may still be on their way
     if (kt + NS - 2 < n_kt) wait_vm<(NS - 2) * C::LPT>();
@@ -520,17 +640,19 @@ attn_fwd_dma_kernel(FwdParams p) {
 }
 
 template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT,
-          bool PAGED>
+          int KV>
 hipError_t launch_dma_one(const FwdParams& p, hipStream_t st) {
   using C = PipeCfg<D, 1, BC, NW, NS>;
-  auto kern = attn_fwd_dma_kernel<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, PAGED>;
+  auto kern = attn_fwd_dma_kernel<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, KV>;
+  // 8-bit caches add the per-slot row scales after the K and V rings
+  constexpr int lds_bytes = C::LDS_BYTES + (KV >= kKvPagedE4m3 ? NS * 2 * BC * 4 : 0);
   static bool attr_set = false;  // idempotent; a benign race between threads
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(p.n_work), dim3(NW * 64), C::LDS_BYTES, st, p);
+  hipLaunchKernelGGL(kern, dim3(p.n_work), dim3(NW * 64), lds_bytes, st, p);
   return hipGetLastError();
 }
 
@@ -553,33 +675,38 @@ template <bool CAUSAL> struct DmaTile<256, CAUSAL> {
 // 4-wave workgroups with a 64 KiB ring, so two run on each CU.
 struct SplitTile128 { static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
 
-template <typename TT, int D, bool CAUSAL, bool VARLEN, bool SPLIT, bool PAGED = false>
+template <typename TT, int D, bool CAUSAL, bool VARLEN, bool SPLIT, int KV = kKvDense>
 hipError_t launch_dma_d(const FwdParams& p, hipStream_t st) {
   using T = DmaTile<D, CAUSAL>;
   if constexpr (SPLIT && D == 128) {
     using S = SplitTile128;
-    return launch_dma_one<TT, D, S::BC, S::NW, S::WPE, S::NS, S::OPT, CAUSAL, VARLEN, SPLIT, PAGED>(p, st);
+    return launch_dma_one<TT, D, S::BC, S::NW, S::WPE, S::NS, S::OPT, CAUSAL, VARLEN, SPLIT, KV>(p, st);
   } else {
-    return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, T::OPT, CAUSAL, VARLEN, SPLIT, PAGED>(p, st);
+    return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, T::OPT, CAUSAL, VARLEN, SPLIT, KV>(p, st);
   }
 }
 
-template <typename TT, bool CAUSAL, bool VARLEN, bool SPLIT, bool PAGED = false>
+template <typename TT, bool CAUSAL, bool VARLEN, bool SPLIT, int KV = kKvDense>
 hipError_t launch_dma_cv(int d, const FwdParams& p, hipStream_t st) {
   switch (d) {
-    case 64: return launch_dma_d<TT, 64, CAUSAL, VARLEN, SPLIT, PAGED>(p, st);
-    case 128: return launch_dma_d<TT, 128, CAUSAL, VARLEN, SPLIT, PAGED>(p, st);
-    case 256: return launch_dma_d<TT, 256, CAUSAL, VARLEN, SPLIT, PAGED>(p, st);
+    case 64: return launch_dma_d<TT, 64, CAUSAL, VARLEN, SPLIT, KV>(p, st);
+    case 128: return launch_dma_d<TT, 128, CAUSAL, VARLEN, SPLIT, KV>(p, st);
+    case 256: return launch_dma_d<TT, 256, CAUSAL, VARLEN, SPLIT, KV>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename TT>
-hipError_t launch_dma_t(int d, bool causal, bool varlen, bool split, bool paged, const FwdParams& p,
+hipError_t launch_dma_t(int d, bool causal, bool varlen, bool split, int kv, const FwdParams& p,
                         hipStream_t st) {
-  if (paged) {
+  if (kv != kKvDense) {
     if (!split || varlen || causal) return hipErrorInvalidValue;
-    return launch_dma_cv<TT, false, false, true, true>(d, p, st);
+    switch (kv) {
+      case kKvPaged: return launch_dma_cv<TT, false, false, true, kKvPaged>(d, p, st);
+      case kKvPagedE4m3: return launch_dma_cv<TT, false, false, true, kKvPagedE4m3>(d, p, st);
+      case kKvPagedInt8: return launch_dma_cv<TT, false, false, true, kKvPagedInt8>(d, p, st);
+      default: return hipErrorInvalidValue;
+    }
   }
   if (split) {
     if (varlen) return hipErrorInvalidValue;
@@ -614,10 +741,10 @@ int fwd_split_tile_keys(int d) {
   }
 }
 
-hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, bool paged, const FwdParams& p,
+hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, int kv, const FwdParams& p,
                       hipStream_t st) {
-  if (dtype == 0) return launch_dma_t<f16_t>(d, causal, varlen, split, paged, p, st);
-  return launch_dma_t<bf16_t>(d, causal, varlen, split, paged, p, st);
+  if (dtype == 0) return launch_dma_t<f16_t>(d, causal, varlen, split, kv, p, st);
+  return launch_dma_t<bf16_t>(d, causal, varlen, split, kv, p, st);
 }
 
 }  // namespace attn

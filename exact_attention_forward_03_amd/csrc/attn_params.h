@@ -20,7 +20,7 @@ struct FwdParams {
   int tiles_per_head;    // query tiles per (b, h) (varlen: upper bound per head)
   int n_work;            // workgroups launched
   const float* q_scale;  // fp8 only: [B, H, ceil(Nq/128)]
-  const float* k_scale;
+  const float* k_scale;  // fp8: [B, H, ceil(Nk/128)]; 8-bit paged cache: [num_pages, page_size, H]
   const float* v_scale;
   int n_split;           // key chunks (split launches only)
   int split_len;         // keys per chunk
@@ -86,7 +86,9 @@ int fwd_split_block_rows(int dtype, int d, bool causal);  // key-chunk launches
 int fwd_split_tile_keys(int d);  // key rows per tile of key-chunk launches (chunk lengths are multiples)
 int fwd_fp8_block_rows(bool causal);
 
-hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, bool paged, const FwdParams& p,
+// kv: 0 dense K/V, 1 paged 16-bit cache, 2 paged e4m3 cache, 3 paged int8
+// cache (8-bit caches: per-(token, head) scales in k_scale / v_scale)
+hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, int kv, const FwdParams& p,
                       hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_fwd_fp8(int d, bool causal, const FwdParams& p, hipStream_t st);

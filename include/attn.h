@@ -44,7 +44,8 @@ typedef enum {
   ATTN_DT_F16 = 0,      /* IEEE binary16 */
   ATTN_DT_BF16 = 1,     /* bfloat16 */
   ATTN_DT_FP8_E4M3 = 2, /* OCP e4m3fn codes (uint8), with fp32 block scales */
-  ATTN_DT_F32 = 3       /* float32: only as the input of attn_fp8_quantize */
+  ATTN_DT_F32 = 3,      /* float32: only as the input of attn_fp8_quantize */
+  ATTN_DT_INT8 = 4      /* signed 8-bit codes: only as an attn_fwd_paged cache */
 } attn_dtype_t;
 
 enum {
@@ -174,11 +175,16 @@ int attn_merge(const float* o_part, const float* lse_part, int num_splits, int B
  * page through the table, no contiguous copy is made), computed over
  * `num_splits` key chunks and merged as attn_fwd_splitkv.  Non-causal: every
  * query of sequence b attends to all its seqlens_k[b] cached keys (the
- * decoding setting).
+ * decoding setting).  The cache may hold 8-bit codes (INT8 and FP8 KV
+ * caches, §4.1.3 of the same post).
  *   q [B, H, Nq, d]; o [B, H, Nq, d] (same dtype, ATTN_DT_F16/BF16);
  *   lse fp32 [B, H, Nq];
- *   k_cache, v_cache [num_pages, page_size, H, d] of the same dtype: row
- *     (page, i, h) holds head h of one token;
+ *   k_cache, v_cache [num_pages, page_size, H, d]: row (page, i, h) holds
+ *     head h of one token; of type kv_dtype: `dtype` (16-bit cache, k_scale
+ *     and v_scale ignored), ATTN_DT_FP8_E4M3 (OCP e4m3fn codes) or
+ *     ATTN_DT_INT8 (signed codes);
+ *   k_scale, v_scale fp32 [num_pages, page_size, H] (8-bit caches): the
+ *     cached key/value of a (token, head) is scale * decode(code);
  *   block_table int32 [B, max_pages]: token t of sequence b is row
  *     t % page_size of page block_table[b][t / page_size];
  *   seqlens_k int32 [B]: keys of each sequence (clamped to
@@ -193,10 +199,10 @@ int attn_merge(const float* o_part, const float* lse_part, int num_splits, int B
  *   4-byte aligned; NULL allowed only when Nq = 0.  fp8: UNSUPPORTED.  Same
  *   stream and error rules as attn_fwd_stream.
  */
-int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
-                   const int32_t* seqlens_k, void* o, float* lse, int B, int H, int Nq, int d, int num_pages,
-                   int page_size, int max_pages, float scale, int dtype, int num_splits, float* o_part,
-                   float* lse_part, void* hip_stream);
+int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                   const float* v_scale, const int32_t* block_table, const int32_t* seqlens_k, void* o, float* lse,
+                   int B, int H, int Nq, int d, int num_pages, int page_size, int max_pages, float scale, int dtype,
+                   int kv_dtype, int num_splits, float* o_part, float* lse_part, void* hip_stream);
 
 /*
  * attn_bwd — gradients of the attention computed by attn_fwd: given dO =

@@ -229,13 +229,14 @@ def test_bwd_unsupported_and_empty(lib):
 
 
 def paged_call(**over):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, o=FAKE, lse=FAKE, B=2, H=4, Nq=1, d=128, num_pages=64,
-             page_size=128, max_pages=16, scale=0.125, dtype=attn.ATTN_DT_BF16, num_splits=4, o_part=FAKE,
-             lse_part=FAKE)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=None, vs=None, table=FAKE, lens=FAKE, o=FAKE, lse=FAKE, B=2, H=4, Nq=1, d=128,
+             num_pages=64, page_size=128, max_pages=16, scale=0.125, dtype=attn.ATTN_DT_BF16, kv_dtype=None,
+             num_splits=4, o_part=FAKE, lse_part=FAKE)
     a.update(over)
-    return attn.attn_fwd_paged(a["q"], a["k"], a["v"], a["table"], a["lens"], a["o"], a["lse"], a["B"], a["H"],
-                               a["Nq"], a["d"], a["num_pages"], a["page_size"], a["max_pages"], a["scale"],
-                               a["dtype"], a["num_splits"], a["o_part"], a["lse_part"], None)
+    kvd = a["dtype"] if a["kv_dtype"] is None else a["kv_dtype"]
+    return attn.attn_fwd_paged(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["table"], a["lens"], a["o"], a["lse"],
+                               a["B"], a["H"], a["Nq"], a["d"], a["num_pages"], a["page_size"], a["max_pages"],
+                               a["scale"], a["dtype"], kvd, a["num_splits"], a["o_part"], a["lse_part"], None)
 
 
 PAGED_INVALID = [
@@ -244,6 +245,9 @@ PAGED_INVALID = [
     dict(page_size=0), dict(max_pages=0), dict(scale=float("nan")), dict(dtype=9), dict(num_splits=0),
     dict(num_splits=1025), dict(q=FAKE + 8), dict(k=FAKE + 8), dict(table=FAKE + 2), dict(lens=FAKE + 1),
     dict(o_part=FAKE + 4), dict(max_pages=1 << 24, page_size=1 << 10),
+    dict(kv_dtype=attn.ATTN_DT_F16), dict(kv_dtype=attn.ATTN_DT_F32),
+    dict(kv_dtype=attn.ATTN_DT_INT8), dict(kv_dtype=attn.ATTN_DT_FP8_E4M3, ks=FAKE),
+    dict(kv_dtype=attn.ATTN_DT_INT8, ks=FAKE, vs=FAKE + 2),
 ]
 
 
@@ -256,7 +260,7 @@ def test_paged_unsupported_and_empty(lib):
     assert paged_call(d=96) == attn.ATTN_ERR_UNSUPPORTED
     assert paged_call(page_size=96) == attn.ATTN_ERR_UNSUPPORTED
     assert paged_call(page_size=16) == attn.ATTN_ERR_UNSUPPORTED
-    assert paged_call(dtype=attn.ATTN_DT_FP8_E4M3) == attn.ATTN_ERR_UNSUPPORTED
+    assert paged_call(dtype=attn.ATTN_DT_FP8_E4M3, ks=FAKE, vs=FAKE) == attn.ATTN_ERR_UNSUPPORTED
     assert paged_call(Nq=0) == attn.ATTN_OK
     none = dict(q=None, k=None, v=None, table=None, lens=None, o=None, lse=None, o_part=None, lse_part=None)
     assert paged_call(Nq=0, **none) == attn.ATTN_OK

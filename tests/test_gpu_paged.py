@@ -91,3 +91,69 @@ def test_paged_matches_contiguous_splitkv(gpu_lib):
                                      num_splits=4)
     torch.cuda.synchronize()
     assert torch.equal(l1, l2) and torch.equal(o1, o2)
+
+
+# ---------------------------------------------------------------- 8-bit caches
+
+QCASES = [
+    # B, H, Nq, d, dtype, page_size, lens, splits, kind
+    (3, 4, 1, 128, "bf16", 64, [1000, 70, 513], 4, "e4m3"),
+    (2, 2, 5, 128, "f16", 128, [2048, 1], 3, "int8"),
+    (4, 2, 1, 64, "bf16", 64, [300, 0, 64, 129], 3, "int8"),
+    (2, 2, 2, 256, "bf16", 128, [900, 777], 2, "e4m3"),
+    (2, 8, 1, 128, "bf16", 256, [8192, 3000], None, "e4m3"),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,d,dtype,page_size,lens,splits,kind", QCASES)
+def test_paged_8bit_vs_oracle(gpu_lib, B, H, Nq, d, dtype, page_size, lens, splits, kind):
+    import workloads as W
+
+    seed = sum(lens) + d + len(kind)
+    kc32, _, table = make_cache(B, H, lens, d, page_size, dtype, seed)  # only the table and cache shape
+    n_pages, P = kc32.shape[0], kc32.shape[1]
+    if kind == "e4m3":
+        kcodes = W.random_e4m3_codes(kc32.shape, seed + 1)
+        vcodes = W.random_e4m3_codes(kc32.shape, seed + 2)
+        ks = W.random_scales(kc32.shape[:3], seed + 3, 0.02, 0.05)
+        vs = W.random_scales(kc32.shape[:3], seed + 4, 0.02, 0.05)
+    else:
+        rng = np.random.default_rng(seed)
+        kcodes = rng.integers(0, 256, size=kc32.shape, dtype=np.uint8)
+        vcodes = rng.integers(0, 256, size=kc32.shape, dtype=np.uint8)
+        ks = W.random_scales(kc32.shape[:3], seed + 3, 0.005, 0.01)
+        vs = W.random_scales(kc32.shape[:3], seed + 4, 0.005, 0.01)
+    rng = np.random.default_rng(seed + 5)
+    qd, q = to_device(rng.standard_normal((B, H, Nq, d), dtype=np.float32), dtype)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    o, lse = gpu_lib.forward_paged(qd, t(kcodes), t(vcodes), t(table), torch.tensor(lens, dtype=torch.int32).cuda(),
+                                   k_scale=t(ks), v_scale=t(vs), kv_dtype=kind, num_splits=splits)
+    torch.cuda.synchronize()
+    ref_o, ref_l = PG.attention_paged_quant(q, kcodes, vcodes, ks, vs, table, np.array(lens), 1.0 / np.sqrt(d), kind)
+    check(o.double().cpu().numpy(), lse.double().cpu().numpy(), ref_o, ref_l, dtype,
+          f"paged {kind} B{B} H{H} Nq{Nq} d{d} P{page_size} lens{lens} S{splits}")
+    assert n_pages * P >= max(lens)
+
+
+def test_paged_8bit_equals_16bit_cache(gpu_lib):
+    """int8 codes with scale 1 are small integers: the same values stored as a
+    bf16 cache give the same attention (both exact inputs to the kernel; the
+    8-bit path only adds the multiplications by 1)."""
+    B, H, d, P = 2, 4, 128, 128
+    lens = [1000, 333]
+    kc32, _, table = make_cache(B, H, lens, d, P, "bf16", 21)
+    rng = np.random.default_rng(21)
+    kcodes = rng.integers(-3, 4, size=kc32.shape).astype(np.int8)
+    vcodes = rng.integers(-3, 4, size=kc32.shape).astype(np.int8)
+    ones = torch.ones(kc32.shape[:3], dtype=torch.float32, device="cuda")
+    q = torch.from_numpy(rng.standard_normal((B, H, 1, d), dtype=np.float32) * 0.1).to(torch.bfloat16).cuda()
+    td = torch.from_numpy(table).cuda()
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    k8 = torch.from_numpy(kcodes.view(np.uint8)).cuda()
+    v8 = torch.from_numpy(vcodes.view(np.uint8)).cuda()
+    o1, l1 = gpu_lib.forward_paged(q, k8, v8, td, ld, k_scale=ones, v_scale=ones, kv_dtype="int8", num_splits=2)
+    kb = torch.from_numpy(kcodes.astype(np.float32)).to(torch.bfloat16).cuda()
+    vb = torch.from_numpy(vcodes.astype(np.float32)).to(torch.bfloat16).cuda()
+    o2, l2 = gpu_lib.forward_paged(q, kb, vb, td, ld, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2) and torch.equal(o1, o2)
