@@ -147,6 +147,7 @@ def bench_detail(attn, steps, warmup):
         out[name] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                      "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
         del q, k, v, o, lse
+    out["hbm_copy_gbs"] = copy_bandwidth()
     out.update(bench_decode(attn, steps, warmup))
     out.update(bench_backward(attn, steps, warmup))
     fp8 = bench_fp8(attn, steps, warmup)
@@ -159,7 +160,9 @@ def bench_decode(attn, steps, warmup):
     """Decoding (B=2 H=32, one query per head, Nk=32768, d=128, bf16): attention
     over key chunks plus the merge, against HBM bandwidth (the K and V bytes
     are the algorithmic traffic); the single-pass kernel on the same shape
-    for comparison; the same keys and values read from a paged cache."""
+    for comparison; the same keys and values read from a paged cache, and a
+    paged cache of e4m3 codes with per-(token, head) scales (bytes: codes and
+    scales)."""
     import numpy as np
     import torch
 
@@ -216,6 +219,26 @@ def bench_decode(attn, steps, warmup):
     out["decode_bf16_paged"] = {"ms": round(msp, 4), "gbs": round(gbp, 1), "frac_hbm": round(gbp / HBM_PEAK_GBS, 4),
                                 "page_size": P, "num_splits": splits, "vs_contiguous": round(msp / ms, 4),
                                 "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
+
+    # an e4m3 cache of the same shape (random codes, per-(token, head) scales)
+    k8 = torch.from_numpy(W.random_e4m3_codes(tuple(kc.shape), 2)).cuda()
+    v8 = torch.from_numpy(W.random_e4m3_codes(tuple(kc.shape), 3)).cuda()
+    ks = torch.from_numpy(W.random_scales(tuple(kc.shape[:3]), 4)).cuda()
+    vs = torch.from_numpy(W.random_scales(tuple(kc.shape[:3]), 5)).cuda()
+    del kc, vc
+
+    def run_paged8():
+        attn.forward_paged(q, k8, v8, table, lens, scale=w.scale, k_scale=ks, v_scale=vs, kv_dtype="e4m3",
+                           num_splits=splits, out=o, lse=lse, o_part=op, lse_part=lp)
+
+    for _ in range(warmup):
+        run_paged8()
+    ms8 = float(np.mean(timed_launches(run_paged8, steps, stream)))
+    b8 = 2 * (k8.numel() + ks.numel() * 4)
+    gb8 = b8 / (ms8 / 1e3) / 1e9
+    out["decode_e4m3_paged"] = {"ms": round(ms8, 4), "gbs": round(gb8, 1), "frac_hbm": round(gb8 / HBM_PEAK_GBS, 4),
+                                "page_size": P, "num_splits": splits, "vs_bf16_paged": round(ms8 / msp, 4),
+                                "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
     return out
 
 
@@ -252,6 +275,24 @@ def bench_backward(attn, steps, warmup):
                               "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
         del q, k, v, do, o, lse, dq, dk, dv, delta
     return out
+
+
+def copy_bandwidth(steps: int = 10) -> float:
+    """GB/s (bytes read + written) of a plain 1 GiB device-to-device copy:
+    the HBM rate a streaming kernel reaches on this GPU, next to the spec
+    peak, for the memory-bound rows."""
+    import numpy as np
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    ms = float(np.mean(timed_launches(lambda: b.copy_(a), steps, torch.cuda.current_stream())))
+    del a, b
+    return round(2 * n / (ms / 1e3) / 1e9, 1)
 
 
 def bench_fp8(attn, steps, warmup):
