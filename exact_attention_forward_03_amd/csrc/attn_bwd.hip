@@ -143,8 +143,7 @@ __global__ void __launch_bounds__(kDeltaThreads) attn_bwd_delta_kernel(BwdParams
 // dK, dV.
 // ---------------------------------------------------------------------------
 template <typename TT, int D, int NW, int WPE, int NS, bool CAUSAL>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
-attn_bwd_dkdv_kernel(BwdParams p) {
+__device__ __forceinline__ void dkdv_body(const BwdParams& p, const int head, const int kt) {
   using T = Tile<D>;
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int TILEB = 32 * T::ROWB;            // one 32-row tile of Q or dO
@@ -154,20 +153,6 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   static_assert((2 * BLK) % NW == 0, "each wave issues the same number of loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  // Non-causal: the key tiles of one head run on one XCD (shared L2 copy of
-  // the head's Q and dO).  Causal: tile kt sees the queries from kt*32*NW
-  // on, so the work falls with kt; all heads' tile 0 go first, then tile 1,
-  // ..., dealt round-robin over the XCDs.
-  int head, kt;
-  if constexpr (CAUSAL) {
-    const int heads = p.B * p.H;
-    kt = blockIdx.x / heads;
-    head = blockIdx.x - kt * heads;
-  } else {
-    const int work = xcd_remap(blockIdx.x, p.n_work);
-    head = work / p.tiles_per_head;
-    kt = work - head * p.tiles_per_head;
-  }
   const int64_t q_row0 = (int64_t)head * p.Nq, k_row0 = (int64_t)head * p.Nk;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -290,12 +275,33 @@ attn_bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// The key tiles of one head run on one XCD (shared L2 copy of the head's Q
+// and dO).  Causal: key tile kt sees the queries from kt*32*NW on, so the
+// work falls with kt; a workgroup takes tiles j and T-1-j of one head in
+// turn (p.n_work counts the pairs), so that all do the same work.
+template <typename TT, int D, int NW, int WPE, int NS, bool CAUSAL>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
+attn_bwd_dkdv_kernel(BwdParams p) {
+  const int w = xcd_remap(blockIdx.x, p.n_work);
+  if constexpr (CAUSAL) {
+    const int T = p.tiles_per_head, half = (T + 1) / 2;
+    const int head = w / half, j = w - head * half;
+    dkdv_body<TT, D, NW, WPE, NS, CAUSAL>(p, head, j);
+    if (T - 1 - j != j) {
+      __syncthreads();
+      dkdv_body<TT, D, NW, WPE, NS, CAUSAL>(p, head, T - 1 - j);
+    }
+  } else {
+    const int head = w / p.tiles_per_head;
+    dkdv_body<TT, D, NW, WPE, NS, CAUSAL>(p, head, w - head * p.tiles_per_head);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dQ.
 // ---------------------------------------------------------------------------
 template <typename TT, int D, int BC, int NW, int WPE, int NS, bool CAUSAL>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
-attn_bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void dq_body(const BwdParams& p, const int head, const int qt) {
   using T = Tile<D>;
   constexpr int KS = D / 16, DB = D / 32, MB = BC / 32;
   constexpr int TILEB = BC * T::ROWB;
@@ -305,10 +311,6 @@ attn_bwd_dq_kernel(BwdParams p) {
   static_assert((2 * BLK) % NW == 0, "each wave issues the same number of loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const int work = xcd_remap(blockIdx.x, p.n_work);
-  const int head = work / p.tiles_per_head;
-  int qt = work - head * p.tiles_per_head;
-  if (CAUSAL) qt = p.tiles_per_head - 1 - qt;  // heaviest query tiles first
   const int64_t q_row0 = (int64_t)head * p.Nq, k_row0 = (int64_t)head * p.Nk;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -408,6 +410,26 @@ attn_bwd_dq_kernel(BwdParams p) {
   if (my_q < p.Nq) store_rows<TT, DB>((uint16_t*)p.dq + (q_row0 + my_q) * D, acc, p.scale, hh);
 }
 
+// Causal: query tile qt sees the keys up to its last row; a workgroup takes
+// tiles T-1-j (the heaviest) and j in turn (p.n_work counts the pairs).
+template <typename TT, int D, int BC, int NW, int WPE, int NS, bool CAUSAL>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
+attn_bwd_dq_kernel(BwdParams p) {
+  const int w = xcd_remap(blockIdx.x, p.n_work);
+  if constexpr (CAUSAL) {
+    const int T = p.tiles_per_head, half = (T + 1) / 2;
+    const int head = w / half, j = w - head * half;
+    dq_body<TT, D, BC, NW, WPE, NS, CAUSAL>(p, head, T - 1 - j);
+    if (T - 1 - j != j) {
+      __syncthreads();
+      dq_body<TT, D, BC, NW, WPE, NS, CAUSAL>(p, head, j);
+    }
+  } else {
+    const int head = w / p.tiles_per_head;
+    dq_body<TT, D, BC, NW, WPE, NS, CAUSAL>(p, head, w - head * p.tiles_per_head);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Launch configurations.
 // ---------------------------------------------------------------------------
@@ -443,7 +465,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t st) {
       return e;
     BwdParams pk = p;
     pk.tiles_per_head = (p.Nk + 32 * C::NW - 1) / (32 * C::NW);
-    pk.n_work = p.B * p.H * pk.tiles_per_head;
+    pk.n_work = p.B * p.H * (CAUSAL ? (pk.tiles_per_head + 1) / 2 : pk.tiles_per_head);
     hipLaunchKernelGGL(kern, dim3(pk.n_work), dim3(C::NW * 64), lds, st, pk);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
@@ -456,7 +478,7 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t st) {
       return e;
     BwdParams pq = p;
     pq.tiles_per_head = (p.Nq + 32 * C::DQ_NW - 1) / (32 * C::DQ_NW);
-    pq.n_work = p.B * p.H * pq.tiles_per_head;
+    pq.n_work = p.B * p.H * (CAUSAL ? (pq.tiles_per_head + 1) / 2 : pq.tiles_per_head);
     hipLaunchKernelGGL(kern, dim3(pq.n_work), dim3(C::DQ_NW * 64), lds, st, pq);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
