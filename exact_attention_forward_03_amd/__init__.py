@@ -67,7 +67,7 @@ def load():
         lib.attn_fwd_paged.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i,
                                         _i, _p, _p, _p]
         lib.attn_fwd_paged.restype = _i
-        lib.attn_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _p]
+        lib.attn_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _p, _i, _p]
         lib.attn_bwd.restype = _i
         lib.attn_fp8_quantize.argtypes = [_p, _i, _p, _p, _i, _i, _i, _i, _p, _i, _p]
         lib.attn_fp8_quantize.restype = _i
@@ -108,9 +108,10 @@ def attn_fwd_paged(q, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k
                                  lse_part, hip_stream)
 
 
-def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, dtype, hip_stream) -> int:
-    return load().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, dtype,
-                           hip_stream)
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q, cu_seqlens_k,
+             dtype, hip_stream) -> int:
+    return load().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q,
+                           cu_seqlens_k, dtype, hip_stream)
 
 
 def attn_fp8_quantize(x, x_dtype, x_fp8, x_scale, B, H, N, d, signs, per_tensor, hip_stream) -> int:
@@ -331,13 +332,15 @@ def merge(o_part, lse_part, *, out_dtype=None, out=None, lse=None):
     return out, lse
 
 
-def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None, dq=None, dk=None,
-             dv=None, delta=None):
+def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None, cu_seqlens_q=None,
+             cu_seqlens_k=None, dq=None, dk=None, dv=None, delta=None):
     """Gradients (dq, dk, dv) of ``forward(q, k, v)`` for the output gradient
-    ``dout``, through ``attn_bwd``.  Dense fp16/bf16, d = 64 or 128:
+    ``dout``, through ``attn_bwd``.  fp16/bf16, d = 64 or 128.  Dense:
     q, o, dout [B, H, Nq, d]; k, v [B, H, Nk, d]; lse float32 [B, H, Nq] from
-    the forward.  ``delta`` float32 [B, H, Nq] is the workspace (allocated
-    here if not given; it holds rowsum(dout * o) afterwards)."""
+    the forward.  Varlen (cu_seqlens_q/k int32 [B+1] on the device):
+    q, o, dout [H, Tq, d], k, v [H, Tk, d], lse [H, Tq].  ``delta`` float32
+    (the shape of lse) is the workspace (allocated here if not given; it
+    holds rowsum(dout * o) afterwards)."""
     import torch
 
     for t in (q, k, v, o, dout, lse):
@@ -346,21 +349,29 @@ def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[flo
     dt = _dtype_code(q)
     if any(_dtype_code(t) != dt for t in (k, v, o, dout)):
         raise TypeError("q, k, v, o, dout must share one dtype")
-    if q.dim() != 4 or k.shape != v.shape or o.shape != q.shape or dout.shape != q.shape:
-        raise ValueError("q, o, dout must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]):
-        raise ValueError("lse must be float32 [B, H, Nq]")
-    B, H, Nq, d = q.shape
-    Nk = k.shape[2]
+    varlen = cu_seqlens_q is not None
+    nd = 3 if varlen else 4
+    if q.dim() != nd or k.shape != v.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, o, dout must be [B, H, Nq, d] ([H, Tq, d] varlen) and k, v alike")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:-1]):
+        raise ValueError("lse must be float32 with the shape of q without its last axis")
+    if varlen:
+        H, Nq, d = q.shape
+        Nk = k.shape[1]
+        B = cu_seqlens_q.numel() - 1
+    else:
+        B, H, Nq, d = q.shape
+        Nk = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if delta is None:
-        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        delta = torch.empty(tuple(lse.shape), dtype=torch.float32, device=q.device)
     rc = attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                  _ptr(delta), B, H, Nq, Nk, d, float(scale), int(bool(causal)), dt, _stream(q.device))
+                  _ptr(delta), B, H, Nq, Nk, d, float(scale), int(bool(causal)), _ptr(cu_seqlens_q),
+                  _ptr(cu_seqlens_k), dt, _stream(q.device))
     _check(rc)
     return dq, dk, dv
 

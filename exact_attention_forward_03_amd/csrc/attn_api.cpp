@@ -215,13 +215,15 @@ int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, cons
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
              void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq, int Nk, int d, float scale,
-             int causal, int dtype, void* hip_stream) {
+             int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, void* hip_stream) {
   if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return ATTN_ERR_INVALID_ARG;
   // query-side arrays may be NULL only without queries, key-side ones only without keys
   if (Nq > 0 && (!q || !o || !lse || !dout || !dq || !delta)) return ATTN_ERR_INVALID_ARG;
   if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if ((cu_seqlens_q == nullptr) != (cu_seqlens_k == nullptr)) return ATTN_ERR_INVALID_ARG;
+  if (cu_seqlens_q && (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16 && dtype != ATTN_DT_FP8_E4M3) return ATTN_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
@@ -229,9 +231,11 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
   if (dtype == ATTN_DT_FP8_E4M3 || d == 256) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)B * H > (int64_t)INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
-  const int64_t kt = ((int64_t)Nk + attn::bwd_key_block(d) - 1) / attn::bwd_key_block(d);
-  const int64_t qt = ((int64_t)Nq + attn::bwd_query_block(d) - 1) / attn::bwd_query_block(d);
-  if ((int64_t)B * H * kt > INT32_MAX || (int64_t)B * H * qt > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  const bool varlen = cu_seqlens_q != nullptr;
+  const int64_t heads = varlen ? H : (int64_t)B * H;  // varlen: [H, T, d], B sequences
+  const int64_t kt = ((int64_t)Nk + attn::bwd_key_block(d) - 1) / attn::bwd_key_block(d) + (varlen ? B : 0);
+  const int64_t qt = ((int64_t)Nq + attn::bwd_query_block(d) - 1) / attn::bwd_query_block(d) + (varlen ? B : 0);
+  if (heads * kt > INT32_MAX || heads * qt > INT32_MAX) return ATTN_ERR_INVALID_ARG;
   if (Nq == 0 && Nk == 0) return ATTN_OK;
   attn::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
@@ -239,7 +243,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk;
   p.scale = scale;
   p.c = scale * 1.4426950408889634f;
-  const hipError_t e = attn::launch_bwd(dtype, d, causal != 0, p, (hipStream_t)hip_stream);
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  const hipError_t e = attn::launch_bwd(dtype, d, causal != 0, varlen, p, (hipStream_t)hip_stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -99,6 +99,40 @@ __device__ __forceinline__ uint4 pack8(bf16_t t, const f32x16_t& v, int b) {
                     pack2(t, v[b + 6], v[b + 7]));
 }
 
+// The rows one work item sees: its sequence's queries and keys for one
+// head (dense batches: the whole head).
+struct SeqView {
+  int64_t q_row0, k_row0;  // first row of the sequence in the [.., N, d] arrays
+  int q_len, k_len;
+};
+
+// Sequence of tile t of a variable-length batch whose sequence s has
+// ceil(len_s / rows) tiles (lengths from the clamped prefix sums); false if
+// t is past the last tile.
+__device__ __forceinline__ bool varlen_tile(const BwdParams& p, int head, int t, int rows, bool by_keys, SeqView& v,
+                                            int& local) {
+  int acc = 0;
+  for (int sq = 0; sq < p.B; ++sq) {
+    const int qa = min(max(p.cu_q[sq], 0), p.Nq), qb = min(max(p.cu_q[sq + 1], qa), p.Nq);
+    const int ka = min(max(p.cu_k[sq], 0), p.Nk), kb = min(max(p.cu_k[sq + 1], ka), p.Nk);
+    const int nt = ((by_keys ? kb - ka : qb - qa) + rows - 1) / rows;
+    if (t < acc + nt) {
+      v.q_row0 = (int64_t)head * p.Nq + qa;
+      v.k_row0 = (int64_t)head * p.Nk + ka;
+      v.q_len = qb - qa;
+      v.k_len = kb - ka;
+      local = t - acc;
+      return true;
+    }
+    acc += nt;
+  }
+  return false;
+}
+
+__device__ __forceinline__ SeqView dense_view(const BwdParams& p, int head) {
+  return SeqView{(int64_t)head * p.Nq, (int64_t)head * p.Nk, p.Nq, p.Nk};
+}
+
 // Store a 32-row block of a transposed accumulator: lane l owns output row
 // `row` (a key or a query) and columns 32 db + 8 g + 4 (l / 32) + (0..3).
 template <typename TT, int DB>
@@ -143,7 +177,7 @@ __global__ void __launch_bounds__(kDeltaThreads) attn_bwd_delta_kernel(BwdParams
 // dK, dV.
 // ---------------------------------------------------------------------------
 template <typename TT, int D, int NW, int WPE, int NS, bool CAUSAL>
-__device__ __forceinline__ void dkdv_body(const BwdParams& p, const int head, const int kt) {
+__device__ __forceinline__ void dkdv_body(const BwdParams& p, const SeqView sv, const int kt) {
   using T = Tile<D>;
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int TILEB = 32 * T::ROWB;            // one 32-row tile of Q or dO
@@ -153,7 +187,8 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, const int head, co
   static_assert((2 * BLK) % NW == 0, "each wave issues the same number of loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const int64_t q_row0 = (int64_t)head * p.Nq, k_row0 = (int64_t)head * p.Nk;
+  const int64_t q_row0 = sv.q_row0, k_row0 = sv.k_row0;
+  const int q_len = sv.q_len, k_len = sv.k_len;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
@@ -169,11 +204,11 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, const int head, co
     constexpr int VBLK = 32 * NW * T::ROWB / 1024;
 #pragma unroll
     for (int i = 0; i < VBLK / NW; ++i)
-      T::load_block((const uint8_t*)p.v, k_row0, p.Nk, k0, ldsV, wv * (VBLK / NW) + i, lane);
+      T::load_block((const uint8_t*)p.v, k_row0, k_len, k0, ldsV, wv * (VBLK / NW) + i, lane);
   }
   uint4 kf[KS];
   {
-    const int key = min(my_key, p.Nk - 1);
+    const int key = min(my_key, k_len - 1);
     const uint16_t* kr = (const uint16_t*)p.k + (k_row0 + key) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const uint4*)(kr + ks * 16);
@@ -189,7 +224,7 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, const int head, co
   // first key (for the later waves the first blocks are fully masked: they
   // run them rather than branch around them, which costs the compiler
   // dozens of registers)
-  const int n_qb = (p.Nq + 31) / 32;
+  const int n_qb = (q_len + 31) / 32;
   const int qb0 = CAUSAL ? min(k0 / 32, n_qb) : 0;
   const int n_steps = n_qb - qb0;
 
@@ -198,12 +233,12 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, const int head, co
 #pragma unroll
     for (int i = 0; i < 2 * BLK / NW; ++i) {
       const int blk = wv * (2 * BLK / NW) + i;  // blocks 0..BLK-1: Q, BLK..: dO
-      if (blk < BLK) T::load_block((const uint8_t*)p.q, q_row0, p.Nq, qb * 32, st, blk, lane);
-      else T::load_block((const uint8_t*)p.dout, q_row0, p.Nq, qb * 32, st + TILEB, blk - BLK, lane);
+      if (blk < BLK) T::load_block((const uint8_t*)p.q, q_row0, q_len, qb * 32, st, blk, lane);
+      else T::load_block((const uint8_t*)p.dout, q_row0, q_len, qb * 32, st + TILEB, blk - BLK, lane);
     }
     // lse and delta: 64 floats, 16 per wave (4-byte direct-to-LDS loads)
     const int idx = 16 * (wv & 3) + (lane & 15);
-    const int q = min(qb * 32 + (idx & 31), p.Nq - 1);
+    const int q = min(qb * 32 + (idx & 31), q_len - 1);
     const float* src = (idx < 32 ? p.lse : p.delta) + q_row0 + q;
     if (wv < 4 && lane < 16)
       __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(st + 2 * TILEB + 64 * (wv & 3)), 4, 0, 0);
@@ -231,11 +266,11 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, const int head, co
         s = mfma32(TT{}, T::rows_frag(tq, c, ks, hh), kf[ks], s);
         dp = mfma32(TT{}, T::rows_frag(tdo, c, ks, hh), T::rows_frag(ldsV, 32 * wv + c, ks, hh), dp);
       }
-      const bool masked = (CAUSAL && qb * 32 < kw0 + 31) || qb * 32 + 32 > p.Nq;
+      const bool masked = (CAUSAL && qb * 32 < kw0 + 31) || qb * 32 + 32 > q_len;
       // element (g, j) is query q = qb*32 + 4 hh + 8 g + j: it exists iff
       // 8 g + j < q_lim and sees this lane's key iff 8 g + j >= key_rel
       // (comparisons against constants, nothing kept live across blocks)
-      const int q_lim = p.Nq - qb * 32 - 4 * hh;
+      const int q_lim = q_len - qb * 32 - 4 * hh;
       const int key_rel = my_key - qb * 32 - 4 * hh;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -269,7 +304,7 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, const int head, co
     slot = (slot + 1 == NS) ? 0 : slot + 1;
   }
 
-  if (my_key < p.Nk) {
+  if (my_key < k_len) {
     store_rows<TT, DB>((uint16_t*)p.dk + (k_row0 + my_key) * D, dk, p.scale, hh);
     store_rows<TT, DB>((uint16_t*)p.dv + (k_row0 + my_key) * D, dv, 1.f, hh);
   }
@@ -279,21 +314,29 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, const int head, co
 // and dO).  Causal: key tile kt sees the queries from kt*32*NW on, so the
 // work falls with kt; a workgroup takes tiles j and T-1-j of one head in
 // turn (p.n_work counts the pairs), so that all do the same work.
-template <typename TT, int D, int NW, int WPE, int NS, bool CAUSAL>
+// Variable-length batches: a head's key tiles are numbered sequence after
+// sequence (p.tiles_per_head bounds their count; surplus workgroups exit).
+template <typename TT, int D, int NW, int WPE, int NS, bool CAUSAL, bool VARLEN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 attn_bwd_dkdv_kernel(BwdParams p) {
   const int w = xcd_remap(blockIdx.x, p.n_work);
-  if constexpr (CAUSAL) {
+  if constexpr (VARLEN) {
+    const int head = w / p.tiles_per_head;
+    SeqView sv;
+    int kt;
+    if (varlen_tile(p, head, w - head * p.tiles_per_head, 32 * NW, true, sv, kt))
+      dkdv_body<TT, D, NW, WPE, NS, CAUSAL>(p, sv, kt);
+  } else if constexpr (CAUSAL) {
     const int T = p.tiles_per_head, half = (T + 1) / 2;
     const int head = w / half, j = w - head * half;
-    dkdv_body<TT, D, NW, WPE, NS, CAUSAL>(p, head, j);
+    dkdv_body<TT, D, NW, WPE, NS, CAUSAL>(p, dense_view(p, head), j);
     if (T - 1 - j != j) {
       __syncthreads();
-      dkdv_body<TT, D, NW, WPE, NS, CAUSAL>(p, head, T - 1 - j);
+      dkdv_body<TT, D, NW, WPE, NS, CAUSAL>(p, dense_view(p, head), T - 1 - j);
     }
   } else {
     const int head = w / p.tiles_per_head;
-    dkdv_body<TT, D, NW, WPE, NS, CAUSAL>(p, head, w - head * p.tiles_per_head);
+    dkdv_body<TT, D, NW, WPE, NS, CAUSAL>(p, dense_view(p, head), w - head * p.tiles_per_head);
   }
 }
 
@@ -301,7 +344,7 @@ attn_bwd_dkdv_kernel(BwdParams p) {
 // dQ.
 // ---------------------------------------------------------------------------
 template <typename TT, int D, int BC, int NW, int WPE, int NS, bool CAUSAL>
-__device__ __forceinline__ void dq_body(const BwdParams& p, const int head, const int qt) {
+__device__ __forceinline__ void dq_body(const BwdParams& p, const SeqView sv, const int qt) {
   using T = Tile<D>;
   constexpr int KS = D / 16, DB = D / 32, MB = BC / 32;
   constexpr int TILEB = BC * T::ROWB;
@@ -311,7 +354,8 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, const int head, cons
   static_assert((2 * BLK) % NW == 0, "each wave issues the same number of loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const int64_t q_row0 = (int64_t)head * p.Nq, k_row0 = (int64_t)head * p.Nk;
+  const int64_t q_row0 = sv.q_row0, k_row0 = sv.k_row0;
+  const int q_len = sv.q_len, k_len = sv.k_len;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
@@ -322,7 +366,7 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, const int head, cons
   uint4 qf[KS], df[KS];
   float lse2 = 0.f, dl = 0.f;
   {
-    const int q = min(my_q, p.Nq - 1);
+    const int q = min(my_q, q_len - 1);
     const uint16_t* qr = (const uint16_t*)p.q + (q_row0 + q) * D + 8 * hh;
     const uint16_t* dr = (const uint16_t*)p.dout + (q_row0 + q) * D + 8 * hh;
 #pragma unroll
@@ -337,22 +381,22 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, const int head, cons
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
 
-  int n_kt = (p.Nk + BC - 1) / BC, wave_kt = n_kt;
+  int n_kt = (k_len + BC - 1) / BC, wave_kt = n_kt;
   if (CAUSAL) {
-    const int last_wg = min(q0 + 32 * NW, p.Nq) - 1;  // the workgroup's last query
+    const int last_wg = min(q0 + 32 * NW, q_len) - 1;  // the workgroup's last query
     n_kt = last_wg < 0 ? 0 : min(n_kt, last_wg / BC + 1);
-    const int last_w = min(qw0 + 31, p.Nq - 1);
+    const int last_w = min(qw0 + 31, q_len - 1);
     wave_kt = last_w < 0 ? 0 : min(n_kt, last_w / BC + 1);
   }
-  if (qw0 >= p.Nq) wave_kt = 0;
+  if (qw0 >= q_len) wave_kt = 0;
 
   auto load_stage = [&](int kt, int slot) {
     uint8_t* st = lds + slot * STAGE;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int blk = wv * LPT + i;
-      if (blk < BLK) T::load_block((const uint8_t*)p.k, k_row0, p.Nk, kt * BC, st, blk, lane);
-      else T::load_block((const uint8_t*)p.v, k_row0, p.Nk, kt * BC, st + TILEB, blk - BLK, lane);
+      if (blk < BLK) T::load_block((const uint8_t*)p.k, k_row0, k_len, kt * BC, st, blk, lane);
+      else T::load_block((const uint8_t*)p.v, k_row0, k_len, kt * BC, st + TILEB, blk - BLK, lane);
     }
   };
 
@@ -380,10 +424,10 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, const int head, cons
           dp[mb] = mfma32(TT{}, T::rows_frag(tv, mb * 32 + c, ks, hh), df[ks], dp[mb]);
         }
       }
-      const bool masked = (CAUSAL && kt * BC + BC - 1 > qw0) || kt * BC + BC > p.Nk;
+      const bool masked = (CAUSAL && kt * BC + BC - 1 > qw0) || kt * BC + BC > k_len;
       // element (mb, i) is key kt*BC + 4 hh + e with e = 32 mb + 8 (i/4) + i%4:
       // it exists iff e < k_lim and is visible to this lane's query iff e <= q_rel
-      const int k_lim = p.Nk - kt * BC - 4 * hh;
+      const int k_lim = k_len - kt * BC - 4 * hh;
       const int q_rel = my_q - kt * BC - 4 * hh;
       uint4 dsp[MB][2];
 #pragma unroll
@@ -407,26 +451,32 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, const int head, cons
     }
     slot = (slot + 1 == NS) ? 0 : slot + 1;
   }
-  if (my_q < p.Nq) store_rows<TT, DB>((uint16_t*)p.dq + (q_row0 + my_q) * D, acc, p.scale, hh);
+  if (my_q < q_len) store_rows<TT, DB>((uint16_t*)p.dq + (q_row0 + my_q) * D, acc, p.scale, hh);
 }
 
 // Causal: query tile qt sees the keys up to its last row; a workgroup takes
 // tiles T-1-j (the heaviest) and j in turn (p.n_work counts the pairs).
-template <typename TT, int D, int BC, int NW, int WPE, int NS, bool CAUSAL>
+template <typename TT, int D, int BC, int NW, int WPE, int NS, bool CAUSAL, bool VARLEN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 attn_bwd_dq_kernel(BwdParams p) {
   const int w = xcd_remap(blockIdx.x, p.n_work);
-  if constexpr (CAUSAL) {
+  if constexpr (VARLEN) {
+    const int head = w / p.tiles_per_head;
+    SeqView sv;
+    int qt;
+    if (varlen_tile(p, head, w - head * p.tiles_per_head, 32 * NW, false, sv, qt))
+      dq_body<TT, D, BC, NW, WPE, NS, CAUSAL>(p, sv, qt);
+  } else if constexpr (CAUSAL) {
     const int T = p.tiles_per_head, half = (T + 1) / 2;
     const int head = w / half, j = w - head * half;
-    dq_body<TT, D, BC, NW, WPE, NS, CAUSAL>(p, head, T - 1 - j);
+    dq_body<TT, D, BC, NW, WPE, NS, CAUSAL>(p, dense_view(p, head), T - 1 - j);
     if (T - 1 - j != j) {
       __syncthreads();
-      dq_body<TT, D, BC, NW, WPE, NS, CAUSAL>(p, head, j);
+      dq_body<TT, D, BC, NW, WPE, NS, CAUSAL>(p, dense_view(p, head), j);
     }
   } else {
     const int head = w / p.tiles_per_head;
-    dq_body<TT, D, BC, NW, WPE, NS, CAUSAL>(p, head, w - head * p.tiles_per_head);
+    dq_body<TT, D, BC, NW, WPE, NS, CAUSAL>(p, dense_view(p, head), w - head * p.tiles_per_head);
   }
 }
 
@@ -446,9 +496,10 @@ struct BwdCfg {
   static constexpr int DQ_BC = 64, DQ_NW = 4, DQ_WPE = 2, DQ_NS = 2;
 };
 
-template <typename TT, int D, bool CAUSAL>
+template <typename TT, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd_t(BwdParams p, hipStream_t st) {
-  const int64_t rows = (int64_t)p.B * p.H * p.Nq;
+  const int64_t heads = VARLEN ? p.H : (int64_t)p.B * p.H;  // varlen arrays are [H, T, d]
+  const int64_t rows = heads * p.Nq;
   if (rows > 0) {
     constexpr int RPB = kDeltaThreads / (D / 8);
     hipLaunchKernelGGL((attn_bwd_delta_kernel<TT, D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
@@ -459,37 +510,43 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t st) {
     using C = BwdCfg<D>;
     constexpr int STAGE = 2 * 32 * D * 2 + 256;
     constexpr int lds = C::NS * STAGE + 32 * C::NW * D * 2;
-    auto kern = attn_bwd_dkdv_kernel<TT, D, C::NW, C::WPE, C::NS, CAUSAL>;
+    auto kern = attn_bwd_dkdv_kernel<TT, D, C::NW, C::WPE, C::NS, CAUSAL, VARLEN>;
     if (hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         e != hipSuccess)
       return e;
     BwdParams pk = p;
-    pk.tiles_per_head = (p.Nk + 32 * C::NW - 1) / (32 * C::NW);
-    pk.n_work = p.B * p.H * (CAUSAL ? (pk.tiles_per_head + 1) / 2 : pk.tiles_per_head);
+    pk.tiles_per_head = (p.Nk + 32 * C::NW - 1) / (32 * C::NW) + (VARLEN ? p.B : 0);
+    pk.n_work = (int)heads * (CAUSAL && !VARLEN ? (pk.tiles_per_head + 1) / 2 : pk.tiles_per_head);
     hipLaunchKernelGGL(kern, dim3(pk.n_work), dim3(C::NW * 64), lds, st, pk);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   if (p.Nq > 0) {
     using C = BwdCfg<D>;
     constexpr int lds = C::DQ_NS * 2 * C::DQ_BC * D * 2;
-    auto kern = attn_bwd_dq_kernel<TT, D, C::DQ_BC, C::DQ_NW, C::DQ_WPE, C::DQ_NS, CAUSAL>;
+    auto kern = attn_bwd_dq_kernel<TT, D, C::DQ_BC, C::DQ_NW, C::DQ_WPE, C::DQ_NS, CAUSAL, VARLEN>;
     if (hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         e != hipSuccess)
       return e;
     BwdParams pq = p;
-    pq.tiles_per_head = (p.Nq + 32 * C::DQ_NW - 1) / (32 * C::DQ_NW);
-    pq.n_work = p.B * p.H * (CAUSAL ? (pq.tiles_per_head + 1) / 2 : pq.tiles_per_head);
+    pq.tiles_per_head = (p.Nq + 32 * C::DQ_NW - 1) / (32 * C::DQ_NW) + (VARLEN ? p.B : 0);
+    pq.n_work = (int)heads * (CAUSAL && !VARLEN ? (pq.tiles_per_head + 1) / 2 : pq.tiles_per_head);
     hipLaunchKernelGGL(kern, dim3(pq.n_work), dim3(C::DQ_NW * 64), lds, st, pq);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
+template <typename TT, int D>
+hipError_t launch_bwd_cv(bool causal, bool varlen, const BwdParams& p, hipStream_t st) {
+  if (varlen) return causal ? launch_bwd_t<TT, D, true, true>(p, st) : launch_bwd_t<TT, D, false, true>(p, st);
+  return causal ? launch_bwd_t<TT, D, true, false>(p, st) : launch_bwd_t<TT, D, false, false>(p, st);
+}
+
 template <typename TT>
-hipError_t launch_bwd_d(int d, bool causal, const BwdParams& p, hipStream_t st) {
+hipError_t launch_bwd_d(int d, bool causal, bool varlen, const BwdParams& p, hipStream_t st) {
   switch (d) {
-    case 64: return causal ? launch_bwd_t<TT, 64, true>(p, st) : launch_bwd_t<TT, 64, false>(p, st);
-    case 128: return causal ? launch_bwd_t<TT, 128, true>(p, st) : launch_bwd_t<TT, 128, false>(p, st);
+    case 64: return launch_bwd_cv<TT, 64>(causal, varlen, p, st);
+    case 128: return launch_bwd_cv<TT, 128>(causal, varlen, p, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -499,8 +556,8 @@ hipError_t launch_bwd_d(int d, bool causal, const BwdParams& p, hipStream_t st) 
 int bwd_key_block(int d) { return 32 * (d == 64 ? BwdCfg<64>::NW : BwdCfg<128>::NW); }
 int bwd_query_block(int d) { return 32 * (d == 64 ? BwdCfg<64>::DQ_NW : BwdCfg<128>::DQ_NW); }
 
-hipError_t launch_bwd(int dtype, int d, bool causal, BwdParams p, hipStream_t st) {
-  return dtype == 0 ? launch_bwd_d<f16_t>(d, causal, p, st) : launch_bwd_d<bf16_t>(d, causal, p, st);
+hipError_t launch_bwd(int dtype, int d, bool causal, bool varlen, BwdParams p, hipStream_t st) {
+  return dtype == 0 ? launch_bwd_d<f16_t>(d, causal, varlen, p, st) : launch_bwd_d<bf16_t>(d, causal, varlen, p, st);
 }
 
 }  // namespace attn

@@ -75,11 +75,13 @@ struct BwdParams {
   float c;               // scale * log2(e)
   int tiles_per_head;    // set per launch: key tiles (dK/dV) or query tiles (dQ) per head
   int n_work;
+  const int32_t* cu_q;   // varlen only: [B+1] prefix sums over the packed tokens
+  const int32_t* cu_k;
 };
 
 int bwd_key_block(int d);    // keys per dK/dV workgroup
 int bwd_query_block(int d);  // queries per dQ workgroup
-hipError_t launch_bwd(int dtype, int d, bool causal, BwdParams p, hipStream_t st);
+hipError_t launch_bwd(int dtype, int d, bool causal, bool varlen, BwdParams p, hipStream_t st);
 
 int fwd_block_rows(int dtype, int d, bool causal);
 int fwd_split_block_rows(int dtype, int d, bool causal);  // key-chunk launches

@@ -216,10 +216,14 @@ int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, cons
  * stored.
  *   q, o, dout, dq [B, H, Nq, d]; k, v, dk, dv [B, H, Nk, d]; all of dtype
  *     ATTN_DT_F16 or ATTN_DT_BF16, contiguous, 16-byte aligned;
+ *   cu_seqlens_q / cu_seqlens_k: NULL (dense) or, both, int32 [B+1] prefix
+ *     sums as in attn_fwd: then q, o, dout, dq are [H, Nq, d], k, v, dk, dv
+ *     [H, Nk, d], lse and delta [H, Nq] over B packed sequences (causal
+ *     masks per sequence, local indices);
  *   o, lse: the forward's outputs for the same q, k, v, scale, causal;
  *   delta: fp32 workspace [B, H, Nq], caller-owned, 4-byte aligned; on
  *     return it holds delta_i = sum_c dO_ic O_ic;
- *   d ∈ {64, 128} (256 and fp8: ATTN_ERR_UNSUPPORTED); dense batches only.
+ *   d ∈ {64, 128} (256 and fp8: ATTN_ERR_UNSUPPORTED).
  *   Query-side arrays may be NULL only if Nq = 0, key-side arrays only if
  *   Nk = 0.  Nk = 0 gives dQ = 0; Nq = 0 gives dK = dV = 0.  dQ is
  *   accumulated per query row in one workgroup (no atomics): results are
@@ -228,7 +232,7 @@ int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, cons
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
              void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq, int Nk, int d, float scale,
-             int causal, int dtype, void* hip_stream);
+             int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, void* hip_stream);
 
 /* attn_strerror — a static, human-readable name for a return code. */
 const char* attn_strerror(int code);

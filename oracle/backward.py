@@ -63,3 +63,17 @@ def intermediates(q, k, v, do, scale: float, causal: bool = False):
     dp = np.matmul(do, np.swapaxes(v, -1, -2))
     delta = (p * dp).sum(axis=-1)
     return {"P": p, "dP": dp, "delta": delta, "dS": p * (dp - delta[..., None])}
+
+
+def attention_backward_varlen(q, k, v, do, cu_q, cu_k, scale: float, causal: bool = False):
+    """Gradients for a packed variable-length batch: q, do [H, Tq, d], k, v
+    [H, Tk, d], sequence s owning rows cu_q[s]:cu_q[s+1] (queries) and
+    cu_k[s]:cu_k[s+1] (keys); each sequence is an independent attention, so
+    its gradients are ``attention_backward`` on its rows (zero elsewhere)."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for s in range(len(cu_q) - 1):
+        qa, qb, ka, kb = int(cu_q[s]), int(cu_q[s + 1]), int(cu_k[s]), int(cu_k[s + 1])
+        g = attention_backward(q[:, qa:qb], k[:, ka:kb], v[:, ka:kb], do[:, qa:qb], scale, causal)
+        dq[:, qa:qb], dk[:, ka:kb], dv[:, ka:kb] = g
+    return dq, dk, dv

@@ -199,10 +199,11 @@ def test_merge_unsupported_and_empty(lib):
 
 def bwd_call(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, delta=FAKE, B=1, H=2,
-             Nq=256, Nk=256, d=128, scale=0.125, causal=0, dtype=attn.ATTN_DT_BF16)
+             Nq=256, Nk=256, d=128, scale=0.125, causal=0, cu_q=None, cu_k=None, dtype=attn.ATTN_DT_BF16)
     a.update(over)
     return attn.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"], a["delta"],
-                         a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+                         a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["cu_q"], a["cu_k"],
+                         a["dtype"], None)
 
 
 BWD_INVALID = [
@@ -210,7 +211,7 @@ BWD_INVALID = [
     dict(dk=None), dict(dv=None), dict(delta=None), dict(B=0), dict(H=0), dict(Nq=-1), dict(Nk=-5),
     dict(scale=float("inf")), dict(scale=-1.0), dict(causal=2), dict(dtype=7), dict(q=FAKE + 8),
     dict(dout=FAKE + 4), dict(dq=FAKE + 2), dict(dk=FAKE + 8), dict(dv=FAKE + 8), dict(o=FAKE + 8),
-    dict(lse=FAKE + 2), dict(delta=FAKE + 1),
+    dict(lse=FAKE + 2), dict(delta=FAKE + 1), dict(cu_q=FAKE), dict(cu_k=FAKE), dict(cu_q=FAKE + 2, cu_k=FAKE),
 ]
 
 

@@ -195,3 +195,25 @@ def test_mutations(name):
         except (AssertionError, ValueError, FloatingPointError, IndexError):
             caught += 1
     assert caught > 0, f"no pin catches: {name}"
+
+
+def test_varlen_is_per_sequence():
+    """A packed batch's gradients equal the dense gradients of each sequence,
+    and keys of one sequence get nothing from another's queries."""
+    rng = np.random.default_rng(12)
+    H, d = 2, 4
+    lq, lk = [3, 0, 5], [4, 2, 5]
+    cu_q, cu_k = np.cumsum([0] + lq), np.cumsum([0] + lk)
+    q = rng.standard_normal((H, cu_q[-1], d))
+    k = rng.standard_normal((H, cu_k[-1], d))
+    v = rng.standard_normal((H, cu_k[-1], d))
+    do = rng.standard_normal((H, cu_q[-1], d))
+    for causal in (False, True):
+        dq, dk, dv = BW.attention_backward_varlen(q, k, v, do, cu_q, cu_k, 0.6, causal)
+        for s in range(3):
+            sl_q, sl_k = slice(cu_q[s], cu_q[s + 1]), slice(cu_k[s], cu_k[s + 1])
+            rq, rk, rv = BW.attention_backward(q[:, sl_q], k[:, sl_k], v[:, sl_k], do[:, sl_q], 0.6, causal)
+            np.testing.assert_array_equal(dq[:, sl_q], rq)
+            np.testing.assert_array_equal(dk[:, sl_k], rk)
+            np.testing.assert_array_equal(dv[:, sl_k], rv)
+        assert np.all(dk[:, cu_k[1]:cu_k[2]] == 0.0)  # sequence 1 has no queries
