@@ -60,10 +60,10 @@ def load_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(reps_heads: int = 8):
-    """The fp64 oracle on a bounded sample: B=1, `reps_heads` heads of the
-    dense bf16 workload, each run non-causal and causal (inputs on the host
-    in fp64, generation excluded)."""
+def cpu_baseline(chunk_heads: int = 8):
+    """The fp64 oracle on one whole step of the dense bf16 workload (all
+    B*H = 32 heads, non-causal and causal), fed `chunk_heads` heads per call
+    to bound its memory; inputs on the host in fp64, generation excluded."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -71,18 +71,21 @@ def cpu_baseline(reps_heads: int = 8):
     import workloads as W
 
     w = W.WORKLOADS["dense_bf16"]
+    heads = w.B * w.H
     rng = np.random.default_rng(0)
-    shape = (1, reps_heads, w.Nq, w.d)
+    shape = (heads, w.Nq, w.d)
     q, k, v = (W.to_dtype(rng.standard_normal(shape, dtype=np.float32), "bf16").double().numpy() for _ in range(3))
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, w.scale, False)
-    oracle.attention(q, k, v, w.scale, True)
+    for h in range(0, heads, chunk_heads):
+        sl = slice(h, h + chunk_heads)
+        oracle.attention(q[sl], k[sl], v[sl], w.scale, False)
+        oracle.attention(q[sl], k[sl], v[sl], w.scale, True)
     dt = time.perf_counter() - t0
-    flops = 4.0 * reps_heads * w.Nq * w.Nk * w.d * 1.5
+    flops = 4.0 * heads * w.Nq * w.Nk * w.d * 1.5
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"B=1 H={reps_heads} N=4096 d=128 bf16 inputs in fp64, non-causal + causal "
-                      f"({reps_heads}/32 of the heads of one step), {dt:.1f} s"}
+            "sample": f"one whole step: B*H={heads} heads of N=4096 d=128 bf16 inputs in fp64, "
+                      f"non-causal + causal, {chunk_heads} heads per oracle call, {dt:.1f} s"}
 
 
 def measured_mfma_tflops():
