@@ -60,6 +60,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr float kSplitBelowP = 8.0f;
 
+// Word 3 of a raw buffer resource on gfx950: 32-bit data format, no
+// swizzle, no stride; with num_records in bytes, out-of-range reads return 0.
+constexpr int kBufferFlags = 0x00020000;
+
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maximum).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -269,6 +273,40 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
     const int pg = min(max(load_uniform(p.block_table, (int64_t)b * p.max_pages + j), 0), p.num_pages - 1);
     return ((int64_t)pg * p.page_size + (ka0 - j * p.page_size)) * p.H + h;
   };
+  // Dense K or V tile: the wave's i-th load fills 1 KiB block i * NW + wv.
+  // The rows come through a buffer resource based at the tile's first key,
+  // so the per-lane byte offset (row within the block, swizzled chunk) is the
+  // same for every tile and the block offset is a wave-uniform scalar: a full
+  // tile costs no vector instructions.  The resource covers only the tile's
+  // keys; the last tile, when it runs past them, clamps its rows per lane to
+  // the last key, so no read goes out of range.
+  auto dense_load = [&](const uint8_t* base, uint8_t* ring, int kt, int buf, bool is_v) {
+    auto chunk = [&](int r, int ch) { return is_v ? v_chunk<C::CHUNKS>(r, ch) : k_chunk<C::CHUNKS>(r, ch); };
+    const int rows = min(BC, k_len - kt * BC);  // >= 1: only tiles holding keys are loaded
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (int64_t)kt * BC * C::ROWB), 0, rows * C::ROWB, kBufferFlags);
+    if (rows == BC) {
+#pragma unroll
+      for (int i = 0; i < C::LOADS / NW; ++i) {
+        const int blk = i * NW + wv;
+        // the swizzles read the row mod 16, which is the same for every i
+        // when a round of NW blocks spans a multiple of 16 rows
+        const int r = (NW * RPB) % 16 == 0 ? wv * RPB + lane / C::CHUNKS : blk * RPB + lane / C::CHUNKS;
+        const uint32_t voff = (uint32_t)((lane / C::CHUNKS) * C::ROWB + chunk(r, lane % C::CHUNKS) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(ring + buf * C::TILEB + blk * 1024), 16, voff,
+                                                 (uint32_t)(blk * 1024), 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::LOADS / NW; ++i) {
+        const int blk = i * NW + wv;
+        const int r = blk * RPB + lane / C::CHUNKS;
+        const uint32_t voff = (uint32_t)(min(r, rows - 1) * C::ROWB + chunk(r, lane % C::CHUNKS) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(ring + buf * C::TILEB + blk * 1024), 16, voff,
+                                                 0, 0, 0);
+      }
+    }
+  };
   auto load_k = [&](int kt, int buf) {
     if constexpr (PAGED) {
       const uint8_t* base = (const uint8_t*)p.k + paged_row(kt) * C::ROWB;
@@ -281,14 +319,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
         __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsK + buf * C::TILEB + blk * 1024), 16, 0, 0);
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < C::LOADS / NW; ++i) {
-        const int blk = wv * (C::LOADS / NW) + i;
-        const int r = blk * RPB + lane / C::CHUNKS;
-        const int key = min(kt * BC + r, k_len - 1);
-        const uint8_t* src = Kb + (int64_t)key * C::ROWB + k_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsK + buf * C::TILEB + blk * 1024), 16, 0, 0);
-      }
+      dense_load(Kb, ldsK, kt, buf, false);
     }
   };
   auto load_v = [&](int kt, int buf) {
@@ -303,14 +334,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
         __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsV + buf * C::TILEB + blk * 1024), 16, 0, 0);
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < C::LOADS / NW; ++i) {
-        const int blk = wv * (C::LOADS / NW) + i;
-        const int r = blk * RPB + lane / C::CHUNKS;
-        const int key = min(kt * BC + r, k_len - 1);
-        const uint8_t* src = Vb + (int64_t)key * C::ROWB + v_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsV + buf * C::TILEB + blk * 1024), 16, 0, 0);
-      }
+      dense_load(Vb, ldsV, kt, buf, true);
     }
   };
 
