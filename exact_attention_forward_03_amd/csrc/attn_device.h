@@ -100,6 +100,10 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// Word 3 of a raw buffer resource on gfx950: 32-bit data format, no
+// swizzle, no stride; num_records counts bytes.
+constexpr int kBufferFlags = 0x00020000;
+
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 }  // namespace attn

@@ -12,8 +12,10 @@
 //   wave's softmax can overlap the other's MFMAs.  The LDS fragment reads
 //   of each MFMA chain are issued a fixed number of MFMAs ahead, and a wave
 //   raises its issue priority while it runs an MFMA chain.
-// * K and V tiles go from HBM/L2 straight into LDS (global_load_lds_dwordx4:
-//   no staging registers, no VALU, no LDS write instructions), through a
+// * K and V tiles go from HBM/L2 straight into LDS (buffer_load_dwordx4 with
+//   the lds bit through a resource per tile, or global_load_lds_dwordx4 for
+//   paged caches: no staging registers, no LDS write instructions, and for
+//   dense tensors no vector instructions at all), through a
 //   ring of NS buffers: the load of tile j+NS-1 is issued at step j, so a
 //   tile has NS-1 steps to arrive.  Rows are stored unpadded with the
 //   16-byte chunks of each row XOR-permuted by a function of the row, which
@@ -59,10 +61,6 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr float kSplitBelowP = 8.0f;
-
-// Word 3 of a raw buffer resource on gfx950: 32-bit data format, no
-// swizzle, no stride; with num_records in bytes, out-of-range reads return 0.
-constexpr int kBufferFlags = 0x00020000;
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maximum).
 template <int N>

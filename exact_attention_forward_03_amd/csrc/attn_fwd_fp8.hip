@@ -136,26 +136,52 @@ attn_fwd_fp8_kernel(FwdParams p) {
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
 
   // Direct-to-LDS load of one tile into ring slot `buf`: the wave's i-th
-  // instruction fills 1 KiB block wv * LPW + i (8 rows); lane l writes
-  // physical chunk l % 8 of row 8 * block + l / 8 and fetches the logical
-  // chunk stored there.  Rows past the end of the keys re-read the last key
-  // (finite codes, masked).
+  // instruction fills 1 KiB block i * NW + wv (8 rows) of K and of V; lane l
+  // writes physical chunk l % 8 of row 8 * block + l / 8 and fetches the
+  // logical chunk stored there.  The rows come through buffer resources
+  // based at the tile's first key: the swizzles read the row mod 16, which
+  // does not depend on i, so a lane's byte offset is the same for every
+  // load and tile and the block offset is a scalar.  The resources cover only
+  // the tile's keys; a last tile that runs past them re-reads the last key
+  // (finite codes, masked) through per-lane clamped offsets.
+  static_assert((NW * 8) % 16 == 0, "block rounds span whole swizzle periods");
   auto load_tile = [&](int kt, int buf) {
+    const int rows = min(BC, k_len - kt * BC);  // >= 1: only tiles holding keys are loaded
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kp + (int64_t)kt * BC * kRowB), 0, rows * kRowB, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Vp + (int64_t)kt * BC * kRowB), 0, rows * kRowB, kBufferFlags);
+    const int r0 = wv * 8 + (lane >> 3);  // row of the lane's first block; later blocks agree mod 16
+    if (rows == BC) {
+      const uint32_t offk = (uint32_t)((lane >> 3) * kRowB + k8_chunk(r0, lane & 7) * 16);
+      const uint32_t offv = (uint32_t)((lane >> 3) * kRowB + v8_chunk(r0, lane & 7) * 16);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int blk = wv * LPW + i;
-      const int r = blk * 8 + (lane >> 3);
-      const int key = min(kt * BC + r, k_len - 1);
-      const uint8_t* srck = Kp + (int64_t)key * kRowB + k8_chunk(r, lane & 7) * 16;
-      __builtin_amdgcn_global_load_lds(srck, (lds_void_t*)(ldsK + buf * kTileB + blk * 1024), 16, 0, 0);
-    }
+      for (int i = 0; i < LPW; ++i) {
+        const int blk = i * NW + wv;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(ldsK + buf * kTileB + blk * 1024), 16, offk,
+                                                 (uint32_t)(blk * 1024), 0, 0);
+      }
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int blk = wv * LPW + i;
-      const int r = blk * 8 + (lane >> 3);
-      const int key = min(kt * BC + r, k_len - 1);
-      const uint8_t* srcv = Vp + (int64_t)key * kRowB + v8_chunk(r, lane & 7) * 16;
-      __builtin_amdgcn_global_load_lds(srcv, (lds_void_t*)(ldsV + buf * kTileB + blk * 1024), 16, 0, 0);
+      for (int i = 0; i < LPW; ++i) {
+        const int blk = i * NW + wv;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(ldsV + buf * kTileB + blk * 1024), 16, offv,
+                                                 (uint32_t)(blk * 1024), 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int blk = i * NW + wv;
+        const int r = blk * 8 + (lane >> 3);
+        const uint32_t off = (uint32_t)(min(r, rows - 1) * kRowB + k8_chunk(r, lane & 7) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(ldsK + buf * kTileB + blk * 1024), 16, off, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int blk = i * NW + wv;
+        const int r = blk * 8 + (lane >> 3);
+        const uint32_t off = (uint32_t)(min(r, rows - 1) * kRowB + v8_chunk(r, lane & 7) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(ldsV + buf * kTileB + blk * 1024), 16, off, 0, 0, 0);
+      }
     }
   };
 
