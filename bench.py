@@ -121,7 +121,8 @@ def timed_launches(fn, n, stream):
 
 
 def bench_detail(attn, steps, warmup):
-    """Per-shape throughput of the other workloads (mean over `steps` launches)."""
+    """Per-shape throughput of the other workloads (mean and median over
+    `steps` launches)."""
     import numpy as np
     import torch
 
@@ -145,9 +146,11 @@ def bench_detail(attn, steps, warmup):
 
         for _ in range(warmup):
             run()
-        ms = float(np.mean(timed_launches(run, steps, stream)))
+        ts = timed_launches(run, steps, stream)
+        ms, med = float(np.mean(ts)), float(np.median(ts))
         tf = w.flops() / (ms / 1e3) / 1e12
         out[name] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "ms_median": round(med, 4), "tflops_median": round(w.flops() / (med / 1e3) / 1e12, 2),
                      "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
         del q, k, v, o, lse
     out["hbm_copy_gbs"] = copy_bandwidth()
@@ -330,11 +333,14 @@ def bench_fp8(attn, steps, warmup):
     for _ in range(warmup):
         run_attn()
         run_prep()
-    ms = float(np.mean(timed_launches(run_attn, steps, stream)))
+    ts = timed_launches(run_attn, steps, stream)
+    ms, med = float(np.mean(ts)), float(np.median(ts))
     ms_prep = float(np.mean(timed_launches(run_prep, steps, stream)))
     tf = w.flops() / (ms / 1e3) / 1e12
     prep_bytes = 3 * q32.numel() * (4 + 1) + 3 * sq.numel() * 4
     return {"fp8_outlier": {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                            "ms_median": round(med, 4),
+                            "tflops_median": round(w.flops() / (med / 1e3) / 1e12, 2),
                             "shape": [w.B, w.H, w.Nq, w.Nk, w.d]},
             "fp8_prep_qkv": {"ms": round(ms_prep, 4), "gbs": round(prep_bytes / (ms_prep / 1e3) / 1e9, 1),
                              "frac_hbm": round(prep_bytes / (ms_prep / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}}
@@ -445,7 +451,7 @@ def main():
     result["roofline"]["measured_mfma_peak"] = mb16
     result["roofline"]["frac_of_measured_peak"] = round(ach / mb16, 4) if mb16 else None
     if not args.no_detail:
-        result["detail"] = bench_detail(attn, max(5, args.steps // 5), 2)
+        result["detail"] = bench_detail(attn, max(10, args.steps // 2), 3)
         if mf8 and "fp8_outlier" in result["detail"]:
             fp8 = result["detail"]["fp8_outlier"]
             fp8["measured_mfma_peak"] = mf8
