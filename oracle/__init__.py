@@ -24,7 +24,8 @@ Modules:
   normalised form the blog prints and the deferred-normalisation form;
 * ``fp8``: e4m3 rounding from the format definition, the Sylvester Hadamard
   and its fast transform, the rotation, block/per-tensor quantisation, and
-  an fp64 emulation of fp8 attention;
+  an fp64 emulation of fp8 attention, and both for variable-length batches
+  (scale tiles restarting at every sequence);
 * ``splitkv``: attention over key chunks and the (O, lse) merge of the
   partial results;
 * ``backward``: the gradients dQ, dK, dV of the attention definition (the

@@ -288,6 +288,99 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     return o, lse
 
 
+# --------------------------------------------------------------------------
+# Variable-length batches: sequences packed along the token axis
+# --------------------------------------------------------------------------
+
+def varlen_scale_len(total: int, nseq: int, tile: int = 128) -> int:
+    """Scale entries per head for a packed tensor of `total` tokens in `nseq`
+    sequences: ceil(total / tile) + nseq, an upper bound on the tiles
+    sum_b ceil(L_b / tile) that needs no sequence length."""
+    return (int(total) + tile - 1) // tile + int(nseq)
+
+
+def varlen_tile_offsets(cu, tile: int = 128) -> np.ndarray:
+    """First scale entry of each sequence: the tiles of the earlier ones,
+    sum_{b' < b} ceil(L_b' / tile) (scale tiles restart at every sequence,
+    so none straddles two sequences)."""
+    lens = np.diff(np.asarray(cu, dtype=np.int64))
+    nt = (lens + tile - 1) // tile
+    return np.concatenate([[0], np.cumsum(nt)[:-1]]).astype(np.int64)
+
+
+def quantize_varlen(x, cu, signs=None, per_tensor: bool = False, tile: int = 128):
+    """Rotate and quantise a packed tensor x [H, T, d] whose sequence b holds
+    tokens [cu[b], cu[b+1]).
+
+    Block mode: each sequence is quantised on its own (`quantize` of its
+    [H, L_b, d] slice), its scales stored at entries
+    varlen_tile_offsets(cu)[b] + t of a [H, varlen_scale_len] array; entries
+    past the last sequence's tiles are 1.  Per-tensor mode: one scale for the
+    whole tensor (as `quantize` of all of x), in every entry.
+    Returns ``(codes uint8 [H, T, d], scales float32 [H, varlen_scale_len])``.
+    """
+    x64 = _f64(x)
+    cu = np.asarray(cu, dtype=np.int64)
+    H, T, d = x64.shape
+    nseq = len(cu) - 1
+    scales = np.ones((H, varlen_scale_len(T, nseq, tile)), dtype=np.float32)
+    if per_tensor:
+        codes, s = quantize(x64[None], signs, per_tensor=True, tile=tile)
+        scales[...] = s.reshape(-1)[0] if s.size else np.float32(1.0)
+        return codes[0], scales
+    codes = np.zeros((H, T, d), dtype=np.uint8)
+    offs = varlen_tile_offsets(cu, tile)
+    for b in range(nseq):
+        a, e = int(cu[b]), int(cu[b + 1])
+        if e <= a:
+            continue
+        c, s = quantize(x64[:, a:e], signs, per_tensor=False, tile=tile)
+        codes[:, a:e] = c
+        scales[:, offs[b]:offs[b] + s.shape[-1]] = s
+    return codes, scales
+
+
+def attention_fp8_varlen(q8, k8, v8, sq, sk, sv, cu_q, cu_k, scale: float, causal: bool = False,
+                         tile: int = 128, quantize_p: bool = True, ambiguity: float = 0.0, parts: bool = False):
+    """fp8 attention of a variable-length batch: codes [H, T, d] packed along
+    tokens, scales [H, varlen_scale_len] laid out as by `quantize_varlen`.
+
+    Each sequence is an independent problem ("Flash Attention 3：让 GPU 跑满的
+    注意力计算", §5.2): `attention_fp8` of its slices and of its own scale
+    entries (so the V-scale normalisation uses the largest V scale of that
+    sequence and head), causal with indices local to the sequence.
+    Returns float64 ``(O [H, Tq, d], lse [H, Tq])`` (and the flip bound with
+    ``ambiguity > 0``); ``parts=True`` returns a list with, per non-empty
+    query sequence, ``(first query row, parts dict of attention_fp8)``.
+    """
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    H, Tq, d = q8.shape
+    o = np.zeros((H, Tq, d))
+    lse = np.full((H, Tq), -np.inf)
+    flip = np.zeros((H, Tq, d)) if ambiguity > 0 else None
+    out_parts = []
+    oq, ok = varlen_tile_offsets(cu_q, tile), varlen_tile_offsets(cu_k, tile)
+    for b in range(len(cu_q) - 1):
+        qa, qe, ka, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if qe <= qa:
+            continue
+        ntq, ntk = (qe - qa + tile - 1) // tile, (ke - ka + tile - 1) // tile
+        r = attention_fp8(q8[:, qa:qe], k8[:, ka:ke], v8[:, ka:ke], sq[:, oq[b]:oq[b] + ntq],
+                          sk[:, ok[b]:ok[b] + ntk], sv[:, ok[b]:ok[b] + ntk], scale, causal, tile=tile,
+                          quantize_p=quantize_p, ambiguity=ambiguity, parts=True)
+        o[:, qa:qe] = r["o"]
+        lse[:, qa:qe] = r["lse"]
+        if flip is not None:
+            flip[:, qa:qe] = r["flip"]
+        out_parts.append((qa, r))
+    if parts:
+        return out_parts
+    if flip is not None:
+        return o, lse, flip
+    return o, lse
+
+
 def rmse(a, b) -> float:
     """sqrt(mean((a - b)^2)) over all elements, in float64."""
     a = _f64(a)

@@ -289,3 +289,107 @@ def test_mutation_wrong_fp8_max(monkeypatch):
     monkeypatch.setattr(F, "E4M3_MAX", 240.0)
     with pytest.raises(AssertionError):
         test_quantize_properties(False, True)
+
+
+# ------------------------------------------------------------------ variable-length batches
+
+VARLEN_LENS = [130, 1, 0, 256, 300, 127]  # ragged, a one-token and an empty sequence
+
+
+def _packed(lens, d, seed):
+    cu = W.cu_seqlens(lens)
+    x = np.random.default_rng(seed).standard_normal((3, int(cu[-1]), d)).astype(np.float32)
+    x *= np.exp(np.random.default_rng(seed + 1).uniform(-3, 3, (3, int(cu[-1]), 1))).astype(np.float32)
+    return x, cu
+
+
+def test_varlen_tile_layout():
+    cu = W.cu_seqlens(VARLEN_LENS)
+    # tiles per sequence: 2, 1, 0, 2, 3, 1 -> first entries 0, 2, 3, 3, 5, 8
+    assert F.varlen_tile_offsets(cu).tolist() == [0, 2, 3, 3, 5, 8]
+    assert F.varlen_scale_len(int(cu[-1]), len(VARLEN_LENS)) == (814 + 127) // 128 + 6
+    assert F.varlen_tile_offsets(cu)[-1] + 1 <= F.varlen_scale_len(int(cu[-1]), len(VARLEN_LENS))
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+def test_quantize_varlen_tiles_restart_per_sequence(rotate):
+    """Each sequence's tiles start at its first token: the largest magnitude
+    of every (head, sequence tile) lands on 448 and the codes round to
+    nearest, checked per sequence with the dense property checker; entries
+    past the last tile stay 1."""
+    d = 64
+    x, cu = _packed(VARLEN_LENS, d, 5)
+    s = RNG.choice([-1.0, 1.0], d).astype(np.float32) if rotate else None
+    codes, scales = F.quantize_varlen(x, cu, s)
+    assert codes.shape == x.shape and scales.shape == (3, F.varlen_scale_len(x.shape[1], len(VARLEN_LENS)))
+    offs = F.varlen_tile_offsets(cu)
+    x_rot = F.rotate(x, s) if rotate else x.astype(np.float64)
+    for b in range(len(VARLEN_LENS)):
+        a, e = int(cu[b]), int(cu[b + 1])
+        if e > a:
+            nt = (e - a + 127) // 128
+            _check_quantized(x_rot[:, a:e], codes[:, a:e], scales[:, offs[b]:offs[b] + nt], 128, False)
+    used = int(offs[-1]) + (VARLEN_LENS[-1] + 127) // 128
+    assert np.all(scales[:, used:] == 1.0)
+
+
+def test_quantize_varlen_aligned_equals_dense():
+    """Sequences whose lengths are multiples of 128 tile the packed tensor
+    exactly as the dense layout does, so codes and scales coincide with
+    `quantize` of the whole tensor as one batch entry."""
+    x, cu = _packed([256, 128, 384], 64, 9)
+    codes, scales = F.quantize_varlen(x, cu)
+    ref_c, ref_s = F.quantize(x[None])
+    assert np.array_equal(codes, ref_c[0])
+    assert np.array_equal(scales[:, :6], ref_s[0])
+
+
+def test_quantize_varlen_per_tensor_equals_dense():
+    x, cu = _packed(VARLEN_LENS, 64, 13)
+    codes, scales = F.quantize_varlen(x, cu, per_tensor=True)
+    ref_c, ref_s = F.quantize(x[None], per_tensor=True)
+    assert np.array_equal(codes, ref_c[0])
+    assert np.all(scales == ref_s.flat[0])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_varlen_reduces_to_exact_varlen(causal):
+    """With P unrounded the fp8 emulation of a packed batch equals the exact
+    variable-length definition on the dequantised inputs (each sequence with
+    its own scale tiles; a different code path: exact.attention_varlen)."""
+    d = 32
+    lens_q, lens_k = [130, 1, 0, 200], [130, 5, 3, 129]
+    cq, ck = W.cu_seqlens(lens_q), W.cu_seqlens(lens_k)
+    nq, nk = int(cq[-1]), int(ck[-1])
+    q8 = W.random_e4m3_codes((2, nq, d), 21, max_exp_field=9)
+    k8 = W.random_e4m3_codes((2, nk, d), 22, max_exp_field=9)
+    v8 = W.random_e4m3_codes((2, nk, d), 23, max_exp_field=9)
+    sq = W.random_scales((2, F.varlen_scale_len(nq, 4)), 24)
+    sk = W.random_scales((2, F.varlen_scale_len(nk, 4)), 25)
+    sv = W.random_scales((2, F.varlen_scale_len(nk, 4)), 26)
+    o, lse = F.attention_fp8_varlen(q8, k8, v8, sq, sk, sv, cq, ck, 0.3, causal, quantize_p=False)
+
+    def deq(codes, scales, cu):  # dequantise each sequence with its own tiles
+        out = np.zeros(codes.shape)
+        offs = F.varlen_tile_offsets(cu)
+        for b in range(len(cu) - 1):
+            a, e = int(cu[b]), int(cu[b + 1])
+            vals = F.e4m3_decode(codes[:, a:e])
+            rows = offs[b] + np.arange(e - a) // 128
+            out[:, a:e] = vals * scales[:, rows].astype(np.float64)[..., None]
+        return out
+
+    ref_o, ref_l = oracle.attention_varlen(deq(q8, sq, cq), deq(k8, sk, ck), deq(v8, sv, ck), cq, ck, 0.3, causal)
+    np.testing.assert_allclose(o, ref_o, rtol=0, atol=1e-12)
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(fin, np.isfinite(lse))
+    np.testing.assert_allclose(lse[fin], ref_l[fin], rtol=1e-13, atol=1e-12)
+
+
+def test_fp8_varlen_single_sequence_equals_dense():
+    q8, k8, v8, sq, sk, sv = _codes_problem(300, 300, 32, 31)
+    cu = np.array([0, 300])
+    pad = lambda s: np.concatenate([s, np.ones((2, 1), np.float32)], axis=-1)  # noqa: E731
+    o, lse = F.attention_fp8_varlen(q8, k8, v8, pad(sq), pad(sk), pad(sv), cu, cu, 0.3, True)
+    ref_o, ref_l = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, True)
+    assert np.array_equal(o, ref_o) and np.array_equal(lse, ref_l)
