@@ -4,8 +4,9 @@
 The C entry points are exposed under their own names with plain integer
 pointers (argument marshalling only): ``attn_fwd``, ``attn_fwd_stream``,
 ``attn_fwd_splitkv``, ``attn_fwd_paged``, ``attn_merge``, ``attn_bwd``,
-``attn_fp8_quantize``, ``attn_strerror``.  ``forward``, ``forward_splitkv``,
-``forward_paged``, ``merge``, ``backward`` and ``fp8_quantize`` are the
+``attn_fp8_quantize``, ``attn_fp8_quantize_varlen``, ``attn_strerror``.
+``forward``, ``forward_splitkv``, ``forward_paged``, ``merge``, ``backward``,
+``fp8_quantize`` and ``fp8_quantize_varlen`` are the
 torch-facing conveniences: they allocate the
 outputs (and workspaces) with torch on the inputs' device, pass
 ``data_ptr()``s and torch's current HIP stream, and raise ``RuntimeError`` on
@@ -24,8 +25,8 @@ __all__ = [
     "ATTN_DT_F16", "ATTN_DT_BF16", "ATTN_DT_FP8_E4M3", "ATTN_DT_F32", "ATTN_DT_INT8",
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP",
     "load", "lib_path", "attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_fp8_quantize",
-    "attn_fwd_paged", "attn_bwd", "attn_strerror", "forward", "forward_splitkv", "forward_paged", "merge",
-    "backward", "fp8_quantize",
+    "attn_fwd_paged", "attn_bwd", "attn_strerror", "attn_fp8_quantize_varlen", "forward", "forward_splitkv",
+    "forward_paged", "merge", "backward", "fp8_quantize", "fp8_quantize_varlen",
     "default_splits", "EXPORTS",
 ]
 
@@ -33,7 +34,7 @@ ATTN_DT_F16, ATTN_DT_BF16, ATTN_DT_FP8_E4M3, ATTN_DT_F32, ATTN_DT_INT8 = 0, 1, 2
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
 
 EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_fwd_paged", "attn_merge", "attn_bwd",
-           "attn_fp8_quantize", "attn_strerror")
+           "attn_fp8_quantize", "attn_fp8_quantize_varlen", "attn_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -71,6 +72,8 @@ def load():
         lib.attn_bwd.restype = _i
         lib.attn_fp8_quantize.argtypes = [_p, _i, _p, _p, _i, _i, _i, _i, _p, _i, _p]
         lib.attn_fp8_quantize.restype = _i
+        lib.attn_fp8_quantize_varlen.argtypes = [_p, _i, _p, _p, _i, _i, _i, _p, _i, _p, _i, _p]
+        lib.attn_fp8_quantize_varlen.restype = _i
         lib.attn_strerror.argtypes = [_i]
         lib.attn_strerror.restype = ctypes.c_char_p
         _LIB = lib
@@ -118,6 +121,12 @@ def attn_fp8_quantize(x, x_dtype, x_fp8, x_scale, B, H, N, d, signs, per_tensor,
     return load().attn_fp8_quantize(x, x_dtype, x_fp8, x_scale, B, H, N, d, signs, per_tensor, hip_stream)
 
 
+def attn_fp8_quantize_varlen(x, x_dtype, x_fp8, x_scale, H, T, d, cu_seqlens, nseq, signs, per_tensor,
+                             hip_stream) -> int:
+    return load().attn_fp8_quantize_varlen(x, x_dtype, x_fp8, x_scale, H, T, d, cu_seqlens, nseq, signs,
+                                           per_tensor, hip_stream)
+
+
 def attn_strerror(code: int) -> str:
     return load().attn_strerror(code).decode()
 
@@ -160,7 +169,8 @@ def forward(q, k, v, *, causal: bool = False, scale: Optional[float] = None, cu_
     Dense: q [B, H, Nq, d], k/v [B, H, Nk, d] -> (o [B, H, Nq, d], lse [B, H, Nq]).
     Varlen (cu_seqlens_q/k int32 [B+1] on the device): q [H, Tq, d],
     k/v [H, Tk, d] -> (o [H, Tq, d], lse [H, Tq]).
-    fp8 (q, k, v uint8 e4m3 codes with fp32 scales [B, H, ceil(N/128)]):
+    fp8 (q, k, v uint8 e4m3 codes with fp32 scales [B, H, ceil(N/128)], or
+    for varlen [H, ceil(T/128) + B] as ``fp8_quantize_varlen`` writes them):
     o is bfloat16.  Tensors must be contiguous and on one GPU.
     """
     import torch
@@ -392,5 +402,29 @@ def fp8_quantize(x, signs=None, per_tensor: bool = False, out=None, scales=None)
         scales = torch.empty((B, H, (N + 127) // 128), dtype=torch.float32, device=x.device)
     rc = attn_fp8_quantize(_ptr(x), _dtype_code(x), _ptr(out), _ptr(scales), B, H, N, d, _ptr(signs),
                            int(bool(per_tensor)), _stream(x.device))
+    _check(rc)
+    return out, scales
+
+
+def fp8_quantize_varlen(x, cu_seqlens, signs=None, per_tensor: bool = False, out=None, scales=None):
+    """``fp8_quantize`` of a packed batch x [H, T, d] (sequence b on tokens
+    [cu_seqlens[b], cu_seqlens[b+1]), cu_seqlens int32 on the device), with
+    the 128-row tiles restarting at every sequence.
+
+    Returns ``(codes uint8 [H, T, d], scales float32 [H, ceil(T/128) + nseq])``
+    in the layout ``forward`` reads for fp8 with cu_seqlens.
+    """
+    import torch
+
+    if x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [H, T, d] tensor")
+    H, T, d = x.shape
+    nseq = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((H, (T + 127) // 128 + nseq), dtype=torch.float32, device=x.device)
+    rc = attn_fp8_quantize_varlen(_ptr(x), _dtype_code(x), _ptr(out), _ptr(scales), H, T, d, _ptr(cu_seqlens),
+                                  nseq, _ptr(signs), int(bool(per_tensor)), _stream(x.device))
     _check(rc)
     return out, scales

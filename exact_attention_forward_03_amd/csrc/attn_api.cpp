@@ -38,7 +38,7 @@ int validate_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4)) return ATTN_ERR_INVALID_ARG;
   }
   if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
-  if (dtype == ATTN_DT_FP8_E4M3 && (d != 128 || cu_q)) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_DT_FP8_E4M3 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (cu_q == nullptr && (int64_t)B * H > (int64_t)INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
   return ATTN_OK;
 }
@@ -92,7 +92,7 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   hipStream_t st = (hipStream_t)hip_stream;
   hipError_t e;
   if (dtype == ATTN_DT_FP8_E4M3)
-    e = attn::launch_fwd_fp8(d, causal != 0, p, st);
+    e = attn::launch_fwd_fp8(d, causal != 0, varlen, p, st);
   else
     e = attn::launch_fwd(dtype, d, causal != 0, varlen, false, 0, p, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -263,6 +263,30 @@ int attn_fp8_quantize(const void* x, int x_dtype, void* x_fp8, float* x_scale, i
   attn::PrepParams p{};
   p.x = x; p.x_dtype = x_dtype; p.x8 = (uint8_t*)x_fp8; p.scale = x_scale;
   p.BH = B * H; p.N = N; p.d = d; p.signs = signs; p.mode = 0;
+  hipError_t e = attn::launch_fp8_prep(p, per_tensor != 0, (hipStream_t)hip_stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fp8_quantize_varlen(const void* x, int x_dtype, void* x_fp8, float* x_scale, int H, int T, int d,
+                             const int32_t* cu_seqlens, int nseq, const float* signs, int per_tensor,
+                             void* hip_stream) {
+  if (!x || !x_fp8 || !x_scale || !cu_seqlens) return ATTN_ERR_INVALID_ARG;
+  if (H < 1 || T < 0 || nseq < 1) return ATTN_ERR_INVALID_ARG;
+  if (x_dtype != ATTN_DT_F32 && x_dtype != ATTN_DT_BF16 && x_dtype != ATTN_DT_F16) return ATTN_ERR_INVALID_ARG;
+  if (per_tensor != 0 && per_tensor != 1) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(x_fp8, 16) || !aligned(x_scale, 4) || !aligned(cu_seqlens, 4))
+    return ATTN_ERR_INVALID_ARG;
+  if (signs && !aligned(signs, 4)) return ATTN_ERR_INVALID_ARG;
+  if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
+  // scale entries per head: ceil(T / 128) + nseq; the grid is H times that
+  if (((int64_t)T + 127) / 128 + nseq > INT32_MAX / 2 ||
+      (int64_t)H * (((int64_t)T + 127) / 128 + nseq) > INT32_MAX)
+    return ATTN_ERR_INVALID_ARG;
+  if (T == 0) return ATTN_OK;
+  attn::PrepParams p{};
+  p.x = x; p.x_dtype = x_dtype; p.x8 = (uint8_t*)x_fp8; p.scale = x_scale;
+  p.BH = H; p.N = T; p.d = d; p.signs = signs; p.mode = 0;
+  p.cu = cu_seqlens; p.nseq = nseq;
   hipError_t e = attn::launch_fp8_prep(p, per_tensor != 0, (hipStream_t)hip_stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

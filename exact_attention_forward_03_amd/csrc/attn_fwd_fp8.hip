@@ -63,8 +63,11 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return (uint32_t)w;
 }
 
-// NW waves per workgroup (32 query rows each), NS LDS ring slots.
-template <bool CAUSAL, int NW, int NS>
+// NW waves per workgroup (32 query rows each), NS LDS ring slots.  VARLEN:
+// a packed batch [H, T, d] with cu_seqlens; the work item is (head,
+// sequence, query tile) and the scales of sequence s start at entry
+// sum_{s' < s} ceil(L_s' / 128) of the head's ceil(T / 128) + B entries.
+template <bool CAUSAL, int NW, int NS, bool VARLEN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
 attn_fwd_fp8_kernel(FwdParams p) {
   constexpr int D = kFp8D, BC = kFp8BC;
@@ -81,14 +84,47 @@ attn_fwd_fp8_kernel(FwdParams p) {
   const int work = xcd_remap(blockIdx.x, p.n_work);
   const int head = work / p.tiles_per_head;
   const int t = work - head * p.tiles_per_head;
-  const int qt = CAUSAL ? (p.tiles_per_head - 1 - t) : t;
-  const int q_len = p.Nq, k_len = p.Nk;
+  int qt, q_len, k_len;
+  int64_t q_row0, k_row0, sq0, sk0;  // first rows of the (sequence,) head; its first scale entries
+  if constexpr (!VARLEN) {
+    qt = CAUSAL ? (p.tiles_per_head - 1 - t) : t;
+    q_len = p.Nq;
+    k_len = p.Nk;
+    q_row0 = (int64_t)head * p.Nq;
+    k_row0 = (int64_t)head * p.Nk;
+    sq0 = (int64_t)head * ((q_len + BC - 1) / BC);
+    sk0 = (int64_t)head * ((k_len + BC - 1) / BC);
+  } else {
+    // sequence of query tile t (tiles of BR rows per sequence), and the
+    // scale tiles (BC = 128 rows) of the sequences before it
+    int acc = 0, seq = -1, qb = 0, qe = 0, kb = 0, ke = 0, nts = 0, tq = 0, tk = 0;
+    for (int s = 0; s < p.B; ++s) {
+      const int a = min(max(p.cu_q[s], 0), p.Nq);
+      const int b = min(max(p.cu_q[s + 1], a), p.Nq);
+      const int ka = min(max(p.cu_k[s], 0), p.Nk);
+      const int kz = min(max(p.cu_k[s + 1], ka), p.Nk);
+      const int nt = (b - a + BR - 1) / BR;
+      if (t < acc + nt) {
+        seq = s; qb = a; qe = b; kb = ka; ke = kz; nts = nt;
+        break;
+      }
+      acc += nt;
+      tq += (b - a + BC - 1) / BC;
+      tk += (kz - ka + BC - 1) / BC;
+    }
+    if (seq < 0) return;  // surplus work item (the grid is an upper bound)
+    qt = CAUSAL ? (nts - 1 - (t - acc)) : (t - acc);
+    q_len = qe - qb;
+    k_len = ke - kb;
+    q_row0 = (int64_t)head * p.Nq + qb;
+    k_row0 = (int64_t)head * p.Nk + kb;
+    sq0 = (int64_t)head * ((p.Nq + BC - 1) / BC + p.B) + tq;
+    sk0 = (int64_t)head * ((p.Nk + BC - 1) / BC + p.B) + tk;
+  }
   const int q0 = qt * BR;
-  const int64_t q_row0 = (int64_t)head * p.Nq, k_row0 = (int64_t)head * p.Nk;
-  const int nqs = (q_len + BC - 1) / BC;
   const int nks = (k_len + BC - 1) / BC;
-  const float* __restrict__ sk = p.k_scale + (int64_t)head * nks;
-  const float* __restrict__ sv = p.v_scale + (int64_t)head * nks;
+  const float* __restrict__ sk = p.k_scale + sk0;
+  const float* __restrict__ sv = p.v_scale + sk0;
 
   const uint8_t* __restrict__ Qp = (const uint8_t*)p.q + q_row0 * D;
   const uint8_t* __restrict__ Kp = (const uint8_t*)p.k + k_row0 * D;
@@ -108,7 +144,7 @@ attn_fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) sv_max = fmaxf(sv_max, __shfl_xor(sv_max, s));
   const float lsv_max = sv_max > 0.f ? __log2f(sv_max) : 0.f;
-  const float sq = wave_live ? p.q_scale[(int64_t)head * nqs + qw0 / BC] : 0.f;
+  const float sq = wave_live ? p.q_scale[sq0 + qw0 / BC] : 0.f;
 
   // Q fragments (B operand of S^T): row my_q, bytes [64 ks + 32 hh, +32)
   uint4 qf[KS][2];
@@ -364,10 +400,10 @@ attn_fwd_fp8_kernel(FwdParams p) {
   }
 }
 
-template <bool CAUSAL, int NW, int NS>
+template <bool CAUSAL, int NW, int NS, bool VARLEN>
 hipError_t launch_fp8(const FwdParams& p, hipStream_t st) {
   constexpr int lds = 2 * NS * kTileB;
-  auto kern = attn_fwd_fp8_kernel<CAUSAL, NW, NS>;
+  auto kern = attn_fwd_fp8_kernel<CAUSAL, NW, NS, VARLEN>;
   static bool attr_set = false;  // idempotent; a benign race between threads
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -387,10 +423,10 @@ bool fp8_small_wg(bool causal) { return causal; }
 
 int fwd_fp8_block_rows(bool causal) { return fp8_small_wg(causal) ? 128 : 256; }
 
-hipError_t launch_fwd_fp8(int d, bool causal, const FwdParams& p, hipStream_t st) {
+hipError_t launch_fwd_fp8(int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
   if (d != kFp8D) return hipErrorInvalidValue;
-  if (fp8_small_wg(causal)) return causal ? launch_fp8<true, 4, 2>(p, st) : launch_fp8<false, 4, 2>(p, st);
-  return causal ? launch_fp8<true, 8, 3>(p, st) : launch_fp8<false, 8, 3>(p, st);
+  if (varlen) return causal ? launch_fp8<true, 4, 2, true>(p, st) : launch_fp8<false, 8, 3, true>(p, st);
+  return causal ? launch_fp8<true, 4, 2, false>(p, st) : launch_fp8<false, 8, 3, false>(p, st);
 }
 
 }  // namespace attn

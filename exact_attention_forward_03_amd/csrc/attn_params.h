@@ -19,8 +19,8 @@ struct FwdParams {
   const int32_t* cu_k;   // varlen only
   int tiles_per_head;    // query tiles per (b, h) (varlen: upper bound per head)
   int n_work;            // workgroups launched
-  const float* q_scale;  // fp8 only: [B, H, ceil(Nq/128)]
-  const float* k_scale;  // fp8: [B, H, ceil(Nk/128)]; 8-bit paged cache: [num_pages, page_size, H]
+  const float* q_scale;  // fp8 only: [B, H, ceil(Nq/128)]; varlen [H, ceil(Nq/128) + B]
+  const float* k_scale;  // fp8: [B, H, ceil(Nk/128)] (varlen [H, ceil(Nk/128) + B]); 8-bit paged cache: [num_pages, page_size, H]
   const float* v_scale;
   int n_split;           // key chunks (split launches only)
   int split_len;         // keys per chunk
@@ -55,6 +55,11 @@ struct PrepParams {
   int BH, N, d;
   const float* signs;    // NULL: no rotation
   int mode;              // 0: block scales; 1: tile amax only; 2: quantise with the tensor amax
+  // variable-length batch (cu non-NULL): x is [H, N, d] with sequence s on
+  // tokens [cu[s], cu[s+1]); scale is [H, ceil(N/128) + nseq], sequence s's
+  // tiles from entry sum_{s' < s} ceil(L_s' / 128)
+  const int32_t* cu;
+  int nseq;
 };
 
 // Query rows per workgroup of each kernel variant (sizes the grid).
@@ -93,7 +98,7 @@ int fwd_fp8_block_rows(bool causal);
 hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, int kv, const FwdParams& p,
                       hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
-hipError_t launch_fwd_fp8(int d, bool causal, const FwdParams& p, hipStream_t st);
+hipError_t launch_fwd_fp8(int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st);
 hipError_t launch_fp8_prep(const PrepParams& p, bool per_tensor, hipStream_t st);
 
 }  // namespace attn

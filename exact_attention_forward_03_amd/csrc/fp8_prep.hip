@@ -14,6 +14,9 @@
 // code = e4m3(x' / s): x' / s correctly rounded to fp32, then rounded to
 // nearest even e4m3.
 //
+// A variable-length batch ([H, T, d] with cu_seqlens) restarts the tiles at
+// every sequence, so no tile (and no scale) spans two sequences.
+//
 // Per-tensor mode runs three launches: the tile amaxes into the scale array,
 // one workgroup turning their maximum into s for every entry, and the
 // quantisation with that s.
@@ -112,12 +115,39 @@ __global__ void __launch_bounds__(kPrepThreads) fp8_prep_kernel(PrepParams p) {
   constexpr int PASSES = kTileRows / RPP;
   __shared__ float red[kPrepThreads / 64];
 
-  const int nt = (p.N + kTileRows - 1) / kTileRows;
+  const int nt = (p.N + kTileRows - 1) / kTileRows + (p.cu ? p.nseq : 0);  // scale entries per head
   const int bh = blockIdx.x / nt;
   const int tile = blockIdx.x - bh * nt;
   const int tid = threadIdx.x;
   const int rl = tid / L, cl = tid % L;
   const int64_t base = (int64_t)bh * p.N;
+  // rows [row0, row_end) of this tile; a variable-length batch restarts the
+  // tiles at every sequence (entry `tile` = the earlier sequences' tiles +
+  // the tile's index in its sequence; prefix sums clamped into [0, N])
+  int row0 = tile * kTileRows, row_end = p.N;
+  if (p.cu) {
+    int acc = 0;
+    bool found = false;
+    for (int s = 0; s < p.nseq; ++s) {
+      const int a = min(max(p.cu[s], 0), p.N);
+      const int b = min(max(p.cu[s + 1], a), p.N);
+      const int n = (b - a + kTileRows - 1) / kTileRows;
+      if (tile < acc + n) {
+        row0 = a + (tile - acc) * kTileRows;
+        row_end = b;
+        found = true;
+        break;
+      }
+      acc += n;
+    }
+    if (!found) {
+      // an entry past the last sequence's tiles: 1 (block scales), 0 (tile
+      // amax, so it does not raise the tensor amax); the tensor-scale pass
+      // then overwrites it
+      if (MODE != 2 && tid == 0) p.scale[bh * nt + tile] = MODE == 1 ? 0.f : 1.f;
+      return;
+    }
+  }
 
   float sg[8];
 #pragma unroll
@@ -128,8 +158,8 @@ __global__ void __launch_bounds__(kPrepThreads) fp8_prep_kernel(PrepParams p) {
   float amax = 0.f;
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
-    const int row = tile * kTileRows + ps * RPP + rl;
-    if (row < p.N) {
+    const int row = row0 + ps * RPP + rl;
+    if (row < row_end) {
       const int64_t off = (base + row) * D + cl * 8;
       if constexpr (IN == 3) load8((const float*)p.x + off, v[ps]);
       else if constexpr (IN == 1) load8((const uint16_t*)p.x + off, v[ps], bf16_t{});
@@ -190,8 +220,8 @@ __global__ void __launch_bounds__(kPrepThreads) fp8_prep_kernel(PrepParams p) {
   };
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
-    const int row = tile * kTileRows + ps * RPP + rl;
-    if (row < p.N) {
+    const int row = row0 + ps * RPP + rl;
+    if (row < row_end) {
       float z[8];
       if (markstein) {
 #pragma unroll
@@ -218,7 +248,7 @@ __global__ void __launch_bounds__(kPrepThreads) tensor_scale_kernel(float* scale
 
 template <int IN, int D>
 hipError_t launch_in_d(const PrepParams& p, bool per_tensor, hipStream_t st) {
-  const int nt = (p.N + kTileRows - 1) / kTileRows;
+  const int nt = (p.N + kTileRows - 1) / kTileRows + (p.cu ? p.nseq : 0);
   const int64_t grid = (int64_t)nt * p.BH;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (!per_tensor) {

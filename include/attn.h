@@ -77,6 +77,10 @@ enum {
  *   attn_fp8_quantize, o is bfloat16, and q_scale, k_scale, v_scale are the
  *   fp32 dequantisation multipliers [B, H, ceil(N/128)] (one per 128-row
  *   tile; "FlashAttention-3", "Three techniques" §3: block quantisation).
+ *   fp8 varlen: the tiles restart at every sequence, so no tile spans two
+ *   sequences; the scales are [H, ceil(N/128) + B] with sequence b's tiles
+ *   from entry sum_{b' < b} ceil(L_b' / 128) (the layout
+ *   attn_fp8_quantize_varlen writes; later entries are not read).
  *   For fp16/bf16 the three scale pointers are ignored (may be NULL); for
  *   fp8 they may be NULL only where the tensor is empty (Nq or Nk = 0).
  *   Scales must be >= 0 (attn_fp8_quantize writes positive ones).
@@ -86,8 +90,7 @@ enum {
  * B, H >= 1; Nq, Nk >= 0.  Nq = 0 is a no-op; Nk = 0 (or an empty key
  * sequence) gives O = 0 and lse = -inf.  q, o, lse may be NULL only if
  * Nq = 0, and k, v only if Nk = 0.  Pointers must be 16-byte aligned
- * (cu_seqlens and the scales: 4-byte).  fp8 with cu_seqlens returns
- * ATTN_ERR_UNSUPPORTED.
+ * (cu_seqlens and the scales: 4-byte).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Nq, int Nk, int d, float scale, int causal,
@@ -125,6 +128,30 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
 int attn_fp8_quantize(const void* x, int x_dtype, void* x_fp8, float* x_scale,
                       int B, int H, int N, int d, const float* signs, int per_tensor,
                       void* hip_stream);
+
+/*
+ * attn_fp8_quantize_varlen — attn_fp8_quantize for a variable-length batch
+ * ("Flash Attention 3：让 GPU 跑满的注意力计算", §5.2 packed sequences with
+ * cu_seqlens; "FlashAttention-3", "Three techniques" §3 block quantisation).
+ *
+ *   x [H, T, d] of x_dtype: nseq sequences packed along the token axis,
+ *     sequence b on tokens [cu_seqlens[b], cu_seqlens[b+1]) (int32 device
+ *     array of nseq+1 cumulative lengths; clamped into [0, T]).
+ *   Rotation (signs) and quantisation as attn_fp8_quantize, with the
+ *     128-row tiles restarting at every sequence: a tile never spans two
+ *     sequences, as the attention kernel reads one scale per (sequence,
+ *     128-row tile).
+ *   Outputs: x_fp8 uint8 [H, T, d]; x_scale fp32 [H, ceil(T/128) + nseq]
+ *     (a size that needs no sequence lengths on the host): sequence b's
+ *     tiles from entry sum_{b' < b} ceil(L_b' / 128); the entries after the
+ *     last sequence's tiles are written too (1, or the tensor scale with
+ *     per_tensor = 1) and never read.
+ *   H, nseq >= 1; T >= 0 (T = 0 is a no-op).  cu_seqlens must be non-NULL.
+ *   Same pointer, stream and error rules as attn_fp8_quantize.
+ */
+int attn_fp8_quantize_varlen(const void* x, int x_dtype, void* x_fp8, float* x_scale,
+                             int H, int T, int d, const int32_t* cu_seqlens, int nseq,
+                             const float* signs, int per_tensor, void* hip_stream);
 
 /*
  * attn_fwd_splitkv — attn_fwd (dense layout only) computed over key chunks

@@ -95,7 +95,7 @@ def test_invalid_arguments(lib, entry, over):
 UNSUPPORTED = [
     dict(d=96), dict(d=32), dict(d=512), dict(d=0),
     dict(dtype=attn.ATTN_DT_FP8_E4M3, d=64, q_scale=FAKE, k_scale=FAKE, v_scale=FAKE),
-    dict(dtype=attn.ATTN_DT_FP8_E4M3, d=128, q_scale=FAKE, k_scale=FAKE, v_scale=FAKE,
+    dict(dtype=attn.ATTN_DT_FP8_E4M3, d=256, q_scale=FAKE, k_scale=FAKE, v_scale=FAKE,
          cu_seqlens_q=FAKE, cu_seqlens_k=FAKE),
 ]
 
@@ -132,6 +132,28 @@ def test_quantize_invalid(lib, over):
 def test_quantize_unsupported_and_noop(lib):
     assert quant(d=96) == attn.ATTN_ERR_UNSUPPORTED
     assert quant(N=0) == attn.ATTN_OK
+
+
+def quant_varlen(**over):
+    a = dict(x=FAKE, x_dtype=attn.ATTN_DT_F32, x_fp8=FAKE, x_scale=FAKE, H=2, T=300, d=128, cu=FAKE, nseq=3,
+             signs=None, per_tensor=0)
+    a.update(over)
+    return attn.attn_fp8_quantize_varlen(a["x"], a["x_dtype"], a["x_fp8"], a["x_scale"], a["H"], a["T"], a["d"],
+                                         a["cu"], a["nseq"], a["signs"], a["per_tensor"], None)
+
+
+@pytest.mark.parametrize("over", [dict(x=None), dict(x_fp8=None), dict(x_scale=None), dict(cu=None), dict(H=0),
+                                  dict(T=-1), dict(nseq=0), dict(x_dtype=attn.ATTN_DT_FP8_E4M3),
+                                  dict(per_tensor=2), dict(x=FAKE + 4), dict(cu=FAKE + 2), dict(signs=FAKE + 2),
+                                  dict(T=2 ** 31 - 1, nseq=2 ** 30, H=4)],
+                         ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_quantize_varlen_invalid(lib, over):
+    assert quant_varlen(**over) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_quantize_varlen_unsupported_and_noop(lib):
+    assert quant_varlen(d=96) == attn.ATTN_ERR_UNSUPPORTED
+    assert quant_varlen(T=0) == attn.ATTN_OK
 
 
 def test_binding_has_no_cpu_fallback():

@@ -263,3 +263,94 @@ def test_fp8_full_outlier_gates(gpu_lib):
           f"per-tensor {g_pt:.3e} (emulation {e_pt:.3e}); ratio {g_pt / g_blk:.2f}")
     assert g_pt / g_blk >= 2.0
     assert g_blk <= 1.1 * e_blk and g_pt <= 1.1 * e_pt
+
+
+# ---------------------------------------------------------------- variable-length batches
+
+VARLEN_LENS = [300, 1, 0, 128, 129, 513, 100]  # ragged, a one-token and an empty sequence
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_prep_varlen_no_rotation_bitwise(gpu_lib, in_dtype, d, per_tensor):
+    """Tiles restart at every sequence: codes and scales equal the oracle's
+    per-sequence quantisation bit for bit, including the entries past the
+    last sequence's tiles."""
+    cu = W.cu_seqlens(VARLEN_LENS)
+    rng = np.random.default_rng(d + 5)
+    x = rng.standard_normal((3, int(cu[-1]), d), dtype=np.float32) * np.float32(2.0)
+    x[1, 300:301] = 0.0  # the one-token sequence of head 1 is all zero: scale 1
+    xt = torch.from_numpy(x) if in_dtype == "f32" else W.to_dtype(x, in_dtype)
+    codes, scales = gpu_lib.fp8_quantize_varlen(xt.cuda(), _dev(cu), None, per_tensor)
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = F.quantize_varlen(xt.double().numpy().astype(np.float32), cu, None, per_tensor)
+    assert np.array_equal(scales.cpu().numpy(), ref_scales)
+    bad = np.argwhere(codes.cpu().numpy() != ref_codes)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
+
+
+def _exact_varlen_problem(H, lens_q, lens_k, seed):
+    d = 128
+    cq, ck = W.cu_seqlens(lens_q), W.cu_seqlens(lens_k)
+    nq, nk, B = int(cq[-1]), int(ck[-1]), len(lens_q)
+    q8 = W.random_codes_from(EXACT_CODES, (H, nq, d), seed)
+    k8 = W.random_codes_from(EXACT_CODES, (H, nk, d), seed + 1)
+    v8 = W.random_codes_from(EXACT_CODES, (H, nk, d), seed + 2)
+    sq = W.random_pow2_scales((H, F.varlen_scale_len(nq, B)), seed + 3, -1, 0)
+    sk = W.random_pow2_scales((H, F.varlen_scale_len(nk, B)), seed + 4, -1, 0)
+    sv = W.random_pow2_scales((H, F.varlen_scale_len(nk, B)), seed + 5, -7, -4)
+    return q8, k8, v8, sq, sk, sv, cq, ck
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lens_q,lens_k", [(VARLEN_LENS, VARLEN_LENS), ([200, 0, 300, 7], [90, 5, 400, 0])],
+                         ids=["same", "q_ne_k"])
+def test_fp8_varlen_kernel_vs_emulation(gpu_lib, causal, lens_q, lens_k):
+    """Each sequence against the oracle's fp8 emulation of it, with its own
+    scale tiles and V-scale normalisation (same bar and allowances as the
+    dense kernel test)."""
+    q8, k8, v8, sq, sk, sv, cq, ck = _exact_varlen_problem(3, lens_q, lens_k, seed=len(lens_q) + 17)
+    o, lse = gpu_lib.forward(_dev(q8), _dev(k8), _dev(v8), causal=causal, scale=0.0884, cu_seqlens_q=_dev(cq),
+                             cu_seqlens_k=_dev(ck), q_scale=_dev(sq), k_scale=_dev(sk), v_scale=_dev(sv))
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16 and o.shape == q8.shape and lse.shape == q8.shape[:2]
+    o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    ref_o = np.zeros(q8.shape)
+    ref_l = np.full(q8.shape[:2], -np.inf)
+    allow = np.zeros(q8.shape)
+    for qa, r in F.attention_fp8_varlen(q8, k8, v8, sq, sk, sv, cq, ck, 0.0884, causal, ambiguity=3e-5,
+                                        parts=True):
+        n = r["o"].shape[-2]
+        ref_o[:, qa:qa + n], ref_l[:, qa:qa + n] = r["o"], r["lse"]
+        allow[:, qa:qa + n] = r["flip"] + _pv_bound(r)
+    _check(o, lse, ref_o, ref_l, f"fp8 varlen causal{causal}", allow=allow)
+    assert np.mean(allow) <= 0.25 * np.mean(np.abs(ref_o)) + 1e-6
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_varlen_end_to_end_rmse(gpu_lib, causal):
+    """fp32 packed inputs -> rotation and per-sequence block quantisation ->
+    fp8 attention, all on the device, against the fp64 attention of the fp32
+    originals: RMSE <= 3e-2 on N(0,1) inputs, and close to the emulation's."""
+    lens = [700, 129, 1, 400]
+    cu = W.cu_seqlens(lens)
+    T, H, d = int(cu[-1]), 4, 128
+    rng = np.random.default_rng(41)
+    q, k, v = (rng.standard_normal((H, T, d), dtype=np.float32) for _ in range(3))
+    signs = rng.choice([-1.0, 1.0], d).astype(np.float32)
+    cud, sd = _dev(cu), _dev(signs)
+    q8, sq = gpu_lib.fp8_quantize_varlen(_dev(q), cud, sd)
+    k8, sk = gpu_lib.fp8_quantize_varlen(_dev(k), cud, sd)
+    v8, sv = gpu_lib.fp8_quantize_varlen(_dev(v), cud, None)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = gpu_lib.forward(q8, k8, v8, causal=causal, scale=scale, cu_seqlens_q=cud, cu_seqlens_k=cud,
+                             q_scale=sq, k_scale=sk, v_scale=sv)
+    torch.cuda.synchronize()
+    truth_o, _ = oracle.attention_varlen(q, k, v, cu, cu, scale, causal)
+    err = F.rmse(o.double().cpu().numpy(), truth_o)
+    emu_o, _ = F.attention_fp8_varlen(q8.cpu().numpy(), k8.cpu().numpy(), v8.cpu().numpy(), sq.cpu().numpy(),
+                                      sk.cpu().numpy(), sv.cpu().numpy(), cu, cu, scale, causal)
+    emu = F.rmse(emu_o, truth_o)
+    assert err <= 3e-2, err
+    assert err <= 1.1 * emu + 1e-3, (err, emu)
