@@ -343,7 +343,43 @@ def bench_fp8(attn, steps, warmup):
                             "tflops_median": round(w.flops() / (med / 1e3) / 1e12, 2),
                             "shape": [w.B, w.H, w.Nq, w.Nk, w.d]},
             "fp8_prep_qkv": {"ms": round(ms_prep, 4), "gbs": round(prep_bytes / (ms_prep / 1e3) / 1e9, 1),
-                             "frac_hbm": round(prep_bytes / (ms_prep / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}}
+                             "frac_hbm": round(prep_bytes / (ms_prep / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+            **bench_fp8_varlen(attn, steps, warmup)}
+
+
+def bench_fp8_varlen(attn, steps, warmup):
+    """The variable-length causal workload (8 sequences, H=32, d=128) in fp8:
+    Q, K rotated and quantised per sequence tile on the device, then the
+    e4m3 attention kernel alone is timed."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+
+    w = W.WORKLOADS["varlen_bf16_causal"]
+    x = W.make_inputs(w)
+    cu = torch.from_numpy(x["cu_seqlens"]).cuda()
+    signs = torch.from_numpy(np.random.default_rng(w.seed).choice([-1.0, 1.0], w.d).astype(np.float32)).cuda()
+    q8, sq = attn.fp8_quantize_varlen(torch.from_numpy(x["q"]).cuda(), cu, signs)
+    k8, sk = attn.fp8_quantize_varlen(torch.from_numpy(x["k"]).cuda(), cu, signs)
+    v8, sv = attn.fp8_quantize_varlen(torch.from_numpy(x["v"]).cuda(), cu, None)
+    o, lse = attn.forward(q8, k8, v8, causal=True, scale=w.scale, cu_seqlens_q=cu, cu_seqlens_k=cu,
+                          q_scale=sq, k_scale=sk, v_scale=sv)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        attn.forward(q8, k8, v8, causal=True, scale=w.scale, cu_seqlens_q=cu, cu_seqlens_k=cu,
+                     q_scale=sq, k_scale=sk, v_scale=sv, out=o, lse=lse)
+
+    for _ in range(warmup):
+        run()
+    ts = timed_launches(run, steps, stream)
+    ms, med = float(np.mean(ts)), float(np.median(ts))
+    tf = w.flops() / (ms / 1e3) / 1e12
+    return {"fp8_varlen_causal": {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                                  "ms_median": round(med, 4),
+                                  "tflops_median": round(w.flops() / (med / 1e3) / 1e12, 2),
+                                  "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}}
 
 
 def copy_calib():
