@@ -65,7 +65,7 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   if (rc != ATTN_OK) return rc;
   if (Nq == 0) return ATTN_OK;
   const bool varlen = cu_seqlens_q != nullptr;
-  const int br = attn::fwd_block_rows(dtype, d, causal != 0);
+  const int br = attn::fwd_block_rows(dtype, d, causal != 0, varlen);
 
   attn::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;

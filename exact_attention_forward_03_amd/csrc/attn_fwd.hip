@@ -708,18 +708,23 @@ hipError_t launch_dma_one(const FwdParams& p, hipStream_t st) {
 
 // Tile configuration per head dimension and masking: key rows per tile,
 // waves per workgroup (query rows = 32 x waves), waves per SIMD, LDS ring
-// depth and loop options.  Causal attention at d = 128 runs 4-wave
-// workgroups, two per CU: their diagonal tiles and early exits then do not
-// hold a whole 8-wave workgroup at its barriers.
+// depth and loop options.  Dense causal launches at d = 128 use the
+// non-causal configuration: every workgroup runs a pair of query tiles of
+// equal total work (+8 % over 4-wave workgroups with 64-key tiles, measured
+// at N = 4096 and 8192).  Variable-length causal launches have no pairs and
+// run 4-wave workgroups, two per CU, so that one workgroup's diagonal tiles
+// and early exits do not hold a whole 8-wave workgroup at its barriers.
 template <int D, bool CAUSAL> struct DmaTile;
 template <bool CAUSAL> struct DmaTile<64, CAUSAL> {
   static constexpr int BC = 64, NW = 8, WPE = 2, NS = 3, OPT = kOptPin | kOptPrio;
 };
-template <> struct DmaTile<128, false> { static constexpr int BC = 128, NW = 8, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
-template <> struct DmaTile<128, true> { static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
+template <bool CAUSAL> struct DmaTile<128, CAUSAL> {
+  static constexpr int BC = 128, NW = 8, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio;
+};
 template <bool CAUSAL> struct DmaTile<256, CAUSAL> {
   static constexpr int BC = 64, NW = 4, WPE = 1, NS = 2, OPT = kOptPin;
 };
+struct VarlenCausalTile128 { static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
 
 // Key-chunk launches at d = 128 (decoding and long keys with few queries):
 // 4-wave workgroups with a 64 KiB ring, so two run on each CU.
@@ -731,6 +736,9 @@ hipError_t launch_dma_d(const FwdParams& p, hipStream_t st) {
   if constexpr (SPLIT && D == 128) {
     using S = SplitTile128;
     return launch_dma_one<TT, D, S::BC, S::NW, S::WPE, S::NS, S::OPT, CAUSAL, VARLEN, SPLIT, KV>(p, st);
+  } else if constexpr (CAUSAL && VARLEN && D == 128) {
+    using V = VarlenCausalTile128;
+    return launch_dma_one<TT, D, V::BC, V::NW, V::WPE, V::NS, V::OPT, CAUSAL, VARLEN, SPLIT, KV>(p, st);
   } else {
     return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, T::OPT, CAUSAL, VARLEN, SPLIT, KV>(p, st);
   }
@@ -771,14 +779,16 @@ hipError_t launch_dma_t(int d, bool causal, bool varlen, bool split, int kv, con
 
 int fwd_split_block_rows(int dtype, int d, bool causal) {
   if (d == 128) return 32 * SplitTile128::NW;
-  return fwd_block_rows(dtype, d, causal);
+  return fwd_block_rows(dtype, d, causal, false);
 }
 
-int fwd_block_rows(int dtype, int d, bool causal) {
+int fwd_block_rows(int dtype, int d, bool causal, bool varlen) {
   if (dtype == 2) return fwd_fp8_block_rows(causal);
   switch (d) {
     case 64: return 32 * DmaTile<64, false>::NW;
-    case 128: return causal ? 32 * DmaTile<128, true>::NW : 32 * DmaTile<128, false>::NW;
+    case 128:
+      if (causal && varlen) return 32 * VarlenCausalTile128::NW;
+      return causal ? 32 * DmaTile<128, true>::NW : 32 * DmaTile<128, false>::NW;
     default: return 32 * DmaTile<256, false>::NW;
   }
 }

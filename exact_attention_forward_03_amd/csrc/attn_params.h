@@ -88,7 +88,7 @@ int bwd_key_block(int d);    // keys per dK/dV workgroup
 int bwd_query_block(int d);  // queries per dQ workgroup
 hipError_t launch_bwd(int dtype, int d, bool causal, bool varlen, BwdParams p, hipStream_t st);
 
-int fwd_block_rows(int dtype, int d, bool causal);
+int fwd_block_rows(int dtype, int d, bool causal, bool varlen);
 int fwd_split_block_rows(int dtype, int d, bool causal);  // key-chunk launches
 int fwd_split_tile_keys(int d);  // key rows per tile of key-chunk launches (chunk lengths are multiples)
 int fwd_fp8_block_rows(bool causal);

@@ -82,13 +82,16 @@ def test_splitkv_no_keys(gpu_lib):
 
 def test_splitkv_matches_single_pass(gpu_lib):
     """One chunk is the plain kernel on the whole key range; the merge of one
-    part returns it (up to the fp32 -> bf16 rounding of the same values)."""
+    part returns it.  The dense causal launch runs 128-key tiles and the key
+    chunk launch 64-key tiles, so their fp32 sums differ only in order: lse
+    agrees to a few fp32 ulps, O to the bf16 rounding of nearly equal values."""
     rng = np.random.default_rng(3)
     q, k, v = (to_device(rng.standard_normal((1, 4, 200, 128), dtype=np.float32), "bf16")[0] for _ in range(3))
     o1, l1 = gpu_lib.forward(q, k, v, causal=True)
     o2, l2 = gpu_lib.forward_splitkv(q, k, v, causal=True, num_splits=1)
     torch.cuda.synchronize()
-    assert torch.equal(l1, l2)
+    assert torch.equal(torch.isneginf(l1), torch.isneginf(l2))
+    assert (l1 - l2).abs().max().item() <= 8 * 2 ** -23 * max(1.0, l1.abs().max().item())
     assert (o1.float() - o2.float()).abs().max().item() <= 2 ** -8
 
 
