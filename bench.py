@@ -401,7 +401,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)  # the GPU needs ~100 launches to settle
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
@@ -487,7 +487,7 @@ def main():
     result["roofline"]["measured_mfma_peak"] = mb16
     result["roofline"]["frac_of_measured_peak"] = round(ach / mb16, 4) if mb16 else None
     if not args.no_detail:
-        result["detail"] = bench_detail(attn, max(10, args.steps // 2), 3)
+        result["detail"] = bench_detail(attn, max(10, args.steps // 2), 10)
         if mf8 and "fp8_outlier" in result["detail"]:
             fp8 = result["detail"]["fp8_outlier"]
             fp8["measured_mfma_peak"] = mf8
