@@ -198,3 +198,26 @@ def test_full_size_varlen_sampled(gpu_lib):
             rows = sample_rows(e - a, 8, seed=b + h)
             o_ref, l_ref = OX.attention_rows(q64[h, a:e], k64[h, a:e], v64[h, a:e], rows, w.scale, True)
             check(o[h, a:e][rows], lse[h, a:e][rows], o_ref, l_ref, "bf16", f"varlen full h{h} seq{b}")
+
+
+def test_query_tile_pair_paths(gpu_lib):
+    """Dense launches may run two query tiles per workgroup: across heads h
+    and h + heads/2 when the head count is even (the full-size tests), within
+    one head (t, T-1-t) when it is odd.  Odd head counts: causal (always
+    paired) on the whole output, and non-causal with enough tiles for pairs
+    to cover every CU (B1 H5 N=26624: 5 x 52 pairs) on sampled rows of
+    every head, including the middle tile of an odd tile count."""
+    q, k, v = W.random_problem(1, 3, 1000, 1000, 128, seed=77)
+    o, lse, (q64, k64, v64, s) = run_dense(gpu_lib, q, k, v, "bf16", True)
+    o_ref, l_ref = oracle.attention(q64, k64, v64, s, True)
+    check(o, lse, o_ref, l_ref, "bf16", "causal, 3 heads")
+
+    n = 26624 - 256  # 103 tiles of 256 rows: an odd count, the middle tile alone
+    q, k, v = W.random_problem(1, 5, n, n, 128, seed=78)
+    o, lse, (q64, k64, v64, s) = run_dense(gpu_lib, q, k, v, "bf16", False)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    mid = 51 * 256
+    for h in range(5):
+        rows = np.unique(np.concatenate([sample_rows(n, 24, seed=h), [mid, mid + 255]]))
+        o_ref, l_ref = OX.attention_rows(q64[0, h], k64[0, h], v64[0, h], rows, s, False)
+        check(o[0, h][rows], lse[0, h][rows], o_ref, l_ref, "bf16", f"non-causal paired, head {h}")
