@@ -250,7 +250,8 @@ def bench_decode(attn, steps, warmup):
 
 def bench_backward(attn, steps, warmup):
     """Backward pass (attn_bwd: delta, dK/dV and dQ kernels) on the dense
-    bf16 shape B=2 H=16 N=4096 d=128, non-causal and causal.  FLOPs are those
+    bf16 shape B=2 H=16 N=4096 d=128, non-causal and causal, and on the
+    large-head shape B=1 H=16 N=8192 d=256 (non-causal).  FLOPs are those
     of the five products of the gradient (S, dP, dV, dK, dQ: 10 B H N^2 d,
     halved for causal); the kernels recompute S and dP once more for dQ."""
     import numpy as np
@@ -260,7 +261,7 @@ def bench_backward(attn, steps, warmup):
 
     out = {}
     stream = torch.cuda.current_stream()
-    for name in ("dense_bf16", "dense_bf16_causal"):
+    for name in ("dense_bf16", "dense_bf16_causal", "hdim256_bf16"):
         w = W.WORKLOADS[name]
         rng = np.random.default_rng(5)
         shape = (w.B, w.H, w.Nq, w.d)

@@ -345,7 +345,7 @@ def merge(o_part, lse_part, *, out_dtype=None, out=None, lse=None):
 def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None, cu_seqlens_q=None,
              cu_seqlens_k=None, dq=None, dk=None, dv=None, delta=None):
     """Gradients (dq, dk, dv) of ``forward(q, k, v)`` for the output gradient
-    ``dout``, through ``attn_bwd``.  fp16/bf16, d = 64 or 128.  Dense:
+    ``dout``, through ``attn_bwd``.  fp16/bf16, d = 64, 128 or 256.  Dense:
     q, o, dout [B, H, Nq, d]; k, v [B, H, Nk, d]; lse float32 [B, H, Nq] from
     the forward.  Varlen (cu_seqlens_q/k int32 [B+1] on the device):
     q, o, dout [H, Tq, d], k, v [H, Tk, d], lse [H, Tq].  ``delta`` float32

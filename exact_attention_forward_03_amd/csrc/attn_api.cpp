@@ -229,7 +229,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
     return ATTN_ERR_INVALID_ARG;
   if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
-  if (dtype == ATTN_DT_FP8_E4M3 || d == 256) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_DT_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)B * H > (int64_t)INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
   const bool varlen = cu_seqlens_q != nullptr;
   const int64_t heads = varlen ? H : (int64_t)B * H;  // varlen: [H, T, d], B sequences

@@ -495,6 +495,14 @@ struct BwdCfg {
   static constexpr int NW = 4, WPE = 2, NS = 2;
   static constexpr int DQ_BC = 64, DQ_NW = 4, DQ_WPE = 2, DQ_NS = 2;
 };
+// d = 256: the dK and dV accumulators alone take 256 registers per lane, so
+// one wave per SIMD (512 registers, accumulators in AGPRs); LDS 128.5 KiB
+// (dK/dV: two 32-row Q/dO stages and 128 V rows) and 128 KiB (dQ).
+template <>
+struct BwdCfg<256> {
+  static constexpr int NW = 4, WPE = 1, NS = 2;
+  static constexpr int DQ_BC = 64, DQ_NW = 4, DQ_WPE = 1, DQ_NS = 2;
+};
 
 template <typename TT, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd_t(BwdParams p, hipStream_t st) {
@@ -547,14 +555,19 @@ hipError_t launch_bwd_d(int d, bool causal, bool varlen, const BwdParams& p, hip
   switch (d) {
     case 64: return launch_bwd_cv<TT, 64>(causal, varlen, p, st);
     case 128: return launch_bwd_cv<TT, 128>(causal, varlen, p, st);
+    case 256: return launch_bwd_cv<TT, 256>(causal, varlen, p, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-int bwd_key_block(int d) { return 32 * (d == 64 ? BwdCfg<64>::NW : BwdCfg<128>::NW); }
-int bwd_query_block(int d) { return 32 * (d == 64 ? BwdCfg<64>::DQ_NW : BwdCfg<128>::DQ_NW); }
+int bwd_key_block(int d) {
+  return 32 * (d == 64 ? BwdCfg<64>::NW : d == 128 ? BwdCfg<128>::NW : BwdCfg<256>::NW);
+}
+int bwd_query_block(int d) {
+  return 32 * (d == 64 ? BwdCfg<64>::DQ_NW : d == 128 ? BwdCfg<128>::DQ_NW : BwdCfg<256>::DQ_NW);
+}
 
 hipError_t launch_bwd(int dtype, int d, bool causal, bool varlen, BwdParams p, hipStream_t st) {
   return dtype == 0 ? launch_bwd_d<f16_t>(d, causal, varlen, p, st) : launch_bwd_d<bf16_t>(d, causal, varlen, p, st);

@@ -250,7 +250,7 @@ int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, cons
  *   o, lse: the forward's outputs for the same q, k, v, scale, causal;
  *   delta: fp32 workspace [B, H, Nq], caller-owned, 4-byte aligned; on
  *     return it holds delta_i = sum_c dO_ic O_ic;
- *   d ∈ {64, 128} (256 and fp8: ATTN_ERR_UNSUPPORTED).
+ *   d ∈ {64, 128, 256} (fp8: ATTN_ERR_UNSUPPORTED).
  *   Query-side arrays may be NULL only if Nq = 0, key-side arrays only if
  *   Nk = 0.  Nk = 0 gives dQ = 0; Nq = 0 gives dK = dV = 0.  dQ is
  *   accumulated per query row in one workgroup (no atomics): results are

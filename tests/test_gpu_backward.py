@@ -106,6 +106,9 @@ CASES = [
     (1, 1, 1, 1, 64, "bf16", False),
     (1, 2, 129, 127, 128, "bf16", True),
     (1, 1, 640, 640, 64, "bf16", True),
+    (1, 2, 300, 300, 256, "bf16", False),
+    (1, 2, 333, 200, 256, "f16", True),
+    (2, 1, 129, 520, 256, "bf16", True),
 ]
 
 
@@ -186,6 +189,7 @@ VARLEN_CASES = [
     (3, [200, 0, 77], [150, 40, 300], 64, "f16", False),
     (2, [513, 260], [513, 260], 64, "bf16", True),
     (2, [100, 33, 250], [90, 0, 250], 128, "bf16", False),
+    (2, [300, 129, 1], [300, 129, 1], 256, "bf16", True),
 ]
 
 
