@@ -68,8 +68,7 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
 // sequence, query tile) and the scales of sequence s start at entry
 // sum_{s' < s} ceil(L_s' / 128) of the head's ceil(T / 128) + B entries.
 template <bool CAUSAL, int NW, int NS, bool VARLEN>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
-attn_fwd_fp8_kernel(FwdParams p) {
+__device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   constexpr int D = kFp8D, BC = kFp8BC;
   constexpr int BR = NW * 32;
   constexpr int KS = D / 64;    // MFMA k-steps of S^T
@@ -81,7 +80,6 @@ attn_fwd_fp8_kernel(FwdParams p) {
   static_assert(kLoads % NW == 0, "each wave issues the same number of tile loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
 
-  const int work = xcd_remap(blockIdx.x, p.n_work);
   const int head = work / p.tiles_per_head;
   const int t = work - head * p.tiles_per_head;
   int qt, q_len, k_len;
@@ -400,6 +398,35 @@ attn_fwd_fp8_kernel(FwdParams p) {
   }
 }
 
+// The kernel: one work item, or for dense causal launches a pair of query
+// tiles of equal total work, one after the other: tile t of head h and tile
+// T-1-t of head h + heads/2 (an even head count), else tiles t and T-1-t of
+// one head; p.n_work counts pairs then.
+template <bool CAUSAL, int NW, int NS, bool VARLEN>
+__global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
+attn_fwd_fp8_kernel(FwdParams p) {
+  const int w = xcd_remap(blockIdx.x, p.n_work);
+  if constexpr (CAUSAL && !VARLEN) {
+    const int T = p.tiles_per_head, heads = p.B * p.H;
+    if (heads % 2 == 0) {
+      const int h = w / T, t = w - h * T;
+      fp8_body<CAUSAL, NW, NS, VARLEN>(p, h * T + t);
+      __syncthreads();
+      fp8_body<CAUSAL, NW, NS, VARLEN>(p, (h + heads / 2) * T + (T - 1 - t));
+    } else {
+      const int half = (T + 1) / 2;
+      const int head = w / half, t = w - head * half;
+      fp8_body<CAUSAL, NW, NS, VARLEN>(p, head * T + t);
+      if (T - 1 - t != t) {
+        __syncthreads();
+        fp8_body<CAUSAL, NW, NS, VARLEN>(p, head * T + (T - 1 - t));
+      }
+    }
+  } else {
+    fp8_body<CAUSAL, NW, NS, VARLEN>(p, w);
+  }
+}
+
 template <bool CAUSAL, int NW, int NS, bool VARLEN>
 hipError_t launch_fp8(const FwdParams& p, hipStream_t st) {
   constexpr int lds = 2 * NS * kTileB;
@@ -410,7 +437,12 @@ hipError_t launch_fp8(const FwdParams& p, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(p.n_work), dim3(NW * 64), lds, st, p);
+  FwdParams pp = p;
+  if constexpr (CAUSAL && !VARLEN) {
+    const int64_t heads = p.n_work / p.tiles_per_head;
+    pp.n_work = (int)(heads % 2 == 0 ? heads / 2 * p.tiles_per_head : heads * ((p.tiles_per_head + 1) / 2));
+  }
+  hipLaunchKernelGGL(kern, dim3(pp.n_work), dim3(NW * 64), lds, st, pp);
   return hipGetLastError();
 }
 

@@ -354,3 +354,15 @@ def test_fp8_varlen_end_to_end_rmse(gpu_lib, causal):
     emu = F.rmse(emu_o, truth_o)
     assert err <= 3e-2, err
     assert err <= 1.1 * emu + 1e-3, (err, emu)
+
+
+def test_fp8_causal_pairs_odd_heads(gpu_lib):
+    """Causal fp8 launches run two query tiles per workgroup: across heads h
+    and h + heads/2 for an even head count (the tests above), within one
+    head (t, T-1-t) for an odd one, with the middle tile alone when the
+    tile count is odd (9 tiles of 128 rows here)."""
+    q8, k8, v8, sq, sk, sv = _exact_problem(1, 3, 1100, 1100, seed=91)
+    o, lse = _run_fp8(gpu_lib, q8, k8, v8, sq, sk, sv, 0.0884, True)
+    ref = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.0884, True, ambiguity=3e-5, parts=True)
+    allow = ref["flip"] + _pv_bound(ref)
+    _check(o, lse, ref["o"], ref["lse"], "fp8 causal, 3 heads", allow=allow)
