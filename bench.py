@@ -345,6 +345,9 @@ def bench_fp8(attn, steps, warmup):
                             "shape": [w.B, w.H, w.Nq, w.Nk, w.d]},
             "fp8_prep_qkv": {"ms": round(ms_prep, 4), "gbs": round(prep_bytes / (ms_prep / 1e3) / 1e9, 1),
                              "frac_hbm": round(prep_bytes / (ms_prep / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+            # fp32 Q, K, V in HBM -> rotation and block quantisation -> e4m3 attention
+            "fp8_end_to_end": {"ms": round(ms + ms_prep, 4),
+                               "tflops": round(w.flops() / ((ms + ms_prep) / 1e3) / 1e12, 2)},
             **bench_fp8_varlen(attn, steps, warmup)}
 
 
