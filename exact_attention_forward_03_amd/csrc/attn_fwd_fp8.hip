@@ -252,19 +252,30 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   // registers); the four transposing reads m = 0..3 of a fragment deliver
   // k-indices 8m .. 8m+7.  In 16-lane group G (h = G / 2), source lane s
   // reads row key(8m + s / 2) at columns 32 db + 16 (G % 2) + 8 (s % 2) ..+8.
+  // The swizzle of row r reads bits 1 and 3 of r only, which come from the
+  // lane's part of the row (the rest is a multiple of 16): each lane's byte
+  // offset within a tile is one of DB loop-invariant values (one per output
+  // block), and the row steps are immediate offsets of the reads.
+  uint32_t vlane[DB];
+  {
+    const int G = lane >> 4, s16 = lane & 15, b = s16 >> 1;
+    const int lr = 8 * (b >> 2) + 4 * hh + (b & 3);  // the lane's row within 16
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      vlane[db] = (uint32_t)(lr * kRowB + v8_chunk(lr, 2 * db + (G & 1)) * 16 + 8 * (s16 & 1));
+  }
   auto pv_pass = [&](int vbuf, const uint4 (&pp)[PG][2]) {
     const uint8_t* vb = ldsV + vbuf * kTileB;
-    const int G = lane >> 4, s16 = lane & 15, b = s16 >> 1;
     constexpr int N = DB * PG;
     auto frag = [&](int i, uint4 (&f)[2]) {
       const int db = i % DB, g = i / DB;
-      const int ch = 2 * db + (G & 1);
+      const uint8_t* base = vb + vlane[db];
       uint32_t w[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int r = 64 * g + 32 * (m >> 1) + 16 * (m & 1) + 8 * (b >> 2) + 4 * hh + (b & 3);
+        const int rstep = 64 * g + 32 * (m >> 1) + 16 * (m & 1);  // multiple of 16 rows
         const i32x2_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) i32x2_t*)(vb + r * kRowB + v8_chunk(r, ch) * 16 + 8 * (s16 & 1)));
+            (__attribute__((address_space(3))) i32x2_t*)(base + rstep * kRowB));
         w[2 * m] = (uint32_t)x[0];
         w[2 * m + 1] = (uint32_t)x[1];
       }
