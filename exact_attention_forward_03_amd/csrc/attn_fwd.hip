@@ -47,10 +47,14 @@
 // * Workgroup order: the hardware id is remapped so that consecutive work
 //   items — the query tiles of one head — run on the same XCD and share its
 //   L2 copy of that head's K and V.  Dense causal launches give each
-//   workgroup two query tiles, t (which sees the most keys) and T-1-t (the
-//   fewest), one after the other: every workgroup then does the same work
-//   and the launch needs no dynamic balancing (+18 % over one tile per
-//   workgroup in heaviest-first order, measured at N = 4096).
+//   workgroup two query tiles, one that sees the most keys (t) and one that
+//   sees the fewest (T-1-t), one after the other: every workgroup then does
+//   the same work and the launch needs no dynamic balancing (+18 % over one
+//   tile per workgroup in heaviest-first order, measured at N = 4096).
+//   Dense non-causal launches pair tiles too when the pairs still cover
+//   every CU (one round of workgroups instead of two).  With an even number
+//   of heads the two tiles of a pair belong to heads h and h + heads/2, so
+//   the workgroups running at one time on an XCD share two heads' K/V.
 #include "attn_device.h"
 #include "attn_params.h"
 

@@ -21,7 +21,11 @@
 //   * V stays row-major in LDS; the V^T operand comes from the 8-bit
 //     transposing LDS read (ds_read_b64_tr_b8: within a 16-lane group, lane
 //     i receives byte i % 8 of the 8-byte pieces read by lanes 2j + i / 8),
-//     so each lane reads the 8 keys of one V column that its P bytes need.
+//     so each lane reads the 8 keys of one V column that its P bytes need;
+//   * variable-length batches restart the scale tiles at every sequence
+//     (the work item is (head, sequence, query tile));
+//   * dense causal launches run pairs of query tiles of equal total work
+//     per workgroup, as the fp16/bf16 kernel does.
 #include "attn_device.h"
 #include "attn_params.h"
 
