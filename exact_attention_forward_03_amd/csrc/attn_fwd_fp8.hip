@@ -461,9 +461,10 @@ hipError_t launch_fp8(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Configurations: non-causal, 8-wave workgroups with a 3-slot ring (one per
-// CU); causal, 4-wave workgroups with a 2-slot ring (64 KiB: two per CU, so
-// one workgroup's short diagonal tiles do not idle the CU; +3 % measured).
+// Configurations: non-causal, 8-wave workgroups with a 4-slot ring (one per
+// CU, 128 KiB; 1.5-2 % over 3 slots, measured at N = 4096 and 8192);
+// causal, 4-wave workgroups with a 2-slot ring (64 KiB: two per CU, so one
+// workgroup's short diagonal tiles do not idle the CU; +3 % measured).
 bool fp8_small_wg(bool causal) { return causal; }
 
 }  // namespace
@@ -472,8 +473,8 @@ int fwd_fp8_block_rows(bool causal) { return fp8_small_wg(causal) ? 128 : 256; }
 
 hipError_t launch_fwd_fp8(int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
   if (d != kFp8D) return hipErrorInvalidValue;
-  if (varlen) return causal ? launch_fp8<true, 4, 2, true>(p, st) : launch_fp8<false, 8, 3, true>(p, st);
-  return causal ? launch_fp8<true, 4, 2, false>(p, st) : launch_fp8<false, 8, 3, false>(p, st);
+  if (varlen) return causal ? launch_fp8<true, 4, 2, true>(p, st) : launch_fp8<false, 8, 4, true>(p, st);
+  return causal ? launch_fp8<true, 4, 2, false>(p, st) : launch_fp8<false, 8, 4, false>(p, st);
 }
 
 }  // namespace attn
