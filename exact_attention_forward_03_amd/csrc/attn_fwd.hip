@@ -110,6 +110,11 @@ __device__ __forceinline__ int v_chunk(int r, int ch) { return ch ^ ((r & 3) << 
 // the chain is not starved by the softmax VALU work of the other wave on the
 // SIMD.
 constexpr int kOptPin = 1, kOptPrio = 2;
+// kOptLateLoad: a step issues its tile loads after the S chain instead of
+// before it (the d = 256 configuration: one wave per SIMD, where the S
+// chain then starts at once after the barrier; +2.7 % measured there, and
+// -10 % at d = 128, where the loads need the whole step to land).
+constexpr int kOptLateLoad = 16;
 
 // A wave-uniform int32 read through the scalar data cache (s_load): it does
 // not count against the vector-memory counter that paces the tile loads.
@@ -168,7 +173,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
   constexpr int KVQ = KV >= kKvPagedE4m3 ? KV : 0;  // 8-bit cache kind, 0 for 16-bit
   static_assert(!(SPLIT && VARLEN), "key chunks are for dense batches");
   static_assert(!PAGED || (SPLIT && !CAUSAL), "paged caches are read by non-causal key-chunk launches");
-  constexpr bool PIN = OPT & kOptPin, PRIO = OPT & kOptPrio;
+  constexpr bool PIN = OPT & kOptPin, PRIO = OPT & kOptPrio, LATE = OPT & kOptLateLoad;
   constexpr int kPreD = 4;  // LDS fragment reads in flight ahead of their MFMA
   constexpr int NQB = 1;
   using C = PipeCfg<D, NQB, BC, NW, NS>;
@@ -617,17 +622,20 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
     if (kt + NS - 2 < n_kt) wait_vm<(NS - 2) * C::LPT>();
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // refill the slot tile kt-1 used (every wave is past it now)
-    if (kt + NS - 1 < n_kt) {
-      const int fs = (slot == 0) ? NS - 1 : slot - 1;
+    // refill the slot tile kt-1 used (every wave is past it now), before
+    // or after this step's S chain
+    const int fs = (slot == 0) ? NS - 1 : slot - 1;
+    if (!LATE && kt + NS - 1 < n_kt) {
       load_k(kt + NS - 1, fs);
       load_v(kt + NS - 1, fs);
     }
-    if (kt < wave_kt) {
-      f32x16_t s[NQB][C::MB];
-      compute_s(slot, s);
-      softmax_pv(kt, slot, s);
+    f32x16_t s[NQB][C::MB];
+    if (kt < wave_kt) compute_s(slot, s);
+    if (LATE && kt + NS - 1 < n_kt) {
+      load_k(kt + NS - 1, fs);
+      load_v(kt + NS - 1, fs);
     }
+    if (kt < wave_kt) softmax_pv(kt, slot, s);
     slot = (slot + 1 == NS) ? 0 : slot + 1;
   }
 
@@ -763,7 +771,7 @@ template <bool CAUSAL> struct DmaTile<128, CAUSAL> {
   static constexpr int BC = 128, NW = 8, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio;
 };
 template <bool CAUSAL> struct DmaTile<256, CAUSAL> {
-  static constexpr int BC = 64, NW = 4, WPE = 1, NS = 2, OPT = kOptPin;
+  static constexpr int BC = 64, NW = 4, WPE = 1, NS = 2, OPT = kOptPin | kOptLateLoad;
 };
 struct VarlenCausalTile128 { static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
 
