@@ -111,9 +111,10 @@ __device__ __forceinline__ int v_chunk(int r, int ch) { return ch ^ ((r & 3) << 
 // SIMD.
 constexpr int kOptPin = 1, kOptPrio = 2;
 // kOptLateLoad: a step issues its tile loads after the S chain instead of
-// before it (the d = 256 configuration: one wave per SIMD, where the S
-// chain then starts at once after the barrier; +2.7 % measured there, and
-// -10 % at d = 128, where the loads need the whole step to land).
+// before it, so the chain starts at once after the barrier.  Measured: +6 %
+// at d = 256 (one wave per SIMD), +9 % for variable-length causal launches
+// at d = 128 (4-wave workgroups); -10 % for dense d = 128 launches, whose
+// loads need the whole step to land; no change for key-chunk launches.
 constexpr int kOptLateLoad = 16;
 
 // A wave-uniform int32 read through the scalar data cache (s_load): it does
@@ -773,7 +774,9 @@ template <bool CAUSAL> struct DmaTile<128, CAUSAL> {
 template <bool CAUSAL> struct DmaTile<256, CAUSAL> {
   static constexpr int BC = 64, NW = 4, WPE = 1, NS = 2, OPT = kOptPin | kOptLateLoad;
 };
-struct VarlenCausalTile128 { static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio; };
+struct VarlenCausalTile128 {
+  static constexpr int BC = 64, NW = 4, WPE = 2, NS = 2, OPT = kOptPin | kOptPrio | kOptLateLoad;
+};
 
 // Key-chunk launches at d = 128 (decoding and long keys with few queries):
 // 4-wave workgroups with a 64 KiB ring, so two run on each CU.
