@@ -254,7 +254,11 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, const SeqView sv, 
     if (it + NS - 2 < n_steps) bwd_wait_vm<(NS - 2) * LPT>();
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (it + NS - 1 < n_steps) load_stage(qb + NS - 1, slot == 0 ? NS - 1 : slot - 1);
+    // non-causal: the stage loads go out after the S and dP chain, which then
+    // starts at once after the barrier (+2 % at d = 128, +4 % at d = 256;
+    // causal launches lose as much and issue them first)
+    const bool refill = it + NS - 1 < n_steps;
+    if (CAUSAL && refill) load_stage(qb + NS - 1, slot == 0 ? NS - 1 : slot - 1);
     {
       const uint8_t* tq = lds + slot * STAGE;
       const uint8_t* tdo = tq + TILEB;
@@ -266,6 +270,7 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, const SeqView sv, 
         s = mfma32(TT{}, T::rows_frag(tq, c, ks, hh), kf[ks], s);
         dp = mfma32(TT{}, T::rows_frag(tdo, c, ks, hh), T::rows_frag(ldsV, 32 * wv + c, ks, hh), dp);
       }
+      if (!CAUSAL && refill) load_stage(qb + NS - 1, slot == 0 ? NS - 1 : slot - 1);
       const bool masked = (CAUSAL && qb * 32 < kw0 + 31) || qb * 32 + 32 > q_len;
       // element (g, j) is query q = qb*32 + 4 hh + 8 g + j: it exists iff
       // 8 g + j < q_lim and sees this lane's key iff 8 g + j >= key_rel
@@ -408,7 +413,10 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, const SeqView sv, co
     if (kt + NS - 2 < n_kt) bwd_wait_vm<(NS - 2) * LPT>();
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + NS - 1 < n_kt) load_stage(kt + NS - 1, slot == 0 ? NS - 1 : slot - 1);
+    // non-causal: a live wave issues the stage loads after its S and dP
+    // chain (as in the dK/dV kernel)
+    const bool refill = kt + NS - 1 < n_kt;
+    if ((CAUSAL || kt >= wave_kt) && refill) load_stage(kt + NS - 1, slot == 0 ? NS - 1 : slot - 1);
     if (kt < wave_kt) {
       const uint8_t* tk = lds + slot * STAGE;
       const uint8_t* tv = tk + TILEB;
@@ -424,6 +432,7 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, const SeqView sv, co
           dp[mb] = mfma32(TT{}, T::rows_frag(tv, mb * 32 + c, ks, hh), df[ks], dp[mb]);
         }
       }
+      if (!CAUSAL && refill) load_stage(kt + NS - 1, slot == 0 ? NS - 1 : slot - 1);
       const bool masked = (CAUSAL && kt * BC + BC - 1 > qw0) || kt * BC + BC > k_len;
       // element (mb, i) is key kt*BC + 4 hh + e with e = 32 mb + 8 (i/4) + i%4:
       // it exists iff e < k_lim and is visible to this lane's query iff e <= q_rel
