@@ -221,3 +221,84 @@ def test_query_tile_pair_paths(gpu_lib):
         rows = np.unique(np.concatenate([sample_rows(n, 24, seed=h), [mid, mid + 255]]))
         o_ref, l_ref = OX.attention_rows(q64[0, h], k64[0, h], v64[0, h], rows, s, False)
         check(o[0, h][rows], lse[0, h][rows], o_ref, l_ref, "bf16", f"non-causal paired, head {h}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_offsets_beyond_2_31_elements(gpu_lib, causal):
+    """Q and O of more than 2^31 elements (B1 H3, Nq = 2^23 + 37, d = 128:
+    head 2 starts at element 2^31 + 9472, byte 2^32 + 18944) against 64 keys,
+    so the 64-bit row offsets of the loads and of the O and lse stores are
+    exercised at a cost of a few milliseconds.  Q row g (g = head * Nq + i)
+    is row (g * 2654435761 + 12345) mod 4096 of a seeded N(0,1) bank,
+    gathered on the device; the host recomputes the index for sampled rows.
+    Rows >= 63 see all 64 keys, causal or not."""
+    H, nq, nk, d, R = 3, 2 ** 23 + 37, 64, 128, 4096
+    bank32, _, _ = W.random_problem(1, 1, R, 1, d, seed=91)
+    _, k32, v32 = W.random_problem(1, H, 1, nk, d, seed=92)
+    bank_d, bank64 = to_device(bank32[0, 0], "bf16")
+    kd, k64 = to_device(k32, "bf16")
+    vd, v64 = to_device(v32, "bf16")
+
+    def bank_index(g):
+        return (g * 2654435761 + 12345) % R
+
+    g = torch.arange(H * nq, dtype=torch.int64, device="cuda")
+    qd = bank_d.index_select(0, bank_index(g)).view(1, H, nq, d)
+    del g
+    scale = 1.0 / np.sqrt(d)
+    o, lse = gpu_lib.forward(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert (int(qd.numel()) > 2 ** 31) and qd.stride(1) * 2 > 2 ** 31
+    for h in range(H):
+        rows = np.unique(np.concatenate([sample_rows(nq, 24, seed=h), np.arange(0, 64, 9), [nq - 1]]))
+        ri = torch.from_numpy(rows).cuda()
+        o_h = o[0, h].index_select(0, ri).double().cpu().numpy()
+        l_h = lse[0, h].index_select(0, ri).double().cpu().numpy()
+        q_rows = bank64[bank_index(np.int64(h) * nq + rows.astype(np.int64))]
+        far = rows >= nk - 1
+        o_ref = np.empty_like(o_h)
+        l_ref = np.empty_like(l_h)
+        o_ref[far], l_ref[far] = OX.attention_rows(q_rows[far], k64[0, h], v64[0, h], np.arange(far.sum()),
+                                                   scale, False)
+        if np.any(~far):
+            q_head = bank64[bank_index(np.int64(h) * nq + np.arange(nk, dtype=np.int64))]
+            o_ref[~far], l_ref[~far] = OX.attention_rows(q_head, k64[0, h], v64[0, h], rows[~far], scale, causal)
+        check(o_h, l_h, o_ref, l_ref, "bf16", f"offsets beyond 2^31, head {h}, causal {causal}")
+    del qd, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_key_offsets_beyond_2_31_elements(gpu_lib):
+    """K and V of more than 2^31 elements (B1 H3, Nk = 4099 * 2047 = 8390653,
+    d = 128: head 2 starts past element 2^31 and byte 2^32; the last key tile
+    holds 125 keys) for 77 queries, one pass and in 8 key chunks.  Key j of
+    head h is row j mod 4099 of that head's seeded N(0,1) bank (K and V
+    alike), so every (key, value) pair of the bank appears exactly m = 2047
+    times.  Repeating each pair m times leaves the softmax average O
+    unchanged and adds ln m to the logsumexp, so the oracle runs on the bank
+    alone.  4099 is prime: an offset cut at 2^32 bytes (2^24 rows) lands on
+    other rows, and the banks differ per head."""
+    H, nq, d, R, m = 3, 77, 128, 4099, 2047
+    nk = R * m
+    q32, kb32, vb32 = W.random_problem(1, H, nq, R, d, seed=93)
+    qd, q64 = to_device(q32, "bf16")
+    kb_d, kb64 = to_device(kb32, "bf16")
+    vb_d, vb64 = to_device(vb32, "bf16")
+    idx = torch.arange(nk, dtype=torch.int64, device="cuda") % R
+    kd = kb_d[0].index_select(1, idx).view(1, H, nk, d)
+    vd = vb_d[0].index_select(1, idx).view(1, H, nk, d)
+    del idx
+    assert kd.stride(1) * 2 > 2 ** 31
+    scale = 1.0 / np.sqrt(d)
+    runs = {"one pass": gpu_lib.forward(qd, kd, vd, causal=False, scale=scale),
+            "8 key chunks": gpu_lib.forward_splitkv(qd, kd, vd, causal=False, scale=scale, num_splits=8)}
+    torch.cuda.synchronize()
+    for what, (o, lse) in runs.items():
+        o = o.double().cpu().numpy()
+        lse = lse.double().cpu().numpy()
+        for h in range(H):
+            rows = np.arange(nq)
+            o_ref, l_ref = OX.attention_rows(q64[0, h], kb64[0, h], vb64[0, h], rows, scale, False)
+            check(o[0, h], lse[0, h], o_ref, l_ref + np.log(m), "bf16", f"{what}, head {h}")
+    del qd, kd, vd, runs
+    torch.cuda.empty_cache()

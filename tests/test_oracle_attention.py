@@ -178,9 +178,24 @@ def check_rows_helper():
         np.testing.assert_allclose(lrow, lse[rows], atol=1e-13)
 
 
+def check_repeated_pairs():
+    """Every (key, value) pair repeated m times, in any order: the softmax
+    weights of the copies of one pair add up to that pair's weight, so O is
+    unchanged and every row sum is m times larger (lse + ln m).  The
+    full-size GPU test of key offsets beyond 2^31 elements relies on it."""
+    q, k, v = RNG.standard_normal((7, 5)), RNG.standard_normal((11, 5)), RNG.standard_normal((11, 3))
+    m = 4
+    perm = RNG.permutation(11 * m)
+    kr, vr = np.tile(k, (m, 1))[perm], np.tile(v, (m, 1))[perm]
+    o, lse = oracle.attention(q, k, v, 0.6)
+    o_r, lse_r = oracle.attention(q, kr, vr, 0.6)
+    np.testing.assert_allclose(o_r, o, atol=1e-13)
+    np.testing.assert_allclose(lse_r, lse + math.log(m), atol=1e-13)
+
+
 PINS = [check_brute_force, check_torch_sdpa, check_rows_sum_to_one, check_shift_invariance,
         check_identical_keys, check_masked_prefix, check_closed_forms, check_varlen_is_concatenation,
-        check_rows_helper]
+        check_rows_helper, check_repeated_pairs]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
