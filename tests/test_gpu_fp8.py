@@ -366,3 +366,53 @@ def test_fp8_causal_pairs_odd_heads(gpu_lib):
     ref = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.0884, True, ambiguity=3e-5, parts=True)
     allow = ref["flip"] + _pv_bound(ref)
     _check(o, lse, ref["o"], ref["lse"], "fp8 causal, 3 heads", allow=allow)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_offsets_beyond_2_31(gpu_lib, causal):
+    """e4m3 Q of more than 2^31 codes (B1 H3, Nq = 2^23 + 37, d = 128: head
+    2 starts at byte 2^31 + 9472) and bf16 O of more than 2^32 bytes, against
+    64 keys.  Q row g (g = head * Nq + i) is row (g * 2654435761 + 12345)
+    mod 4096 of a seeded bank of exact codes, gathered on the device; the Q
+    tile scales are drawn per tile.  The oracle sees each sampled row as row
+    0 of a 128-row tile of its own with that row's tile scale (rows >= 63
+    see all 64 keys; causal rows below that are checked within tile 0)."""
+    H, nq, nk, d, R = 3, 2 ** 23 + 37, 64, 128, 4096
+    nt = (nq + 127) // 128
+    bank = W.random_codes_from(EXACT_CODES, (R, d), 95)
+    _, k8, v8, _, sk, sv = _exact_problem(1, H, 1, nk, seed=96)
+    sq = W.random_pow2_scales((1, H, nt), 97, -1, 0)
+
+    def bank_index(g):
+        return (g * 2654435761 + 12345) % R
+
+    g = torch.arange(H * nq, dtype=torch.int64, device="cuda")
+    qd = _dev(bank).index_select(0, bank_index(g)).view(1, H, nq, d)
+    del g
+    assert qd.stride(1) * 2 > 2 ** 31
+    scale = 0.0884
+    o, lse = gpu_lib.forward(qd, _dev(k8), _dev(v8), causal=causal, scale=scale,
+                             q_scale=_dev(sq), k_scale=_dev(sk), v_scale=_dev(sv))
+    torch.cuda.synchronize()
+    for h in range(H):
+        rows = np.unique(np.concatenate([sample_rows(nq, 24, seed=h), np.arange(0, 64, 9), [nq - 1]]))
+        ri = torch.from_numpy(rows).cuda()
+        o_h = o[0, h].index_select(0, ri).double().cpu().numpy()
+        l_h = lse[0, h].index_select(0, ri).double().cpu().numpy()
+        far = rows >= nk - 1
+        rf = rows[far]
+        q_pad = np.zeros((len(rf) * 128, d), dtype=np.uint8)
+        q_pad[::128] = bank[bank_index(np.int64(h) * nq + rf.astype(np.int64))]
+        ref = F.attention_fp8(q_pad, k8[0, h], v8[0, h], sq[0, h][rf // 128], sk[0, h], sv[0, h], scale, False,
+                              rows=np.arange(len(rf)) * 128, ambiguity=3e-5, parts=True)
+        _check(o_h[far], l_h[far], ref["o"], ref["lse"], f"fp8 offsets, head {h}, causal {causal}",
+               allow=ref["flip"] + _pv_bound(ref))
+        near = rows[~far]
+        if near.size:
+            q_t0 = bank[bank_index(np.int64(h) * nq + np.arange(128, dtype=np.int64))]
+            ref = F.attention_fp8(q_t0, k8[0, h], v8[0, h], sq[0, h][:1], sk[0, h], sv[0, h], scale, causal,
+                                  rows=near, ambiguity=3e-5, parts=True)
+            _check(o_h[~far], l_h[~far], ref["o"], ref["lse"], f"fp8 offsets tile 0, head {h}, causal {causal}",
+                   allow=ref["flip"] + _pv_bound(ref))
+    del qd, o, lse
+    torch.cuda.empty_cache()
