@@ -4,7 +4,7 @@
 // techniques" §3: block quantisation; incoherent processing Q' = QM, K' = KM
 // with M a Hadamard matrix times random +-1, applied before quantising).
 //
-// One workgroup (256 threads) per (b*h, 128-row tile); the whole tile stays
+// One workgroup (4 d threads) per (b*h, 128-row tile); the whole tile stays
 // in registers, so x is read once and the codes are written once.  A row of d
 // values is spread over d/8 lanes, 8 consecutive values per lane.  The
 // Hadamard transform H_d (Sylvester order) is a product of one butterfly
@@ -26,7 +26,12 @@
 namespace attn {
 namespace {
 
-constexpr int kPrepThreads = 256;
+constexpr int kPrepThreads = 256;  // the tensor-scale pass
+// Quantisation workgroups: 4 d threads, so each thread holds four row pieces
+// of 8 values (measured fastest for d = 64, 128 and 256; fewer, larger
+// pieces per thread left the last round of workgroups half empty).
+template <int D>
+constexpr int kTileThreads = 4 * D;
 constexpr int kTileRows = 128;
 constexpr float kE4m3Max = 448.0f;
 
@@ -94,6 +99,8 @@ __device__ __forceinline__ void lane_stage(float (&v)[8], int cl) {
   }
 }
 
+// Maximum over a workgroup of NT threads (red: NT / 64 floats of LDS).
+template <int NT>
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
@@ -102,18 +109,19 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   __syncthreads();
   float m = red[0];
 #pragma unroll
-  for (int i = 1; i < kPrepThreads / 64; ++i) m = fmaxf(m, red[i]);
+  for (int i = 1; i < NT / 64; ++i) m = fmaxf(m, red[i]);
   return m;
 }
 
 // MODE 0: block scales; 1: write the tile amax only; 2: quantise with the
 // scale already stored for the tile (per-tensor).
 template <int IN, int D, int MODE>
-__global__ void __launch_bounds__(kPrepThreads) fp8_prep_kernel(PrepParams p) {
+__global__ void __launch_bounds__(kTileThreads<D>) fp8_prep_kernel(PrepParams p) {
+  constexpr int NT = kTileThreads<D>;
   constexpr int L = D / 8;                // lanes per row
-  constexpr int RPP = kPrepThreads / L;   // rows per pass
+  constexpr int RPP = NT / L;             // rows per pass
   constexpr int PASSES = kTileRows / RPP;
-  __shared__ float red[kPrepThreads / 64];
+  __shared__ float red[NT / 64];
 
   const int nt = (p.N + kTileRows - 1) / kTileRows + (p.cu ? p.nseq : 0);  // scale entries per head
   const int bh = blockIdx.x / nt;
@@ -199,7 +207,7 @@ __global__ void __launch_bounds__(kPrepThreads) fp8_prep_kernel(PrepParams p) {
   if constexpr (MODE == 2) {
     s = p.scale[sidx];
   } else {
-    const float tmax = block_max(amax, red);
+    const float tmax = block_max<NT>(amax, red);
     if constexpr (MODE == 1) {
       if (tid == 0) p.scale[sidx] = tmax;
       return;
@@ -241,7 +249,7 @@ __global__ void __launch_bounds__(kPrepThreads) tensor_scale_kernel(float* scale
   __shared__ float red[kPrepThreads / 64];
   float m = 0.f;
   for (int i = threadIdx.x; i < n; i += kPrepThreads) m = fmaxf(m, scale[i]);
-  m = block_max(m, red);
+  m = block_max<kPrepThreads>(m, red);
   const float s = m > 0.f ? m / kE4m3Max : 1.0f;
   for (int i = threadIdx.x; i < n; i += kPrepThreads) scale[i] = s;
 }
@@ -252,16 +260,16 @@ hipError_t launch_in_d(const PrepParams& p, bool per_tensor, hipStream_t st) {
   const int64_t grid = (int64_t)nt * p.BH;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (!per_tensor) {
-    hipLaunchKernelGGL((fp8_prep_kernel<IN, D, 0>), dim3((unsigned)grid), dim3(kPrepThreads), 0, st, p);
+    hipLaunchKernelGGL((fp8_prep_kernel<IN, D, 0>), dim3((unsigned)grid), dim3(kTileThreads<D>), 0, st, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((fp8_prep_kernel<IN, D, 1>), dim3((unsigned)grid), dim3(kPrepThreads), 0, st, p);
+  hipLaunchKernelGGL((fp8_prep_kernel<IN, D, 1>), dim3((unsigned)grid), dim3(kTileThreads<D>), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(kPrepThreads), 0, st, p.scale, (int)grid);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fp8_prep_kernel<IN, D, 2>), dim3((unsigned)grid), dim3(kPrepThreads), 0, st, p);
+  hipLaunchKernelGGL((fp8_prep_kernel<IN, D, 2>), dim3((unsigned)grid), dim3(kTileThreads<D>), 0, st, p);
   return hipGetLastError();
 }
 
