@@ -223,3 +223,39 @@ def test_backward_varlen_vs_oracle(gpu_lib, H, lq, lk, d, dtype, causal):
             continue
         ref, bnd = bounds(q[:, sq], k[:, sk], v[:, sk], do[:, sq], o[:, sq], lse[:, sq], scale, causal, dtype)
         check_grads((dq[:, sq], dk[:, sk], dv[:, sk]), ref, bnd, f"{what} seq {s}")
+
+
+def test_backward_key_offsets_beyond_2_31(gpu_lib):
+    """K, V, dK and dV of more than 2^31 elements (B1 H3, 77 queries, Nk =
+    4099 * 2047, d = 128: head 2 starts past element 2^31).  Key j of head h
+    is row j mod 4099 of that head's seeded bank (K and V alike), so each
+    (key, value) pair appears m = 2047 times.  Each copy then takes 1/m of
+    the pair's softmax weight: dQ equals dQ of the bank problem, and dK and
+    dV of every copy are the bank problem's dK and dV over m (the forward's
+    lse is ln m above the bank's).  dQ is checked on every row, dK and dV on
+    sampled copies, with the bounds above scaled the same way."""
+    H, nq, d, R, m = 3, 77, 128, 4099, 2047
+    nk = R * m
+    (qd, q), (kbd, kb), (vbd, vb), (dod, do) = _inputs(1, H, nq, R, d, "bf16", seed=99)
+    idx = torch.arange(nk, dtype=torch.int64, device="cuda") % R
+    kd = kbd[0].index_select(1, idx).view(1, H, nk, d)
+    vd = vbd[0].index_select(1, idx).view(1, H, nk, d)
+    del idx
+    assert kd.stride(1) * 2 > 2 ** 31
+    scale = 1.0 / np.sqrt(d)
+    o, lse = gpu_lib.forward(qd, kd, vd, scale=scale)
+    dq, dk, dv = gpu_lib.backward(qd, kd, vd, o, lse, dod, scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    js = np.unique(np.concatenate([[0, 1, R - 1, R, nk // 2, nk - 2, nk - 1], rng.integers(0, nk, 40)]))
+    jt = torch.from_numpy(js).cuda()
+    f = lambda t: t.double().cpu().numpy()  # noqa: E731
+    dk_s = f(dk.view(H, nk, d).index_select(1, jt))[None]
+    dv_s = f(dv.view(H, nk, d).index_select(1, jt))[None]
+    o_n, lse_n, dq_n = f(o), f(lse), f(dq)
+    del kd, vd, dk, dv
+    torch.cuda.empty_cache()
+    (rq, rk, rv), (bq, bk, bv) = bounds(q, kb, vb, do, o_n, lse_n - np.log(m), scale, False, "bf16")
+    r = js % R
+    check_grads((dq_n, dk_s, dv_s), (rq, rk[:, :, r] / m, rv[:, :, r] / m), (bq, bk[:, :, r] / m, bv[:, :, r] / m),
+                "bwd offsets beyond 2^31")

@@ -111,7 +111,24 @@ def pin_no_keys(grad):
     assert dk.shape == k.shape and dv.shape == v.shape
 
 
-PINS = [pin_finite_differences, pin_two_keys_closed_form, pin_one_key, pin_symmetries, pin_masking, pin_no_keys]
+def pin_repeated_pairs(grad):
+    """Every (key, value) pair repeated m times, in any order: each copy takes
+    1/m of the pair's softmax weight, so dQ is unchanged and each copy's dK
+    and dV are the pair's over m.  The GPU test of key offsets beyond 2^31
+    elements relies on it."""
+    q, k, v, do = _problem((2,), 6, 5, 4, seed=11)
+    m = 3
+    perm = np.random.default_rng(2).permutation(5 * m)
+    src = np.tile(np.arange(5), m)[perm]  # pair of each repeated key
+    dq, dk, dv = grad(q, k, v, do, 0.8, False)
+    dq_r, dk_r, dv_r = grad(q, k[:, src], v[:, src], do, 0.8, False)
+    np.testing.assert_allclose(dq_r, dq, atol=1e-13)
+    np.testing.assert_allclose(dk_r, dk[:, src] / m, atol=1e-13)
+    np.testing.assert_allclose(dv_r, dv[:, src] / m, atol=1e-13)
+
+
+PINS = [pin_finite_differences, pin_two_keys_closed_form, pin_one_key, pin_symmetries, pin_masking, pin_no_keys,
+        pin_repeated_pairs]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
