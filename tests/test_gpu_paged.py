@@ -157,3 +157,59 @@ def test_paged_8bit_equals_16bit_cache(gpu_lib):
     o2, l2 = gpu_lib.forward_paged(q, kb, vb, td, ld, num_splits=2)
     torch.cuda.synchronize()
     assert torch.equal(l1, l2) and torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "e4m3"])
+def test_paged_offsets_beyond_2_31(gpu_lib, kind):
+    """A cache of more than 2^31 elements (40000 pages of 256 tokens, H2,
+    d128: page p starts at element 65536 p, past 2^31 from page 32768) read
+    through a table of 1025 pages drawn across the whole cache.  The
+    sequence has 4099 * 64 keys (the last page holds 192); key g of head h
+    is row g mod 4099 of that head's seeded bank (bf16 values, or e4m3 codes
+    with per-(token, head) scales), so each (key, value) pair appears m = 64
+    times: O equals attention over the bank alone and lse is ln m above its
+    lse."""
+    import workloads as W
+    from oracle import exact as OX
+
+    H, nq, d, P, n_pages, R, m = 2, 3, 128, 256, 40000, 4099, 64
+    L = R * m
+    n_used = -(-L // P)
+    rng = np.random.default_rng(17)
+    phys = rng.choice(n_pages, n_used, replace=False).astype(np.int64)
+    assert phys.max() * P * H * d > 2 ** 31
+    qd, q = to_device(rng.standard_normal((1, H, nq, d), dtype=np.float32), "bf16")
+    gi = torch.arange(n_used * P, dtype=torch.int64, device="cuda") % R
+    pt = torch.from_numpy(phys).cuda()
+
+    def paged(bank_d, dtype):  # [H, R, ...] bank -> [n_pages, P, H, ...] cache with the sequence's pages at phys
+        c = torch.zeros((n_pages, P, H) + tuple(bank_d.shape[2:]), dtype=dtype, device="cuda")
+        src = bank_d.index_select(1, gi).view((H, n_used, P) + tuple(bank_d.shape[2:]))
+        c[pt] = src.permute((1, 2, 0) + tuple(range(3, src.dim()))).contiguous()
+        return c
+
+    table = torch.from_numpy(phys.astype(np.int32)[None]).cuda()
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    scale = 1.0 / np.sqrt(d)
+    if kind == "bf16":
+        kb_d, kb = to_device(rng.standard_normal((H, R, d), dtype=np.float32), "bf16")
+        vb_d, vb = to_device(rng.standard_normal((H, R, d), dtype=np.float32), "bf16")
+        kc, vc = paged(kb_d, torch.bfloat16), paged(vb_d, torch.bfloat16)
+        o, lse = gpu_lib.forward_paged(qd, kc, vc, table, lens, scale=scale)
+    else:
+        kcodes, vcodes = W.random_e4m3_codes((H, R, d), 21), W.random_e4m3_codes((H, R, d), 22)
+        ks, vs = W.random_scales((H, R), 23, 0.02, 0.05), W.random_scales((H, R), 24, 0.02, 0.05)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+        kc, vc = paged(t(kcodes), torch.uint8), paged(t(vcodes), torch.uint8)
+        ksc, vsc = paged(t(ks), torch.float32), paged(t(vs), torch.float32)
+        o, lse = gpu_lib.forward_paged(qd, kc, vc, table, lens, scale=scale, k_scale=ksc, v_scale=vsc,
+                                       kv_dtype="e4m3")
+        kb, vb = PG.dequantize(kcodes, ks, "e4m3"), PG.dequantize(vcodes, vs, "e4m3")
+        del ksc, vsc
+    torch.cuda.synchronize()
+    o_n, lse_n = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    del kc, vc, o, lse
+    torch.cuda.empty_cache()
+    for h in range(H):
+        o_ref, l_ref = OX.attention_rows(q[0, h], kb[h], vb[h], np.arange(nq), scale, False)
+        check(o_n[0, h], lse_n[0, h], o_ref, l_ref + np.log(m), "bf16", f"paged {kind} offsets beyond 2^31, head {h}")
