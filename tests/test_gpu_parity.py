@@ -302,3 +302,82 @@ def test_key_offsets_beyond_2_31_elements(gpu_lib):
             check(o[0, h], lse[0, h], o_ref, l_ref + np.log(m), "bf16", f"{what}, head {h}")
     del qd, kd, vd, runs
     torch.cuda.empty_cache()
+
+
+def test_varlen_offsets_beyond_2_31_elements(gpu_lib):
+    """Packed batches whose rows of head 2 start past element 2^31, H3 d128.
+
+    Non-causal, long keys: 2 sequences of 70 and 57 queries over 4099 * 1024
+    and 4099 * 1023 keys; key g of sequence b is row g mod 4099 of that
+    (head, sequence)'s bank, so O is attention over the bank and lse is ln m
+    above it.  Causal, long queries: 2^22 + 37 and 2^22 + 11 queries over 64
+    keys each (Q row g of the pack is row (g * 2654435761 + 12345) mod 4096 of
+    a seeded bank); rows >= 63 of a sequence see all of its keys, rows below
+    that are checked against the first 64 rows."""
+    H, d, R = 3, 128, 4099
+    scale = 1.0 / np.sqrt(d)
+    # -- non-causal, long keys
+    lq, ms = [70, 57], [1024, 1023]
+    lk = [R * m for m in ms]
+    tk = sum(lk)
+    assert 2 * tk * d > 2 ** 31
+    q32, _, _ = W.random_problem(1, H, sum(lq), 1, d, seed=31)
+    qd, q64 = to_device(q32[0], "bf16")
+    banks = [to_device(W.random_problem(1, H, 1, R, d, seed=32 + b)[1][0], "bf16") for b in range(4)]
+    (kb0, k64_0), (kb1, k64_1), (vb0, v64_0), (vb1, v64_1) = banks
+    kd = torch.cat([kb0.index_select(1, torch.arange(lk[0], device="cuda") % R),
+                    kb1.index_select(1, torch.arange(lk[1], device="cuda") % R)], dim=1).contiguous()
+    vd = torch.cat([vb0.index_select(1, torch.arange(lk[0], device="cuda") % R),
+                    vb1.index_select(1, torch.arange(lk[1], device="cuda") % R)], dim=1).contiguous()
+    cq = torch.tensor([0, lq[0], lq[0] + lq[1]], dtype=torch.int32, device="cuda")
+    ck = torch.tensor([0, lk[0], tk], dtype=torch.int32, device="cuda")
+    o, lse = gpu_lib.forward(qd, kd, vd, causal=False, scale=scale, cu_seqlens_q=cq, cu_seqlens_k=ck)
+    torch.cuda.synchronize()
+    o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    del kd, vd
+    torch.cuda.empty_cache()
+    for h in range(H):
+        for b, (kb64, vb64) in enumerate([(k64_0, v64_0), (k64_1, v64_1)]):
+            a = 0 if b == 0 else lq[0]
+            rows = np.arange(lq[b])
+            o_ref, l_ref = OX.attention_rows(q64[h, a:a + lq[b]], kb64[h], vb64[h], rows, scale, False)
+            check(o[h, a:a + lq[b]], lse[h, a:a + lq[b]], o_ref, l_ref + np.log(ms[b]), "bf16",
+                  f"varlen long keys, head {h}, seq {b}")
+    # -- causal, long queries
+    lq2, nk = [2 ** 22 + 37, 2 ** 22 + 11], 64
+    tq = sum(lq2)
+    assert 2 * tq * d > 2 ** 31
+    bank32, _, _ = W.random_problem(1, 1, 4096, 1, d, seed=41)
+    _, k32, v32 = W.random_problem(1, H, 1, 2 * nk, d, seed=42)
+    bank_d, bank64 = to_device(bank32[0, 0], "bf16")
+    kd, k64 = to_device(k32[0], "bf16")
+    vd, v64 = to_device(v32[0], "bf16")
+
+    def bank_index(g):
+        return (g * 2654435761 + 12345) % 4096
+
+    g = torch.arange(H * tq, dtype=torch.int64, device="cuda")
+    qd = bank_d.index_select(0, bank_index(g)).view(H, tq, d)
+    del g
+    cq = torch.tensor([0, lq2[0], tq], dtype=torch.int32, device="cuda")
+    ck = torch.tensor([0, nk, 2 * nk], dtype=torch.int32, device="cuda")
+    o, lse = gpu_lib.forward(qd, kd, vd, causal=True, scale=scale, cu_seqlens_q=cq, cu_seqlens_k=ck)
+    torch.cuda.synchronize()
+    for h in range(H):
+        for b in range(2):
+            a = 0 if b == 0 else lq2[0]
+            rows = np.unique(np.concatenate([sample_rows(lq2[b], 16, seed=h + 3 * b), np.arange(0, 64, 9)]))
+            ri = torch.from_numpy(a + rows).cuda()
+            o_h = o[h].index_select(0, ri).double().cpu().numpy()
+            l_h = lse[h].index_select(0, ri).double().cpu().numpy()
+            ks, vs = k64[h, b * nk:(b + 1) * nk], v64[h, b * nk:(b + 1) * nk]
+            far = rows >= nk - 1
+            o_ref, l_ref = np.empty_like(o_h), np.empty_like(l_h)
+            qf = bank64[bank_index(np.int64(h) * tq + a + rows[far].astype(np.int64))]
+            o_ref[far], l_ref[far] = OX.attention_rows(qf, ks, vs, np.arange(far.sum()), scale, False)
+            if np.any(~far):
+                q0 = bank64[bank_index(np.int64(h) * tq + a + np.arange(nk, dtype=np.int64))]
+                o_ref[~far], l_ref[~far] = OX.attention_rows(q0, ks, vs, rows[~far], scale, True)
+            check(o_h, l_h, o_ref, l_ref, "bf16", f"varlen long queries causal, head {h}, seq {b}")
+    del qd, o, lse
+    torch.cuda.empty_cache()
