@@ -27,11 +27,12 @@
 //   pieces read by lanes 4j + i / 4, so 4 lanes reading 4 consecutive rows
 //   give every lane 4 consecutive keys of one column.
 // * Softmax in base 2 with an integer reference maximum.  For each row the
-//   kernel keeps M = ceil(max of the scores seen so far, times scale log2 e),
-//   p = 2^(S scale log2 e - M) <= 1, l = sum p (fp32, unrounded) and
-//   O = sum p v.  M only moves when a tile raises the row max past the
-//   current integer; then O and l are multiplied by 2^(M_old - M_new), an
-//   exact power of two, and only if some row of the wave moved.  O / l and
+//   kernel keeps Mx = ceil(max of the scores seen so far, times scale log2 e),
+//   a reference M <= Mx, p = 2^(S scale log2 e - M) <= 2^(Mx - M),
+//   l = sum p (fp32, unrounded) and O = sum p v.  M only moves when some row
+//   of the wave would exceed its reference by more than kLazyBits; then
+//   every row's M becomes its Mx and O and l are multiplied by
+//   2^(M_old - M_new), an exact power of two.  O / l and
 //   lse = (M + log2 l) ln 2 equal the page's recurrence (which rescales by
 //   e^{m_old - m_new} at every tile) up to rounding: the reference point of
 //   the exponentials does not change the sum they define.
@@ -65,6 +66,11 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr float kSplitBelowP = 8.0f;
+// Slack of the reference max M: a row's scores may exceed M by up to
+// kLazyBits (p = 2^(t - M) <= 2^kLazyBits) before the wave rescales O and l.
+// O and lse do not depend on M (up to rounding); on N(0,1) scores this takes
+// a wave's rescales from about every second key tile to almost none.
+constexpr float kLazyBits = 4.0f;
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maximum).
 template <int N>
@@ -408,9 +414,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
   };
 
   const float cs = p.c;
-  float M[NQB], l[NQB];
+  float M[NQB], l[NQB], Mx[NQB];  // reference max, row sum (relative to M), running integer max
 #pragma unroll
-  for (int nb = 0; nb < NQB; ++nb) { M[nb] = -INFINITY; l[nb] = 0.f; }
+  for (int nb = 0; nb < NQB; ++nb) { M[nb] = -INFINITY; l[nb] = 0.f; Mx[nb] = -INFINITY; }
   f32x16_t oacc[NQB][C::DB];
 #pragma unroll
   for (int nb = 0; nb < NQB; ++nb)
@@ -469,16 +475,19 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
     float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
     if (!masked) tmax *= cs;
     tmax = max_halves(tmax);
-    const float m_new = fmaxf(M[0], __builtin_ceilf(tmax));
-    if (__any(m_new > M[0])) {
+    const float m_cand = __builtin_ceilf(tmax);
+    Mx[0] = fmaxf(Mx[0], m_cand);
+    if (__any(m_cand > M[0] + kLazyBits)) {
+      // every row of the wave moves its reference to its running max
+      const float m_new = Mx[0];
       const float alpha = (m_new == M[0]) ? 1.f : __builtin_amdgcn_exp2f(M[0] - m_new);
       l[0] *= alpha;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[0][db][i] *= alpha;
+      M[0] = m_new;
     }
-    M[0] = m_new;
     m_use[0] = (M[0] == -INFINITY) ? 0.f : M[0];
   };
 
@@ -575,7 +584,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
     uint4 pf[NQB][C::MB][2];
     prepare(kt, s, m_use, masked);
     exps(slot, s, m_use, masked, pf);
-    const bool split = __any(l[0] < kSplitBelowP);
+    // l against the largest p the row can hold, 2^(Mx - M): the weight sits
+    // on fewer than kSplitBelowP keys' worth
+    const bool split = __any(l[0] < kSplitBelowP * (Mx[0] == M[0] ? 1.f : __builtin_amdgcn_exp2f(Mx[0] - M[0])));
     // the residual is formed before the first product, so the fp32 P dies
     // there and only the two packed copies stay live through the MFMAs
     uint4 pl[NQB][C::MB][2];
