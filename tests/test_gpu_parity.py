@@ -381,3 +381,45 @@ def test_varlen_offsets_beyond_2_31_elements(gpu_lib):
             check(o_h, l_h, o_ref, l_ref, "bf16", f"varlen long queries causal, head {h}, seq {b}")
     del qd, o, lse
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", ["rising", "falling", "spiky"])
+def test_drifting_row_max(gpu_lib, dtype, causal, shape):
+    """Score rows whose maximum drifts across key tiles.  Channel 0 of every
+    query is 1 and channel 0 of key j is a ramp, so each row's scores climb
+    (or fall) by about 0.03 in base 2 per key: several bits per key tile, with
+    a jump of 20 at key 700 on the rising ramp.  The running max then moves on
+    most tiles, the reference of the exponentials lags it, and P can exceed
+    1 (up to the kernel's slack) before a rescale; the other channels are
+    small N(0,1) noise.  "spiky": one key per 128 keys (index 37 mod 128)
+    stands 3 more bits above the previous one and the rest 40 below, so
+    the weight of a row sits on about one key while the reference lags the
+    row max by up to 3 bits.  V is uniform in (-3.9, 3.9), so many |O| lie
+    in [2, 4): there the output rounding alone takes up to half an ulp of
+    the bar, and P rounded to 16 bits would add up to 2^-9 |V| in bf16 unless
+    the kernel takes its residual pass.
+    d = 64 and 128, Nk = 1000 (a ragged last tile)."""
+    for d in (64, 128):
+        rng = np.random.default_rng(5 + d)
+        nq, nk = 300, 1000
+        q = 0.1 * rng.standard_normal((1, 2, nq, d)).astype(np.float32)
+        k = 0.1 * rng.standard_normal((1, 2, nk, d)).astype(np.float32)
+        v = rng.standard_normal((1, 2, nk, d)).astype(np.float32)
+        q[..., 0] = 1.0
+        step = 0.03 / (np.log2(np.e) / np.sqrt(d))  # base-2 increase per key
+        ramp = step * np.arange(nk, dtype=np.float64)
+        if shape == "rising":
+            ramp[700:] += 20.0 / (np.log2(np.e) / np.sqrt(d))
+        elif shape == "falling":
+            ramp = ramp[::-1].copy()
+        else:
+            j = np.arange(nk)
+            bits = np.where(j % 128 == 37, 3.0 * (j // 128), -40.0)
+            ramp = bits / (np.log2(np.e) / np.sqrt(d))
+            v[:] = rng.uniform(-3.9, 3.9, v.shape)
+        k[..., 0] = ramp.astype(np.float32)
+        o, lse, (q64, k64, v64, s) = run_dense(gpu_lib, q, k, v, dtype, causal)
+        o_ref, l_ref = oracle.attention(q64, k64, v64, s, causal)
+        check(o, lse, o_ref, l_ref, dtype, f"drifting max {shape} d{d} causal{causal}")
