@@ -25,7 +25,10 @@ design notes):
   head, applied along the head dimension; V is not rotated;
 * one fp32 scale per (tensor, batch, head, 128-row tile): s = amax / 448
   over the tile after rotation (amax = 0 gives s = 1), code = e4m3(x / s),
-  x ~= s * code.  Per-tensor mode uses one amax over the whole tensor;
+  x ~= s * code.  Per-tensor mode uses one amax over the whole tensor.  A
+  tile whose amax / 448 underflows fp32 (amax < 448 * 2^-149) takes the
+  smallest positive fp32, 2^-149, so that its codes stay finite (x / s is
+  then exact and below 448);
 * the quantisation decisions are taken in fp32, as the device does: the
   rotated values are rounded to fp32, s = fp32(amax / 448) and the code is
   the e4m3 rounding of fp32(x / s);
@@ -36,7 +39,11 @@ design notes):
   unrounded 2^(t - M); O = (max s_v) 2^-8 sum_j P8_j v8_j / l.  Because M is
   an integer, any running reference max M' <= M gives the same codes up to
   an exact power of two (outside the subnormal range), so a tiled kernel
-  can reach this result exactly.
+  can reach this result exactly.  A head whose V scales are all 0 has
+  w = 0 (O = 0).  The P scale 2^8 puts the largest weight of a row in the
+  tile of the largest V scale at code 2^8 = 256 exactly when the row max is
+  an integer, and weights down to 2^-17 (the smallest subnormal code 2^-9,
+  divided by 2^8) survive the rounding.
 """
 
 from __future__ import annotations
@@ -46,6 +53,7 @@ import numpy as np
 from .exact import _f64
 
 E4M3_MAX = 448.0
+F32_TINY = np.float32(2.0 ** -149)  # smallest positive fp32 (a subnormal)
 E4M3_MIN_NORMAL_EXP = -6  # smallest normal 2^-6
 E4M3_MANT_BITS = 3
 LOG2E = 1.4426950408889634  # log2(e)
@@ -184,13 +192,14 @@ def quantize(x, signs=None, per_tensor: bool = False, tile: int = 128):
     scales = np.ones(lead + (nt,), dtype=np.float32)
     if per_tensor:
         amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
-        s = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+        s = max(np.float32(amax / np.float32(E4M3_MAX)), F32_TINY) if amax > 0 else np.float32(1.0)
         scales[...] = s
     else:
         for t in range(nt):
             blk = np.abs(x32[..., t * tile:(t + 1) * tile, :])
             amax = blk.reshape(lead + (-1,)).max(axis=-1) if blk.size else np.zeros(lead, np.float32)
-            s = np.where(amax > 0, (amax / np.float32(E4M3_MAX)).astype(np.float32), np.float32(1.0))
+            s = np.where(amax > 0, np.maximum((amax / np.float32(E4M3_MAX)).astype(np.float32), F32_TINY),
+                         np.float32(1.0))
             scales[..., t] = s.astype(np.float32)
     row_scale = np.repeat(scales, tile, axis=-1)[..., :n]
     y32 = (x32 / row_scale[..., None]).astype(np.float32)
@@ -214,8 +223,8 @@ P_SCALE_LOG2 = 8  # P is rounded as e4m3(2^8 * p), p <= 1, so codes stay <= 256
 
 
 def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
-                  tile: int = 128, quantize_p: bool = True, rows=None, ambiguity: float = 0.0,
-                  parts: bool = False):
+                  tile: int = 128, quantize_p: bool = True, rows=None, ambiguity=0.0,
+                  parts: bool = False, p_mode: str = "folded"):
     """fp8 attention of one or more heads: codes [..., N, d], scales [..., nt].
 
     S = scale * (sq q8)(sk k8)^T, softmax statistics in float64, and P
@@ -229,11 +238,20 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     every P element lying within relative distance delta of a rounding
     midpoint could cause.  A computation whose pre-rounding values differ
     from these by less than delta (relative) can land anywhere within it.
+    delta may also be an array broadcastable to [..., Nq, Nk] (one relative
+    distance per P element).
+
+    ``p_mode`` selects the reading of the P rounding: "folded" (the module
+    docstring: the V tile's scale enters P before rounding) or "rowmax" (the
+    other plain reading: P8 = e4m3(2^8 * 2^(t - M)) for every key, and each
+    key tile's partial product is multiplied by its own V scale in full
+    precision, O = 2^-8 sum_tiles s_v(tile) sum_{j in tile} P8_j v8_j / l).
 
     ``parts=True`` returns a dict instead, with the intermediate values:
     "o", "lse", "flip" (if requested), "p8" (the rounded P, in code units,
-    [..., Nq, Nk]), "l" [..., Nq], "sv_max" [...] and "v_codes" (values of
-    the V codes).
+    [..., Nq, Nk]), "x" (P before rounding, in code units), "t" (the base-2
+    scores), "M" [..., Nq], "l" [..., Nq], "sv_max" [...] and "v_codes"
+    (values of the V codes).
     """
     qd = dequantize(q8, sq, tile)
     qrow = np.arange(qd.shape[-2])
@@ -253,17 +271,26 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     M = np.where(live, np.ceil(np.where(live, tmax, 0.0)), 0.0)
     p = np.where(live[..., None], np.exp2(t - M[..., None]), 0.0)  # <= 1
     l = p.sum(axis=-1)
+    if p_mode not in ("folded", "rowmax"):
+        raise ValueError("p_mode must be 'folded' or 'rowmax'")
     sv_max = sv.max(axis=-1) if sv.shape[-1] else np.ones(sv.shape[:-1])
-    w_tile = sv / sv_max[..., None]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        w_tile = np.where(sv_max[..., None] > 0, sv / np.where(sv_max > 0, sv_max, 1.0)[..., None], 0.0)
     w = np.repeat(w_tile, tile, axis=-1)[..., :nk]
-    pw = p * w[..., None, :]
+    # folded: the weight enters P before rounding; rowmax: after (full precision)
+    pw = p * w[..., None, :] if p_mode == "folded" else p
     if quantize_p:
         p8 = e4m3_round_f32((pw * 2.0 ** P_SCALE_LOG2).astype(np.float32))
     else:
         p8 = pw * 2.0 ** P_SCALE_LOG2
-    o_acc = np.matmul(p8, v_codes)
+    if p_mode == "folded":
+        o_acc = np.matmul(p8, v_codes)
+    else:
+        o_acc = np.matmul(p8 * w[..., None, :], v_codes)
     flip = None
-    if ambiguity > 0:
+    if np.any(np.asarray(ambiguity) > 0):
+        if p_mode != "folded":
+            raise ValueError("the ambiguity bound follows the folded reading")
         x = pw * 2.0 ** P_SCALE_LOG2
         with np.errstate(divide="ignore"):
             e = np.maximum(np.floor(np.log2(np.where(x > 0, x, 1.0))), E4M3_MIN_NORMAL_EXP)
@@ -282,7 +309,8 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
                             flip * (sv_max[..., None, None] * 2.0 ** -P_SCALE_LOG2) / np.where(live, l, 1.0)[..., None],
                             0.0)
     if parts:
-        return {"o": o, "lse": lse, "flip": flip, "p8": p8, "l": l, "sv_max": sv_max, "v_codes": v_codes}
+        return {"o": o, "lse": lse, "flip": flip, "p8": p8, "l": l, "sv_max": sv_max, "v_codes": v_codes,
+                "x": pw * 2.0 ** P_SCALE_LOG2, "t": t, "M": M}
     if flip is not None:
         return o, lse, flip
     return o, lse

@@ -393,3 +393,131 @@ def test_fp8_varlen_single_sequence_equals_dense():
     o, lse = F.attention_fp8_varlen(q8, k8, v8, pad(sq), pad(sk), pad(sv), cu, cu, 0.3, True)
     ref_o, ref_l = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, True)
     assert np.array_equal(o, ref_o) and np.array_equal(lse, ref_l)
+
+
+# ------------------------------------------------------------------ P-code scale and V scales
+
+def _two_key_row(t1: float):
+    """One query, two keys in one 128-key tile, scales 1: key 0 scores t = 0
+    (so M = 0 and its weight is 1), key 1 scores t1 (base 2).  V: key 0 is
+    the zero row, key 1 the all-ones row, so O = (code of key 1) 2^-8 / l in
+    every column."""
+    d = 16
+    one, sixteen = F.e4m3_encode(1.0), F.e4m3_encode(16.0)
+    q8 = np.zeros((1, d), np.uint8)
+    q8[0, 0] = one
+    k8 = np.zeros((2, d), np.uint8)
+    k8[1, 0] = F.e4m3_encode(-16.0)
+    v8 = np.zeros((2, d), np.uint8)
+    v8[1, :] = one
+    ones = np.ones(1, np.float32)
+    scale = -t1 / (16.0 * F.LOG2E)  # t(key 1) = scale * (-16) * log2(e) = t1
+    assert sixteen != 0
+    return q8, k8, v8, ones, ones, ones, scale
+
+
+@pytest.mark.parametrize("t1,code", [(-17.4, 2.0 ** -9), (-17.9, 2.0 ** -9), (-16.4, 2.0 ** -8),
+                                     (-18.2, 0.0), (-12.0, 2.0 ** -4)])
+def test_p_scale_smallest_weights(t1, code):
+    """The P codes are e4m3(2^8 p): a weight p = 2^t1 lands on the code of
+    2^(t1 + 8), so the smallest subnormal code 2^-9 holds weights from just
+    above 2^-18 (the tie at 2^-18 rounds to 0) up to 1.5 * 2^-17, and O of
+    the two-key row is that code times 2^-8 over l = 1 + 2^t1 (closed form)."""
+    q8, k8, v8, sq, sk, sv, scale = _two_key_row(t1)
+    r = F.attention_fp8(q8, k8, v8, sq, sk, sv, scale, parts=True)
+    assert r["M"][0] == 0.0 and r["p8"][0, 0] == 256.0
+    assert r["p8"][0, 1] == code
+    expect = code * 2.0 ** -8 / (1.0 + 2.0 ** t1)
+    np.testing.assert_allclose(r["o"][0], np.full(16, expect), rtol=1e-12, atol=0)
+    np.testing.assert_allclose(r["lse"][0], np.log1p(2.0 ** t1), rtol=0, atol=1e-12)
+
+
+def test_p_scale_largest_code():
+    """scale = 0: every weight is 1 (M = 0), so the keys of the tile with the
+    largest V scale code to 2^8 = 256 exactly and those of a tile whose V
+    scale is half of it to 128 (w = 1/2 folded into P)."""
+    q8, k8, v8, sq, sk, sv = _codes_problem(3, 256, 16, 81)
+    sv = np.array([[0.25, 0.5], [0.5, 0.25]], np.float32)
+    r = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.0, parts=True)
+    assert np.all(r["p8"][0, :, :128] == 128.0) and np.all(r["p8"][0, :, 128:] == 256.0)
+    assert np.all(r["p8"][1, :, :128] == 256.0) and np.all(r["p8"][1, :, 128:] == 128.0)
+    ref = F.dequantize(v8, sv).mean(axis=-2)  # every code exact: O is the mean of V
+    np.testing.assert_allclose(r["o"], np.broadcast_to(ref[:, None, :], r["o"].shape), rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("log2_scale", [7, 9])
+def test_mutation_p_scale(monkeypatch, log2_scale):
+    """A P scale of 2^7 drops the weights between 2^-18 and 2^-17 (and a
+    2^-17.4 weight codes to 0); 2^9 codes the largest weights to 448
+    (saturation) and moves the small ones up a code: each pin catches both."""
+    monkeypatch.setattr(F, "P_SCALE_LOG2", log2_scale)
+    with pytest.raises(AssertionError):
+        test_p_scale_smallest_weights(-17.4, 2.0 ** -9)
+    with pytest.raises(AssertionError):
+        test_p_scale_largest_code()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_v_scale_tile(causal):
+    """A V tile whose scale is 0 (the caller's scales may be 0): its keys
+    still count in the softmax sum l, and they add nothing to O.  Against
+    plain attention on the dequantised inputs (that tile's V rows are 0),
+    exact with P unrounded and within the P-rounding bound with it."""
+    q8, k8, v8, sq, sk, sv = _codes_problem(150, 300, 32, 91)
+    sv = sv.copy()
+    sv[0, 1] = 0.0
+    qd, kd, vd = F.dequantize(q8, sq), F.dequantize(k8, sk), F.dequantize(v8, sv)
+    assert np.all(vd[0, 128:256] == 0)
+    ref_o, ref_l = oracle.attention(qd, kd, vd, 0.3, causal)
+    o, lse = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, causal, quantize_p=False)
+    np.testing.assert_allclose(o, ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_l, rtol=1e-13, atol=1e-12)
+    o8, lse8 = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, causal)
+    np.testing.assert_allclose(lse8, ref_l, rtol=1e-13, atol=1e-12)
+    p, _, _ = oracle.softmax_rows(oracle.scores(qd, kd, 0.3, causal))
+    bound = (2.0 ** -4 * p + 2.0 ** -18) @ np.abs(vd) * 1.000001
+    assert np.all(np.abs(o8 - ref_o) <= bound + 1e-12)
+
+
+def test_all_zero_v_scales():
+    q8, k8, v8, sq, sk, _ = _codes_problem(20, 130, 16, 93)
+    sv = np.zeros((2, 2), np.float32)
+    o, lse = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, False)
+    _, ref_l = oracle.attention(F.dequantize(q8, sq), F.dequantize(k8, sk), np.zeros((2, 130, 16)), 0.3)
+    assert np.all(o == 0) and not np.any(np.isnan(o))
+    np.testing.assert_allclose(lse, ref_l, rtol=1e-13, atol=1e-12)
+
+
+def test_rowmax_reading():
+    """The other plain reading of the P rounding (V scale applied per tile
+    after the product): unrounded, both readings are plain attention on the
+    dequantised inputs; with equal V scales (w = 1) they round identically;
+    with unequal scales they differ."""
+    q8, k8, v8, sq, sk, sv = _codes_problem(90, 300, 32, 95)
+    a = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, quantize_p=False, p_mode="rowmax")
+    b = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, quantize_p=False)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-13)
+    eq = np.full_like(sv, 0.125)
+    a = F.attention_fp8(q8, k8, v8, sq, sk, eq, 0.3, p_mode="rowmax")
+    b = F.attention_fp8(q8, k8, v8, sq, sk, eq, 0.3)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    a = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, p_mode="rowmax")
+    b = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3)
+    assert not np.allclose(a[0], b[0], rtol=0, atol=1e-9)
+
+
+def test_quantize_tiny_amax():
+    """amax below 448 * 2^-149: amax / 448 underflows fp32, so the scale is
+    the smallest positive fp32 2^-149, and each code is x / 2^-149, an
+    integer (x is a multiple of 2^-149) rounded to e4m3."""
+    x = np.zeros((1, 1, 128, 64), np.float32)
+    vals = np.array([1, 3, 17, 100, 300], np.float64)
+    x[0, 0, 0, :5] = (vals * 2.0 ** -149).astype(np.float32)
+    x[0, 0, 1, :5] = -x[0, 0, 0, :5]
+    assert np.array_equal(x[0, 0, 0, :5].astype(np.float64) * 2.0 ** 149, vals)
+    codes, scales = F.quantize(x)
+    assert scales[0, 0, 0] == np.float32(2.0 ** -149)
+    got = F.e4m3_decode(codes[0, 0, :2, :5])
+    expect = F.e4m3_round(vals)  # 17 -> 16, 100 -> 96, 300 -> 288
+    assert np.array_equal(got[0], expect) and np.array_equal(got[1], -expect)
+    assert list(expect) == [1.0, 3.0, 16.0, 96.0, 288.0]
