@@ -322,8 +322,14 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
     if (kt < wave_kt) {
       const float cs = p.c * sq * sk[kt];
       const float svt = sv[kt];
-      // log2 of 2^8 w: P codes are e4m3(2^(t - M) * 2^8 * s_v / max s_v)
-      const float bias = 8.f + (svt > 0.f ? __log2f(svt) - lsv_max : -INFINITY);
+      // log2 of 2^8 w: P codes are e4m3(2^(t - M) * 2^8 * s_v / max s_v).
+      // With 2^8 w <= 2^-11 every code of the tile is 0 (values <= 2^-10
+      // round to 0): the tile then skips the PV product, and its
+      // exponentials are taken with bias 8 so that l still gets its mass.
+      // That covers a V scale of 0 (bias -inf).
+      const float bias_w = 8.f + (svt > 0.f ? __log2f(svt) - lsv_max : -INFINITY);
+      const bool pv_zero = !(bias_w >= -11.f);
+      const float bias = pv_zero ? 8.f : bias_w;
 
       f32x16_t s[MB];
       compute_s(slot, s);
@@ -384,7 +390,11 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
       }
       const float rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
       // rs sums 2^(t - M) * 2^bias; l keeps the unweighted sum
-      l += bias == -INFINITY ? 0.f : rs * __builtin_amdgcn_exp2f(-bias);
+      l += rs * __builtin_amdgcn_exp2f(-bias);
+      if (pv_zero) {
+        slot = (slot + 1 == NS) ? 0 : slot + 1;
+        continue;  // wave-uniform: the tile's V scale is the same for every lane
+      }
 
       // P codes: step g takes key blocks 2g (bytes 0..15) and 2g+1 (16..31)
       uint4 pp[PG][2];

@@ -10,7 +10,8 @@
 // Hadamard transform H_d (Sylvester order) is a product of one butterfly
 // (a, b) -> (a + b, a - b) per bit of the column index: the three low bits are
 // done inside the lane, the others between lanes (lane ^ 1, ^ 2, ...).
-// Then the tile's amax, s = amax / 448 (1 if the tile is all zero), and
+// Then the tile's amax, s = amax / 448 (1 if the tile is all zero; at least
+// 2^-149, the smallest positive fp32, where amax / 448 would underflow), and
 // code = e4m3(x' / s): x' / s correctly rounded to fp32, then rounded to
 // nearest even e4m3.
 //
@@ -34,6 +35,9 @@ template <int D>
 constexpr int kTileThreads = 4 * D;
 constexpr int kTileRows = 128;
 constexpr float kE4m3Max = 448.0f;
+// Smallest positive fp32: the scale of a tile whose amax / 448 underflows
+// (amax < 448 * 2^-149), so its codes x / s stay finite (and exact).
+constexpr float kF32Tiny = 0x1p-149f;
 
 __device__ __forceinline__ void load8(const float* src, float v[8]) {
   const float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
@@ -212,7 +216,7 @@ __global__ void __launch_bounds__(kTileThreads<D>) fp8_prep_kernel(PrepParams p)
       if (tid == 0) p.scale[sidx] = tmax;
       return;
     }
-    s = tmax > 0.f ? tmax / kE4m3Max : 1.0f;
+    s = tmax > 0.f ? fmaxf(tmax / kE4m3Max, kF32Tiny) : 1.0f;
     if (tid == 0) p.scale[sidx] = s;
   }
 
@@ -250,7 +254,7 @@ __global__ void __launch_bounds__(kPrepThreads) tensor_scale_kernel(float* scale
   float m = 0.f;
   for (int i = threadIdx.x; i < n; i += kPrepThreads) m = fmaxf(m, scale[i]);
   m = block_max<kPrepThreads>(m, red);
-  const float s = m > 0.f ? m / kE4m3Max : 1.0f;
+  const float s = m > 0.f ? fmaxf(m / kE4m3Max, kF32Tiny) : 1.0f;
   for (int i = threadIdx.x; i < n; i += kPrepThreads) scale[i] = s;
 }
 

@@ -83,7 +83,10 @@ enum {
  *   attn_fp8_quantize_varlen writes; later entries are not read).
  *   For fp16/bf16 the three scale pointers are ignored (may be NULL); for
  *   fp8 they may be NULL only where the tensor is empty (Nq or Nk = 0).
- *   Scales must be >= 0 (attn_fp8_quantize writes positive ones).
+ *   Scales must be >= 0 (attn_fp8_quantize writes positive ones).  A V
+ *   tile whose scale is 0 (or so small against the head's largest V scale
+ *   that its rounded weights are all 0) adds nothing to O but its keys still
+ *   count in the softmax sum.
  *
  * d ∈ {64, 128, 256} (else ATTN_ERR_UNSUPPORTED; fp8: d = 128 only).
  * scale: finite and >= 0 (typically 1/sqrt(d)).  causal ∈ {0, 1}.
@@ -115,8 +118,9 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
  *     matrix applied along d by a fast Walsh-Hadamard transform (used for Q
  *     and K; V is passed with signs == NULL).
  *   Then block quantisation: for every (b, h, 128-row tile) t,
- *     s_t = amax_t / 448 (s_t = 1 if the tile is all zero), with amax over
- *     the tile's rotated values, and x_fp8 = e4m3(x' / s_t) rounded to
+ *     s_t = amax_t / 448 (s_t = 1 if the tile is all zero; s_t = 2^-149,
+ *     the smallest positive fp32, where amax_t / 448 underflows), with amax
+ *     over the tile's rotated values, and x_fp8 = e4m3(x' / s_t) rounded to
  *     nearest-even in fp32; x' ~= s_t * x_fp8.
  *   per_tensor = 1 replaces the per-tile amax by one amax over the whole
  *     tensor (every entry of x_scale then holds the same s): the per-tensor

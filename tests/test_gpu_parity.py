@@ -383,10 +383,10 @@ def test_varlen_offsets_beyond_2_31_elements(gpu_lib):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("shape", ["rising", "falling", "spiky"])
-def test_drifting_row_max(gpu_lib, dtype, causal, shape):
+DRIFT_SHAPES = ["rising", "falling", "spiky", "partial"]
+
+
+def _drift_problem(nq, nk, d, shape, seed, heads=2):
     """Score rows whose maximum drifts across key tiles.  Channel 0 of every
     query is 1 and channel 0 of key j is a ramp, so each row's scores climb
     (or fall) by about 0.03 in base 2 per key: several bits per key tile, with
@@ -394,32 +394,190 @@ def test_drifting_row_max(gpu_lib, dtype, causal, shape):
     most tiles, the reference of the exponentials lags it, and P can exceed
     1 (up to the kernel's slack) before a rescale; the other channels are
     small N(0,1) noise.  "spiky": one key per 128 keys (index 37 mod 128)
-    stands 3 more bits above the previous one and the rest 40 below, so
-    the weight of a row sits on about one key while the reference lags the
-    row max by up to 3 bits.  V is uniform in (-3.9, 3.9), so many |O| lie
-    in [2, 4): there the output rounding alone takes up to half an ulp of
-    the bar, and P rounded to 16 bits would add up to 2^-9 |V| in bf16 unless
-    the kernel takes its residual pass.
-    d = 64 and 128, Nk = 1000 (a ragged last tile)."""
-    for d in (64, 128):
-        rng = np.random.default_rng(5 + d)
-        nq, nk = 300, 1000
-        q = 0.1 * rng.standard_normal((1, 2, nq, d)).astype(np.float32)
-        k = 0.1 * rng.standard_normal((1, 2, nk, d)).astype(np.float32)
-        v = rng.standard_normal((1, 2, nk, d)).astype(np.float32)
-        q[..., 0] = 1.0
-        step = 0.03 / (np.log2(np.e) / np.sqrt(d))  # base-2 increase per key
-        ramp = step * np.arange(nk, dtype=np.float64)
-        if shape == "rising":
-            ramp[700:] += 20.0 / (np.log2(np.e) / np.sqrt(d))
-        elif shape == "falling":
-            ramp = ramp[::-1].copy()
-        else:
-            j = np.arange(nk)
-            bits = np.where(j % 128 == 37, 3.0 * (j // 128), -40.0)
-            ramp = bits / (np.log2(np.e) / np.sqrt(d))
-            v[:] = rng.uniform(-3.9, 3.9, v.shape)
-        k[..., 0] = ramp.astype(np.float32)
-        o, lse, (q64, k64, v64, s) = run_dense(gpu_lib, q, k, v, dtype, causal)
-        o_ref, l_ref = oracle.attention(q64, k64, v64, s, causal)
-        check(o, lse, o_ref, l_ref, dtype, f"drifting max {shape} d{d} causal{causal}")
+    stands 3 more bits above the previous one and the rest 40 below, so the
+    weight of a row sits on about one key while the reference lags the row
+    max by up to 3 bits; V is then uniform in (-3.9, 3.9), so many |O| lie in
+    [2, 4): there the output rounding alone takes up to half an ulp of the
+    bar, and P rounded to 16 bits would add up to 2^-9 |V| in bf16 unless the
+    kernel takes its residual pass.  "partial": the rising ramp reaches only
+    every third query row (the others see the noise alone), so one row's
+    trigger moves the reference of rows that lag it by less than the slack.
+    Returns fp32 q [1, heads, nq, d], k, v [1, heads, nk, d]."""
+    rng = np.random.default_rng(seed)
+    q = 0.1 * rng.standard_normal((1, heads, nq, d)).astype(np.float32)
+    k = 0.1 * rng.standard_normal((1, heads, nk, d)).astype(np.float32)
+    v = rng.standard_normal((1, heads, nk, d)).astype(np.float32)
+    q[..., 0] = 1.0
+    step = 0.03 / (np.log2(np.e) / np.sqrt(d))  # base-2 increase per key
+    ramp = step * np.arange(nk, dtype=np.float64)
+    if shape in ("rising", "partial"):
+        ramp[700:] += 20.0 / (np.log2(np.e) / np.sqrt(d))
+        if shape == "partial":
+            q[..., np.arange(nq) % 3 != 0, 0] = 0.0
+    elif shape == "falling":
+        ramp = ramp[::-1].copy()
+    else:
+        j = np.arange(nk)
+        bits = np.where(j % 128 == 37, 3.0 * (j // 128), -40.0)
+        ramp = bits / (np.log2(np.e) / np.sqrt(d))
+        v[:] = rng.uniform(-3.9, 3.9, v.shape)
+    k[..., 0] = ramp.astype(np.float32)
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", DRIFT_SHAPES)
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_drifting_row_max(gpu_lib, dtype, causal, shape, d):
+    """Drifting row maxima (``_drift_problem``) through the dense launches,
+    Nk = 1000 (a ragged last tile): d = 64 and 128 at two waves per SIMD,
+    d = 256 with its 64-key tiles at one wave per SIMD and late tile loads."""
+    q, k, v = _drift_problem(300, 1000, d, shape, seed=5 + d)
+    o, lse, (q64, k64, v64, s) = run_dense(gpu_lib, q, k, v, dtype, causal)
+    o_ref, l_ref = oracle.attention(q64, k64, v64, s, causal)
+    check(o, lse, o_ref, l_ref, dtype, f"drifting max {shape} d{d} causal{causal}")
+
+
+@pytest.mark.parametrize("shape", DRIFT_SHAPES)
+@pytest.mark.parametrize("d", [128, 256])
+def test_drifting_row_max_varlen_causal(gpu_lib, shape, d):
+    """The same rows packed as a variable-length causal batch of two
+    sequences (1000 and 345 tokens, the second with its own ramp): at d = 128
+    the 4-wave, 64-key tile configuration with late loads."""
+    qa, ka, va = _drift_problem(1000, 1000, d, shape, seed=11 + d)
+    qb, kb, vb = _drift_problem(345, 345, d, shape, seed=12 + d)
+    cu = np.array([0, 1000, 1345], dtype=np.int32)
+    q = np.concatenate([qa[0], qb[0]], axis=1)
+    k = np.concatenate([ka[0], kb[0]], axis=1)
+    v = np.concatenate([va[0], vb[0]], axis=1)
+    qd, q64 = to_device(q, "bf16")
+    kd, k64 = to_device(k, "bf16")
+    vd, v64 = to_device(v, "bf16")
+    cud = torch.from_numpy(cu).cuda()
+    s = 1.0 / np.sqrt(d)
+    o, lse = gpu_lib.forward(qd, kd, vd, causal=True, scale=s, cu_seqlens_q=cud, cu_seqlens_k=cud)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_varlen(q64, k64, v64, cu, cu, s, True)
+    check(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref, "bf16",
+          f"drifting max varlen causal {shape} d{d}")
+
+
+@pytest.mark.parametrize("shape", DRIFT_SHAPES)
+@pytest.mark.parametrize("d,causal", [(128, False), (128, True), (256, False)])
+def test_drifting_row_max_splitkv(gpu_lib, shape, d, causal):
+    """Drifting maxima through the key-chunk launches (3 chunks of 334 keys:
+    the ramp's maximum moves inside every chunk) and the merge."""
+    q, k, v = _drift_problem(300, 1000, d, shape, seed=21 + d)
+    qd, q64 = to_device(q, "bf16")
+    kd, k64 = to_device(k, "bf16")
+    vd, v64 = to_device(v, "bf16")
+    s = 1.0 / np.sqrt(d)
+    o, lse = gpu_lib.forward_splitkv(qd, kd, vd, causal=causal, scale=s, num_splits=3)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(q64, k64, v64, s, causal)
+    check(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref, "bf16",
+          f"drifting max split-KV {shape} d{d} causal{causal}")
+
+
+@pytest.mark.parametrize("shape", DRIFT_SHAPES)
+def test_drifting_row_max_paged_e4m3(gpu_lib, shape):
+    """Drifting maxima read from a paged e4m3 cache with per-(token, head)
+    scales (64-token pages in shuffled order, d = 128, 7 queries).  Key j's
+    channel 0 holds the code +-448 and its scale is |ramp_j| / 448, so the
+    dequantised channel 0 is the ramp; the other channels are codes of
+    magnitude <= 2 times that scale.  V: codes in [2, 3.75] with scales in
+    [0.5, 1], so |V| reaches [2, 3.75] (spiky rows then have |O| in [2, 4)),
+    and P, up to the slack's 16, is multiplied by the V scale before the
+    16-bit packing."""
+    from oracle import fp8 as F
+    from oracle import paged as PG
+
+    d, nk, H, nq, P = 128, 1000, 2, 7, 64
+    q, k, _ = _drift_problem(nq, nk, d, shape, seed=31, heads=H)
+    rng = np.random.default_rng(33)
+    ramp = k[0, :, :, 0].astype(np.float64)  # [H, nk]
+    small = F.e4m3_encode(rng.choice([-2.0, -1.0, -0.5, 0.0, 0.5, 1.0, 2.0], (H, nk, d)))
+    kcode = small.copy()
+    kcode[..., 0] = F.e4m3_encode(np.where(ramp < 0, -448.0, 448.0))
+    ksc = np.maximum(np.abs(ramp) / 448.0, 1e-6).astype(np.float32)
+    vcode = F.e4m3_encode(rng.choice([2.0, 2.5, 3.0, 3.5, 3.75], (H, nk, d)) * rng.choice([-1.0, 1.0], (H, nk, d)))
+    vsc = rng.uniform(0.5, 1.0, (H, nk)).astype(np.float32)
+    n_pages = -(-nk // P) + 3
+    perm = rng.permutation(n_pages)[: -(-nk // P)]
+    kc = np.zeros((n_pages, P, H, d), np.uint8)
+    vc = np.zeros((n_pages, P, H, d), np.uint8)
+    ks = np.ones((n_pages, P, H), np.float32)
+    vs = np.ones((n_pages, P, H), np.float32)
+    for j, pg in enumerate(perm):
+        rows = slice(j * P, min(nk, (j + 1) * P))
+        n = rows.stop - rows.start
+        kc[pg, :n] = np.transpose(kcode[:, rows], (1, 0, 2))
+        vc[pg, :n] = np.transpose(vcode[:, rows], (1, 0, 2))
+        ks[pg, :n] = ksc[:, rows].T
+        vs[pg, :n] = vsc[:, rows].T
+    table = perm.astype(np.int32)[None]
+    qd, q64 = to_device(q, "bf16")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    s = 1.0 / np.sqrt(d)
+    o, lse = gpu_lib.forward_paged(qd, t(kc), t(vc), t(table), torch.tensor([nk], dtype=torch.int32).cuda(),
+                                   scale=s, k_scale=t(ks), v_scale=t(vs), kv_dtype="e4m3", num_splits=3)
+    torch.cuda.synchronize()
+    ref_o, ref_l = PG.attention_paged_quant(q64, kc, vc, ks, vs, table, np.array([nk]), s, "e4m3")
+    kd = PG.dequantize(kc, ks, "e4m3")[perm[0], :5, 0, 0]
+    assert np.allclose(kd, ramp[0, :5], rtol=1e-6, atol=1e-3)  # channel 0 carries the ramp
+    check(o.double().cpu().numpy(), lse.double().cpu().numpy(), ref_o, ref_l, "bf16",
+          f"drifting max paged e4m3 {shape}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_attn_fwd_null_stream(gpu_lib, dtype):
+    """The entry point with the specified argument list, attn_fwd, which
+    enqueues on the null stream (the other tests go through attn_fwd_stream
+    on torch's current stream), called through the C ABI with raw pointers:
+    bf16 and e4m3 codes, causal, B2 H3 Nq 300 Nk 700, against the oracle."""
+    from oracle import fp8 as F
+
+    B, H, nq, nk, d = 2, 3, 300, 700, 128
+    scale = 0.09
+    torch.cuda.synchronize()
+    if dtype == "bf16":
+        q, k, v = W.random_problem(B, H, nq, nk, d, seed=77)
+        qd, q64 = to_device(q, "bf16")
+        kd, k64 = to_device(k[:, :, :nk], "bf16")
+        vd, v64 = to_device(v[:, :, :nk], "bf16")
+        o = torch.full_like(qd, float("nan"))
+        lse = torch.full((B, H, nq), float("nan"), dtype=torch.float32, device="cuda")
+        rc = gpu_lib.attn_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, nq,
+                              nk, d, scale, 1, None, None, gpu_lib.ATTN_DT_BF16, None, None, None)
+        assert rc == gpu_lib.ATTN_OK
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention(q64, k64, v64, scale, True)
+        check(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref, "bf16", "attn_fwd bf16")
+    else:
+        nt = lambda n: (n + 127) // 128  # noqa: E731
+        codes = [0x38, 0x3C, 0x40, 0x44, 0x48, 0xB8, 0xBC, 0xC0, 0xC4, 0xC8]
+        q8 = W.random_codes_from(codes, (B, H, nq, d), 78)
+        k8 = W.random_codes_from(codes, (B, H, nk, d), 79)
+        v8 = W.random_codes_from(codes, (B, H, nk, d), 80)
+        sq = W.random_pow2_scales((B, H, nt(nq)), 81, -1, 0)
+        sk = W.random_pow2_scales((B, H, nt(nk)), 82, -1, 0)
+        sv = W.random_pow2_scales((B, H, nt(nk)), 83, -7, -4)
+        dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+        tq, tk, tv, tsq, tsk, tsv = dv(q8), dv(k8), dv(v8), dv(sq), dv(sk), dv(sv)
+        o = torch.full((B, H, nq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((B, H, nq), float("nan"), dtype=torch.float32, device="cuda")
+        rc = gpu_lib.attn_fwd(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, nq,
+                              nk, d, scale, 1, None, None, gpu_lib.ATTN_DT_FP8_E4M3, tsq.data_ptr(), tsk.data_ptr(),
+                              tsv.data_ptr())
+        assert rc == gpu_lib.ATTN_OK
+        torch.cuda.synchronize()
+        ref = F.attention_fp8(q8, k8, v8, sq, sk, sv, scale, True, ambiguity=3e-5, parts=True)
+        err = np.abs(o.double().cpu().numpy() - ref["o"]) - ref["flip"]
+        # bf16 output rounding + fp32 accumulation (|O| < 0.5 here) and the
+        # e4m3 MFMA's truncation of the PV sums (bounded as in test_gpu_fp8)
+        from test_gpu_fp8 import _pv_bound
+
+        assert np.all(err <= 4e-3 + _pv_bound(ref)), float(err.max())
+        l = lse.double().cpu().numpy()
+        assert np.all(np.abs(l - ref["lse"]) <= 1e-3 * np.maximum(1.0, np.abs(ref["lse"])))
