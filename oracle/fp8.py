@@ -32,18 +32,24 @@ design notes):
 * the quantisation decisions are taken in fp32, as the device does: the
   rotated values are rounded to fp32, s = fp32(amax / 448) and the code is
   the e4m3 rounding of fp32(x / s);
-* in the PV product, P is rounded to e4m3 as P8 = e4m3(2^8 * 2^(t - M) * w)
-  with t = S log2(e) the scores in base 2, M = ceil(max_j t) the row's
-  integer reference max and w = s_v(tile of j) / max_tiles s_v the key
-  tile's V scale relative to the largest V scale of that head; l sums the
-  unrounded 2^(t - M); O = (max s_v) 2^-8 sum_j P8_j v8_j / l.  Because M is
-  an integer, any running reference max M' <= M gives the same codes up to
-  an exact power of two (outside the subnormal range), so a tiled kernel
-  can reach this result exactly.  A head whose V scales are all 0 has
-  w = 0 (O = 0).  The P scale 2^8 puts the largest weight of a row in the
-  tile of the largest V scale at code 2^8 = 256 exactly when the row max is
-  an integer, and weights down to 2^-17 (the smallest subnormal code 2^-9,
-  divided by 2^8) survive the rounding.
+* in the PV product, P is rounded to e4m3 tile by tile, in the order of the
+  online-softmax recurrence ("Flash Attention 3：让 GPU 跑满的注意力计算",
+  §2.2: the term of key block j enters as exp(S_j - m_new) V_j, m_new the
+  running max after block j).  The key blocks are the 128-key scale tiles;
+  t = S log2(e) are the scores in base 2; M_j = max(M_{j-1}, ceil(max of t
+  over tile j)) is the running integer max (M = M_last = ceil(max_j t));
+  w = s_v(tile) / max_tiles s_v is the tile's V scale relative to the
+  largest V scale of that head.  Tile j's codes are
+  P8 = e4m3(2^8 * 2^(t - M_j) * w), and they enter O with the exact factor
+  2^(M_j - M); l sums the unrounded 2^(t - M);
+  O = (max s_v) 2^-8 sum_j 2^(M_j - M) sum_{k in j} P8_k v8_k / l.  For codes
+  in the normal range the factor is exact either way, so only weights
+  below 2^-6 (in code units) depend on the tile in which M last rose.  A
+  head whose V scales are all 0 has w = 0 (O = 0).  The P scale 2^8 puts
+  the largest weight of a row in the tile of the largest V scale at code
+  2^8 = 256 exactly when the row max is an integer, and weights down to
+  2^-17 of the running max (the smallest subnormal code 2^-9, divided by
+  2^8) survive the rounding.
 """
 
 from __future__ import annotations
@@ -248,10 +254,11 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     precision, O = 2^-8 sum_tiles s_v(tile) sum_{j in tile} P8_j v8_j / l).
 
     ``parts=True`` returns a dict instead, with the intermediate values:
-    "o", "lse", "flip" (if requested), "p8" (the rounded P, in code units,
-    [..., Nq, Nk]), "x" (P before rounding, in code units), "t" (the base-2
-    scores), "M" [..., Nq], "l" [..., Nq], "sv_max" [...] and "v_codes"
-    (values of the V codes).
+    "o", "lse", "flip" (if requested), "p8" (the rounded P in code units of
+    the final M, [..., Nq, Nk]), "x" (P before rounding, in code units of its
+    tile's running max), "shift" (M_j - M per key), "t" (the base-2 scores),
+    "M" [..., Nq], "M_tile" (the running max per key tile), "l" [..., Nq],
+    "sv_max" [...] and "v_codes" (values of the V codes).
     """
     qd = dequantize(q8, sq, tile)
     qrow = np.arange(qd.shape[-2])
@@ -271,6 +278,16 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     M = np.where(live, np.ceil(np.where(live, tmax, 0.0)), 0.0)
     p = np.where(live[..., None], np.exp2(t - M[..., None]), 0.0)  # <= 1
     l = p.sum(axis=-1)
+    # running integer max M_j of the 128-key tiles, in key order
+    nkt = (nk + tile - 1) // tile
+    tpad = np.concatenate([t, np.full(t.shape[:-1] + (nkt * tile - nk,), -np.inf)], axis=-1)
+    tile_max = tpad.reshape(t.shape[:-1] + (nkt, tile)).max(axis=-1) if nk else np.zeros(t.shape[:-1] + (0,))
+    with np.errstate(invalid="ignore"):
+        run = np.maximum.accumulate(np.ceil(tile_max), axis=-1) if nkt else tile_max
+    Mj = np.repeat(run, tile, axis=-1)[..., :nk]  # -inf before a row's first visible key (those keys are masked)
+    fin = np.isfinite(t)
+    shift = np.where(fin, Mj - M[..., None], 0.0)  # <= 0, an integer
+    p_tile = np.where(fin, np.exp2(np.where(fin, t - Mj, 0.0)), 0.0)  # P relative to the running max
     if p_mode not in ("folded", "rowmax"):
         raise ValueError("p_mode must be 'folded' or 'rowmax'")
     sv_max = sv.max(axis=-1) if sv.shape[-1] else np.ones(sv.shape[:-1])
@@ -278,11 +295,12 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
         w_tile = np.where(sv_max[..., None] > 0, sv / np.where(sv_max > 0, sv_max, 1.0)[..., None], 0.0)
     w = np.repeat(w_tile, tile, axis=-1)[..., :nk]
     # folded: the weight enters P before rounding; rowmax: after (full precision)
-    pw = p * w[..., None, :] if p_mode == "folded" else p
+    pw = p_tile * w[..., None, :] if p_mode == "folded" else p_tile
     if quantize_p:
-        p8 = e4m3_round_f32((pw * 2.0 ** P_SCALE_LOG2).astype(np.float32))
+        p8_tile = e4m3_round_f32((pw * 2.0 ** P_SCALE_LOG2).astype(np.float32))
     else:
-        p8 = pw * 2.0 ** P_SCALE_LOG2
+        p8_tile = pw * 2.0 ** P_SCALE_LOG2
+    p8 = p8_tile * np.exp2(shift)  # in units of the final M (exact: a power of two)
     if p_mode == "folded":
         o_acc = np.matmul(p8, v_codes)
     else:
@@ -291,14 +309,14 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     if np.any(np.asarray(ambiguity) > 0):
         if p_mode != "folded":
             raise ValueError("the ambiguity bound follows the folded reading")
-        x = pw * 2.0 ** P_SCALE_LOG2
+        x = pw * 2.0 ** P_SCALE_LOG2  # in the units of the running max of its tile
         with np.errstate(divide="ignore"):
             e = np.maximum(np.floor(np.log2(np.where(x > 0, x, 1.0))), E4M3_MIN_NORMAL_EXP)
         spacing = np.ldexp(1.0, (e - E4M3_MANT_BITS).astype(np.int64))
         frac = x / spacing - np.floor(x / spacing)  # position between neighbouring codes
         near_mid = np.abs(frac - 0.5) * spacing <= ambiguity * x
         # a value just below a power of two can also round across the binade edge
-        flip = np.matmul(np.where(near_mid & (x > 0), spacing, 0.0), np.abs(v_codes))
+        flip = np.matmul(np.where(near_mid & (x > 0), spacing * np.exp2(shift), 0.0), np.abs(v_codes))
     with np.errstate(invalid="ignore", divide="ignore"):
         o = np.where(live[..., None],
                      o_acc * (sv_max[..., None, None] * 2.0 ** -P_SCALE_LOG2) / np.where(live, l, 1.0)[..., None],
@@ -310,7 +328,7 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
                             0.0)
     if parts:
         return {"o": o, "lse": lse, "flip": flip, "p8": p8, "l": l, "sv_max": sv_max, "v_codes": v_codes,
-                "x": pw * 2.0 ** P_SCALE_LOG2, "t": t, "M": M}
+                "x": pw * 2.0 ** P_SCALE_LOG2, "shift": shift, "t": t, "M": M, "M_tile": run}
     if flip is not None:
         return o, lse, flip
     return o, lse

@@ -521,3 +521,38 @@ def test_quantize_tiny_amax():
     expect = F.e4m3_round(vals)  # 17 -> 16, 100 -> 96, 300 -> 288
     assert np.array_equal(got[0], expect) and np.array_equal(got[1], -expect)
     assert list(expect) == [1.0, 3.0, 16.0, 96.0, 288.0]
+
+
+def test_p_rounding_follows_the_running_max():
+    """P is rounded tile by tile against the running integer max, the order
+    of the blog's online-softmax recurrence (§2.2: block j's term enters as
+    exp(S_j - m_new) V_j).  One query; 256 keys in two 128-key tiles with V
+    scales 1: tile 0 holds t = 0 (key 0) and t = -17.4 (key 1), tile 1 holds
+    t = 9.7875 (key 128); every other key scores -487 (weight 0).  Running
+    max: M_0 = 0, then M_1 = M = 10.  V rows one-hot (key 0 -> column 0,
+    key 1 -> 1, key 128 -> 2), so column c of O is the effective code of its
+    key times 2^-8 / l:
+      key 0:   e4m3(2^8) 2^(0 - 10)        = 2^-2
+      key 1:   e4m3(2^-9.4) 2^-10 = 2^-9 2^-10  (rounded against M = 10 it
+               would be e4m3(2^-19.4) = 0)
+      key 128: e4m3(2^7.7875) = 224
+    with l = 2^-10 + 2^-27.4 + 2^-0.2125."""
+    d = 16
+    q8 = np.zeros((1, d), np.uint8)
+    q8[0, 0] = F.e4m3_encode(1.0)
+    k8 = np.zeros((256, d), np.uint8)
+    kv = np.full(256, -448.0)
+    kv[0], kv[1], kv[128] = 0.0, -16.0, 9.0
+    k8[:, 0] = F.e4m3_encode(kv)
+    v8 = np.zeros((256, d), np.uint8)
+    v8[0, 0] = v8[1, 1] = v8[128, 2] = F.e4m3_encode(1.0)
+    ones = np.ones(2, np.float32)
+    scale = 17.4 / (16.0 * F.LOG2E)  # t(key 1) = -17.4, t(key 128) = 17.4 * 9 / 16 = 9.7875
+    r = F.attention_fp8(q8, k8, v8, ones[:1], ones, ones, scale, parts=True)
+    assert r["M"][0] == 10.0 and list(r["M_tile"][0]) == [0.0, 10.0]
+    l = 2.0 ** -10 + 2.0 ** (-17.4 - 10) + 2.0 ** (9.7875 - 10)
+    np.testing.assert_allclose(r["l"][0], l, rtol=1e-12)
+    expect = np.array([2.0 ** -2, 2.0 ** -19, 224.0]) * 2.0 ** -8 / l
+    np.testing.assert_allclose(r["o"][0, :3], expect, rtol=1e-12, atol=0)
+    assert np.all(r["o"][0, 3:] == 0)
+    np.testing.assert_allclose(r["lse"][0], (10 + np.log2(l)) / F.LOG2E, rtol=0, atol=1e-12)
