@@ -2,20 +2,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-detail]
 
-Workload (one "step"): the dense bf16 problem B=2, H=16, Nq=Nk=4096, d=128,
-scale 1/sqrt(128), seeded N(0,1) inputs already resident in HBM, run once
-non-causal and once causal (top-left) through the C ABI (attn_fwd_stream on
-torch's current stream).  value = (FLOPs of both runs) / (time per step),
-FLOPs = 4 B H Nq Nk d, halved for causal.
+Workload (one "step"): the dense bf16 problem B=2, H=16, Nq=Nk=8192, d=128,
+scale 1/sqrt(128), non-causal, seeded N(0,1) inputs already resident in HBM,
+one launch through the C ABI (attn_fwd_stream on torch's current stream).
+value = FLOPs / (time per step), FLOPs = 4 B H Nq Nk d.
 
-Prints ONE JSON line with the roofline of the dominant kernel (the
-non-causal launch: algorithmic FLOPs / its mean duration from HIP events on
-its stream, against the dense bf16 MFMA peak of 2.5 PFLOP/s; also against
-the MFMA rate a register-only probe kernel sustains on this GPU) and the CPU
-baseline (the fp64 oracle, timed on a bounded sample of the same workload).
-"detail" adds the other shapes (d=256, N=8192, variable length, decoding
-over key chunks, the backward pass, fp8 when available), each with its own
-TFLOP/s (or GB/s) and fraction of peak.
+Prints ONE JSON line with the roofline of that kernel (algorithmic FLOPs /
+its mean launch duration from HIP events on its stream, against the dense
+bf16 MFMA peak of 2.5 PFLOP/s; also against the MFMA rate a register-only
+probe kernel sustains on this GPU) and the CPU baseline (the fp64 oracle,
+timed on a bounded sample of the same workload: some of its heads).
+"detail" adds the other shapes (B2 H16 N4096 d128 non-causal and causal,
+d=256, variable length, the e4m3 kernel with its own roofline against the
+fp8 peak of 5.0 PFLOP/s, decoding over key chunks, the backward pass), each
+with its own TFLOP/s (or GB/s) and fraction of peak.  The detail rows run
+before the timed step.
 
 --copy-calib runs only a plain device copy of known size (for scaling the
 HBM byte counters) and prints its byte count.
@@ -38,7 +39,8 @@ PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["exact_attention_forward_03_amd/csrc/attn_fwd.hip",
                   "exact_attention_forward_03_amd/csrc/attn_device.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_d128_n4096_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_d128_n8192_traffic.json")
+HEADLINE = "n8k_bf16"  # B2 H16 Nq=Nk=8192 d128 bf16 non-causal
 
 
 def kernel_hash() -> str:
@@ -60,32 +62,45 @@ def load_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(chunk_heads: int = 8):
-    """The fp64 oracle on one whole step of the dense bf16 workload (all
-    B*H = 32 heads, non-causal and causal), fed `chunk_heads` heads per call
-    to bound its memory; inputs on the host in fp64, generation excluded."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(sample_heads: int = 8, chunk_heads: int = 2):
+    """The fp64 oracle on a bounded sample of the headline workload: the
+    first `sample_heads` of its B*H = 32 heads (seeded N(0,1) inputs rounded
+    to bf16, then held in fp64 on the host), `chunk_heads` heads per oracle
+    call to bound memory; generation excluded.  TFLOP/s uses the same FLOP
+    count per head as the GPU line."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
     import workloads as W
 
-    w = W.WORKLOADS["dense_bf16"]
-    heads = w.B * w.H
+    w = W.WORKLOADS[HEADLINE]
     rng = np.random.default_rng(0)
-    shape = (heads, w.Nq, w.d)
+    shape = (sample_heads, w.Nq, w.d)
     q, k, v = (W.to_dtype(rng.standard_normal(shape, dtype=np.float32), "bf16").double().numpy() for _ in range(3))
     t0 = time.perf_counter()
-    for h in range(0, heads, chunk_heads):
+    for h in range(0, sample_heads, chunk_heads):
         sl = slice(h, h + chunk_heads)
-        oracle.attention(q[sl], k[sl], v[sl], w.scale, False)
-        oracle.attention(q[sl], k[sl], v[sl], w.scale, True)
+        oracle.attention(q[sl], k[sl], v[sl], w.scale, w.causal)
     dt = time.perf_counter() - t0
-    flops = 4.0 * heads * w.Nq * w.Nk * w.d * 1.5
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one whole step: B*H={heads} heads of N=4096 d=128 bf16 inputs in fp64, "
-                      f"non-causal + causal, {chunk_heads} heads per oracle call, {dt:.1f} s"}
+    flops = 4.0 * sample_heads * w.Nq * w.Nk * w.d
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] + [1])
+    vendor = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in blas) or "unknown"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{sample_heads} of the {w.B * w.H} heads of the B2 H16 N8192 d128 bf16 non-causal workload "
+                      f"(inputs in fp64), {chunk_heads} heads per oracle call, {dt:.1f} s",
+            "cpu_model": _cpu_model(), "blas": vendor, "blas_threads": int(threads)}
 
 
 def measured_mfma_tflops():
@@ -120,39 +135,44 @@ def timed_launches(fn, n, stream):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def bench_detail(attn, steps, warmup):
-    """Per-shape throughput of the other workloads (mean and median over
-    `steps` launches)."""
+def bench_one(attn, name, steps, warmup):
+    """Mean and median launch time of one fp16/bf16 workload (seeded inputs
+    resident in HBM, launches on torch's current stream)."""
     import numpy as np
     import torch
 
     import workloads as W
 
-    out = {}
     stream = torch.cuda.current_stream()
-    for name in ("n8k_bf16", "hdim256_bf16", "varlen_bf16_causal", "tiny_f16"):
-        w = W.WORKLOADS[name]
-        x = W.make_inputs(w)
-        q, k, v = (W.to_dtype(x[n], w.dtype).cuda() for n in ("q", "k", "v"))
-        kw = {}
-        if w.varlen:
-            cu = torch.from_numpy(x["cu_seqlens"]).cuda()
-            kw = dict(cu_seqlens_q=cu, cu_seqlens_k=cu)
-        o = torch.empty_like(q)
-        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    w = W.WORKLOADS[name]
+    x = W.make_inputs(w)
+    q, k, v = (W.to_dtype(x[n], w.dtype).cuda() for n in ("q", "k", "v"))
+    kw = {}
+    if w.varlen:
+        cu = torch.from_numpy(x["cu_seqlens"]).cuda()
+        kw = dict(cu_seqlens_q=cu, cu_seqlens_k=cu)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
 
-        def run():
-            attn.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, **kw)
+    def run():
+        attn.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, **kw)
 
-        for _ in range(warmup):
-            run()
-        ts = timed_launches(run, steps, stream)
-        ms, med = float(np.mean(ts)), float(np.median(ts))
-        tf = w.flops() / (ms / 1e3) / 1e12
-        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                     "ms_median": round(med, 4), "tflops_median": round(w.flops() / (med / 1e3) / 1e12, 2),
-                     "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
-        del q, k, v, o, lse
+    for _ in range(warmup):
+        run()
+    ts = timed_launches(run, steps, stream)
+    ms, med = float(np.mean(ts)), float(np.median(ts))
+    tf = w.flops() / (ms / 1e3) / 1e12
+    return {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "ms_median": round(med, 4), "tflops_median": round(w.flops() / (med / 1e3) / 1e12, 2),
+            "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
+
+
+def bench_detail(attn, steps, warmup):
+    """Per-shape throughput of the other workloads (mean and median over
+    `steps` launches)."""
+    out = {}
+    for name in ("dense_bf16", "dense_bf16_causal", "hdim256_bf16", "varlen_bf16_causal", "tiny_f16"):
+        out[name] = bench_one(attn, name, steps, warmup)
     out["hbm_copy_gbs"] = copy_bandwidth()
     out.update(bench_decode(attn, steps, warmup))
     out.update(bench_backward(attn, steps, warmup))
@@ -302,7 +322,7 @@ def copy_bandwidth(steps: int = 10) -> float:
     return round(2 * n / (ms / 1e3) / 1e9, 1)
 
 
-def bench_fp8(attn, steps, warmup):
+def bench_fp8(attn, steps, warmup, varlen=True):
     """fp8 workload (B=2 H=16 N=8192 d=128, outlier channels): the attention
     kernel alone and the pre-processing of Q, K, V; None if not built."""
     import numpy as np
@@ -342,13 +362,17 @@ def bench_fp8(attn, steps, warmup):
     return {"fp8_outlier": {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_FP8_TFLOPS, 4),
                             "ms_median": round(med, 4),
                             "tflops_median": round(w.flops() / (med / 1e3) / 1e12, 2),
-                            "shape": [w.B, w.H, w.Nq, w.Nk, w.d]},
+                            "shape": [w.B, w.H, w.Nq, w.Nk, w.d],
+                            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                                         "kernel": "attn_fwd_fp8_kernel<non-causal, 8 waves, 4 slots>",
+                                         "mean_launch_ms": round(ms, 4)}},
             "fp8_prep_qkv": {"ms": round(ms_prep, 4), "gbs": round(prep_bytes / (ms_prep / 1e3) / 1e9, 1),
                              "frac_hbm": round(prep_bytes / (ms_prep / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
             # fp32 Q, K, V in HBM -> rotation and block quantisation -> e4m3 attention
             "fp8_end_to_end": {"ms": round(ms + ms_prep, 4),
                                "tflops": round(w.flops() / ((ms + ms_prep) / 1e3) / 1e12, 2)},
-            **bench_fp8_varlen(attn, steps, warmup)}
+            **(bench_fp8_varlen(attn, steps, warmup) if varlen else {})}
 
 
 def bench_fp8_varlen(attn, steps, warmup):
@@ -409,6 +433,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="time one workload alone (a name of workloads.WORKLOADS, or fp8_outlier for the e4m3 "
+                         "kernel) and print its own line: for profiling single kernels")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this library runs on one GPU; multi-GPU runs are not part of it "
@@ -426,44 +453,44 @@ def main():
     import workloads as W
 
     attn.load()
-    w_nc = W.WORKLOADS["dense_bf16"]
-    w_c = W.WORKLOADS["dense_bf16_causal"]
-    x = W.make_inputs(w_nc)  # same seed and shape for both runs of the step
+    if args.only:
+        if args.only == "fp8_outlier":
+            res = bench_fp8(attn, args.steps, args.warmup, varlen=False)["fp8_outlier"]
+        else:
+            res = bench_one(attn, args.only, args.steps, args.warmup)
+        print(json.dumps({"only": args.only, **res}), flush=True)
+        return
+    detail = None
+    if not args.no_detail:
+        detail = bench_detail(attn, max(10, args.steps // 2), 10)
+    w = W.WORKLOADS[HEADLINE]
+    x = W.make_inputs(w)
     q, k, v = (W.to_dtype(x[n], "bf16").cuda() for n in ("q", "k", "v"))
+    del x
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def run_nc():
-        attn.forward(q, k, v, causal=False, scale=w_nc.scale, out=o, lse=lse)
-
-    def run_c():
-        attn.forward(q, k, v, causal=True, scale=w_c.scale, out=o, lse=lse)
+    def step():
+        attn.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
 
     for _ in range(args.warmup):
-        run_nc()
-        run_c()
+        step()
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, synchronised on both sides
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b, c in ev:
+    for a, b in ev:
         a.record(stream)
-        run_nc()
+        step()
         b.record(stream)
-        run_c()
-        c.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    nc_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
-    c_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
-    step_ms = float(np.mean(nc_ms + c_ms))
-    flops_step = w_nc.flops() + w_c.flops()
-    value = flops_step / (step_ms / 1e3) / 1e12
-    ach = w_nc.flops() / (float(np.mean(nc_ms)) / 1e3) / 1e12
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    step_ms = float(np.mean(ms))
+    value = w.flops() / (step_ms / 1e3) / 1e12
 
     result = {
         "metric": "attention fwd TFLOP/s and % MFMA peak (bf16 + fp8), hdim 128/256, 1 GPU",
@@ -478,24 +505,23 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "dense bf16 attention fwd, B=2 H=16 Nq=Nk=4096 d=128, non-causal + causal",
-                   "B": 2, "H": 16, "seq_len": 4096, "head_dim": 128, "causal": [False, True],
-                   "wall_s_timed": round(wall, 4)},
-        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(),
-                     "kernel": "attn_fwd_dma_kernel<bf16, d=128, non-causal>",
-                     "mean_launch_ms": round(float(np.mean(nc_ms)), 4),
-                     "causal_launch_ms": round(float(np.mean(c_ms)), 4)},
+        "config": {"workload": "dense bf16 attention fwd, B=2 H=16 Nq=Nk=8192 d=128, non-causal",
+                   "B": w.B, "H": w.H, "seq_len": w.Nq, "head_dim": w.d, "causal": w.causal,
+                   "wall_s_timed": round(wall, 4), "ms_per_step_median": round(float(np.median(ms)), 4)},
+        "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(),
+                     "kernel": "attn_fwd_dma_kernel<bf16, d=128, non-causal>, 512 workgroups of 512 threads",
+                     "mean_launch_ms": round(step_ms, 4)},
     }
     mb16, mf8 = measured_mfma_tflops()
     result["roofline"]["measured_mfma_peak"] = mb16
-    result["roofline"]["frac_of_measured_peak"] = round(ach / mb16, 4) if mb16 else None
-    if not args.no_detail:
-        result["detail"] = bench_detail(attn, max(10, args.steps // 2), 10)
-        if mf8 and "fp8_outlier" in result["detail"]:
-            fp8 = result["detail"]["fp8_outlier"]
+    result["roofline"]["frac_of_measured_peak"] = round(value / mb16, 4) if mb16 else None
+    if detail is not None:
+        if mf8 and "fp8_outlier" in detail:
+            fp8 = detail["fp8_outlier"]
             fp8["measured_mfma_peak"] = mf8
             fp8["frac_of_measured_peak"] = round(fp8["tflops"] / mf8, 4)
+        result["detail"] = detail
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     else:

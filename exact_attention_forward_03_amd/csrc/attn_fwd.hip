@@ -56,6 +56,8 @@
 //   every CU (one round of workgroups instead of two).  With an even number
 //   of heads the two tiles of a pair belong to heads h and h + heads/2, so
 //   the workgroups running at one time on an XCD share two heads' K/V.
+#include <atomic>
+
 #include "attn_device.h"
 #include "attn_params.h"
 
@@ -729,6 +731,26 @@ attn_fwd_dma_kernel(FwdParams p) {
   attn_fwd_body<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, KV>(p, w);
 }
 
+// Compute units of the current device, asked of the runtime once per device
+// (the launch decides on it for every dense non-causal call).
+hipError_t device_cu_count(int* cus) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // 0: not asked yet
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) cache[dev].store(*cus, std::memory_order_relaxed);
+  return e;
+}
+
 template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT,
           int KV>
 hipError_t launch_dma_one(const FwdParams& p, hipStream_t st) {
@@ -751,9 +773,8 @@ hipError_t launch_dma_one(const FwdParams& p, hipStream_t st) {
     const int64_t pairs = heads % 2 == 0 ? heads / 2 * p.tiles_per_head : heads * ((p.tiles_per_head + 1) / 2);
     bool pair = CAUSAL;
     if (!CAUSAL) {
-      int dev = 0, cus = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      int cus = 0;
+      const hipError_t e = device_cu_count(&cus);
       if (e != hipSuccess) return e;
       pair = pairs >= cus;
     }
