@@ -216,10 +216,11 @@ def _quantiser_allowance(q8, k8, v8, sq, sk, sv, scale, causal, tile=128):
     other neighbour (the emulation's ``ambiguity`` bound with a per-element
     delta); (b) l, an fp32 sum of the unrounded p, moves by the p-weighted
     mean of delta (plus 1e-5 for its fp32 additions), and O = sum P8 v / l
-    with it; (c) where the row max lies within dt of an integer, the kernel's
-    M may be the neighbouring integer: every code is then formed at half (or
-    twice) the emulation's value, which is exact for normal codes and moves a
-    code below 2^-4 by less than 2^-7.  Returns (the emulation's parts,
+    with it; (c) where the running max of a key tile lies within dt of an
+    integer, the kernel's running M may be the neighbouring integer from
+    there on: the codes are then formed at half (or twice) the emulation's
+    values, which is exact for normal codes and moves a code below 2^-4 (in
+    its tile's units) by less than 2^-7.  Returns (the emulation's parts,
     allowance [..., Nq, d], lse bound [..., Nq])."""
     ref = F.attention_fp8(q8, k8, v8, sq, sk, sv, scale, causal, parts=True)
     nq, nk = q8.shape[-2], k8.shape[-2]
@@ -235,13 +236,18 @@ def _quantiser_allowance(q8, k8, v8, sq, sk, sv, scale, causal, tile=128):
     with np.errstate(invalid="ignore", divide="ignore"):
         dl = np.where(l > 0, (p * delta).sum(-1) / np.where(l > 0, l, 1.0), 0.0) + 1e-5
     lchg = np.abs(ref["o"]) * (dl / (1.0 - dl))[..., None]
-    tmax = np.where(fin, t, -np.inf).max(-1)
+    # the running max of the 128-key tiles (before its ceiling): where one lies
+    # within dt of an integer, the kernel's running M may differ by one there
+    nkt = (nk + tile - 1) // tile
+    tpad = np.concatenate([np.where(fin, t, -np.inf), np.full(t.shape[:-1] + (nkt * tile - nk,), -np.inf)], -1)
+    run = np.maximum.accumulate(tpad.reshape(t.shape[:-1] + (nkt, tile)).max(-1), axis=-1)
     dmax = dt.max(-1)
-    near = np.abs(tmax - np.rint(tmax)) <= dmax
+    with np.errstate(invalid="ignore"):
+        near = np.any(np.abs(run - np.rint(run)) <= dmax[..., None], axis=-1)
     small = (ref["x"] < 2.0 ** -4) & fin
     with np.errstate(invalid="ignore", divide="ignore"):
         norm = np.where(l > 0, ref["sv_max"][..., None] * 2.0 ** -8 / np.where(l > 0, l, 1.0), 0.0)
-    m_amb = np.matmul(small * 2.0 ** -7, np.abs(ref["v_codes"])) * (norm * near)[..., None]
+    m_amb = np.matmul(small * 2.0 ** -7 * np.exp2(ref["shift"]), np.abs(ref["v_codes"])) * (norm * near)[..., None]
     lse_bound = np.log(2.0) * (dmax + dl)
     return ref, flip + lchg + m_amb + _pv_bound(ref), lse_bound
 
