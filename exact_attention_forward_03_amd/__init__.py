@@ -23,7 +23,8 @@ from typing import Optional
 
 __all__ = [
     "ATTN_DT_F16", "ATTN_DT_BF16", "ATTN_DT_FP8_E4M3", "ATTN_DT_F32", "ATTN_DT_INT8",
-    "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP",
+    "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP", "ATTN_ERR_TOO_LARGE",
+    "ATTN_NOALLOC_SCRATCH_BYTES", "attn_fwd_splitkv_noalloc", "forward_splitkv_noalloc",
     "load", "lib_path", "attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_fp8_quantize",
     "attn_fwd_paged", "attn_bwd", "attn_strerror", "attn_fp8_quantize_varlen", "forward", "forward_splitkv",
     "forward_paged", "merge", "backward", "fp8_quantize", "fp8_quantize_varlen",
@@ -31,10 +32,11 @@ __all__ = [
 ]
 
 ATTN_DT_F16, ATTN_DT_BF16, ATTN_DT_FP8_E4M3, ATTN_DT_F32, ATTN_DT_INT8 = 0, 1, 2, 3, 4
-ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_TOO_LARGE = 0, -1, -2, -3, -4
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20  # the fixed device scratch of attn_fwd_splitkv_noalloc (include/attn.h)
 
-EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_fwd_paged", "attn_merge", "attn_bwd",
-           "attn_fp8_quantize", "attn_fp8_quantize_varlen", "attn_strerror")
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_fwd_paged",
+           "attn_merge", "attn_bwd", "attn_fp8_quantize", "attn_fp8_quantize_varlen", "attn_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -63,6 +65,8 @@ def load():
         lib.attn_fwd_stream.restype = _i
         lib.attn_fwd_splitkv.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p, _p, _p]
         lib.attn_fwd_splitkv.restype = _i
+        lib.attn_fwd_splitkv_noalloc.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p]
+        lib.attn_fwd_splitkv_noalloc.restype = _i
         lib.attn_merge.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]
         lib.attn_merge.restype = _i
         lib.attn_fwd_paged.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i,
@@ -98,6 +102,12 @@ def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num
                      hip_stream) -> int:
     return load().attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num_splits, o_part,
                                    lse_part, hip_stream)
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num_splits,
+                             hip_stream) -> int:
+    return load().attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num_splits,
+                                           hip_stream)
 
 
 def attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, o_dtype, hip_stream) -> int:
@@ -260,6 +270,39 @@ def forward_splitkv(q, k, v, *, causal: bool = False, scale: Optional[float] = N
     rc = attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
                           int(bool(causal)), dt, int(num_splits), _ptr(o_part), _ptr(lse_part),
                           _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def forward_splitkv_noalloc(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
+                            num_splits: Optional[int] = None, out=None, lse=None):
+    """``forward_splitkv`` through ``attn_fwd_splitkv_noalloc``: the per-chunk
+    partials go to the library's fixed device scratch, so with ``out`` and
+    ``lse`` given nothing is allocated.  Raises if the call exceeds the
+    scratch (ATTN_ERR_TOO_LARGE)."""
+    import torch
+
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        num_splits = default_splits(B, H, Nq, Nk, target_workgroups=2 * cus)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    rc = attn_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                                  int(bool(causal)), dt, int(num_splits), _stream(q.device))
     _check(rc)
     return out, lse
 

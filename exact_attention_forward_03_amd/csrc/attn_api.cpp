@@ -45,6 +45,25 @@ int validate_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 }  // namespace
 
+namespace attn {
+
+int validate_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                     int d, float scale, int causal, int dtype, int num_splits, const float* o_part,
+                     const float* lse_part) {
+  // fp8 is not offered here: validate the rest as for bf16, then refuse it
+  const int vdt = dtype == ATTN_DT_FP8_E4M3 ? ATTN_DT_BF16 : dtype;
+  const int rc = validate_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, nullptr, nullptr, vdt, nullptr,
+                              nullptr, nullptr);
+  if (rc != ATTN_OK) return rc;
+  if (num_splits < 1 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
+  if (Nq > 0 && (!o_part || !lse_part)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(o_part, 16) || !aligned(lse_part, 4)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+}  // namespace attn
+
 extern "C" {
 
 const char* attn_strerror(int code) {
@@ -53,6 +72,9 @@ const char* attn_strerror(int code) {
     case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
     case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: unsupported configuration";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: HIP runtime error";
+    case ATTN_ERR_TOO_LARGE:
+      return "ATTN_ERR_TOO_LARGE: the call's partial outputs exceed the fixed device scratch "
+             "(ATTN_NOALLOC_SCRATCH_BYTES) of attn_fwd_splitkv_noalloc";
     default: return "unknown attn error code";
   }
 }
@@ -126,15 +148,9 @@ int attn_merge(const float* o_part, const float* lse_part, int num_splits, int B
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
                      int d, float scale, int causal, int dtype, int num_splits, float* o_part, float* lse_part,
                      void* hip_stream) {
-  // fp8 is not offered here: validate the rest as for bf16, then refuse it
-  const int vdt = dtype == ATTN_DT_FP8_E4M3 ? ATTN_DT_BF16 : dtype;
-  const int rc = validate_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, nullptr, nullptr, vdt, nullptr,
-                              nullptr, nullptr);
+  const int rc = attn::validate_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num_splits, o_part,
+                                        lse_part);
   if (rc != ATTN_OK) return rc;
-  if (num_splits < 1 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
-  if (Nq > 0 && (!o_part || !lse_part)) return ATTN_ERR_INVALID_ARG;
-  if (!aligned(o_part, 16) || !aligned(lse_part, 4)) return ATTN_ERR_INVALID_ARG;
-  if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16) return ATTN_ERR_UNSUPPORTED;
   if (Nq == 0) return ATTN_OK;
   const int br = attn::fwd_split_block_rows(dtype, d, causal != 0);
   const int64_t tiles = ((int64_t)Nq + br - 1) / br;

@@ -89,6 +89,11 @@ int bwd_key_block(int d);    // keys per dK/dV workgroup
 int bwd_query_block(int d);  // queries per dQ workgroup
 hipError_t launch_bwd(int dtype, int d, bool causal, bool varlen, BwdParams p, hipStream_t st);
 
+// Argument checks of attn_fwd_splitkv (host only): ATTN_OK or an error code.
+int validate_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                     int d, float scale, int causal, int dtype, int num_splits, const float* o_part,
+                     const float* lse_part);
+
 int fwd_block_rows(int dtype, int d, bool causal, bool varlen);
 int fwd_split_block_rows(int dtype, int d, bool causal);  // key-chunk launches
 int fwd_split_tile_keys(int d);  // key rows per tile of key-chunk launches (chunk lengths are multiples)

@@ -52,7 +52,8 @@ enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad flag, bad scale */
   ATTN_ERR_UNSUPPORTED = -2, /* valid request this build does not implement (e.g. d = 96) */
-  ATTN_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
+  ATTN_ERR_HIP = -3,         /* the HIP runtime reported an error at launch */
+  ATTN_ERR_TOO_LARGE = -4    /* attn_fwd_splitkv_noalloc: the partial outputs exceed its fixed scratch */
 };
 
 /*
@@ -181,6 +182,29 @@ int attn_fp8_quantize_varlen(const void* x, int x_dtype, void* x_fp8, float* x_s
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
                      int num_splits, float* o_part, float* lse_part, void* hip_stream);
+
+/*
+ * attn_fwd_splitkv_noalloc — attn_fwd_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without o_part and
+ * lse_part, the same result (the same kernels and key chunks).  The
+ * partial outputs go to a fixed device array inside the library,
+ * ATTN_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs on
+ * holds until the process ends; the call itself allocates nothing (its first
+ * call on a device looks the array's address up once).
+ *
+ *   Needs num_splits * B * H * Nq * (d + 1) * 4 bytes (the O parts rounded
+ *   up to 256 bytes) <= ATTN_NOALLOC_SCRATCH_BYTES, else ATTN_ERR_TOO_LARGE
+ *   (nothing is launched).  Other errors as attn_fwd_splitkv.
+ *   Every call on one GPU uses the same array: calls that overlap in time on
+ *   one GPU (two streams, two host threads) race and give wrong results;
+ *   calls on one stream are ordered and safe.  Nothing in the array needs
+ *   to be cleared between calls (every entry read is written first).
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                             int num_splits, void* hip_stream);
 
 /*
  * attn_merge — combine results over disjoint key chunks (the online-softmax

@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_strerror(lib):
     assert attn.attn_strerror(attn.ATTN_OK) == "ATTN_OK"
-    for code in (attn.ATTN_ERR_INVALID_ARG, attn.ATTN_ERR_UNSUPPORTED, attn.ATTN_ERR_HIP):
+    for code in (attn.ATTN_ERR_INVALID_ARG, attn.ATTN_ERR_UNSUPPORTED, attn.ATTN_ERR_HIP, attn.ATTN_ERR_TOO_LARGE):
         assert "ATTN_ERR" in attn.attn_strerror(code)
     assert "unknown" in attn.attn_strerror(12345)
 
@@ -191,6 +191,40 @@ def test_splitkv_unsupported_and_empty(lib):
     assert split_call(dtype=attn.ATTN_DT_FP8_E4M3) == attn.ATTN_ERR_UNSUPPORTED
     assert split_call(Nq=0) == attn.ATTN_OK
     assert split_call(Nq=0, q=None, o=None, lse=None, o_part=None, lse_part=None) == attn.ATTN_OK
+
+
+def noalloc_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=1, Nk=4096, d=128, scale=0.125, causal=0,
+             dtype=attn.ATTN_DT_BF16, num_splits=8)
+    a.update(over)
+    return attn.attn_fwd_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                                         a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["num_splits"], None)
+
+
+NOALLOC_INVALID = [o for o in SPLIT_INVALID if "o_part" not in o and "lse_part" not in o]
+
+
+@pytest.mark.parametrize("over", NOALLOC_INVALID, ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_splitkv_noalloc_invalid(lib, over):
+    assert noalloc_call(**over) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_splitkv_noalloc_limits(lib):
+    """The fixed scratch holds num_splits * B * H * Nq rows of d + 1 fp32
+    values (O parts rounded up to 256 bytes): calls past it return
+    ATTN_ERR_TOO_LARGE before any HIP call (none of these reaches the
+    device), as do sizes whose product would overflow."""
+    cap = attn.ATTN_NOALLOC_SCRATCH_BYTES
+    assert cap == 32 << 20
+    rows_max = cap // (129 * 4)  # d = 128, ignoring the 256-byte rounding
+    assert noalloc_call(B=1, H=1, Nq=rows_max + 1, num_splits=1) == attn.ATTN_ERR_TOO_LARGE
+    assert noalloc_call(B=64, H=64, Nq=64, num_splits=8) == attn.ATTN_ERR_TOO_LARGE
+    assert noalloc_call(B=2 ** 20, H=2 ** 9, Nq=2 ** 30, num_splits=1024) == attn.ATTN_ERR_TOO_LARGE
+    assert noalloc_call(d=96) == attn.ATTN_ERR_UNSUPPORTED
+    assert noalloc_call(dtype=attn.ATTN_DT_FP8_E4M3) == attn.ATTN_ERR_UNSUPPORTED
+    assert noalloc_call(Nq=0) == attn.ATTN_OK
+    assert noalloc_call(Nq=0, q=None, o=None, lse=None) == attn.ATTN_OK
+    assert "scratch" in attn.attn_strerror(attn.ATTN_ERR_TOO_LARGE)
 
 
 def merge_call(**over):
