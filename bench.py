@@ -38,6 +38,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["exact_attention_forward_03_amd/csrc/attn_fwd.hip",
+                  "exact_attention_forward_03_amd/csrc/attn_tile.h",
                   "exact_attention_forward_03_amd/csrc/attn_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_d128_n8192_traffic.json")
 HEADLINE = "n8k_bf16"  # B2 H16 Nq=Nk=8192 d128 bf16 non-causal
@@ -104,18 +105,21 @@ def cpu_baseline(sample_heads: int = 8, chunk_heads: int = 2):
 
 
 def measured_mfma_tflops():
-    """Dense MFMA rate measured by the probe library on this GPU: (bf16, fp8)
-    TFLOP/s, or (None, None) if the probe is not built."""
+    """Dense MFMA rates measured by the probe library on this GPU, TFLOP/s:
+    (bf16, fp8) on constant operands and (bf16, fp8) on random operand bits
+    (the chip lowers its clock under the power of switching bits, so the
+    second pair is what real data can reach); Nones if the probe is not
+    built."""
     import ctypes
 
     path = os.path.join(ROOT, "exact_attention_forward_03_amd", "libattn_probe.so")
     if not os.path.exists(path):
-        return None, None
+        return None, None, None, None
     lib = ctypes.CDLL(path)
     lib.attn_probe_mfma_tflops.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
     lib.attn_probe_mfma_tflops.restype = ctypes.c_int
     out = []
-    for kind in (0, 1):
+    for kind in (0, 1, 2, 3):
         v = ctypes.c_double(0.0)
         rc = lib.attn_probe_mfma_tflops(kind, ctypes.byref(v), None)
         out.append(round(v.value, 1) if rc == 0 else None)
@@ -513,14 +517,18 @@ def main():
                      "kernel": "attn_fwd_dma_kernel<bf16, d=128, non-causal>, 512 workgroups of 512 threads",
                      "mean_launch_ms": round(step_ms, 4)},
     }
-    mb16, mf8 = measured_mfma_tflops()
+    mb16, mf8, rb16, rf8 = measured_mfma_tflops()
     result["roofline"]["measured_mfma_peak"] = mb16
     result["roofline"]["frac_of_measured_peak"] = round(value / mb16, 4) if mb16 else None
+    result["roofline"]["measured_mfma_peak_random_operands"] = rb16
+    result["roofline"]["frac_of_measured_peak_random_operands"] = round(value / rb16, 4) if rb16 else None
     if detail is not None:
         if mf8 and "fp8_outlier" in detail:
             fp8 = detail["fp8_outlier"]
             fp8["measured_mfma_peak"] = mf8
             fp8["frac_of_measured_peak"] = round(fp8["tflops"] / mf8, 4)
+            fp8["measured_mfma_peak_random_operands"] = rf8
+            fp8["frac_of_measured_peak_random_operands"] = round(fp8["tflops"] / rf8, 4) if rf8 else None
         result["detail"] = detail
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()

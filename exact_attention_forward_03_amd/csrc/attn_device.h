@@ -104,6 +104,30 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 // swizzle, no stride; num_records counts bytes.
 constexpr int kBufferFlags = 0x00020000;
 
+// A wave-uniform int32 read through the scalar data cache (s_load): it does
+// not count against the vector-memory counter that paces the tile loads.
+__device__ __forceinline__ int load_uniform(const int32_t* ptr, int64_t idx) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(idx & 0xffffffff));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(idx >> 32));
+  const int64_t i = ((int64_t)hi << 32) | (uint32_t)lo;
+  return ((const __attribute__((address_space(4))) int32_t*)ptr)[i];
+}
+__device__ __forceinline__ float load_uniform(const float* ptr, int64_t idx) {
+  return __builtin_bit_cast(float, load_uniform((const int32_t*)ptr, idx));
+}
+
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// f(kw, vw, kr, vr) with four LDS ring buffers passed as restrict pointers;
+// the caller guarantees that they do not overlap.  A step that fills two
+// buffers with direct-to-LDS loads (kw, vw) and reads two others (kr, vr)
+// runs its body through this, so that the compiler knows the reads do not
+// depend on those loads and does not wait for them before the first read.
+template <typename F>
+__device__ __forceinline__ void with_disjoint(uint8_t* __restrict__ kw, uint8_t* __restrict__ vw,
+                                              const uint8_t* __restrict__ kr, const uint8_t* __restrict__ vr, F&& f) {
+  f(kw, vw, kr, vr);
+}
+
 
 }  // namespace attn

@@ -60,56 +60,12 @@
 
 #include "attn_device.h"
 #include "attn_params.h"
+#include "attn_tile.h"
 
 namespace attn {
 namespace {
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-constexpr float kSplitBelowP = 8.0f;
-// Slack of the reference max M: a row's scores may exceed M by up to
-// kLazyBits (p = 2^(t - M) <= 2^kLazyBits) before the wave rescales O and l.
-// O and lse do not depend on M (up to rounding); on N(0,1) scores this takes
-// a wave's rescales from about every second key tile to almost none.
-constexpr float kLazyBits = 4.0f;
-
-// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maximum).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-template <int D, int NQB, int BC, int NW, int NS>
-struct PipeCfg {
-  static constexpr int QW = NQB * 32;        // query rows per wave
-  static constexpr int BR = NW * QW;         // query rows per workgroup
-  static constexpr int NT = NW * 64;
-  static constexpr int ROWB = D * 2;         // bytes per K/V row in LDS (unpadded)
-  static constexpr int CHUNKS = ROWB / 16;   // 16-byte chunks per row
-  static constexpr int TILEB = BC * ROWB;    // bytes per K or V tile
-  static constexpr int KS = D / 16;          // MFMA k-steps of S^T
-  static constexpr int MB = BC / 32;         // 32-key blocks per tile
-  static constexpr int DB = D / 32;          // 32-row blocks of O^T
-  static constexpr int LOADS = TILEB / 1024; // 1 KiB direct-to-LDS loads per tile
-  static constexpr int LDS_BYTES = 2 * NS * TILEB;  // K and V rings of NS slots
-  static constexpr int LPT = 2 * LOADS / NW;  // load instructions per wave per tile (K and V)
-  static_assert(LOADS % NW == 0, "each wave issues the same number of tile loads");
-  static_assert(CHUNKS >= 8, "row swizzle needs at least 8 chunks");
-};
-
-// Physical 16-byte chunk of logical chunk `ch` in K row `r`: all 16 rows of
-// an aligned group land on different chunks (K fragment reads: 16 lanes,
-// 16 rows, same logical chunk).
-template <int CHUNKS>
-__device__ __forceinline__ int k_chunk(int r, int ch) { return ch ^ (r & (CHUNKS >= 16 ? 15 : 7)); }
-// V rows: a transposing read of 32 lanes covers 4 consecutive rows x 4
-// neighbouring chunks (two 16-lane groups, 2 chunks each); XOR-ing with
-// (row & 3) << 2 puts them on 16 different chunks.  Rows of 8 chunks (d = 64)
-// use (row & 3) << 1.
-template <int CHUNKS>
-__device__ __forceinline__ int v_chunk(int r, int ch) { return ch ^ ((r & 3) << (CHUNKS >= 16 ? 2 : 1)); }
+using namespace tile;
 
 // Loop options (bit flags).  kOptPin: the LDS fragment reads are pinned
 // kPreD MFMAs ahead of their use by scheduling barriers (left alone, the
@@ -124,15 +80,6 @@ constexpr int kOptPin = 1, kOptPrio = 2;
 // at d = 128 (4-wave workgroups); -10 % for dense d = 128 launches, whose
 // loads need the whole step to land; no change for key-chunk launches.
 constexpr int kOptLateLoad = 16;
-
-// A wave-uniform int32 read through the scalar data cache (s_load): it does
-// not count against the vector-memory counter that paces the tile loads.
-__device__ __forceinline__ int load_uniform(const int32_t* ptr, int64_t idx) {
-  const int lo = __builtin_amdgcn_readfirstlane((int)(idx & 0xffffffff));
-  const int hi = __builtin_amdgcn_readfirstlane((int)(idx >> 32));
-  const int64_t i = ((int64_t)hi << 32) | (uint32_t)lo;
-  return ((const __attribute__((address_space(4))) int32_t*)ptr)[i];
-}
 
 // SPLIT: the keys of each head are cut into p.n_split chunks of p.split_len
 // rows; a work item is (head, chunk, query tile) and writes the chunk's
@@ -188,52 +135,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
   using C = PipeCfg<D, NQB, BC, NW, NS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  // ---- work item -> (head[, key chunk], query tile) --------------------------
-  const int hs = work / p.tiles_per_head;  // head, or head * n_split + chunk
-  const int t = work - hs * p.tiles_per_head;
-  const int head = SPLIT ? hs / p.n_split : hs;
-  const int split = SPLIT ? hs - head * p.n_split : 0;
-  int64_t q_row0, k_row0;
-  int q_len, k_len, qt;
-  int k_off = 0;  // absolute index of the first key of the range this item sees
-  if constexpr (!VARLEN) {
-    q_len = p.Nq;
-    q_row0 = (int64_t)head * p.Nq;
-    if constexpr (SPLIT) {
-      int64_t nk = p.Nk;
-      if constexpr (PAGED)
-        nk = min(max(load_uniform(p.seqlens_k, head / p.H), 0), p.max_pages * p.page_size);
-      const int64_t kb = min((int64_t)split * p.split_len, nk);
-      const int64_t ke = min(kb + p.split_len, nk);
-      k_off = (int)kb;
-      k_len = (int)(ke - kb);
-    } else {
-      k_len = p.Nk;
-    }
-    k_row0 = PAGED ? 0 : (int64_t)head * p.Nk + k_off;
-    qt = CAUSAL ? (p.tiles_per_head - 1 - t) : t;
-  } else {
-    int acc = 0, seq = -1, qb = 0, qe = 0, nts = 0;
-    for (int s = 0; s < p.B; ++s) {
-      const int a = min(max(p.cu_q[s], 0), p.Nq);
-      const int b = min(max(p.cu_q[s + 1], a), p.Nq);
-      const int nt = (b - a + C::BR - 1) / C::BR;
-      if (t < acc + nt) {
-        seq = s; qb = a; qe = b; nts = nt;
-        break;
-      }
-      acc += nt;
-    }
-    if (seq < 0) return;
-    const int lt = t - acc;
-    qt = CAUSAL ? (nts - 1 - lt) : lt;
-    const int kb = min(max(p.cu_k[seq], 0), p.Nk);
-    const int ke = min(max(p.cu_k[seq + 1], kb), p.Nk);
-    q_len = qe - qb;
-    k_len = ke - kb;
-    q_row0 = (int64_t)head * p.Nq + qb;
-    k_row0 = (int64_t)head * p.Nk + kb;
-  }
+  WorkItem wi;
+  if (!decode_work<C::BR, CAUSAL, VARLEN, SPLIT, PAGED>(p, work, wi)) return;
+  const int64_t q_row0 = wi.q_row0, k_row0 = wi.k_row0;
+  const int q_len = wi.q_len, k_len = wi.k_len, qt = wi.qt, k_off = wi.k_off, head = wi.head, split = wi.split;
   const int q0 = qt * C::BR;
   const uint16_t* __restrict__ Qp = (const uint16_t*)p.q + q_row0 * D;
   const uint8_t* __restrict__ Kb = (const uint8_t*)p.k + k_row0 * D * 2;
@@ -289,41 +194,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
     const int pg = min(max(load_uniform(p.block_table, (int64_t)b * p.max_pages + j), 0), p.num_pages - 1);
     return ((int64_t)pg * p.page_size + (ka0 - j * p.page_size)) * p.H + h;
   };
-  // Dense K or V tile: the wave's i-th load fills 1 KiB block i * NW + wv.
-  // The rows come through a buffer resource based at the tile's first key,
-  // so the per-lane byte offset (row within the block, swizzled chunk) is the
-  // same for every tile and the block offset is a wave-uniform scalar: a full
-  // tile costs no vector instructions.  The resource covers only the tile's
-  // keys; the last tile, when it runs past them, clamps its rows per lane to
-  // the last key, so no read goes out of range.
   auto dense_load = [&](const uint8_t* base, uint8_t* ring, int kt, int buf, bool is_v) {
-    auto chunk = [&](int r, int ch) { return is_v ? v_chunk<C::CHUNKS>(r, ch) : k_chunk<C::CHUNKS>(r, ch); };
-    const int rows = min(BC, k_len - kt * BC);  // >= 1: only tiles holding keys are loaded
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(base + (int64_t)kt * BC * C::ROWB), 0, rows * C::ROWB, kBufferFlags);
-    if (rows == BC) {
-#pragma unroll
-      for (int i = 0; i < C::LOADS / NW; ++i) {
-        const int blk = i * NW + wv;
-        // the swizzles read the row mod 16, which is the same for every i
-        // when a round of NW blocks spans a multiple of 16 rows
-        const int r = (NW * RPB) % 16 == 0 ? wv * RPB + lane / C::CHUNKS : blk * RPB + lane / C::CHUNKS;
-        const uint32_t voff = (uint32_t)((lane / C::CHUNKS) * C::ROWB + chunk(r, lane % C::CHUNKS) * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(ring + buf * C::TILEB + blk * 1024), 16, voff,
-                                                 (uint32_t)(blk * 1024), 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::LOADS / NW; ++i) {
-        const int blk = i * NW + wv;
-        const int r = blk * RPB + lane / C::CHUNKS;
-        const uint32_t voff = (uint32_t)(min(r, rows - 1) * C::ROWB + chunk(r, lane % C::CHUNKS) * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(ring + buf * C::TILEB + blk * 1024), 16, voff,
-                                                 0, 0, 0);
-      }
-    }
+    dense_tile_load<C, BC, NW>(base, ring, kt, buf, is_v, k_len, wv, lane);
   };
-  auto load_k = [&](int kt, int buf) {
+  auto load_k = [&](int kt, uint8_t* dst) {
     if constexpr (PAGED) {
       const uint8_t* base = (const uint8_t*)p.k + paged_row(kt) * C::ROWB;
 #pragma unroll
@@ -332,13 +206,13 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
         const int r = blk * RPB + lane / C::CHUNKS;
         const int rr = min(r, k_len - 1 - kt * BC);
         const uint8_t* src = base + (int64_t)rr * p.H * C::ROWB + k_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsK + buf * C::TILEB + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + blk * 1024), 16, 0, 0);
       }
     } else {
-      dense_load(Kb, ldsK, kt, buf, false);
+      dense_load(Kb, dst, kt, 0, false);
     }
   };
-  auto load_v = [&](int kt, int buf) {
+  auto load_v = [&](int kt, uint8_t* dst) {
     if constexpr (PAGED) {
       const uint8_t* base = (const uint8_t*)p.v + paged_row(kt) * C::ROWB;
 #pragma unroll
@@ -347,10 +221,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
         const int r = blk * RPB + lane / C::CHUNKS;
         const int rr = min(r, k_len - 1 - kt * BC);
         const uint8_t* src = base + (int64_t)rr * p.H * C::ROWB + v_chunk<C::CHUNKS>(r, lane % C::CHUNKS) * 16;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(ldsV + buf * C::TILEB + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + blk * 1024), 16, 0, 0);
       }
     } else {
-      dense_load(Vb, ldsV, kt, buf, true);
+      dense_load(Vb, dst, kt, 0, true);
     }
   };
 
@@ -426,8 +300,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
     for (int db = 0; db < C::DB; ++db) oacc[nb][db] = f32x16_t{};
 
   // S^T for the key tile in K buffer kbuf; fragments read kPreD MFMAs ahead
-  auto compute_s = [&](int kbuf, f32x16_t (&s)[NQB][C::MB]) {
-    const uint8_t* kb = ldsK + kbuf * C::TILEB;
+  auto compute_s = [&](const uint8_t* kb, f32x16_t (&s)[NQB][C::MB]) {
     constexpr int N = C::MB * C::KS;
     // step i: key block i % MB (alternating accumulators), k-step i / MB
     auto frag = [&](int i) {
@@ -530,8 +403,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
   // O^T += V^T P^T for the tile in V buffer vbuf; the V^T fragment of
   // (db, 16-key step) comes from two transposing reads (keys 4h.. and
   // 8+4h..), read kPreD MFMAs ahead.
-  auto pv_pass = [&](int vbuf, const uint4 (&pp)[NQB][C::MB][2]) {
-    const uint8_t* vb = ldsV + vbuf * C::TILEB;
+  auto pv_pass = [&](const uint8_t* vb, const uint4 (&pp)[NQB][C::MB][2]) {
     const int g = (lane >> 4) & 1, s4 = lane & 15;
     constexpr int N = C::DB * 2 * C::MB;
     // step i: output block i % DB (alternating accumulators), 16-key step i / DB
@@ -579,8 +451,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
       }
   };
 
-  // Softmax and second product of tile kt held in s (its K/V ring slot `slot`).
-  auto softmax_pv = [&](int kt, int slot, f32x16_t (&s)[NQB][C::MB]) {
+  // Softmax and second product of tile kt held in s (its K/V ring slot
+  // `slot`, V tile at vb).
+  auto softmax_pv = [&](int kt, int slot, const uint8_t* vb, f32x16_t (&s)[NQB][C::MB]) {
     float m_use[NQB];
     bool masked = false;
     uint4 pf[NQB][C::MB][2];
@@ -593,8 +466,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
     // there and only the two packed copies stay live through the MFMAs
     uint4 pl[NQB][C::MB][2];
     if (split) residual(s, pf, pl);
-    pv_pass(slot, pf);
-    if (split) pv_pass(slot, pl);
+    pv_pass(vb, pf);
+    if (split) pv_pass(vb, pl);
   };
 
   if constexpr (KVQ) {
@@ -615,9 +488,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
       }
       if (kt < wave_kt) {
         f32x16_t s[NQB][C::MB];
-        compute_s(slot, s);
+        compute_s(ldsK + slot * C::TILEB, s);
         scale_by(ldsS + slot * 2 * BC, s);
-        softmax_pv(kt, slot, s);
+        softmax_pv(kt, slot, ldsV + slot * C::TILEB, s);
       }
       slot = nxt;
     }
@@ -626,8 +499,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
     if (!KVQ && j < n_kt) {
-      load_k(j, j);
-      load_v(j, j);
+      load_k(j, ldsK + j * C::TILEB);
+      load_v(j, ldsV + j * C::TILEB);
     }
   int slot = 0;  // ring slot of tile kt
   for (int kt = 0; kt < (KVQ ? 0 : n_kt); ++kt) {
@@ -637,19 +510,28 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
     else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // refill the slot tile kt-1 used (every wave is past it now), before
-    // or after this step's S chain
+    // or after this step's S chain.  The slot filled and the slot read are
+    // different, passed as restrict pointers: the compiler then knows the
+    // reads do not depend on the direct-to-LDS loads just issued and does not
+    // wait for them (it would otherwise wait for every outstanding load before
+    // the first LDS read, leaving the tile no time to arrive).  The explicit
+    // vmcnt wait and barrier above order the reads after the loads of earlier
+    // steps.
     const int fs = (slot == 0) ? NS - 1 : slot - 1;
-    if (!LATE && kt + NS - 1 < n_kt) {
-      load_k(kt + NS - 1, fs);
-      load_v(kt + NS - 1, fs);
-    }
-    f32x16_t s[NQB][C::MB];
-    if (kt < wave_kt) compute_s(slot, s);
-    if (LATE && kt + NS - 1 < n_kt) {
-      load_k(kt + NS - 1, fs);
-      load_v(kt + NS - 1, fs);
-    }
-    if (kt < wave_kt) softmax_pv(kt, slot, s);
+    with_disjoint(ldsK + fs * C::TILEB, ldsV + fs * C::TILEB, ldsK + slot * C::TILEB, ldsV + slot * C::TILEB,
+                  [&](uint8_t* kw, uint8_t* vw, const uint8_t* kr, const uint8_t* vr) __attribute__((always_inline)) {
+      if (!LATE && kt + NS - 1 < n_kt) {
+        load_k(kt + NS - 1, kw);
+        load_v(kt + NS - 1, vw);
+      }
+      f32x16_t s[NQB][C::MB];
+      if (kt < wave_kt) compute_s(kr, s);
+      if (LATE && kt + NS - 1 < n_kt) {
+        load_k(kt + NS - 1, kw);
+        load_v(kt + NS - 1, vw);
+      }
+      if (kt < wave_kt) softmax_pv(kt, slot, vr, s);
+    });
     slot = (slot + 1 == NS) ? 0 : slot + 1;
   }
 
@@ -689,66 +571,17 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, const int work
   }
 }
 
-// The kernel: one work item, or for dense launches with p.pair_tiles two
-// query tiles one after the other; p.n_work counts pairs then.  With an even
-// number of heads the pair is tile t of head h and the partner tile of head
-// h + heads/2; otherwise it is tiles t and T-1-t of one head (with an odd
-// tile count the middle tile runs alone).  The partner of a causal tile t is
-// T-1-t (qt = T-1-t in the body's heaviest-first numbering is tile t, and
-// the other way round), so every workgroup does the same work; causal
-// launches always pair.  Non-causal launches pair when the pairs still
-// cover every CU: one round of workgroups instead of two, which takes the
-// tail of the second round off (N=4096, d=128: 316 -> 305 us).
+// The kernel: one work item, or (dense launches with p.pair_tiles) a pair of
+// query tiles one after the other (run_items).
 template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT,
           int KV>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_dma_kernel(FwdParams p) {
   const int w = xcd_remap(blockIdx.x, p.n_work);
-  if constexpr (!VARLEN && !SPLIT && KV == kKvDense) {
-    if (CAUSAL || p.pair_tiles) {
-      const int T = p.tiles_per_head, heads = p.B * p.H;
-      if (heads % 2 == 0) {
-        // tile t of head h, then the partner tile of head h + heads/2: the
-        // workgroups that run at one time on an XCD share two heads' K/V in
-        // its L2 (as unpaired launches do), not four
-        const int h = w / T, t = w - h * T;
-        attn_fwd_body<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, KV>(p, h * T + t);
-        __syncthreads();
-        attn_fwd_body<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, KV>(
-            p, (h + heads / 2) * T + (CAUSAL ? T - 1 - t : t));
-      } else {
-        const int half = (T + 1) / 2;
-        const int head = w / half, t = w - head * half;
-        attn_fwd_body<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, KV>(p, head * T + t);
-        if (T - 1 - t != t) {
-          __syncthreads();
-          attn_fwd_body<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, KV>(p, head * T + (T - 1 - t));
-        }
-      }
-      return;
-    }
-  }
-  attn_fwd_body<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, KV>(p, w);
-}
-
-// Compute units of the current device, asked of the runtime once per device
-// (the launch decides on it for every dense non-causal call).
-hipError_t device_cu_count(int* cus) {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cache[kMaxDevices];  // 0: not asked yet
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDevices) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) {
-      *cus = c;
-      return hipSuccess;
-    }
-  }
-  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) cache[dev].store(*cus, std::memory_order_relaxed);
-  return e;
+  constexpr bool kPairs = !VARLEN && !SPLIT && KV == kKvDense;
+  run_items<kPairs, CAUSAL>(p, w, [&](int item) __attribute__((always_inline)) {
+    attn_fwd_body<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, KV>(p, item);
+  });
 }
 
 template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT,
@@ -765,23 +598,11 @@ hipError_t launch_dma_one(const FwdParams& p, hipStream_t st) {
     attr_set = true;
   }
   FwdParams pp = p;
-  pp.pair_tiles = 0;
   if constexpr (!VARLEN && !SPLIT && KV == kKvDense) {
-    // pairs across heads (h, h + heads/2) when the head count is even, else
-    // within a head (t, T-1-t); the kernel decodes the same way
-    const int64_t heads = p.n_work / p.tiles_per_head;
-    const int64_t pairs = heads % 2 == 0 ? heads / 2 * p.tiles_per_head : heads * ((p.tiles_per_head + 1) / 2);
-    bool pair = CAUSAL;
-    if (!CAUSAL) {
-      int cus = 0;
-      const hipError_t e = device_cu_count(&cus);
-      if (e != hipSuccess) return e;
-      pair = pairs >= cus;
-    }
-    if (pair) {
-      pp.pair_tiles = 1;
-      pp.n_work = (int)pairs;
-    }
+    const hipError_t e = plan_pairs(pp, CAUSAL);
+    if (e != hipSuccess) return e;
+  } else {
+    pp.pair_tiles = 0;
   }
   if (pp.n_work == 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3(pp.n_work), dim3(NW * 64), lds_bytes, st, pp);
@@ -860,6 +681,26 @@ hipError_t launch_dma_t(int d, bool causal, bool varlen, bool split, int kv, con
 }
 
 }  // namespace
+
+// Compute units of the current device, asked of the runtime once per device
+// (the launch decides on it for every dense non-causal call).
+hipError_t tile::device_cu_count(int* cus) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // 0: not asked yet
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) cache[dev].store(*cus, std::memory_order_relaxed);
+  return e;
+}
 
 int fwd_split_block_rows(int dtype, int d, bool causal) {
   if (d == 128) return 32 * SplitTile128::NW;

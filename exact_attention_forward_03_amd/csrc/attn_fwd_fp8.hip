@@ -183,7 +183,7 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   // the tile's keys; a last tile that runs past them re-reads the last key
   // (finite codes, masked) through per-lane clamped offsets.
   static_assert((NW * 8) % 16 == 0, "block rounds span whole swizzle periods");
-  auto load_tile = [&](int kt, int buf) {
+  auto load_tile = [&](int kt, uint8_t* kdst, uint8_t* vdst) {
     const int rows = min(BC, k_len - kt * BC);  // >= 1: only tiles holding keys are loaded
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(Kp + (int64_t)kt * BC * kRowB), 0, rows * kRowB, kBufferFlags);
@@ -196,13 +196,13 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int blk = i * NW + wv;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(ldsK + buf * kTileB + blk * 1024), 16, offk,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + blk * 1024), 16, offk,
                                                  (uint32_t)(blk * 1024), 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int blk = i * NW + wv;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(ldsV + buf * kTileB + blk * 1024), 16, offv,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + blk * 1024), 16, offv,
                                                  (uint32_t)(blk * 1024), 0, 0);
       }
     } else {
@@ -211,21 +211,20 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
         const int blk = i * NW + wv;
         const int r = blk * 8 + (lane >> 3);
         const uint32_t off = (uint32_t)(min(r, rows - 1) * kRowB + k8_chunk(r, lane & 7) * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(ldsK + buf * kTileB + blk * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + blk * 1024), 16, off, 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int blk = i * NW + wv;
         const int r = blk * 8 + (lane >> 3);
         const uint32_t off = (uint32_t)(min(r, rows - 1) * kRowB + v8_chunk(r, lane & 7) * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(ldsV + buf * kTileB + blk * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + blk * 1024), 16, off, 0, 0, 0);
       }
     }
   };
 
   // S^T of the tile in slot kbuf: step i = (32-key block i % MB, k-step i / MB)
-  auto compute_s = [&](int kbuf, f32x16_t (&s)[MB]) {
-    const uint8_t* kb = ldsK + kbuf * kTileB;
+  auto compute_s = [&](const uint8_t* kb, f32x16_t (&s)[MB]) {
     constexpr int N = MB * KS;
     auto frag = [&](int i, uint4 (&f)[2]) {
       const int r = (i % MB) * 32 + c;
@@ -268,8 +267,7 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
     for (int db = 0; db < DB; ++db)
       vlane[db] = (uint32_t)(lr * kRowB + v8_chunk(lr, 2 * db + (G & 1)) * 16 + 8 * (s16 & 1));
   }
-  auto pv_pass = [&](int vbuf, const uint4 (&pp)[PG][2]) {
-    const uint8_t* vb = ldsV + vbuf * kTileB;
+  auto pv_pass = [&](const uint8_t* vb, const uint4 (&pp)[PG][2]) {
     constexpr int N = DB * PG;
     auto frag = [&](int i, uint4 (&f)[2]) {
       const int db = i % DB, g = i / DB;
@@ -305,7 +303,7 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   // prologue: tiles 0 .. NS-2 in flight (tile j in ring slot j % NS)
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < n_kt) load_tile(j, j);
+    if (j < n_kt) load_tile(j, ldsK + j * kTileB, ldsV + j * kTileB);
 
   int slot = 0;  // ring slot of tile kt
   for (int kt = 0; kt < n_kt; ++kt) {
@@ -314,101 +312,109 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
     __syncthreads();
     // refill the slot tile kt-1 used (every wave is past it now); a live
     // wave issues these loads after its S chain, which then starts at once
-    // after the barrier (+4-6 % measured over loads first)
+    // after the barrier (+4-6 % measured over loads first).  The slot filled
+    // and the slot read are different, passed as restrict pointers: the
+    // compiler then knows the reads do not depend on the direct-to-LDS loads
+    // just issued and does not wait for them (it would otherwise wait for
+    // every outstanding load before the next LDS read).  The explicit vmcnt
+    // wait and barrier above order the reads after the loads of earlier
+    // steps.
     const bool refill = kt + NS - 1 < n_kt;
     const int fs = slot == 0 ? NS - 1 : slot - 1;
-    if (kt >= wave_kt && refill) load_tile(kt + NS - 1, fs);
+    with_disjoint(ldsK + fs * kTileB, ldsV + fs * kTileB, ldsK + slot * kTileB, ldsV + slot * kTileB,
+                  [&](uint8_t* kw, uint8_t* vw, const uint8_t* kr, const uint8_t* vr) __attribute__((always_inline)) {
+      if (kt >= wave_kt && refill) load_tile(kt + NS - 1, kw, vw);
 
-    if (kt < wave_kt) {
-      const float cs = p.c * sq * sk[kt];
-      const float svt = sv[kt];
-      // log2 of 2^8 w: P codes are e4m3(2^(t - M) * 2^8 * s_v / max s_v).
-      // With 2^8 w <= 2^-11 every code of the tile is 0 (values <= 2^-10
-      // round to 0): the tile then skips the PV product, and its
-      // exponentials are taken with bias 8 so that l still gets its mass.
-      // That covers a V scale of 0 (bias -inf).
-      const float bias_w = 8.f + (svt > 0.f ? __log2f(svt) - lsv_max : -INFINITY);
-      const bool pv_zero = !(bias_w >= -11.f);
-      const float bias = pv_zero ? 8.f : bias_w;
+      if (kt < wave_kt) {
+        // the tile's scales through the scalar cache: a vector load here
+        // would make the compiler wait for the tile loads issued before it
+        const float cs = p.c * sq * load_uniform(sk, kt);
+        const float svt = load_uniform(sv, kt);
+        // log2 of 2^8 w: P codes are e4m3(2^(t - M) * 2^8 * s_v / max s_v).
+        // With 2^8 w <= 2^-11 every code of the tile is 0 (values <= 2^-10
+        // round to 0): the tile then skips the PV product, and its
+        // exponentials are taken with bias 8 so that l still gets its mass.
+        // That covers a V scale of 0 (bias -inf).
+        const float bias_w = 8.f + (svt > 0.f ? __log2f(svt) - lsv_max : -INFINITY);
+        const bool pv_zero = !(bias_w >= -11.f);
+        const float bias = pv_zero ? 8.f : bias_w;
 
-      f32x16_t s[MB];
-      compute_s(slot, s);
-      if (refill) load_tile(kt + NS - 1, fs);
+        f32x16_t s[MB];
+        compute_s(kr, s);
+        if (refill) load_tile(kt + NS - 1, kw, vw);
 
-      const int key0 = kt * BC;
-      const bool need_mask = (key0 + BC > k_len) || (CAUSAL && key0 + BC - 1 > qw0);
-      float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      if (need_mask) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            const bool ok = key < k_len && (!CAUSAL || key <= my_q);
-            s[mb][i] = ok ? s[mb][i] * cs : -INFINITY;
-            t4[i & 3] = fmaxf(t4[i & 3], s[mb][i]);
-          }
-      } else {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) t4[i & 3] = fmaxf(t4[i & 3], s[mb][i]);
-      }
-      float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
-      if (!need_mask) tmax *= cs;  // scales are >= 0
-      tmax = max_halves(tmax);
-      const float m_new = fmaxf(M, __builtin_ceilf(tmax));
-      if (__any(m_new > M)) {
-        const float alpha = (m_new == M) ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
-      M = m_new;
-      const float m_use = (M == -INFINITY) ? 0.f : M;
-      const float off = bias - m_use;
+        const int key0 = kt * BC;
+        const bool need_mask = (key0 + BC > k_len) || (CAUSAL && key0 + BC - 1 > qw0);
+        float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (need_mask) {
+  #pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = key0 + mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+              const bool ok = key < k_len && (!CAUSAL || key <= my_q);
+              s[mb][i] = ok ? s[mb][i] * cs : -INFINITY;
+              t4[i & 3] = fmaxf(t4[i & 3], s[mb][i]);
+            }
+        } else {
+  #pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) t4[i & 3] = fmaxf(t4[i & 3], s[mb][i]);
+        }
+        float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+        if (!need_mask) tmax *= cs;  // scales are >= 0
+        tmax = max_halves(tmax);
+        const float m_new = fmaxf(M, __builtin_ceilf(tmax));
+        if (__any(m_new > M)) {
+          const float alpha = (m_new == M) ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
+          l *= alpha;
+  #pragma unroll
+          for (int db = 0; db < DB; ++db)
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        }
+        M = m_new;
+        const float m_use = (M == -INFINITY) ? 0.f : M;
+        const float off = bias - m_use;
 
-      float r4[4] = {0.f, 0.f, 0.f, 0.f};
-      if (need_mask) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            s[mb][i] = __builtin_amdgcn_exp2f(s[mb][i] + off);
-            r4[i & 3] += s[mb][i];
-          }
-      } else {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            s[mb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][i], cs, off));
-            r4[i & 3] += s[mb][i];
-          }
-      }
-      const float rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
-      // rs sums 2^(t - M) * 2^bias; l keeps the unweighted sum
-      l += rs * __builtin_amdgcn_exp2f(-bias);
-      if (pv_zero) {
-        slot = (slot + 1 == NS) ? 0 : slot + 1;
-        continue;  // wave-uniform: the tile's V scale is the same for every lane
-      }
+        float r4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (need_mask) {
+  #pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              s[mb][i] = __builtin_amdgcn_exp2f(s[mb][i] + off);
+              r4[i & 3] += s[mb][i];
+            }
+        } else {
+  #pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              s[mb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][i], cs, off));
+              r4[i & 3] += s[mb][i];
+            }
+        }
+        const float rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+        // rs sums 2^(t - M) * 2^bias; l keeps the unweighted sum
+        l += rs * __builtin_amdgcn_exp2f(-bias);
+        if (pv_zero) return;  // wave-uniform: the tile's V scale is the same for every lane
 
-      // P codes: step g takes key blocks 2g (bytes 0..15) and 2g+1 (16..31)
-      uint4 pp[PG][2];
-#pragma unroll
-      for (int g = 0; g < PG; ++g) {
-        const f32x16_t& a = s[2 * g];
-        const f32x16_t& bb = s[2 * g + 1];
-        pp[g][0] = make_uint4(pack4_e4m3(a[0], a[1], a[2], a[3]), pack4_e4m3(a[4], a[5], a[6], a[7]),
-                              pack4_e4m3(a[8], a[9], a[10], a[11]), pack4_e4m3(a[12], a[13], a[14], a[15]));
-        pp[g][1] = make_uint4(pack4_e4m3(bb[0], bb[1], bb[2], bb[3]), pack4_e4m3(bb[4], bb[5], bb[6], bb[7]),
-                              pack4_e4m3(bb[8], bb[9], bb[10], bb[11]), pack4_e4m3(bb[12], bb[13], bb[14], bb[15]));
+        // P codes: step g takes key blocks 2g (bytes 0..15) and 2g+1 (16..31)
+        uint4 pp[PG][2];
+  #pragma unroll
+        for (int g = 0; g < PG; ++g) {
+          const f32x16_t& a = s[2 * g];
+          const f32x16_t& bb = s[2 * g + 1];
+          pp[g][0] = make_uint4(pack4_e4m3(a[0], a[1], a[2], a[3]), pack4_e4m3(a[4], a[5], a[6], a[7]),
+                                pack4_e4m3(a[8], a[9], a[10], a[11]), pack4_e4m3(a[12], a[13], a[14], a[15]));
+          pp[g][1] = make_uint4(pack4_e4m3(bb[0], bb[1], bb[2], bb[3]), pack4_e4m3(bb[4], bb[5], bb[6], bb[7]),
+                                pack4_e4m3(bb[8], bb[9], bb[10], bb[11]), pack4_e4m3(bb[12], bb[13], bb[14], bb[15]));
+        }
+        pv_pass(vr, pp);
       }
-      pv_pass(slot, pp);
-    }
+    });
     slot = (slot + 1 == NS) ? 0 : slot + 1;
   }
 
