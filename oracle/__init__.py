@@ -32,7 +32,10 @@ Modules:
   chain rule written out; the pages measure a backward pass but print no
   algorithm for it);
 * ``paged``: attention over a paged key/value cache (pages gathered through
-  a page table, then the definition).
+  a page table, then the definition);
+* ``fp8_backward``: e5m2 rounding from the format definition, block
+  quantisation of dO, and an fp64 emulation of the backward pass with its
+  products on fp8 operands (E5M2 for the gradient operands).
 
 Pins (the independent checks each function is held to) live in
 ``tests/test_oracle_*.py``; every function here is pinned, none is "parity
@@ -45,3 +48,4 @@ from . import fp8  # noqa: F401
 from . import splitkv  # noqa: F401
 from . import backward  # noqa: F401
 from . import paged  # noqa: F401
+from . import fp8_backward  # noqa: F401
