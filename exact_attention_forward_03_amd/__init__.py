@@ -4,9 +4,10 @@
 The C entry points are exposed under their own names with plain integer
 pointers (argument marshalling only): ``attn_fwd``, ``attn_fwd_stream``,
 ``attn_fwd_splitkv``, ``attn_fwd_paged``, ``attn_merge``, ``attn_bwd``,
-``attn_fp8_quantize``, ``attn_fp8_quantize_varlen``, ``attn_strerror``.
-``forward``, ``forward_splitkv``, ``forward_paged``, ``merge``, ``backward``,
-``fp8_quantize`` and ``fp8_quantize_varlen`` are the
+``attn_bwd_fp8``, ``attn_fp8_quantize``, ``attn_fp8_quantize_varlen``,
+``attn_strerror``.  ``forward``, ``forward_splitkv``, ``forward_paged``,
+``merge``, ``backward``, ``backward_fp8``, ``fp8_quantize`` and
+``fp8_quantize_varlen`` are the
 torch-facing conveniences: they allocate the
 outputs (and workspaces) with torch on the inputs' device, pass
 ``data_ptr()``s and torch's current HIP stream, and raise ``RuntimeError`` on
@@ -26,8 +27,8 @@ __all__ = [
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP", "ATTN_ERR_TOO_LARGE",
     "ATTN_NOALLOC_SCRATCH_BYTES", "attn_fwd_splitkv_noalloc", "forward_splitkv_noalloc",
     "load", "lib_path", "attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_fp8_quantize",
-    "attn_fwd_paged", "attn_bwd", "attn_strerror", "attn_fp8_quantize_varlen", "forward", "forward_splitkv",
-    "forward_paged", "merge", "backward", "fp8_quantize", "fp8_quantize_varlen",
+    "attn_fwd_paged", "attn_bwd", "attn_bwd_fp8", "attn_strerror", "attn_fp8_quantize_varlen", "forward",
+    "forward_splitkv", "forward_paged", "merge", "backward", "backward_fp8", "fp8_quantize", "fp8_quantize_varlen",
     "default_splits", "EXPORTS",
 ]
 
@@ -36,7 +37,7 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_TOO_
 ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20  # the fixed device scratch of attn_fwd_splitkv_noalloc (include/attn.h)
 
 EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_fwd_paged",
-           "attn_merge", "attn_bwd", "attn_fp8_quantize", "attn_fp8_quantize_varlen", "attn_strerror")
+           "attn_merge", "attn_bwd", "attn_bwd_fp8", "attn_fp8_quantize", "attn_fp8_quantize_varlen", "attn_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -74,6 +75,8 @@ def load():
         lib.attn_fwd_paged.restype = _i
         lib.attn_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _p, _i, _p]
         lib.attn_bwd.restype = _i
+        lib.attn_bwd_fp8.argtypes = [_p] * 15 + [_i, _i, _i, _i, _i, _f, _i, _p]
+        lib.attn_bwd_fp8.restype = _i
         lib.attn_fp8_quantize.argtypes = [_p, _i, _p, _p, _i, _i, _i, _i, _p, _i, _p]
         lib.attn_fp8_quantize.restype = _i
         lib.attn_fp8_quantize_varlen.argtypes = [_p, _i, _p, _p, _i, _i, _i, _p, _i, _p, _i, _p]
@@ -125,6 +128,12 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, c
              dtype, hip_stream) -> int:
     return load().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q,
                            cu_seqlens_k, dtype, hip_stream)
+
+
+def attn_bwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o, lse, dout, dq, dk, dv, delta, do8, do_scale, B, H, Nq,
+                 Nk, d, scale, causal, hip_stream) -> int:
+    return load().attn_bwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o, lse, dout, dq, dk, dv, delta, do8,
+                               do_scale, B, H, Nq, Nk, d, scale, causal, hip_stream)
 
 
 def attn_fp8_quantize(x, x_dtype, x_fp8, x_scale, B, H, N, d, signs, per_tensor, hip_stream) -> int:
@@ -425,6 +434,49 @@ def backward(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[flo
     rc = attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                   _ptr(delta), B, H, Nq, Nk, d, float(scale), int(bool(causal)), _ptr(cu_seqlens_q),
                   _ptr(cu_seqlens_k), dt, _stream(q.device))
+    _check(rc)
+    return dq, dk, dv
+
+
+def backward_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o, lse, dout, *, causal: bool = False,
+                 scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) in bfloat16 of the fp8 ``forward`` on the e4m3
+    codes q8, k8, v8 (uint8 [B, H, N, 128]) with their tile scales (float32
+    [B, H, ceil(N/128)]), for the output gradient ``dout`` (bfloat16, the
+    shape of o), through ``attn_bwd_fp8``.  o (bfloat16) and lse are the
+    forward's outputs.  ``workspace`` is an optional tuple (delta, do8,
+    do_scale) of the shapes attn_bwd_fp8 states (allocated here if absent)."""
+    import torch
+
+    for t in (q8, k8, v8, q_scale, k_scale, v_scale, o, lse, dout):
+        if not t.is_contiguous():
+            raise ValueError("all inputs must be contiguous")
+    if q8.dtype != torch.uint8 or k8.dtype != torch.uint8 or v8.dtype != torch.uint8:
+        raise TypeError("q8, k8, v8 must be uint8 e4m3 codes")
+    if o.dtype != torch.bfloat16 or dout.dtype != torch.bfloat16:
+        raise TypeError("o and dout must be bfloat16")
+    if q8.dim() != 4 or k8.shape != v8.shape or o.shape != q8.shape or dout.shape != q8.shape:
+        raise ValueError("q8, o, dout must be [B, H, Nq, d] and k8, v8 [B, H, Nk, d]")
+    B, H, Nq, d = q8.shape
+    Nk = k8.shape[2]
+    if tuple(q_scale.shape) != (B, H, (Nq + 127) // 128) or tuple(k_scale.shape) != (B, H, (Nk + 127) // 128) \
+            or k_scale.shape != v_scale.shape:
+        raise ValueError("scales must be [B, H, ceil(N/128)]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("lse must be float32 [B, H, Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if dq is None else dq
+    dk = torch.empty(k8.shape, dtype=torch.bfloat16, device=q8.device) if dk is None else dk
+    dv = torch.empty(v8.shape, dtype=torch.bfloat16, device=q8.device) if dv is None else dv
+    if workspace is None:
+        workspace = (torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device),
+                     torch.empty(q8.shape, dtype=torch.uint8, device=q8.device),
+                     torch.empty((B, H, (Nq + 127) // 128), dtype=torch.float32, device=q8.device))
+    delta, do8, do_scale = workspace
+    rc = attn_bwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale), _ptr(o),
+                      _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), _ptr(do8), _ptr(do_scale),
+                      B, H, Nq, Nk, d, float(scale), int(bool(causal)), _stream(q8.device))
     _check(rc)
     return dq, dk, dv
 

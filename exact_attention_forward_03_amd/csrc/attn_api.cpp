@@ -265,6 +265,41 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+int attn_bwd_fp8(const void* q8, const float* q_scale, const void* k8, const float* k_scale, const void* v8,
+                 const float* v_scale, const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                 void* dv, float* delta, void* do8, float* do_scale, int B, int H, int Nq, int Nk, int d,
+                 float scale, int causal, void* hip_stream) {
+  if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return ATTN_ERR_INVALID_ARG;
+  if (Nq > 0 && (!q8 || !q_scale || !o || !lse || !dout || !dq || !delta || !do8 || !do_scale))
+    return ATTN_ERR_INVALID_ARG;
+  if (Nk > 0 && (!k8 || !k_scale || !v8 || !v_scale || !dk || !dv)) return ATTN_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(do8, 16))
+    return ATTN_ERR_INVALID_ARG;
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(lse, 4) ||
+      !aligned(delta, 4) || !aligned(do_scale, 4))
+    return ATTN_ERR_INVALID_ARG;
+  if (d != 128) return ATTN_ERR_UNSUPPORTED;
+  // workgroups: (b, h) x 128-row tiles of either side
+  const int64_t heads = (int64_t)B * H;
+  if (heads * (((int64_t)Nq + 127) / 128) > INT32_MAX || heads * (((int64_t)Nk + 127) / 128) > INT32_MAX)
+    return ATTN_ERR_INVALID_ARG;
+  if (Nq == 0 && Nk == 0) return ATTN_OK;
+  attn::Bwd8Params p{};
+  p.q = (const uint8_t*)q8; p.k = (const uint8_t*)k8; p.v = (const uint8_t*)v8;
+  p.q_scale = q_scale; p.k_scale = k_scale; p.v_scale = v_scale;
+  p.o = o; p.dout = dout; p.lse = lse;
+  p.delta = delta; p.do8 = (uint8_t*)do8; p.do_scale = do_scale;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  const hipError_t e = attn::launch_bwd_fp8(causal != 0, p, (hipStream_t)hip_stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 int attn_fp8_quantize(const void* x, int x_dtype, void* x_fp8, float* x_scale, int B, int H, int N, int d,
                       const float* signs, int per_tensor, void* hip_stream) {
   if (!x || !x_fp8 || !x_scale) return ATTN_ERR_INVALID_ARG;

@@ -85,6 +85,30 @@ struct BwdParams {
   const int32_t* cu_k;
 };
 
+// Backward pass on fp8 operands (dense [B, H, N, 128]).
+struct Bwd8Params {
+  const uint8_t* q;      // e4m3 codes and their per-128-row-tile scales [B, H, ceil(N/128)]
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  const void* o;         // bfloat16 [B, H, Nq, 128]: the forward's output
+  const void* dout;      // bfloat16 [B, H, Nq, 128]
+  const float* lse;      // [B, H, Nq]
+  float* delta;          // workspace [B, H, Nq]: rowsum(dO * O)
+  uint8_t* do8;          // workspace [B, H, Nq, 128]: e5m2 codes of dO
+  float* do_scale;       // workspace [B, H, ceil(Nq/128)]
+  void* dq;              // bfloat16 outputs
+  void* dk;
+  void* dv;
+  int B, H, Nq, Nk;
+  float scale;           // softmax scale
+  float c;               // scale * log2(e)
+  int n_work;            // workgroups of the current launch
+};
+hipError_t launch_bwd_fp8(bool causal, const Bwd8Params& p, hipStream_t st);
+
 int bwd_key_block(int d);    // keys per dK/dV workgroup
 int bwd_query_block(int d);  // queries per dQ workgroup
 hipError_t launch_bwd(int dtype, int d, bool causal, bool varlen, BwdParams p, hipStream_t st);

@@ -289,6 +289,44 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              void* dq, void* dk, void* dv, float* delta, int B, int H, int Nq, int Nk, int d, float scale,
              int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, void* hip_stream);
 
+/*
+ * attn_bwd_fp8 — attn_bwd on the fp8 operands of attn_fwd (dtype
+ * ATTN_DT_FP8_E4M3, d = 128, dense layout), with E5M2 for the gradient
+ * operands ("Flash Attention 3：让 GPU 跑满的注意力计算", §4.1.2: E4M3 for the
+ * forward pass, E5M2 for back-propagation).  The gradients are those of the
+ * attention of the dequantised inputs q = q_scale[tile] * e4m3(q8) etc.
+ * (for inputs that attn_fp8_quantize rotated: with respect to the rotated
+ * Q and K), the five products on fp8 matrix cores with fp32 accumulation:
+ *   dO is quantised to e5m2 with one fp32 scale per 128-row tile,
+ *     s = amax / 57344 (1 for an all-zero tile), codes e5m2(dO / s);
+ *   dV = P^T dO takes P as e4m3(2^8 P s_do(q) / max s_do);
+ *   dK = scale dS^T Q takes dS as e5m2(dS s_q(q) / max s_q);
+ *   dQ = scale dS K takes dS as e5m2(dS s_k(k) / max s_k);
+ *   (max over the (b, h)'s tiles: each product's per-tile scale is folded
+ *   into the factor that is rounded); P = exp(S - lse) from the
+ *   dequantised scores, dP = dO_q V^T, dS = P (dP - delta), delta_i =
+ *   dO_i . O_i in fp32 from the unquantised dO.  Rounding: to nearest even;
+ *   e5m2 values saturate at +-57344.
+ *   q8 uint8 [B, H, Nq, 128], k8, v8 uint8 [B, H, Nk, 128] and q_scale,
+ *     k_scale, v_scale fp32 [B, H, ceil(N/128)]: attn_fwd's fp8 inputs;
+ *   o (bfloat16 [B, H, Nq, 128]) and lse (fp32 [B, H, Nq]): attn_fwd's
+ *     outputs for the same inputs, scale and causal;
+ *   dout bfloat16 [B, H, Nq, 128]; dq, dk, dv bfloat16, shaped as q8, k8, v8;
+ *   workspaces, caller-owned, overwritten: delta fp32 [B, H, Nq] (on return
+ *     delta_i), do8 uint8 [B, H, Nq, 128] (dO's e5m2 codes) and do_scale
+ *     fp32 [B, H, ceil(Nq/128)] (their scales);
+ *   d other than 128: ATTN_ERR_UNSUPPORTED.  2-D arrays 16-byte aligned,
+ *   lse, scales, delta 4-byte aligned.
+ *   Query-side arrays may be NULL only if Nq = 0, key-side arrays only if
+ *   Nk = 0.  Nk = 0 gives dQ = 0; Nq = 0 gives dK = dV = 0.  No atomics:
+ *   results are deterministic.  Same stream, ownership and error rules as
+ *   attn_fwd_stream.
+ */
+int attn_bwd_fp8(const void* q8, const float* q_scale, const void* k8, const float* k_scale, const void* v8,
+                 const float* v_scale, const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                 void* dv, float* delta, void* do8, float* do_scale, int B, int H, int Nq, int Nk, int d,
+                 float scale, int causal, void* hip_stream);
+
 /* attn_strerror — a static, human-readable name for a return code. */
 const char* attn_strerror(int code);
 
