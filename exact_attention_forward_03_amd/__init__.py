@@ -130,9 +130,9 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, c
                            cu_seqlens_k, dtype, hip_stream)
 
 
-def attn_bwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o, lse, dout, dq, dk, dv, delta, do8, do_scale, B, H, Nq,
+def attn_bwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o, lse, dout, dq, dk, dv, stats, do8, do_scale, B, H, Nq,
                  Nk, d, scale, causal, hip_stream) -> int:
-    return load().attn_bwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o, lse, dout, dq, dk, dv, delta, do8,
+    return load().attn_bwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o, lse, dout, dq, dk, dv, stats, do8,
                                do_scale, B, H, Nq, Nk, d, scale, causal, hip_stream)
 
 
@@ -444,7 +444,7 @@ def backward_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o, lse, dout, *, causal:
     codes q8, k8, v8 (uint8 [B, H, N, 128]) with their tile scales (float32
     [B, H, ceil(N/128)]), for the output gradient ``dout`` (bfloat16, the
     shape of o), through ``attn_bwd_fp8``.  o (bfloat16) and lse are the
-    forward's outputs.  ``workspace`` is an optional tuple (delta, do8,
+    forward's outputs.  ``workspace`` is an optional tuple (stats, do8,
     do_scale) of the shapes attn_bwd_fp8 states (allocated here if absent)."""
     import torch
 
@@ -470,12 +470,14 @@ def backward_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o, lse, dout, *, causal:
     dk = torch.empty(k8.shape, dtype=torch.bfloat16, device=q8.device) if dk is None else dk
     dv = torch.empty(v8.shape, dtype=torch.bfloat16, device=q8.device) if dv is None else dv
     if workspace is None:
-        workspace = (torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device),
+        workspace = (torch.empty((3, B, H, Nq), dtype=torch.float32, device=q8.device),
                      torch.empty(q8.shape, dtype=torch.uint8, device=q8.device),
                      torch.empty((B, H, (Nq + 127) // 128), dtype=torch.float32, device=q8.device))
-    delta, do8, do_scale = workspace
+    stats, do8, do_scale = workspace
+    if stats.numel() < 3 * B * H * Nq or do8.numel() < B * H * Nq * d or do_scale.numel() < B * H * ((Nq + 127) // 128):
+        raise ValueError("workspace too small")
     rc = attn_bwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale), _ptr(o),
-                      _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), _ptr(do8), _ptr(do_scale),
+                      _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(stats), _ptr(do8), _ptr(do_scale),
                       B, H, Nq, Nk, d, float(scale), int(bool(causal)), _stream(q8.device))
     _check(rc)
     return dq, dk, dv

@@ -267,10 +267,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
 
 int attn_bwd_fp8(const void* q8, const float* q_scale, const void* k8, const float* k_scale, const void* v8,
                  const float* v_scale, const void* o, const float* lse, const void* dout, void* dq, void* dk,
-                 void* dv, float* delta, void* do8, float* do_scale, int B, int H, int Nq, int Nk, int d,
+                 void* dv, float* stats, void* do8, float* do_scale, int B, int H, int Nq, int Nk, int d,
                  float scale, int causal, void* hip_stream) {
   if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return ATTN_ERR_INVALID_ARG;
-  if (Nq > 0 && (!q8 || !q_scale || !o || !lse || !dout || !dq || !delta || !do8 || !do_scale))
+  if (Nq > 0 && (!q8 || !q_scale || !o || !lse || !dout || !dq || !stats || !do8 || !do_scale))
     return ATTN_ERR_INVALID_ARG;
   if (Nk > 0 && (!k8 || !k_scale || !v8 || !v_scale || !dk || !dv)) return ATTN_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
@@ -279,7 +279,7 @@ int attn_bwd_fp8(const void* q8, const float* q_scale, const void* k8, const flo
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(do8, 16))
     return ATTN_ERR_INVALID_ARG;
   if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(lse, 4) ||
-      !aligned(delta, 4) || !aligned(do_scale, 4))
+      !aligned(stats, 4) || !aligned(do_scale, 4))
     return ATTN_ERR_INVALID_ARG;
   if (d != 128) return ATTN_ERR_UNSUPPORTED;
   // workgroups: (b, h) x 128-row tiles of either side
@@ -291,7 +291,7 @@ int attn_bwd_fp8(const void* q8, const float* q_scale, const void* k8, const flo
   p.q = (const uint8_t*)q8; p.k = (const uint8_t*)k8; p.v = (const uint8_t*)v8;
   p.q_scale = q_scale; p.k_scale = k_scale; p.v_scale = v_scale;
   p.o = o; p.dout = dout; p.lse = lse;
-  p.delta = delta; p.do8 = (uint8_t*)do8; p.do_scale = do_scale;
+  p.stats = stats; p.do8 = (uint8_t*)do8; p.do_scale = do_scale;
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk;
   p.scale = scale;

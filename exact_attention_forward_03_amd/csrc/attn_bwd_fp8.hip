@@ -37,6 +37,8 @@
 // with its k-index in the same order.  Each tile read both ways is stored
 // twice in LDS, once per swizzle (the row reads and the transposing reads
 // are conflict-free under different chunk permutations).
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_params.h"
 
@@ -118,7 +120,7 @@ __device__ __forceinline__ uint4 pack16_e4m3(const f32x16_t& v) {
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
-__device__ __forceinline__ float clamp_e5m2(float x) { return fminf(fmaxf(x, -kE5m2Max), kE5m2Max); }
+__device__ __forceinline__ float clamp_e5m2(float x) { return __builtin_amdgcn_fmed3f(x, -kE5m2Max, kE5m2Max); }
 __device__ __forceinline__ uint4 pack16_e5m2(const f32x16_t& v) {
   uint32_t w[4];
 #pragma unroll
@@ -135,20 +137,73 @@ __device__ __forceinline__ float scale_max(const float* s, int n, int lane) {
   for (int j = lane; j < n; j += 64) m = fmaxf(m, s[j]);
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
-  return m;
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, m)));
 }
 
-// Direct-to-LDS load of 1 KiB block b (8 rows) of a 64-row tile: rows
-// r0 + 8 b .. of src (codes, rows of 128 bytes; rows past n_rows re-read
-// the last row), chunk-permuted by perm.
-template <bool TR>
-__device__ __forceinline__ void load_block8(const uint8_t* src, int64_t row_base, int r0, int n_rows, uint8_t* dst,
-                                            int b, int lane) {
-  const int r = 8 * b + (lane >> 3);
-  const int row = min(r0 + r, n_rows - 1);
-  const int ch = TR ? tr8(r, lane & 7) : rows8(r, lane & 7);
-  __builtin_amdgcn_global_load_lds(src + (row_base + row) * kRowB + ch * 16, (lds_void_t*)(dst + b * 1024), 16, 0,
-                                   0);
+// Byte offsets (within a 1 KiB block of 8 rows) that lane `lane` fetches
+// for a direct-to-LDS tile load: the lane writes physical chunk lane % 8 of
+// row lane / 8 and so fetches the logical chunk stored there.  The chunk
+// permutations read bits 1..3 of the row, and bit 3 is the parity of the
+// block: entry par serves the blocks of that parity.
+struct TileLane {
+  uint32_t vo[2];
+  __device__ TileLane(int lane, bool tr) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int r = 8 * par + (lane >> 3);
+      const int ch = tr ? tr8(r, lane & 7) : rows8(r, lane & 7);
+      vo[par] = (uint32_t)((lane >> 3) * kRowB + ch * 16);
+    }
+  }
+};
+
+// 1 / x (correctly rounded), or 0 for x = 0 (a head whose scales are all 0
+// has an all-zero operand; its fold ratios are then 0).
+__device__ __forceinline__ float recip_or_zero(float x) { return x > 0.f ? 1.0f / x : 0.f; }
+
+// f(w, r) with an LDS ring slot that direct-to-LDS loads fill (w) and one
+// that the step reads (r) passed as restrict pointers: the caller guarantees
+// they do not overlap, and the compiler then does not wait for the loads
+// before the reads.
+template <typename F>
+__device__ __forceinline__ void with_slots(uint8_t* __restrict__ w, const uint8_t* __restrict__ r, F&& f) {
+  f(w, r);
+}
+
+// Direct-to-LDS load of a 64-row tile (8 KiB) by one wave: rows r0 ..
+// r0 + 63 of the rows at `base` (n_rows of them, r0 < n_rows) go to dst
+// with their chunks permuted (rows8, or tr8 if tr).  The rows come through a
+// buffer resource based at row r0, so a full tile costs no vector
+// instructions; a tile that runs past n_rows clamps each lane's row to the
+// last one, so no read goes out of range.
+__device__ __forceinline__ void load_tile64(const uint8_t* base, int r0, int n_rows, uint8_t* dst,
+                                            const TileLane& tl, bool tr, int lane) {
+  const int rows = min(kBlk, n_rows - r0);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)r0 * kRowB), 0, rows * kRowB, kBufferFlags);
+  if (rows == kBlk) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + b * 1024), 16, tl.vo[b & 1],
+                                               (uint32_t)(b * 1024), 0, 0);
+  } else {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int r = 8 * b + (lane >> 3);
+      const int ch = tr ? tr8(r, lane & 7) : rows8(r, lane & 7);
+      const uint32_t off = (uint32_t)(min(r, rows - 1) * kRowB + ch * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + b * 1024), 16, off, 0, 0, 0);
+    }
+  }
+}
+
+// Direct-to-LDS load of 64 floats (rows r0 .. r0 + 63 of the n_rows at
+// base; lanes past the end re-read the last one) to dst.
+__device__ __forceinline__ void load_row_floats(const float* base, int r0, int n_rows, uint8_t* dst, int lane) {
+  const int rows = min(kBlk, n_rows - r0);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + r0), 0, rows * 4, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 4, (uint32_t)(min(lane, rows - 1) * 4), 0, 0, 0);
 }
 
 // Store a 32-row block of a transposed accumulator: lane (c, h) owns output
@@ -166,9 +221,14 @@ __device__ __forceinline__ void store_rows_bf16(uint16_t* dst_row, const f32x16_
 
 // ---------------------------------------------------------------------------
 // Pre-processing: one workgroup per (b*h, 128-row tile) of dO and O.
-// delta_i = sum_c dO_ic O_ic in fp32; s = amax(dO tile) / 57344 (1 if the
-// tile is all zero, at least 2^-149); codes e5m2(dO / s).  Two threads per
-// row, 64 values each.
+// dO: s = amax(dO tile) / 57344 (1 if the tile is all zero, at least
+// 2^-149) and codes e5m2(dO / s).  Row statistics for the other kernels, in
+// the three planes of the stats workspace: L2_i = lse_i log2(e), delta_i =
+// sum_c dO_ic O_ic in fp32, and delta_i f_q with f_q = s_q(tile) / max s_q
+// (the dK pass multiplies P (dP - delta) by f_q; folding it into delta and
+// into dP's scale saves a multiplication per element).  f_q is formed as
+// s_q(tile) * recip_or_zero(max s_q) here and in the dK pass, so both take
+// the same value.  Two threads per row, 64 values each.
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 256;
 
@@ -179,6 +239,9 @@ __global__ void __launch_bounds__(kPrepThreads) bwd8_prep_kernel(Bwd8Params p) {
   const int row = tile * kScaleRows + (threadIdx.x >> 1), half = threadIdx.x & 1;
   const bool live = row < p.Nq;
   const int64_t base = ((int64_t)bh * p.Nq + (live ? row : 0)) * kD + half * 64;
+  const float* sq = p.q_scale + (int64_t)bh * nt;
+  float sq_max = 0.f;
+  for (int j = threadIdx.x & 63; j < nt; j += 64) sq_max = fmaxf(sq_max, sq[j]);
   float v[64];
   float dsum = 0.f, amax = 0.f;
 #pragma unroll
@@ -200,9 +263,18 @@ __global__ void __launch_bounds__(kPrepThreads) bwd8_prep_kernel(Bwd8Params p) {
     }
   }
   dsum += __shfl_xor(dsum, 1);
-  if (live && half == 0) p.delta[(int64_t)bh * p.Nq + row] = dsum;
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) amax = fmaxf(amax, __shfl_xor(amax, s));
+  for (int s = 32; s >= 1; s >>= 1) {
+    amax = fmaxf(amax, __shfl_xor(amax, s));
+    sq_max = fmaxf(sq_max, __shfl_xor(sq_max, s));
+  }
+  if (live && half == 0) {
+    const int64_t r = (int64_t)bh * p.Nq + row;
+    p.stats[r] = p.lse[r] * kLog2e;
+    const int64_t plane = (int64_t)p.B * p.H * p.Nq;
+    p.stats[plane + r] = dsum;
+    p.stats[2 * plane + r] = dsum * (sq[tile] * recip_or_zero(sq_max));
+  }
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
   __syncthreads();
   float tmax = red[0];
@@ -222,11 +294,16 @@ __global__ void __launch_bounds__(kPrepThreads) bwd8_prep_kernel(Bwd8Params p) {
 
 // ---------------------------------------------------------------------------
 // dK, dV: a workgroup of 4 waves owns 128 keys (one K/V scale tile) of one
-// head; 64-row blocks of Q and dO (each stored twice: rows8 and tr8), lse
-// and delta stream through a 2-slot LDS ring.
+// head; 64-row blocks of Q and dO (each stored twice: rows8 and tr8), L2 and
+// delta f_q stream through a 2-slot LDS ring.  A step handles its
+// 64 queries as two 32-row halves (S, dP, then P and dS packed to 8 bits),
+// so that only one half's fp32 values are live: with the 128 accumulator
+// registers of dK and dV the wave fits in 256 registers, two waves per SIMD.
+// Blocks that the causal diagonal or the ends of the sequences cut run the
+// masked variant of the element-wise step; the others run it without masks.
 // ---------------------------------------------------------------------------
 constexpr int kNW = 4;
-constexpr int kStage = 4 * kBlkB + 2 * kBlk * 4;  // Q rows8, Q tr8, dO rows8, dO tr8, lse[64], delta[64]
+constexpr int kStage = 4 * kBlkB + 2 * kBlk * 4;  // Q rows8, Q tr8, dO rows8, dO tr8, L2[64], delta f_q[64]
 
 template <bool CAUSAL>
 __device__ __forceinline__ void dkdv8_body(const Bwd8Params& p, const int head, const int kt) {
@@ -238,11 +315,16 @@ __device__ __forceinline__ void dkdv8_body(const Bwd8Params& p, const int head, 
   const int Nq = p.Nq, Nk = p.Nk;
   const int nqt = (Nq + kScaleRows - 1) / kScaleRows, nkt = (Nk + kScaleRows - 1) / kScaleRows;
   const int k0 = kt * kScaleRows, my_key = k0 + 32 * wv + c;
+  const int kw_last = k0 + 32 * wv + 31;  // the wave's last key
   const int64_t q_row0 = (int64_t)head * Nq, k_row0 = (int64_t)head * Nk;
   const float* sq = p.q_scale + (int64_t)head * nqt;
   const float* sdo = p.do_scale + (int64_t)head * nqt;
+  const float* l2g = p.stats;
+  const float* dlg = p.stats + 2 * (int64_t)p.B * p.H * Nq;
   const float sq_max = scale_max(sq, nqt, lane), sdo_max = scale_max(sdo, nqt, lane);
-  const float skt = p.k_scale[(int64_t)head * nkt + kt], svt = p.v_scale[(int64_t)head * nkt + kt];
+  const float rsq = recip_or_zero(sq_max), rsdo = recip_or_zero(sdo_max);
+  const float skt = load_uniform(p.k_scale, (int64_t)head * nkt + kt);
+  const float svt = load_uniform(p.v_scale, (int64_t)head * nkt + kt);
 
   // this wave's K and V rows (key my_key) as B operands
   uint4 kf[2][2], vf[2][2];
@@ -270,95 +352,125 @@ __device__ __forceinline__ void dkdv8_body(const Bwd8Params& p, const int head, 
   const int n_qb = (Nq + kBlk - 1) / kBlk;
   const int qb0 = CAUSAL ? min(k0 / kBlk, n_qb) : 0;
   const int n_steps = n_qb - qb0;
-  auto load_stage = [&](int qb, uint8_t* st) {
-    // 32 blocks of 1 KiB (four 8 KiB tiles), eight per wave
+
+  // wave w loads tile w of a stage: Q rows8, Q tr8, dO rows8, dO tr8; waves
+  // 0 and 1 also L2 and delta f_q
+  const TileLane tlane(lane, wv & 1);
+  const uint8_t* tile_src = (wv < 2 ? p.q : p.do8) + q_row0 * kRowB;
+  const float* row_src = (wv == 0 ? l2g : dlg) + q_row0;
+  auto load_stage = [&](int qb, uint8_t* st) __attribute__((always_inline)) {
+    load_tile64(tile_src, qb * kBlk, Nq, st + wv * kBlkB, tlane, wv & 1, lane);
+    if (wv < 2) load_row_floats(row_src, qb * kBlk, Nq, st + 4 * kBlkB + wv * 256, lane);
+  };
+
+  // S and dP of query rows 32 nb .. of the block: element i of the
+  // accumulators is query row 32 nb + 8 (i/4) + 4 hh + i%4 of the block
+  auto sdp = [&](const uint8_t* st, const int nb, f32x16_t& s, f32x16_t& dpa) __attribute__((always_inline)) {
+    s = f32x16_t{};
+    dpa = f32x16_t{};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int blk = wv * 8 + i, tile = blk >> 3, b = blk & 7;
-      const uint8_t* src = tile < 2 ? p.q : p.do8;
-      if (tile & 1) load_block8<true>(src, q_row0, qb * kBlk, Nq, st + tile * kBlkB, b, lane);
-      else load_block8<false>(src, q_row0, qb * kBlk, Nq, st + tile * kBlkB, b, lane);
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 a0, a1, b0, b1;
+      row_frag(st, nb * 32 + c, ks, hh, a0, a1);
+      row_frag(st + 2 * kBlkB, nb * 32 + c, ks, hh, b0, b1);
+      s = mfma8<kFmtE4m3, kFmtE4m3>(a0, a1, kf[ks][0], kf[ks][1], s);
+      dpa = mfma8<kFmtE5m2, kFmtE4m3>(b0, b1, vf[ks][0], vf[ks][1], dpa);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (wv < 2) {  // lse (wave 0) and delta (wave 1): 64 floats each, 4-byte loads
-      const int q = min(qb * kBlk + lane, Nq - 1);
-      const float* src = (wv == 0 ? p.lse : p.delta) + q_row0 + q;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(st + 4 * kBlkB + wv * 256), 4, 0, 0);
+  };
+  // P and dS of those rows, rounded and packed four rows (one dword) at a
+  // time: P8 = e4m3(P fp), dS8 = e5m2(P (dP cdp - delta f_q)).  MASK: the
+  // block is cut by the causal diagonal or an end of the sequences.
+  auto elementwise = [&](const uint8_t* st, const int qb, const int nb, const f32x16_t& s, const f32x16_t& dpa,
+                         const float cs, const float cdp, const float fp, uint4& p8, uint4& d8, auto mask_tag)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const float* tl = (const float*)(st + 4 * kBlkB);
+    const float* tdl = tl + kBlk;
+    uint32_t pw[4], dw[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r0 = 32 * nb + 8 * g + 4 * hh;
+      const float4 L = *(const float4*)(tl + r0);
+      const float4 Dl = *(const float4*)(tdl + r0);
+      const float Lv[4] = {L.x, L.y, L.z, L.w}, Dv[4] = {Dl.x, Dl.y, Dl.z, Dl.w};
+      float xp[4], xs[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        float t = __builtin_fmaf(s[i], cs, -Lv[j]);
+        if constexpr (MASK) {
+          const int q = qb * kBlk + r0 + j;
+          const bool ok = (q < Nq) & (my_key < Nk) & (!CAUSAL | (my_key <= q)) & (Lv[j] > -INFINITY);
+          t = ok ? t : -INFINITY;
+        }
+        const float pv = __builtin_amdgcn_exp2f(t);
+        xs[j] = clamp_e5m2(pv * __builtin_fmaf(dpa[i], cdp, -Dv[j]));
+        xp[j] = pv * fp;
+      }
+      pw[g] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+          xp[2], xp[3], __builtin_amdgcn_cvt_pk_fp8_f32(xp[0], xp[1], 0, false), true);
+      dw[g] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(
+          xs[2], xs[3], __builtin_amdgcn_cvt_pk_bf8_f32(xs[0], xs[1], 0, false), true);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    p8 = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+    d8 = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+  };
+
+  auto step = [&](const int qb, const uint8_t* st) __attribute__((always_inline)) {
+    const int qs = (qb * kBlk) / kScaleRows;  // the block's scale tile
+    const float sqb = load_uniform(sq, qs), sdob = load_uniform(sdo, qs);
+    const float cs = p.c * sqb * skt;               // S in base 2
+    const float cdp = sdob * svt * (sqb * rsq);    // dP, times the dK fold f_q (as delta in the stats)
+    const float fp = kPScale * (sdob * rsdo);
+    const bool full = (qb + 1) * kBlk <= Nq && kw_last < Nk && (!CAUSAL || qb * kBlk >= kw_last);
+    uint4 p8[2], d8[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      f32x16_t sv, dpv;
+      sdp(st, nb, sv, dpv);
+      if (full) elementwise(st, qb, nb, sv, dpv, cs, cdp, fp, p8[nb], d8[nb], std::false_type{});
+      else elementwise(st, qb, nb, sv, dpv, cs, cdp, fp, p8[nb], d8[nb], std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dV^T += dO^T P^T, dK^T += Q^T dS^T over the block's 64 queries
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      uint4 a0, a1, b0, b1;
+      tr_frag(st + 3 * kBlkB, tro.off[db], a0, a1);
+      tr_frag(st + kBlkB, tro.off[db], b0, b1);
+      dv[db] = mfma8<kFmtE5m2, kFmtE4m3>(a0, a1, p8[0], p8[1], dv[db]);
+      dk[db] = mfma8<kFmtE4m3, kFmtE5m2>(b0, b1, d8[0], d8[1], dk[db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   if (n_steps > 0) load_stage(qb0, lds);
   for (int it = 0; it < n_steps; ++it) {
-    const int qb = qb0 + it;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    uint8_t* const st = lds + (it & 1) * kStage;
-    if (it + 1 < n_steps) load_stage(qb + 1, lds + ((it + 1) & 1) * kStage);
-    const uint8_t* tq = st;
-    const uint8_t* tqT = st + kBlkB;
-    const uint8_t* tdo = st + 2 * kBlkB;
-    const uint8_t* tdoT = st + 3 * kBlkB;
-    const float* tl = (const float*)(st + 4 * kBlkB);
-    const float* tdl = tl + kBlk;
-
-    const int qs = (qb * kBlk) / kScaleRows;  // the block's scale tile
-    const float sqb = load_uniform(sq, qs), sdob = load_uniform(sdo, qs);
-    const float cs = p.c * sqb * skt;  // S in base 2
-    const float cdp = sdob * svt;
-    const float fp = kPScale * (sdob / sdo_max);
-    const float fs = sqb / sq_max;
-
-    // S = Q K^T and dP = dO V^T for query rows 32 nb .. of the block
-    f32x16_t s[2], dpa[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      s[nb] = f32x16_t{};
-      dpa[nb] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        uint4 a0, a1;
-        row_frag(tq, nb * 32 + c, ks, hh, a0, a1);
-        s[nb] = mfma8<kFmtE4m3, kFmtE4m3>(a0, a1, kf[ks][0], kf[ks][1], s[nb]);
-        row_frag(tdo, nb * 32 + c, ks, hh, a0, a1);
-        dpa[nb] = mfma8<kFmtE5m2, kFmtE4m3>(a0, a1, vf[ks][0], vf[ks][1], dpa[nb]);
-      }
-    }
-    // P, dS; element (nb, i) is query qb*64 + 32 nb + 8 (i/4) + 4 hh + i%4
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 32 * nb + 8 * (i >> 2) + 4 * hh + (i & 3);
-        const int q = qb * kBlk + r;
-        const float L = tl[r];
-        const bool ok = q < Nq && my_key < Nk && (!CAUSAL || my_key <= q) && L > -INFINITY;
-        const float pv = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][i], cs, -L * kLog2e)) : 0.f;
-        const float ds = pv * __builtin_fmaf(dpa[nb][i], cdp, -tdl[r]);
-        s[nb][i] = pv * fp;
-        dpa[nb][i] = ds * fs;
-      }
-    }
-    const uint4 p0 = pack16_e4m3(s[0]), p1 = pack16_e4m3(s[1]);
-    const uint4 d0 = pack16_e5m2(dpa[0]), d1 = pack16_e5m2(dpa[1]);
-    // dV^T += dO^T P^T, dK^T += Q^T dS^T over the block's 64 queries
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      uint4 a0, a1;
-      tr_frag(tdoT, tro.off[db], a0, a1);
-      dv[db] = mfma8<kFmtE5m2, kFmtE4m3>(a0, a1, p0, p1, dv[db]);
-      tr_frag(tqT, tro.off[db], a0, a1);
-      dk[db] = mfma8<kFmtE4m3, kFmtE5m2>(a0, a1, d0, d1, dk[db]);
-    }
+    with_slots(lds + ((it + 1) & 1) * kStage, lds + (it & 1) * kStage,
+               [&](uint8_t* w, const uint8_t* r) __attribute__((always_inline)) {
+                 if (it + 1 < n_steps) load_stage(qb0 + it + 1, w);
+                 step(qb0 + it, r);
+               });
   }
 
   if (my_key < Nk) {
-    store_rows_bf16((uint16_t*)p.dk + (k_row0 + my_key) * kD, dk, p.scale * sq_max, hh);
-    store_rows_bf16((uint16_t*)p.dv + (k_row0 + my_key) * kD, dv, sdo_max / kPScale, hh);
+    // the lane's half, recomputed from the lane id rather than kept live
+    // through the loop
+    const int h2 = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
+    store_rows_bf16((uint16_t*)p.dk + (k_row0 + my_key) * kD, dk, p.scale * sq_max, h2);
+    store_rows_bf16((uint16_t*)p.dv + (k_row0 + my_key) * kD, dv, sdo_max / kPScale, h2);
   }
 }
 
 // ---------------------------------------------------------------------------
 // dQ: a workgroup of 4 waves owns 128 queries (one Q/dO scale tile); 64-key
 // blocks of K (rows8 and tr8) and V (rows8) stream through a 2-slot ring.
+// Each lane's query is one column of S^T, so its L2 and delta are per-lane
+// constants.
 // ---------------------------------------------------------------------------
 constexpr int kStageQ = 3 * kBlkB;
 
@@ -372,13 +484,15 @@ __device__ __forceinline__ void dq8_body(const Bwd8Params& p, const int head, co
   const int Nq = p.Nq, Nk = p.Nk;
   const int nqt = (Nq + kScaleRows - 1) / kScaleRows, nkt = (Nk + kScaleRows - 1) / kScaleRows;
   const int q0 = qt * kScaleRows, my_q = q0 + 32 * wv + c;
+  const int qw_first = q0 + 32 * wv;  // the wave's first query
   const int64_t q_row0 = (int64_t)head * Nq, k_row0 = (int64_t)head * Nk;
   const float* sk = p.k_scale + (int64_t)head * nkt;
   const float* sv = p.v_scale + (int64_t)head * nkt;
-  const float sk_max = scale_max(sk, nkt, lane);
-  const float sqt = p.q_scale[(int64_t)head * nqt + qt], sdot = p.do_scale[(int64_t)head * nqt + qt];
+  const float sk_max = scale_max(sk, nkt, lane), rsk = recip_or_zero(sk_max);
+  const float sqt = load_uniform(p.q_scale, (int64_t)head * nqt + qt);
+  const float sdot = load_uniform(p.do_scale, (int64_t)head * nqt + qt);
 
-  // this wave's Q and dO rows (query my_q) as B operands, and its lse, delta
+  // this wave's Q and dO rows (query my_q) as B operands, and its L2, delta
   uint4 qf[2][2], df[2][2];
   const int qq = min(my_q, Nq - 1);
   {
@@ -392,8 +506,9 @@ __device__ __forceinline__ void dq8_body(const Bwd8Params& p, const int head, co
       df[ks][1] = *(const uint4*)(dr + 64 * ks + 16);
     }
   }
-  const float L = p.lse[q_row0 + qq], dl = p.delta[q_row0 + qq];
-  const bool q_ok = my_q < Nq && L > -INFINITY;
+  const float L = p.stats[q_row0 + qq];
+  const float delta = p.stats[(int64_t)p.B * p.H * Nq + q_row0 + qq];
+  const bool q_ok = (my_q < Nq) & (L > -INFINITY);
   const TrOffsets tro(lane);
   f32x16_t acc[DB];
 #pragma unroll
@@ -401,14 +516,72 @@ __device__ __forceinline__ void dq8_body(const Bwd8Params& p, const int head, co
 
   int n_kb = (Nk + kBlk - 1) / kBlk;
   if (CAUSAL) n_kb = min(n_kb, (min(q0 + kScaleRows, Nq) - 1) / kBlk + 1);
-  auto load_stage = [&](int kb, uint8_t* st) {
-    // 24 blocks of 1 KiB (K rows8, K tr8, V rows8), six per wave
+  // waves 0, 1, 2 load K rows8, K tr8, V rows8 of a stage
+  const TileLane tlane(lane, wv == 1);
+  const uint8_t* tile_src = (wv < 2 ? p.k : p.v) + k_row0 * kRowB;
+  auto load_stage = [&](int kb, uint8_t* st) __attribute__((always_inline)) {
+    if (wv < 3) load_tile64(tile_src, kb * kBlk, Nk, st + wv * kBlkB, tlane, wv == 1, lane);
+  };
+
+  // dS^T of key rows 32 mb .. of block kb, packed four keys (one dword) at a
+  // time: element i is key kb*64 + 32 mb + 8 (i/4) + 4 hh + i%4.  MASK: the
+  // block is cut by the causal diagonal or an end of the sequences.
+  auto half_step = [&](const uint8_t* st, const int kb, const int mb, const float cs, const float cdp,
+                       const float dl, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16_t s = f32x16_t{}, dpa = f32x16_t{};
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int blk = wv * 6 + i, tile = blk >> 3, b = blk & 7;
-      const uint8_t* src = tile < 2 ? p.k : p.v;
-      if (tile == 1) load_block8<true>(src, k_row0, kb * kBlk, Nk, st + tile * kBlkB, b, lane);
-      else load_block8<false>(src, k_row0, kb * kBlk, Nk, st + tile * kBlkB, b, lane);
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 a0, a1, b0, b1;
+      row_frag(st, mb * 32 + c, ks, hh, a0, a1);
+      row_frag(st + 2 * kBlkB, mb * 32 + c, ks, hh, b0, b1);
+      s = mfma8<kFmtE4m3, kFmtE4m3>(a0, a1, qf[ks][0], qf[ks][1], s);
+      dpa = mfma8<kFmtE4m3, kFmtE5m2>(b0, b1, df[ks][0], df[ks][1], dpa);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    uint32_t dw[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float xs[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        float t = __builtin_fmaf(s[i], cs, -L);
+        if constexpr (MASK) {
+          const int key = kb * kBlk + 32 * mb + 8 * g + 4 * hh + j;
+          const bool ok = q_ok & (key < Nk) & (!CAUSAL | (key <= my_q));
+          t = ok ? t : -INFINITY;
+        }
+        const float pv = __builtin_amdgcn_exp2f(t);
+        xs[j] = clamp_e5m2(pv * __builtin_fmaf(dpa[i], cdp, -dl));
+      }
+      dw[g] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(
+          xs[2], xs[3], __builtin_amdgcn_cvt_pk_bf8_f32(xs[0], xs[1], 0, false), true);
+    }
+    return make_uint4(dw[0], dw[1], dw[2], dw[3]);
+  };
+
+  auto step = [&](const int kb, const uint8_t* st) __attribute__((always_inline)) {
+    const int ks_ = (kb * kBlk) / kScaleRows;  // the block's K/V scale tile
+    const float skb = load_uniform(sk, ks_);
+    const float fk = skb * rsk;
+    const float cs = p.c * sqt * skb;
+    const float cdp = sdot * load_uniform(sv, ks_) * fk;  // dP, times the dQ fold
+    const float dl = delta * fk;                          // delta, times the dQ fold
+    const bool full = (kb + 1) * kBlk <= Nk && qw_first + 31 < Nq && (!CAUSAL || kb * kBlk + kBlk - 1 <= qw_first);
+    uint4 d8[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (full) d8[mb] = half_step(st, kb, mb, cs, cdp, dl, std::false_type{});
+      else d8[mb] = half_step(st, kb, mb, cs, cdp, dl, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dQ^T += K^T dS^T over the block's 64 keys
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      uint4 a0, a1;
+      tr_frag(st + kBlkB, tro.off[db], a0, a1);
+      acc[db] = mfma8<kFmtE4m3, kFmtE5m2>(a0, a1, d8[0], d8[1], acc[db]);
     }
   };
 
@@ -416,57 +589,18 @@ __device__ __forceinline__ void dq8_body(const Bwd8Params& p, const int head, co
   for (int kb = 0; kb < n_kb; ++kb) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    uint8_t* const st = lds + (kb & 1) * kStageQ;
-    if (kb + 1 < n_kb) load_stage(kb + 1, lds + ((kb + 1) & 1) * kStageQ);
-    const uint8_t* tk = st;
-    const uint8_t* tkT = st + kBlkB;
-    const uint8_t* tv = st + 2 * kBlkB;
-
-    const int ks_ = (kb * kBlk) / kScaleRows;  // the block's K/V scale tile
-    const float skb = load_uniform(sk, ks_);
-    const float cs = p.c * sqt * skb;
-    const float cdp = sdot * load_uniform(sv, ks_);
-    const float fk = skb / sk_max;
-    // S^T = K Q^T and dP^T = V dO^T for key rows 32 mb .. of the block
-    f32x16_t s[2], dpa[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = f32x16_t{};
-      dpa[mb] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        uint4 a0, a1;
-        row_frag(tk, mb * 32 + c, ks, hh, a0, a1);
-        s[mb] = mfma8<kFmtE4m3, kFmtE4m3>(a0, a1, qf[ks][0], qf[ks][1], s[mb]);
-        row_frag(tv, mb * 32 + c, ks, hh, a0, a1);
-        dpa[mb] = mfma8<kFmtE4m3, kFmtE5m2>(a0, a1, df[ks][0], df[ks][1], dpa[mb]);
-      }
-    }
-    // element (mb, i) is key kb*64 + 32 mb + 8 (i/4) + 4 hh + i%4
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb * kBlk + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
-        const bool ok = q_ok && key < Nk && (!CAUSAL || key <= my_q);
-        const float pv = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][i], cs, -L * kLog2e)) : 0.f;
-        dpa[mb][i] = pv * __builtin_fmaf(dpa[mb][i], cdp, -dl) * fk;
-      }
-    }
-    const uint4 d0 = pack16_e5m2(dpa[0]), d1 = pack16_e5m2(dpa[1]);
-    // dQ^T += K^T dS^T over the block's 64 keys
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      uint4 a0, a1;
-      tr_frag(tkT, tro.off[db], a0, a1);
-      acc[db] = mfma8<kFmtE4m3, kFmtE5m2>(a0, a1, d0, d1, acc[db]);
-    }
+    with_slots(lds + ((kb + 1) & 1) * kStageQ, lds + (kb & 1) * kStageQ,
+               [&](uint8_t* w, const uint8_t* r) __attribute__((always_inline)) {
+                 if (kb + 1 < n_kb) load_stage(kb + 1, w);
+                 step(kb, r);
+               });
   }
   if (my_q < Nq) store_rows_bf16((uint16_t*)p.dq + (q_row0 + my_q) * kD, acc, p.scale * sk_max, hh);
 }
 
 template <bool CAUSAL>
-__global__ void __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64))) bwd8_dkdv_kernel(Bwd8Params p) {
+__global__ void __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64), amdgpu_waves_per_eu(2, 2)))
+bwd8_dkdv_kernel(Bwd8Params p) {
   const int w = xcd_remap(blockIdx.x, p.n_work);
   const int nkt = (p.Nk + kScaleRows - 1) / kScaleRows;
   const int head = w / nkt;
@@ -474,7 +608,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64)))
 }
 
 template <bool CAUSAL>
-__global__ void __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64))) bwd8_dq_kernel(Bwd8Params p) {
+__global__ void __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64), amdgpu_waves_per_eu(2, 2)))
+bwd8_dq_kernel(Bwd8Params p) {
   const int w = xcd_remap(blockIdx.x, p.n_work);
   const int nqt = (p.Nq + kScaleRows - 1) / kScaleRows;
   const int head = w / nqt;

@@ -96,7 +96,7 @@ struct Bwd8Params {
   const void* o;         // bfloat16 [B, H, Nq, 128]: the forward's output
   const void* dout;      // bfloat16 [B, H, Nq, 128]
   const float* lse;      // [B, H, Nq]
-  float* delta;          // workspace [B, H, Nq]: rowsum(dO * O)
+  float* stats;          // workspace [3, B, H, Nq]: lse log2(e); delta = rowsum(dO * O); delta s_q(tile) / max s_q
   uint8_t* do8;          // workspace [B, H, Nq, 128]: e5m2 codes of dO
   float* do_scale;       // workspace [B, H, ceil(Nq/128)]
   void* dq;              // bfloat16 outputs

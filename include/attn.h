@@ -312,9 +312,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  *   o (bfloat16 [B, H, Nq, 128]) and lse (fp32 [B, H, Nq]): attn_fwd's
  *     outputs for the same inputs, scale and causal;
  *   dout bfloat16 [B, H, Nq, 128]; dq, dk, dv bfloat16, shaped as q8, k8, v8;
- *   workspaces, caller-owned, overwritten: delta fp32 [B, H, Nq] (on return
- *     delta_i), do8 uint8 [B, H, Nq, 128] (dO's e5m2 codes) and do_scale
- *     fp32 [B, H, ceil(Nq/128)] (their scales);
+ *   workspaces, caller-owned, overwritten: stats fp32 [3, B, H, Nq] (on
+ *     return lse_i log2(e), delta_i, and delta_i s_q(tile) / max s_q), do8
+ *     uint8 [B, H, Nq, 128] (dO's e5m2 codes) and do_scale fp32
+ *     [B, H, ceil(Nq/128)] (their scales);
  *   d other than 128: ATTN_ERR_UNSUPPORTED.  2-D arrays 16-byte aligned,
  *   lse, scales, delta 4-byte aligned.
  *   Query-side arrays may be NULL only if Nq = 0, key-side arrays only if
@@ -324,7 +325,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  */
 int attn_bwd_fp8(const void* q8, const float* q_scale, const void* k8, const float* k_scale, const void* v8,
                  const float* v_scale, const void* o, const float* lse, const void* dout, void* dq, void* dk,
-                 void* dv, float* delta, void* do8, float* do_scale, int B, int H, int Nq, int Nk, int d,
+                 void* dv, float* stats, void* do8, float* do_scale, int B, int H, int Nq, int Nk, int d,
                  float scale, int causal, void* hip_stream);
 
 /* attn_strerror — a static, human-readable name for a return code. */

@@ -286,19 +286,19 @@ def test_bwd_unsupported_and_empty(lib):
 
 def bwd8_call(**over):
     a = dict(q8=FAKE, sq=FAKE, k8=FAKE, sk=FAKE, v8=FAKE, sv=FAKE, o=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE,
-             dv=FAKE, delta=FAKE, do8=FAKE, sdo=FAKE, B=1, H=2, Nq=256, Nk=256, d=128, scale=0.125, causal=0)
+             dv=FAKE, stats=FAKE, do8=FAKE, sdo=FAKE, B=1, H=2, Nq=256, Nk=256, d=128, scale=0.125, causal=0)
     a.update(over)
     return attn.attn_bwd_fp8(a["q8"], a["sq"], a["k8"], a["sk"], a["v8"], a["sv"], a["o"], a["lse"], a["dout"],
-                             a["dq"], a["dk"], a["dv"], a["delta"], a["do8"], a["sdo"], a["B"], a["H"], a["Nq"],
+                             a["dq"], a["dk"], a["dv"], a["stats"], a["do8"], a["sdo"], a["B"], a["H"], a["Nq"],
                              a["Nk"], a["d"], a["scale"], a["causal"], None)
 
 
 BWD8_INVALID = [dict(**{k: None}) for k in ("q8", "sq", "k8", "sk", "v8", "sv", "o", "lse", "dout", "dq", "dk", "dv",
-                                            "delta", "do8", "sdo")] + [
+                                            "stats", "do8", "sdo")] + [
     dict(B=0), dict(H=0), dict(Nq=-1), dict(Nk=-1), dict(scale=float("nan")), dict(scale=-0.5), dict(causal=3),
     dict(q8=FAKE + 8), dict(k8=FAKE + 4), dict(v8=FAKE + 1), dict(o=FAKE + 8), dict(dout=FAKE + 2),
     dict(dq=FAKE + 8), dict(dk=FAKE + 8), dict(dv=FAKE + 8), dict(do8=FAKE + 8), dict(sq=FAKE + 2),
-    dict(sk=FAKE + 1), dict(sv=FAKE + 3), dict(lse=FAKE + 2), dict(delta=FAKE + 2), dict(sdo=FAKE + 1),
+    dict(sk=FAKE + 1), dict(sv=FAKE + 3), dict(lse=FAKE + 2), dict(stats=FAKE + 2), dict(sdo=FAKE + 1),
     dict(B=1 << 16, H=1 << 14, Nq=1 << 12),  # more than 2^31 - 1 workgroups
 ]
 
@@ -311,7 +311,7 @@ def test_bwd_fp8_invalid(lib, over):
 def test_bwd_fp8_unsupported_and_empty(lib):
     for d in (64, 256, 80):
         assert bwd8_call(d=d) == attn.ATTN_ERR_UNSUPPORTED
-    none = {k: None for k in ("q8", "sq", "k8", "sk", "v8", "sv", "o", "lse", "dout", "dq", "dk", "dv", "delta",
+    none = {k: None for k in ("q8", "sq", "k8", "sk", "v8", "sv", "o", "lse", "dout", "dq", "dk", "dv", "stats",
                               "do8", "sdo")}
     assert bwd8_call(Nq=0, Nk=0, **none) == attn.ATTN_OK
 

@@ -99,7 +99,7 @@ def _problem(B, H, nq, nk, seed, causal, scale, do_kind):
 
 
 def _run(attn, pr, scale, causal):
-    ws = (torch.full(pr["lse32"].shape, float("nan"), dtype=torch.float32, device="cuda"),
+    ws = (torch.full((3,) + pr["lse32"].shape, float("nan"), dtype=torch.float32, device="cuda"),
           torch.full(pr["q8"].shape, 0xFF, dtype=torch.uint8, device="cuda"),
           torch.full(pr["lse32"].shape[:-1] + (_nt(pr["q8"].shape[-2]),), float("nan"), dtype=torch.float32,
                      device="cuda"))
@@ -234,11 +234,15 @@ def test_bwd_fp8_vs_oracle(gpu_lib, causal, nq, nk, do_kind):
     got, ws = _run(gpu_lib, pr, scale, causal)
     parts = _oracle(pr, scale, causal)
     what = f"fp8 bwd causal={causal} {nq}x{nk} dO {do_kind}"
-    # workspace: dO codes and scales bit for bit, delta within its fp32 sum
+    # workspace: dO codes and scales bit for bit; lse log2(e) as one fp32
+    # product; delta within its fp32 sum, and its folded copy
     assert np.array_equal(ws[1], parts["do8"]), f"{what}: dO codes differ"
     assert np.array_equal(ws[2], parts["sdo"]), f"{what}: dO scales differ"
+    assert np.array_equal(ws[0][0], pr["lse32"] * np.float32(F.LOG2E)), f"{what}: lse log2(e)"
     sum_od = np.abs(pr["o16"].double().numpy() * pr["do16"].double().numpy()).sum(-1)
-    assert np.all(np.abs(ws[0] - parts["delta"]) <= 2.0 ** -17 * sum_od + 1e-30), f"{what}: delta"
+    assert np.all(np.abs(ws[0][1] - parts["delta"]) <= 2.0 ** -17 * sum_od + 1e-30), f"{what}: delta"
+    fq = _rows(pr["sq"], nq) / parts["fold"]["sq_max"]
+    assert np.all(np.abs(ws[0][2] - parts["delta"] * fq) <= 2.0 ** -17 * sum_od * fq + 1e-30), f"{what}: delta f_q"
     allow = _allowance(pr, parts, scale)
     _check(got, (parts["dq"], parts["dk"], parts["dv"]), allow, what)
     if nk > 1:  # one key: dQ = dK = 0 (dP = delta), nothing to compare the allowance with
@@ -266,7 +270,7 @@ def test_bwd_fp8_do_quantisation_range(gpu_lib):
 def test_bwd_fp8_empty_sides(gpu_lib):
     """Nk = 0: dQ = 0; Nq = 0: dK = dV = 0."""
     pr = _problem(1, 2, 200, 1, seed=3, causal=False, scale=0.1, do_kind="normal")
-    ws = (torch.empty((1, 2, 200), dtype=torch.float32, device="cuda"),
+    ws = (torch.empty((3, 1, 2, 200), dtype=torch.float32, device="cuda"),
           torch.empty((1, 2, 200, D), dtype=torch.uint8, device="cuda"),
           torch.empty((1, 2, 2), dtype=torch.float32, device="cuda"))
     e8 = torch.empty((1, 2, 0, D), dtype=torch.uint8, device="cuda")
