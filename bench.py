@@ -277,7 +277,10 @@ def bench_backward(attn, steps, warmup):
     bf16 shape B=2 H=16 N=4096 d=128, non-causal and causal, and on the
     large-head shape B=1 H=16 N=8192 d=256 (non-causal).  FLOPs are those
     of the five products of the gradient (S, dP, dV, dK, dQ: 10 B H N^2 d,
-    halved for causal); the kernels recompute S and dP once more for dQ."""
+    halved for causal); the kernels recompute S and dP once more for dQ.
+    The d=128 shapes are also run through attn_bwd_fp8 (e4m3 inputs from
+    attn_fp8_quantize, E5M2 gradient operands), priced against the fp8
+    peak with the same FLOP count."""
     import numpy as np
     import torch
 
@@ -304,6 +307,29 @@ def bench_backward(attn, steps, warmup):
         tf = flops / (ms / 1e3) / 1e12
         out["bwd_" + name] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                               "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
+        if w.d == 128:
+            # the same shape on e4m3 operands with E5M2 gradients (attn_bwd_fp8)
+            q8, sq = attn.fp8_quantize(q)
+            k8, sk = attn.fp8_quantize(k)
+            v8, sv = attn.fp8_quantize(v)
+            o8, lse8 = attn.forward(q8, k8, v8, causal=w.causal, scale=w.scale, q_scale=sq, k_scale=sk,
+                                    v_scale=sv)
+            ws = (torch.empty((3,) + tuple(q.shape[:-1]), dtype=torch.float32, device="cuda"),
+                  torch.empty(q.shape, dtype=torch.uint8, device="cuda"),
+                  torch.empty(tuple(q.shape[:-2]) + ((w.Nq + 127) // 128,), dtype=torch.float32, device="cuda"))
+
+            def run8():
+                attn.backward_fp8(q8, sq, k8, sk, v8, sv, o8, lse8, do, causal=w.causal, scale=w.scale, dq=dq,
+                                  dk=dk, dv=dv, workspace=ws)
+
+            for _ in range(warmup):
+                run8()
+            ms8 = float(np.mean(timed_launches(run8, steps, stream)))
+            tf8 = flops / (ms8 / 1e3) / 1e12
+            out["bwd_fp8_" + name.replace("_bf16", "")] = {
+                "ms": round(ms8, 4), "tflops": round(tf8, 2), "frac": round(tf8 / PEAK_FP8_TFLOPS, 4),
+                "vs_bf16": round(ms8 / ms, 4), "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
+            del q8, k8, v8, o8, lse8, ws
         del q, k, v, do, o, lse, dq, dk, dv, delta
     return out
 
