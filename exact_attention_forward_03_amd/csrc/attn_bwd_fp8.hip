@@ -110,12 +110,14 @@ __device__ __forceinline__ void tr_frag(const uint8_t* t, uint32_t off, uint4& f
 }
 
 // Sixteen fp32 values -> 16 e4m3 / e5m2 codes (round to nearest even; e5m2
-// clamped to +-57344 first).
+// clamped to +-57344 first).  Each first conversion's "old" operand (whose
+// upper half it keeps, and the second conversion overwrites) is its first
+// value's bits, so no register has to be zeroed for it.
 __device__ __forceinline__ uint4 pack16_e4m3(const f32x16_t& v) {
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int x = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i], v[4 * i + 1], 0, false);
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i], v[4 * i + 1], __builtin_bit_cast(int, v[4 * i]), false);
     w[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i + 2], v[4 * i + 3], x, true);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
@@ -125,7 +127,8 @@ __device__ __forceinline__ uint4 pack16_e5m2(const f32x16_t& v) {
   uint32_t w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int x = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_e5m2(v[4 * i]), clamp_e5m2(v[4 * i + 1]), 0, false);
+    const float a = clamp_e5m2(v[4 * i]);
+    int x = __builtin_amdgcn_cvt_pk_bf8_f32(a, clamp_e5m2(v[4 * i + 1]), __builtin_bit_cast(int, a), false);
     w[i] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(clamp_e5m2(v[4 * i + 2]), clamp_e5m2(v[4 * i + 3]), x, true);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
@@ -409,9 +412,9 @@ __device__ __forceinline__ void dkdv8_body(const Bwd8Params& p, const int head, 
         xp[j] = pv * fp;
       }
       pw[g] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
-          xp[2], xp[3], __builtin_amdgcn_cvt_pk_fp8_f32(xp[0], xp[1], 0, false), true);
+          xp[2], xp[3], __builtin_amdgcn_cvt_pk_fp8_f32(xp[0], xp[1], __builtin_bit_cast(int, xp[0]), false), true);
       dw[g] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(
-          xs[2], xs[3], __builtin_amdgcn_cvt_pk_bf8_f32(xs[0], xs[1], 0, false), true);
+          xs[2], xs[3], __builtin_amdgcn_cvt_pk_bf8_f32(xs[0], xs[1], __builtin_bit_cast(int, xs[0]), false), true);
       __builtin_amdgcn_sched_barrier(0);
     }
     p8 = make_uint4(pw[0], pw[1], pw[2], pw[3]);
@@ -556,7 +559,7 @@ __device__ __forceinline__ void dq8_body(const Bwd8Params& p, const int head, co
         xs[j] = clamp_e5m2(pv * __builtin_fmaf(dpa[i], cdp, -dl));
       }
       dw[g] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(
-          xs[2], xs[3], __builtin_amdgcn_cvt_pk_bf8_f32(xs[0], xs[1], 0, false), true);
+          xs[2], xs[3], __builtin_amdgcn_cvt_pk_bf8_f32(xs[0], xs[1], __builtin_bit_cast(int, xs[0]), false), true);
     }
     return make_uint4(dw[0], dw[1], dw[2], dw[3]);
   };

@@ -61,8 +61,11 @@ __device__ __forceinline__ void fp8_wait_vm() {
 __device__ __forceinline__ int k8_chunk(int r, int ch) { return ch ^ ((r >> 1) & 7); }
 __device__ __forceinline__ int v8_chunk(int r, int ch) { return ch ^ (((r >> 1) & 1) << 1) ^ (((r >> 3) & 1) << 2); }
 
+// The first conversion's "old" operand (whose upper half it keeps) is a's
+// own bits: the second conversion overwrites that half, and a dies here, so
+// the result takes a's register and needs no zeroing move.
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
@@ -482,20 +485,23 @@ hipError_t launch_fp8(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Configurations: non-causal, 8-wave workgroups with a 4-slot ring (one per
-// CU, 128 KiB; 1.5-2 % over 3 slots, measured at N = 4096 and 8192);
-// causal, 4-wave workgroups with a 2-slot ring (64 KiB: two per CU, so one
-// workgroup's short diagonal tiles do not idle the CU; +3 % measured).
-bool fp8_small_wg(bool causal) { return causal; }
+// Configuration: 4-wave workgroups with a 2-slot ring (64 KiB), two per CU.
+// The two waves that share a SIMD then belong to different workgroups, whose
+// barriers are independent, so one wave's MFMA chains run while the other
+// does its softmax work.  (One 8-wave workgroup per CU with a 4-slot ring
+// puts two waves of the same workgroup on each SIMD, where the per-tile
+// barrier keeps them in step: 631 -> 593 us at B2 H16 N8192 non-causal.)
+// Causal launches also keep one workgroup's short diagonal tiles from
+// idling the CU.
 
 }  // namespace
 
-int fwd_fp8_block_rows(bool causal) { return fp8_small_wg(causal) ? 128 : 256; }
+int fwd_fp8_block_rows(bool causal) { return 128; }
 
 hipError_t launch_fwd_fp8(int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
   if (d != kFp8D) return hipErrorInvalidValue;
-  if (varlen) return causal ? launch_fp8<true, 4, 2, true>(p, st) : launch_fp8<false, 8, 4, true>(p, st);
-  return causal ? launch_fp8<true, 4, 2, false>(p, st) : launch_fp8<false, 8, 4, false>(p, st);
+  if (varlen) return causal ? launch_fp8<true, 4, 2, true>(p, st) : launch_fp8<false, 4, 2, true>(p, st);
+  return causal ? launch_fp8<true, 4, 2, false>(p, st) : launch_fp8<false, 4, 2, false>(p, st);
 }
 
 }  // namespace attn
