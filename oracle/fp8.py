@@ -35,9 +35,11 @@ design notes):
 * in the PV product, P is rounded to e4m3 tile by tile, in the order of the
   online-softmax recurrence ("Flash Attention 3：让 GPU 跑满的注意力计算",
   §2.2: the term of key block j enters as exp(S_j - m_new) V_j, m_new the
-  running max after block j).  The key blocks are the 128-key scale tiles;
-  t = S log2(e) are the scores in base 2; M_j = max(M_{j-1}, ceil(max of t
-  over tile j)) is the running integer max (M = M_last = ceil(max_j t));
+  running max after block j).  The key blocks are the key tiles of the
+  kernel's recurrence: the 128-key scale tiles for d <= 128, and 64-key
+  halves of them for d = 256 (``block``); t = S log2(e) are the scores in
+  base 2; M_j = max(M_{j-1}, ceil(max of t over block j)) is the running
+  integer max (M = M_last = ceil(max_j t));
   w = s_v(tile) / max_tiles s_v is the tile's V scale relative to the
   largest V scale of that head.  Tile j's codes are
   P8 = e4m3(2^8 * 2^(t - M_j) * w), and they enter O with the exact factor
@@ -230,14 +232,15 @@ P_SCALE_LOG2 = 8  # P is rounded as e4m3(2^8 * p), p <= 1, so codes stay <= 256
 
 def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
                   tile: int = 128, quantize_p: bool = True, rows=None, ambiguity=0.0,
-                  parts: bool = False, p_mode: str = "folded"):
+                  parts: bool = False, p_mode: str = "folded", block=None):
     """fp8 attention of one or more heads: codes [..., N, d], scales [..., nt].
 
     S = scale * (sq q8)(sk k8)^T, softmax statistics in float64, and P
     rounded to e4m3 as stated in the module docstring.  With
     ``quantize_p=False`` P is kept exact (the method without P rounding).
     ``rows`` (query indices) restricts the output to those query rows.
-    Returns float64 ``(O [..., Nq, d], lse [..., Nq])``.
+    ``block`` is the key-block length of the running max (default ``tile``;
+    a divisor of it).  Returns float64 ``(O [..., Nq, d], lse [..., Nq])``.
 
     With ``ambiguity = delta > 0`` a third array [..., Nq, d] is returned:
     the largest change of O that re-rounding, to the other neighbouring code,
@@ -258,7 +261,8 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     the final M, [..., Nq, Nk]), "x" (P before rounding, in code units of its
     tile's running max), "shift" (M_j - M per key), "t" (the base-2 scores),
     "M" [..., Nq], "M_tile" (the running max per key tile), "l" [..., Nq],
-    "sv_max" [...] and "v_codes" (values of the V codes).
+    "sv_max" [...] and "v_codes" (values of the V codes); "M_tile" is per key
+    block.
     """
     qd = dequantize(q8, sq, tile)
     qrow = np.arange(qd.shape[-2])
@@ -278,13 +282,16 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     M = np.where(live, np.ceil(np.where(live, tmax, 0.0)), 0.0)
     p = np.where(live[..., None], np.exp2(t - M[..., None]), 0.0)  # <= 1
     l = p.sum(axis=-1)
-    # running integer max M_j of the 128-key tiles, in key order
-    nkt = (nk + tile - 1) // tile
-    tpad = np.concatenate([t, np.full(t.shape[:-1] + (nkt * tile - nk,), -np.inf)], axis=-1)
-    tile_max = tpad.reshape(t.shape[:-1] + (nkt, tile)).max(axis=-1) if nk else np.zeros(t.shape[:-1] + (0,))
+    # running integer max M_j of the key blocks, in key order
+    blk = tile if block is None else int(block)
+    if blk < 1 or tile % blk:
+        raise ValueError("block must divide tile")
+    nkt = (nk + blk - 1) // blk
+    tpad = np.concatenate([t, np.full(t.shape[:-1] + (nkt * blk - nk,), -np.inf)], axis=-1)
+    tile_max = tpad.reshape(t.shape[:-1] + (nkt, blk)).max(axis=-1) if nk else np.zeros(t.shape[:-1] + (0,))
     with np.errstate(invalid="ignore"):
         run = np.maximum.accumulate(np.ceil(tile_max), axis=-1) if nkt else tile_max
-    Mj = np.repeat(run, tile, axis=-1)[..., :nk]  # -inf before a row's first visible key (those keys are masked)
+    Mj = np.repeat(run, blk, axis=-1)[..., :nk]  # -inf before a row's first visible key (those keys are masked)
     fin = np.isfinite(t)
     shift = np.where(fin, Mj - M[..., None], 0.0)  # <= 0, an integer
     p_tile = np.where(fin, np.exp2(np.where(fin, t - Mj, 0.0)), 0.0)  # P relative to the running max
@@ -387,7 +394,8 @@ def quantize_varlen(x, cu, signs=None, per_tensor: bool = False, tile: int = 128
 
 
 def attention_fp8_varlen(q8, k8, v8, sq, sk, sv, cu_q, cu_k, scale: float, causal: bool = False,
-                         tile: int = 128, quantize_p: bool = True, ambiguity: float = 0.0, parts: bool = False):
+                         tile: int = 128, quantize_p: bool = True, ambiguity: float = 0.0, parts: bool = False,
+                         block=None):
     """fp8 attention of a variable-length batch: codes [H, T, d] packed along
     tokens, scales [H, varlen_scale_len] laid out as by `quantize_varlen`.
 
@@ -414,7 +422,7 @@ def attention_fp8_varlen(q8, k8, v8, sq, sk, sv, cu_q, cu_k, scale: float, causa
         ntq, ntk = (qe - qa + tile - 1) // tile, (ke - ka + tile - 1) // tile
         r = attention_fp8(q8[:, qa:qe], k8[:, ka:ke], v8[:, ka:ke], sq[:, oq[b]:oq[b] + ntq],
                           sk[:, ok[b]:ok[b] + ntk], sv[:, ok[b]:ok[b] + ntk], scale, causal, tile=tile,
-                          quantize_p=quantize_p, ambiguity=ambiguity, parts=True)
+                          quantize_p=quantize_p, ambiguity=ambiguity, parts=True, block=block)
         o[:, qa:qe] = r["o"]
         lse[:, qa:qe] = r["lse"]
         if flip is not None:

@@ -556,3 +556,37 @@ def test_p_rounding_follows_the_running_max():
     np.testing.assert_allclose(r["o"][0, :3], expect, rtol=1e-12, atol=0)
     assert np.all(r["o"][0, 3:] == 0)
     np.testing.assert_allclose(r["lse"][0], (10 + np.log2(l)) / F.LOG2E, rtol=0, atol=1e-12)
+
+
+def test_p_rounding_running_max_per_key_block():
+    """With 64-key blocks (the d = 256 kernel's tiling) the running max rises
+    within a 128-key scale tile.  One query; keys 0 (t = 0) and 1 (t = -17.4)
+    in block 0, key 64 (t = 9.7875) in block 1 of the same scale tile, every
+    other key at weight 0; V rows one-hot.  Blocks of 64: M_0 = 0, so key 1
+    codes as e4m3(2^-9.4) = 2^-9 against M_0 and enters O as 2^-19 (in units
+    of M = 10); blocks of 128: M_0 = 10 already, and key 1's code is
+    e4m3(2^-19.4) = 0.  Without P rounding the two agree exactly."""
+    d = 16
+    q8 = np.zeros((1, d), np.uint8)
+    q8[0, 0] = F.e4m3_encode(1.0)
+    k8 = np.zeros((128, d), np.uint8)
+    kv = np.full(128, -448.0)
+    kv[0], kv[1], kv[64] = 0.0, -16.0, 9.0
+    k8[:, 0] = F.e4m3_encode(kv)
+    v8 = np.zeros((128, d), np.uint8)
+    v8[0, 0] = v8[1, 1] = v8[64, 2] = F.e4m3_encode(1.0)
+    one = np.ones(1, np.float32)
+    scale = 17.4 / (16.0 * F.LOG2E)
+    r64 = F.attention_fp8(q8, k8, v8, one, one, one, scale, parts=True, block=64)
+    r128 = F.attention_fp8(q8, k8, v8, one, one, one, scale, parts=True)
+    assert list(r64["M_tile"][0]) == [0.0, 10.0] and list(r128["M_tile"][0]) == [10.0]
+    l = 2.0 ** -10 + 2.0 ** (-17.4 - 10) + 2.0 ** (9.7875 - 10)
+    np.testing.assert_allclose(r64["o"][0, :3], np.array([2.0 ** -2, 2.0 ** -19, 224.0]) * 2.0 ** -8 / l,
+                               rtol=1e-12, atol=0)
+    np.testing.assert_allclose(r128["o"][0, :3], np.array([2.0 ** -2, 0.0, 224.0]) * 2.0 ** -8 / l,
+                               rtol=1e-12, atol=0)
+    e64 = F.attention_fp8(q8, k8, v8, one, one, one, scale, quantize_p=False, block=64)
+    e128 = F.attention_fp8(q8, k8, v8, one, one, one, scale, quantize_p=False)
+    np.testing.assert_allclose(e64[0], e128[0], rtol=1e-14)
+    with pytest.raises(ValueError):
+        F.attention_fp8(q8, k8, v8, one, one, one, scale, block=48)
