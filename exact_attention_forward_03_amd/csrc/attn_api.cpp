@@ -38,7 +38,6 @@ int validate_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4)) return ATTN_ERR_INVALID_ARG;
   }
   if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
-  if (dtype == ATTN_DT_FP8_E4M3 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (cu_q == nullptr && (int64_t)B * H > (int64_t)INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
   return ATTN_OK;
 }

@@ -10,10 +10,12 @@
 // The kernel has the shape of the fp16/bf16 one (one workgroup per 32*NW
 // query rows, K/V tiles streamed from global memory straight into a ring of
 // LDS slots, S^T = K Q^T so P stays in registers), with these differences:
-//   * 32x32x64 e4m3 MFMA, fp32 accumulation; key tiles of 128 rows, so each
-//     tile has exactly one K scale and one V scale;
+//   * 32x32x64 e4m3 MFMA, fp32 accumulation; head dimension d = 64, 128 or
+//     256; key tiles of 128 rows (64 at d = 256, to fit two waves per SIMD),
+//     so each tile lies within one 128-row tile of K and V scales;
 //   * scores t = acc * (scale log2 e * s_q * s_k) in base 2; M = ceil(max t)
-//     per row (an integer, so rescaling O and l is exact);
+//     per row (an integer, so rescaling O and l is exact), updated once per
+//     key tile;
 //   * P is rounded to e4m3 as e4m3(2^(t - M + 8) * w), w = s_v(tile) /
 //     max_tiles s_v: the V tile's scale is folded into the exponent, so the
 //     PV product needs no per-tile correction of O and the codes stay <= 256;
@@ -35,14 +37,22 @@ namespace {
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kFp8D = 128;
-constexpr int kFp8BC = 128;   // key rows per tile (= rows per scale)
+constexpr int kScaleRows = 128;  // rows per Q/K/V scale
 constexpr int kFp8Pre = 4;    // K fragments (two reads each) in flight ahead of their MFMA
 constexpr int kFp8PvPre = 3;  // V^T fragments (four reads each): at most 12 LDS reads in flight,
                               // within what the 4-bit lgkmcnt counter can track
-constexpr int kRowB = kFp8D;                  // bytes per K/V row
-constexpr int kTileB = kFp8BC * kRowB;        // bytes per K or V tile
-constexpr int kLoads = kTileB / 1024;         // 1 KiB direct-to-LDS loads per tile
+
+// Tile geometry per head dimension: key rows per tile, waves per workgroup,
+// ring slots.  4-wave workgroups with a 2-slot ring, two per CU (see the
+// launch).  d = 256 takes 64-key tiles: with 128 keys the scores (64
+// registers) next to O's 128 accumulators and Q's 32 do not fit the 256
+// registers of two waves per SIMD.
+// KPRE / VPRE: K and V^T fragments in flight ahead of their MFMAs (fewer at
+// d = 256, where the registers are short).
+template <int D> struct Fp8Tile;
+template <> struct Fp8Tile<64> { static constexpr int BC = 128, NW = 4, NS = 2, KPRE = kFp8Pre, VPRE = kFp8PvPre; };
+template <> struct Fp8Tile<128> { static constexpr int BC = 128, NW = 4, NS = 2, KPRE = kFp8Pre, VPRE = kFp8PvPre; };
+template <> struct Fp8Tile<256> { static constexpr int BC = 64, NW = 4, NS = 2, KPRE = 1, VPRE = 1; };
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maximum).
 template <int N>
@@ -51,15 +61,27 @@ __device__ __forceinline__ void fp8_wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Physical 16-byte chunk (of 8 per row) of logical chunk ch in row r.
-// K fragment reads: 16 lanes read 16 consecutive rows at one logical chunk;
-// with 128-byte rows, rows r and r+1 share a bank line, so the chunk is
-// XOR-ed with bits 1..3 of the row: the 16 reads hit 16 different 16-byte
-// bank slots.  V transposing reads: 32 lanes read 8 rows {0..3, 8..11} + 4h
-// (plus a multiple of 16) at two neighbouring chunks; XOR-ing with
-// 2 * bit1 + 4 * bit3 of the row spreads them over 16 slots.
-__device__ __forceinline__ int k8_chunk(int r, int ch) { return ch ^ ((r >> 1) & 7); }
-__device__ __forceinline__ int v8_chunk(int r, int ch) { return ch ^ (((r >> 1) & 1) << 1) ^ (((r >> 3) & 1) << 2); }
+// Physical 16-byte chunk (of D/16 per row) of logical chunk ch in row r.
+// The LDS serves 256 bytes (64 banks) per cycle.  K fragment reads: 16
+// lanes read 16 consecutive rows at one logical chunk; 256/D rows share a
+// bank line, so the chunk is XOR-ed with the row's bank-line index (mod the
+// chunk count): the 16 reads hit 16 different 16-byte bank slots.  V
+// transposing reads: 32 lanes read 8 rows {0..3, 8..11} + 4h (plus a
+// multiple of 16) at two neighbouring chunks, 8 bytes each; the XOR below
+// spreads those 32 pieces over all 64 banks (d = 128: 2 bit1 + 4 bit3 of the
+// row; d = 64: 2 bit3; d = 256: 2 (r mod 4) + 8 bit3).  Both depend on the
+// row mod 16 only.
+template <int D>
+__device__ __forceinline__ int k8_chunk(int r, int ch) {
+  constexpr int CH = D / 16, RPL = D >= 256 ? 1 : 256 / D;
+  return ch ^ ((r / RPL) % CH);
+}
+template <int D>
+__device__ __forceinline__ int v8_chunk(int r, int ch) {
+  if constexpr (D == 64) return ch ^ (((r >> 3) & 1) << 1);
+  else if constexpr (D == 128) return ch ^ (((r >> 1) & 1) << 1) ^ (((r >> 3) & 1) << 2);
+  else return ch ^ ((r & 3) << 1) ^ (((r >> 3) & 1) << 3);
+}
 
 // The first conversion's "old" operand (whose upper half it keeps) is a's
 // own bits: the second conversion overwrites that half, and a dies here, so
@@ -70,14 +92,21 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return (uint32_t)w;
 }
 
-// NW waves per workgroup (32 query rows each), NS LDS ring slots.  VARLEN:
-// a packed batch [H, T, d] with cu_seqlens; the work item is (head,
-// sequence, query tile) and the scales of sequence s start at entry
-// sum_{s' < s} ceil(L_s' / 128) of the head's ceil(T / 128) + B entries.
-template <bool CAUSAL, int NW, int NS, bool VARLEN>
+// D head dimension, BC key rows per tile, NW waves per workgroup (32 query
+// rows each), NS LDS ring slots.  VARLEN: a packed batch [H, T, d] with
+// cu_seqlens; the work item is (head, sequence, query tile) and the scales of
+// sequence s start at entry sum_{s' < s} ceil(L_s' / 128) of the head's
+// ceil(T / 128) + B entries.
+template <int D, int BC, bool CAUSAL, int NW, int NS, bool VARLEN>
 __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
-  constexpr int D = kFp8D, BC = kFp8BC;
+  constexpr int SC = kScaleRows;
+  constexpr int kRowB = D;               // bytes per K/V row
+  constexpr int kTileB = BC * kRowB;     // bytes per K or V tile
+  constexpr int kLoads = kTileB / 1024;  // 1 KiB direct-to-LDS loads per tile
+  constexpr int CH = D / 16;             // 16-byte chunks per row
+  constexpr int RPB = 1024 / D;          // rows per 1 KiB block
   constexpr int BR = NW * 32;
+  static_assert(SC % BR == 0 && SC % BC == 0, "query and key tiles lie within one scale tile");
   constexpr int KS = D / 64;    // MFMA k-steps of S^T
   constexpr int MB = BC / 32;   // 32-key blocks per tile
   constexpr int DB = D / 32;    // 32-row blocks of O^T
@@ -97,11 +126,11 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
     k_len = p.Nk;
     q_row0 = (int64_t)head * p.Nq;
     k_row0 = (int64_t)head * p.Nk;
-    sq0 = (int64_t)head * ((q_len + BC - 1) / BC);
-    sk0 = (int64_t)head * ((k_len + BC - 1) / BC);
+    sq0 = (int64_t)head * ((q_len + SC - 1) / SC);
+    sk0 = (int64_t)head * ((k_len + SC - 1) / SC);
   } else {
     // sequence of query tile t (tiles of BR rows per sequence), and the
-    // scale tiles (BC = 128 rows) of the sequences before it
+    // scale tiles (SC = 128 rows) of the sequences before it
     int acc = 0, seq = -1, qb = 0, qe = 0, kb = 0, ke = 0, nts = 0, tq = 0, tk = 0;
     for (int s = 0; s < p.B; ++s) {
       const int a = min(max(p.cu_q[s], 0), p.Nq);
@@ -114,8 +143,8 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
         break;
       }
       acc += nt;
-      tq += (b - a + BC - 1) / BC;
-      tk += (kz - ka + BC - 1) / BC;
+      tq += (b - a + SC - 1) / SC;
+      tk += (kz - ka + SC - 1) / SC;
     }
     if (seq < 0) return;  // surplus work item (the grid is an upper bound)
     qt = CAUSAL ? (nts - 1 - (t - acc)) : (t - acc);
@@ -123,11 +152,11 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
     k_len = ke - kb;
     q_row0 = (int64_t)head * p.Nq + qb;
     k_row0 = (int64_t)head * p.Nk + kb;
-    sq0 = (int64_t)head * ((p.Nq + BC - 1) / BC + p.B) + tq;
-    sk0 = (int64_t)head * ((p.Nk + BC - 1) / BC + p.B) + tk;
+    sq0 = (int64_t)head * ((p.Nq + SC - 1) / SC + p.B) + tq;
+    sk0 = (int64_t)head * ((p.Nk + SC - 1) / SC + p.B) + tk;
   }
   const int q0 = qt * BR;
-  const int nks = (k_len + BC - 1) / BC;
+  const int nks = (k_len + SC - 1) / SC;
   const float* __restrict__ sk = p.k_scale + sk0;
   const float* __restrict__ sv = p.v_scale + sk0;
 
@@ -137,7 +166,12 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-  const int lane = tid & 63, c = lane & 31, hh = lane >> 5;
+  // the lane index through an empty asm: a launch that runs two bodies one
+  // after the other then forms the per-lane offsets in each body, rather
+  // than once for both, live (and spilled) across the first
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));
+  const int c = lane & 31, hh = lane >> 5;
   const int qw0 = q0 + wv * 32;
   const int my_q = qw0 + c;
   const bool q_ok = my_q < q_len;
@@ -149,7 +183,7 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) sv_max = fmaxf(sv_max, __shfl_xor(sv_max, s));
   const float lsv_max = sv_max > 0.f ? __log2f(sv_max) : 0.f;
-  const float sq = wave_live ? p.q_scale[sq0 + qw0 / BC] : 0.f;
+  const float sq = wave_live ? p.q_scale[sq0 + qw0 / SC] : 0.f;
 
   // Q fragments (B operand of S^T): row my_q, bytes [64 ks + 32 hh, +32)
   uint4 qf[KS][2];
@@ -177,25 +211,25 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
 
   // Direct-to-LDS load of one tile into ring slot `buf`: the wave's i-th
-  // instruction fills 1 KiB block i * NW + wv (8 rows) of K and of V; lane l
-  // writes physical chunk l % 8 of row 8 * block + l / 8 and fetches the
-  // logical chunk stored there.  The rows come through buffer resources
+  // instruction fills 1 KiB block i * NW + wv (RPB rows) of K and of V; lane
+  // l writes physical chunk l % CH of row RPB * block + l / CH and fetches
+  // the logical chunk stored there.  The rows come through buffer resources
   // based at the tile's first key: the swizzles read the row mod 16, which
   // does not depend on i, so a lane's byte offset is the same for every
   // load and tile and the block offset is a scalar.  The resources cover only
   // the tile's keys; a last tile that runs past them re-reads the last key
   // (finite codes, masked) through per-lane clamped offsets.
-  static_assert((NW * 8) % 16 == 0, "block rounds span whole swizzle periods");
+  static_assert((NW * RPB) % 16 == 0, "block rounds span whole swizzle periods");
   auto load_tile = [&](int kt, uint8_t* kdst, uint8_t* vdst) {
     const int rows = min(BC, k_len - kt * BC);  // >= 1: only tiles holding keys are loaded
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(Kp + (int64_t)kt * BC * kRowB), 0, rows * kRowB, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv =
         __builtin_amdgcn_make_buffer_rsrc((void*)(Vp + (int64_t)kt * BC * kRowB), 0, rows * kRowB, kBufferFlags);
-    const int r0 = wv * 8 + (lane >> 3);  // row of the lane's first block; later blocks agree mod 16
+    const int r0 = wv * RPB + lane / CH;  // row of the lane's first block; later blocks agree mod 16
     if (rows == BC) {
-      const uint32_t offk = (uint32_t)((lane >> 3) * kRowB + k8_chunk(r0, lane & 7) * 16);
-      const uint32_t offv = (uint32_t)((lane >> 3) * kRowB + v8_chunk(r0, lane & 7) * 16);
+      const uint32_t offk = (uint32_t)((lane / CH) * kRowB + k8_chunk<D>(r0, lane % CH) * 16);
+      const uint32_t offv = (uint32_t)((lane / CH) * kRowB + v8_chunk<D>(r0, lane % CH) * 16);
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int blk = i * NW + wv;
@@ -209,18 +243,23 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
                                                  (uint32_t)(blk * 1024), 0, 0);
       }
     } else {
+      // the lane index through an empty asm: the per-lane rows and chunks of
+      // this rare path are then computed here, not hoisted out of the tile
+      // loop to occupy registers (or scratch) for the whole kernel
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int blk = i * NW + wv;
-        const int r = blk * 8 + (lane >> 3);
-        const uint32_t off = (uint32_t)(min(r, rows - 1) * kRowB + k8_chunk(r, lane & 7) * 16);
+        const int r = blk * RPB + ln / CH;
+        const uint32_t off = (uint32_t)(min(r, rows - 1) * kRowB + k8_chunk<D>(r, ln % CH) * 16);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + blk * 1024), 16, off, 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int blk = i * NW + wv;
-        const int r = blk * 8 + (lane >> 3);
-        const uint32_t off = (uint32_t)(min(r, rows - 1) * kRowB + v8_chunk(r, lane & 7) * 16);
+        const int r = blk * RPB + ln / CH;
+        const uint32_t off = (uint32_t)(min(r, rows - 1) * kRowB + v8_chunk<D>(r, ln % CH) * 16);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + blk * 1024), 16, off, 0, 0, 0);
       }
     }
@@ -232,21 +271,22 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
     auto frag = [&](int i, uint4 (&f)[2]) {
       const int r = (i % MB) * 32 + c;
       const int ch = 4 * (i / MB) + 2 * hh;
-      f[0] = *(const uint4*)(kb + r * kRowB + k8_chunk(r, ch) * 16);
-      f[1] = *(const uint4*)(kb + r * kRowB + k8_chunk(r, ch + 1) * 16);
+      f[0] = *(const uint4*)(kb + r * kRowB + k8_chunk<D>(r, ch) * 16);
+      f[1] = *(const uint4*)(kb + r * kRowB + k8_chunk<D>(r, ch + 1) * 16);
     };
-    uint4 fr[kFp8Pre][2];
+    constexpr int PRE = Fp8Tile<D>::KPRE < N ? Fp8Tile<D>::KPRE : N;
+    uint4 fr[PRE][2];
 #pragma unroll
-    for (int i = 0; i < kFp8Pre; ++i) frag(i, fr[i]);
+    for (int i = 0; i < PRE; ++i) frag(i, fr[i]);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) s[mb] = f32x16_t{};
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const uint4 a0 = fr[i % kFp8Pre][0], a1 = fr[i % kFp8Pre][1];
+      const uint4 a0 = fr[i % PRE][0], a1 = fr[i % PRE][1];
       s[i % MB] = mfma32_fp8(a0, a1, qf[i / MB][0], qf[i / MB][1], s[i % MB]);
-      if (i + kFp8Pre < N) frag(i + kFp8Pre, fr[i % kFp8Pre]);
+      if (i + PRE < N) frag(i + PRE, fr[i % PRE]);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -262,19 +302,38 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   // lane's part of the row (the rest is a multiple of 16): each lane's byte
   // offset within a tile is one of DB loop-invariant values (one per output
   // block), and the row steps are immediate offsets of the reads.
-  uint32_t vlane[DB];
+  // At d = 256 the eight offsets would not fit beside O's 128 accumulators:
+  // there the lane keeps its row-and-half base and the XOR key of its row
+  // (v8_chunk flips chunk bits 1..3 only, so chunk 2 db + g of row lr sits
+  // at 2 (db ^ key) + g) and forms each offset when the fragment is read.
+  constexpr bool kVlaneArray = D < 256;
+  uint32_t vlane[kVlaneArray ? DB : 1];
+  uint32_t vbase = 0, vkey = 0;
   {
     const int G = lane >> 4, s16 = lane & 15, b = s16 >> 1;
     const int lr = 8 * (b >> 2) + 4 * hh + (b & 3);  // the lane's row within 16
+    if constexpr (kVlaneArray) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      vlane[db] = (uint32_t)(lr * kRowB + v8_chunk(lr, 2 * db + (G & 1)) * 16 + 8 * (s16 & 1));
+      for (int db = 0; db < DB; ++db)
+        vlane[db] = (uint32_t)(lr * kRowB + v8_chunk<D>(lr, 2 * db + (G & 1)) * 16 + 8 * (s16 & 1));
+    } else {
+      vbase = (uint32_t)(lr * kRowB + (G & 1) * 16 + 8 * (s16 & 1));
+      vkey = (uint32_t)(v8_chunk<D>(lr, 0) >> 1);
+    }
   }
   auto pv_pass = [&](const uint8_t* vb, const uint4 (&pp)[PG][2]) {
+    // the key through an empty asm, so that the offsets are formed here and
+    // not hoisted out of the tile loop (eight registers again)
+    uint32_t vk = vkey;
+    if constexpr (!kVlaneArray) asm volatile("" : "+v"(vk));
+    auto v_offset = [&](int db) -> uint32_t {
+      if constexpr (kVlaneArray) return vlane[db];
+      else return vbase + 32u * ((uint32_t)db ^ vk);
+    };
     constexpr int N = DB * PG;
     auto frag = [&](int i, uint4 (&f)[2]) {
       const int db = i % DB, g = i / DB;
-      const uint8_t* base = vb + vlane[db];
+      const uint8_t* base = vb + v_offset(db);
       uint32_t w[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -287,17 +346,18 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
       f[0] = make_uint4(w[0], w[1], w[2], w[3]);
       f[1] = make_uint4(w[4], w[5], w[6], w[7]);
     };
-    uint4 fr[kFp8PvPre][2];
+    constexpr int PRE = Fp8Tile<D>::VPRE < N ? Fp8Tile<D>::VPRE : N;
+    uint4 fr[PRE][2];
 #pragma unroll
-    for (int i = 0; i < kFp8PvPre; ++i) frag(i, fr[i]);
+    for (int i = 0; i < PRE; ++i) frag(i, fr[i]);
     __builtin_amdgcn_s_setprio(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int db = i % DB, g = i / DB;
-      const uint4 a0 = fr[i % kFp8PvPre][0], a1 = fr[i % kFp8PvPre][1];
+      const uint4 a0 = fr[i % PRE][0], a1 = fr[i % PRE][1];
       oacc[db] = mfma32_fp8(a0, a1, pp[g][0], pp[g][1], oacc[db]);
-      if (i + kFp8PvPre < N) frag(i + kFp8PvPre, fr[i % kFp8PvPre]);
+      if (i + PRE < N) frag(i + PRE, fr[i % PRE]);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -331,8 +391,9 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
       if (kt < wave_kt) {
         // the tile's scales through the scalar cache: a vector load here
         // would make the compiler wait for the tile loads issued before it
-        const float cs = p.c * sq * load_uniform(sk, kt);
-        const float svt = load_uniform(sv, kt);
+        const int kst = kt * BC / SC;  // the tile's scale entry
+        const float cs = p.c * sq * load_uniform(sk, kst);
+        const float svt = load_uniform(sv, kst);
         // log2 of 2^8 w: P codes are e4m3(2^(t - M) * 2^8 * s_v / max s_v).
         // With 2^8 w <= 2^-11 every code of the tile is 0 (values <= 2^-10
         // round to 0): the tile then skips the PV product, and its
@@ -441,7 +502,7 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
 // tiles of equal total work, one after the other: tile t of head h and tile
 // T-1-t of head h + heads/2 (an even head count), else tiles t and T-1-t of
 // one head; p.n_work counts pairs then.
-template <bool CAUSAL, int NW, int NS, bool VARLEN>
+template <int D, int BC, bool CAUSAL, int NW, int NS, bool VARLEN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
 attn_fwd_fp8_kernel(FwdParams p) {
   const int w = xcd_remap(blockIdx.x, p.n_work);
@@ -449,27 +510,28 @@ attn_fwd_fp8_kernel(FwdParams p) {
     const int T = p.tiles_per_head, heads = p.B * p.H;
     if (heads % 2 == 0) {
       const int h = w / T, t = w - h * T;
-      fp8_body<CAUSAL, NW, NS, VARLEN>(p, h * T + t);
+      fp8_body<D, BC, CAUSAL, NW, NS, VARLEN>(p, h * T + t);
       __syncthreads();
-      fp8_body<CAUSAL, NW, NS, VARLEN>(p, (h + heads / 2) * T + (T - 1 - t));
+      fp8_body<D, BC, CAUSAL, NW, NS, VARLEN>(p, (h + heads / 2) * T + (T - 1 - t));
     } else {
       const int half = (T + 1) / 2;
       const int head = w / half, t = w - head * half;
-      fp8_body<CAUSAL, NW, NS, VARLEN>(p, head * T + t);
+      fp8_body<D, BC, CAUSAL, NW, NS, VARLEN>(p, head * T + t);
       if (T - 1 - t != t) {
         __syncthreads();
-        fp8_body<CAUSAL, NW, NS, VARLEN>(p, head * T + (T - 1 - t));
+        fp8_body<D, BC, CAUSAL, NW, NS, VARLEN>(p, head * T + (T - 1 - t));
       }
     }
   } else {
-    fp8_body<CAUSAL, NW, NS, VARLEN>(p, w);
+    fp8_body<D, BC, CAUSAL, NW, NS, VARLEN>(p, w);
   }
 }
 
-template <bool CAUSAL, int NW, int NS, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_fp8(const FwdParams& p, hipStream_t st) {
-  constexpr int lds = 2 * NS * kTileB;
-  auto kern = attn_fwd_fp8_kernel<CAUSAL, NW, NS, VARLEN>;
+  constexpr int BC = Fp8Tile<D>::BC, NW = Fp8Tile<D>::NW, NS = Fp8Tile<D>::NS;
+  constexpr int lds = 2 * NS * BC * D;
+  auto kern = attn_fwd_fp8_kernel<D, BC, CAUSAL, NW, NS, VARLEN>;
   static bool attr_set = false;  // idempotent; a benign race between threads
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -496,12 +558,22 @@ hipError_t launch_fp8(const FwdParams& p, hipStream_t st) {
 
 }  // namespace
 
-int fwd_fp8_block_rows(bool causal) { return 128; }
+int fwd_fp8_block_rows(bool causal) { return 32 * Fp8Tile<128>::NW; }
+
+template <int D>
+hipError_t launch_fp8_d(bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
+  static_assert(32 * Fp8Tile<D>::NW == 32 * Fp8Tile<128>::NW, "one query-tile height for every d");
+  if (varlen) return causal ? launch_fp8<D, true, true>(p, st) : launch_fp8<D, false, true>(p, st);
+  return causal ? launch_fp8<D, true, false>(p, st) : launch_fp8<D, false, false>(p, st);
+}
 
 hipError_t launch_fwd_fp8(int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
-  if (d != kFp8D) return hipErrorInvalidValue;
-  if (varlen) return causal ? launch_fp8<true, 4, 2, true>(p, st) : launch_fp8<false, 4, 2, true>(p, st);
-  return causal ? launch_fp8<true, 4, 2, false>(p, st) : launch_fp8<false, 4, 2, false>(p, st);
+  switch (d) {
+    case 64: return launch_fp8_d<64>(causal, varlen, p, st);
+    case 128: return launch_fp8_d<128>(causal, varlen, p, st);
+    case 256: return launch_fp8_d<256>(causal, varlen, p, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace attn

@@ -89,7 +89,7 @@ enum {
  *   that its rounded weights are all 0) adds nothing to O but its keys still
  *   count in the softmax sum.
  *
- * d ∈ {64, 128, 256} (else ATTN_ERR_UNSUPPORTED; fp8: d = 128 only).
+ * d ∈ {64, 128, 256} (else ATTN_ERR_UNSUPPORTED), fp8 included.
  * scale: finite and >= 0 (typically 1/sqrt(d)).  causal ∈ {0, 1}.
  * B, H >= 1; Nq, Nk >= 0.  Nq = 0 is a no-op; Nk = 0 (or an empty key
  * sequence) gives O = 0 and lse = -inf.  q, o, lse may be NULL only if

@@ -94,8 +94,8 @@ def test_invalid_arguments(lib, entry, over):
 
 UNSUPPORTED = [
     dict(d=96), dict(d=32), dict(d=512), dict(d=0),
-    dict(dtype=attn.ATTN_DT_FP8_E4M3, d=64, q_scale=FAKE, k_scale=FAKE, v_scale=FAKE),
-    dict(dtype=attn.ATTN_DT_FP8_E4M3, d=256, q_scale=FAKE, k_scale=FAKE, v_scale=FAKE,
+    dict(dtype=attn.ATTN_DT_FP8_E4M3, d=96, q_scale=FAKE, k_scale=FAKE, v_scale=FAKE),
+    dict(dtype=attn.ATTN_DT_FP8_E4M3, d=512, q_scale=FAKE, k_scale=FAKE, v_scale=FAKE,
          cu_seqlens_q=FAKE, cu_seqlens_k=FAKE),
 ]
 

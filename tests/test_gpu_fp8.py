@@ -129,8 +129,12 @@ def test_prep_rotation(gpu_lib, d, outliers):
 EXACT_CODES = [0x38, 0x3C, 0x40, 0x44, 0x48, 0xB8, 0xBC, 0xC0, 0xC4, 0xC8]
 
 
-def _exact_problem(B, H, nq, nk, seed):
-    d = 128
+# key-block length of the kernel's running max per head dimension (the
+# emulation's ``block``): 128-key tiles, 64 at d = 256
+BLOCK = {64: 128, 128: 128, 256: 64}
+
+
+def _exact_problem(B, H, nq, nk, seed, d=128):
     nt = lambda n: (n + 127) // 128  # noqa: E731
     q8 = W.random_codes_from(EXACT_CODES, (B, H, nq, d), seed)
     k8 = W.random_codes_from(EXACT_CODES, (B, H, nk, d), seed + 1)
@@ -205,7 +209,7 @@ def _s_bound(q8, k8):
     return tot
 
 
-def _quantiser_allowance(q8, k8, v8, sq, sk, sv, scale, causal, tile=128):
+def _quantiser_allowance(q8, k8, v8, sq, sk, sv, scale, causal, tile=128, block=128):
     """Per-element allowance of the e4m3 kernel against the fp8 emulation
     when the S product rounds (``_s_bound``), in O units, and the bound on the
     lse difference.
@@ -222,7 +226,7 @@ def _quantiser_allowance(q8, k8, v8, sq, sk, sv, scale, causal, tile=128):
     values, which is exact for normal codes and moves a code below 2^-4 (in
     its tile's units) by less than 2^-7.  Returns (the emulation's parts,
     allowance [..., Nq, d], lse bound [..., Nq])."""
-    ref = F.attention_fp8(q8, k8, v8, sq, sk, sv, scale, causal, parts=True)
+    ref = F.attention_fp8(q8, k8, v8, sq, sk, sv, scale, causal, parts=True, block=block)
     nq, nk = q8.shape[-2], k8.shape[-2]
     rs = lambda sc, n: np.repeat(np.asarray(sc, np.float64), tile, axis=-1)[..., :n]  # noqa: E731
     cs = abs(scale) * F.LOG2E * rs(sq, nq)[..., :, None] * rs(sk, nk)[..., None, :]
@@ -230,17 +234,17 @@ def _quantiser_allowance(q8, k8, v8, sq, sk, sv, scale, causal, tile=128):
     fin = np.isfinite(t)
     dt = cs * _s_bound(q8, k8) + 4 * 2.0 ** -24 * np.abs(np.where(fin, t, 0.0))
     delta = np.where(fin, np.expm1(dt * np.log(2.0)) + 3e-5, 0.0)
-    flip = F.attention_fp8(q8, k8, v8, sq, sk, sv, scale, causal, ambiguity=delta, parts=True)["flip"]
+    flip = F.attention_fp8(q8, k8, v8, sq, sk, sv, scale, causal, ambiguity=delta, parts=True, block=block)["flip"]
     M, l = ref["M"], ref["l"]
     p = np.where(fin, np.exp2(np.where(fin, t, 0.0) - M[..., None]), 0.0)
     with np.errstate(invalid="ignore", divide="ignore"):
         dl = np.where(l > 0, (p * delta).sum(-1) / np.where(l > 0, l, 1.0), 0.0) + 1e-5
     lchg = np.abs(ref["o"]) * (dl / (1.0 - dl))[..., None]
-    # the running max of the 128-key tiles (before its ceiling): where one lies
+    # the running max of the key blocks (before its ceiling): where one lies
     # within dt of an integer, the kernel's running M may differ by one there
-    nkt = (nk + tile - 1) // tile
-    tpad = np.concatenate([np.where(fin, t, -np.inf), np.full(t.shape[:-1] + (nkt * tile - nk,), -np.inf)], -1)
-    run = np.maximum.accumulate(tpad.reshape(t.shape[:-1] + (nkt, tile)).max(-1), axis=-1)
+    nkt = (nk + block - 1) // block
+    tpad = np.concatenate([np.where(fin, t, -np.inf), np.full(t.shape[:-1] + (nkt * block - nk,), -np.inf)], -1)
+    run = np.maximum.accumulate(tpad.reshape(t.shape[:-1] + (nkt, block)).max(-1), axis=-1)
     dmax = dt.max(-1)
     with np.errstate(invalid="ignore"):
         near = np.any(np.abs(run - np.rint(run)) <= dmax[..., None], axis=-1)
@@ -271,25 +275,30 @@ def _check(o, lse, o_ref, l_ref, what, tol=4e-3, allow=0.0):
     assert rel.size == 0 or rel.max() <= 1e-3, f"{what}: lse rel err {rel.max():.3e}"
 
 
+FP8_SHAPES = [(1, 1), (100, 100), (128, 128), (129, 300), (300, 129), (1000, 1000), (513, 2000)]
+
+
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("nq,nk", [(1, 1), (100, 100), (128, 128), (129, 300), (300, 129), (1000, 1000), (513, 2000)])
-def test_fp8_kernel_vs_emulation(gpu_lib, causal, nq, nk):
-    q8, k8, v8, sq, sk, sv = _exact_problem(2, 2, nq, nk, seed=nq + 3 * nk)
+@pytest.mark.parametrize("d,nq,nk", [(128,) + s for s in FP8_SHAPES]
+                         + [(d, nq, nk) for d in (64, 256) for nq, nk in ((1, 1), (129, 300), (300, 129), (513, 1000))])
+def test_fp8_kernel_vs_emulation(gpu_lib, causal, d, nq, nk):
+    q8, k8, v8, sq, sk, sv = _exact_problem(2, 2, nq, nk, seed=nq + 3 * nk + d, d=d)
     o, lse = _run_fp8(gpu_lib, q8, k8, v8, sq, sk, sv, 0.0884, causal)
-    ref = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.0884, causal, ambiguity=3e-5, parts=True)
+    ref = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.0884, causal, ambiguity=3e-5, parts=True, block=BLOCK[d])
     allow = ref["flip"] + _pv_bound(ref)
-    _check(o, lse, ref["o"], ref["lse"], f"fp8 causal{causal} {nq}x{nk}", allow=allow)
+    _check(o, lse, ref["o"], ref["lse"], f"fp8 d{d} causal{causal} {nq}x{nk}", allow=allow)
     # the allowances stay a small part of the signal
     assert np.mean(allow) <= 0.25 * np.mean(np.abs(ref["o"])) + 1e-6
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_kernel_uniform_closed_form(gpu_lib, causal):
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp8_kernel_uniform_closed_form(gpu_lib, causal, d):
     """scale = 0: every visible key weighs the same and P is exact (2^8 w with
     w a power of two), so O is the mean (causal: prefix mean) of the
     dequantised V rows, up to the bf16 rounding of O."""
     nq = nk = 700
-    q8, k8, v8, sq, sk, sv = _exact_problem(2, 3, nq, nk, seed=33)
+    q8, k8, v8, sq, sk, sv = _exact_problem(2, 3, nq, nk, seed=33, d=d)
     o, lse = _run_fp8(gpu_lib, q8, k8, v8, sq, sk, sv, 0.0, causal)
     vd = F.dequantize(v8, sv)
     if causal:
@@ -302,9 +311,10 @@ def test_fp8_kernel_uniform_closed_form(gpu_lib, causal):
     np.testing.assert_allclose(lse, lref, rtol=0, atol=1e-5)
 
 
-def test_fp8_kernel_empty_keys(gpu_lib):
-    q8, _, _, sq, _, _ = _exact_problem(1, 2, 50, 1, seed=5)
-    z8 = torch.zeros((1, 2, 0, 128), dtype=torch.uint8, device="cuda")
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp8_kernel_empty_keys(gpu_lib, d):
+    q8, _, _, sq, _, _ = _exact_problem(1, 2, 50, 1, seed=5, d=d)
+    z8 = torch.zeros((1, 2, 0, d), dtype=torch.uint8, device="cuda")
     zs = torch.zeros((1, 2, 0), dtype=torch.float32, device="cuda")
     o, lse = gpu_lib.forward(_dev(q8), z8, z8, scale=0.1, q_scale=_dev(sq), k_scale=zs, v_scale=zs)
     torch.cuda.synchronize()
@@ -312,38 +322,40 @@ def test_fp8_kernel_empty_keys(gpu_lib):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_zero_and_tiny_v_scales(gpu_lib, causal):
+@pytest.mark.parametrize("d", [128, 256])
+def test_fp8_zero_and_tiny_v_scales(gpu_lib, causal, d):
     """V tiles whose scale is 0, or so small against the head's largest V
     scale (w = 2^-30) that every rounded weight is 0: their keys still count
     in the softmax sum l and add nothing to O, as in the emulation."""
-    q8, k8, v8, sq, sk, sv = _exact_problem(2, 2, 300, 700, seed=57)
+    q8, k8, v8, sq, sk, sv = _exact_problem(2, 2, 300, 700, seed=57, d=d)
     sv = sv.copy()
     sv[0, 0, 1] = 0.0
     sv[1, 1, 2] = sv[1, 1].max() * np.float32(2.0 ** -30)
     sv[0, 1, :] = 0.0  # a head with every V scale 0: O = 0, lse still finite
     o, lse = _run_fp8(gpu_lib, q8, k8, v8, sq, sk, sv, 0.0884, causal)
-    ref = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.0884, causal, ambiguity=3e-5, parts=True)
+    ref = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.0884, causal, ambiguity=3e-5, parts=True, block=BLOCK[d])
     assert np.all(ref["o"][0, 1] == 0)
-    _check(o, lse, ref["o"], ref["lse"], f"fp8 zero V scales causal{causal}", allow=ref["flip"] + _pv_bound(ref))
+    _check(o, lse, ref["o"], ref["lse"], f"fp8 d{d} zero V scales causal{causal}",
+           allow=ref["flip"] + _pv_bound(ref))
 
 
-# Q channels that carry values: one per accumulation group of the e4m3 MFMA
+# Q carries values in one channel per accumulation group of the e4m3 MFMA
 # (8 channels), so every group holds at most one nonzero product and
-# S = K Q^T rounds only where the group sums add
-SPARSE_Q_CHANNELS = np.arange(0, 128, MFMA_GROUP)
+# S = K Q^T rounds only where the group sums add.
 
 
-def _quantiser_problem(kind, causal, B=2, H=2, nq=1000, nk=2000, seed=0):
+def _quantiser_problem(kind, causal, B=2, H=2, nq=1000, nk=2000, seed=0, d=128):
     """Codes and scales from the oracle's quantiser (fp32 N(0,1) inputs):
     "normal": block scales, K rotated; "outlier_block": Q and K channels 0 and
     16 scaled by 50, block scales, K rotated; "outlier_tensor": the same
     outliers, one scale per tensor, nothing rotated (the normal channels then
-    take small codes and subnormals).  Q carries values only in
-    SPARSE_Q_CHANNELS.  Scales are arbitrary fp32 values."""
-    rng = np.random.default_rng(seed + 100 * causal + len(kind))
-    d = 128
+    take small codes and subnormals).  Q carries values only in every 8th
+    channel (one per MFMA accumulation group).  Scales are arbitrary fp32
+    values."""
+    rng = np.random.default_rng(seed + 100 * causal + len(kind) + d)
+    chans = np.arange(0, d, MFMA_GROUP)
     q = np.zeros((B, H, nq, d), np.float32)
-    q[..., SPARSE_Q_CHANNELS] = rng.standard_normal((B, H, nq, len(SPARSE_Q_CHANNELS)), dtype=np.float32)
+    q[..., chans] = rng.standard_normal((B, H, nq, len(chans)), dtype=np.float32)
     k = rng.standard_normal((B, H, nk, d), dtype=np.float32)
     v = rng.standard_normal((B, H, nk, d), dtype=np.float32)
     signs = rng.choice([-1.0, 1.0], d).astype(np.float32)
@@ -359,19 +371,20 @@ def _quantiser_problem(kind, causal, B=2, H=2, nq=1000, nk=2000, seed=0):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("kind", ["normal", "outlier_block", "outlier_tensor"])
-def test_fp8_kernel_vs_emulation_quantiser(gpu_lib, kind, causal):
+@pytest.mark.parametrize("kind,d", [("normal", 128), ("outlier_block", 128), ("outlier_tensor", 128),
+                                    ("normal", 64), ("outlier_block", 256)])
+def test_fp8_kernel_vs_emulation_quantiser(gpu_lib, kind, d, causal):
     """Element-wise parity on codes from the quantiser (B2 H2, 1000 queries,
     2000 keys): codes up to 448, subnormal Q/K/V and P codes, non-power-of-two
     scales.  Allowance per element (``_quantiser_allowance``): the S product's
     rounding inside the MFMA (zero for these Q rows) through code flips, l and
     the integer M; the PV product's truncation (``_pv_bound``); the bf16
     rounding of O (2^-8 relative) and 2e-5 for fp32 accumulation."""
-    q8, k8, v8, sq, sk, sv, scale = _quantiser_problem(kind, causal)
+    q8, k8, v8, sq, sk, sv, scale = _quantiser_problem(kind, causal, d=d)
     assert np.any(np.abs(F.e4m3_decode(q8)) == 448) and np.any((q8 & 0x78) == 0) and np.any((v8 & 0x7F) == 0x7E)
     assert not np.all(np.log2(sk) == np.rint(np.log2(sk)))
     o, lse = _run_fp8(gpu_lib, q8, k8, v8, sq, sk, sv, scale, causal)
-    ref, allow, lse_bound = _quantiser_allowance(q8, k8, v8, sq, sk, sv, scale, causal)
+    ref, allow, lse_bound = _quantiser_allowance(q8, k8, v8, sq, sk, sv, scale, causal, block=BLOCK[d])
     assert np.any((ref["p8"] > 0) & (ref["p8"] < 2.0 ** -6))  # subnormal P codes occur
     tol = 2.0 ** -8 * (np.abs(ref["o"]) + allow) + allow + 2e-5
     err = np.abs(o - ref["o"])
@@ -490,8 +503,7 @@ def test_prep_varlen_no_rotation_bitwise(gpu_lib, in_dtype, d, per_tensor):
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
 
 
-def _exact_varlen_problem(H, lens_q, lens_k, seed):
-    d = 128
+def _exact_varlen_problem(H, lens_q, lens_k, seed, d=128):
     cq, ck = W.cu_seqlens(lens_q), W.cu_seqlens(lens_k)
     nq, nk, B = int(cq[-1]), int(ck[-1]), len(lens_q)
     q8 = W.random_codes_from(EXACT_CODES, (H, nq, d), seed)
@@ -504,13 +516,14 @@ def _exact_varlen_problem(H, lens_q, lens_k, seed):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("lens_q,lens_k", [(VARLEN_LENS, VARLEN_LENS), ([200, 0, 300, 7], [90, 5, 400, 0])],
-                         ids=["same", "q_ne_k"])
-def test_fp8_varlen_kernel_vs_emulation(gpu_lib, causal, lens_q, lens_k):
+@pytest.mark.parametrize("lens_q,lens_k,d", [(VARLEN_LENS, VARLEN_LENS, 128), ([200, 0, 300, 7], [90, 5, 400, 0], 128),
+                                             (VARLEN_LENS, VARLEN_LENS, 64), (VARLEN_LENS, VARLEN_LENS, 256)],
+                         ids=["same", "q_ne_k", "same_d64", "same_d256"])
+def test_fp8_varlen_kernel_vs_emulation(gpu_lib, causal, lens_q, lens_k, d):
     """Each sequence against the oracle's fp8 emulation of it, with its own
     scale tiles and V-scale normalisation (same bar and allowances as the
     dense kernel test)."""
-    q8, k8, v8, sq, sk, sv, cq, ck = _exact_varlen_problem(3, lens_q, lens_k, seed=len(lens_q) + 17)
+    q8, k8, v8, sq, sk, sv, cq, ck = _exact_varlen_problem(3, lens_q, lens_k, seed=len(lens_q) + 17 + d, d=d)
     o, lse = gpu_lib.forward(_dev(q8), _dev(k8), _dev(v8), causal=causal, scale=0.0884, cu_seqlens_q=_dev(cq),
                              cu_seqlens_k=_dev(ck), q_scale=_dev(sq), k_scale=_dev(sk), v_scale=_dev(sv))
     torch.cuda.synchronize()
@@ -520,7 +533,7 @@ def test_fp8_varlen_kernel_vs_emulation(gpu_lib, causal, lens_q, lens_k):
     ref_l = np.full(q8.shape[:2], -np.inf)
     allow = np.zeros(q8.shape)
     for qa, r in F.attention_fp8_varlen(q8, k8, v8, sq, sk, sv, cq, ck, 0.0884, causal, ambiguity=3e-5,
-                                        parts=True):
+                                        parts=True, block=BLOCK[d]):
         n = r["o"].shape[-2]
         ref_o[:, qa:qa + n], ref_l[:, qa:qa + n] = r["o"], r["lse"]
         allow[:, qa:qa + n] = r["flip"] + _pv_bound(r)
@@ -616,3 +629,31 @@ def test_fp8_offsets_beyond_2_31(gpu_lib, causal):
                    allow=ref["flip"] + _pv_bound(ref))
     del qd, o, lse
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 256])
+def test_fp8_other_head_dims_end_to_end(gpu_lib, d, causal):
+    """d = 64 and 256, all on the device (rotation, block quantisation, e4m3
+    attention) from N(0,1) fp32 inputs (B1 H4 N2000): RMSE against the fp64
+    attention of the originals <= 3e-2, and within 10 % (plus 1e-4) of the
+    oracle's quantiser and emulation on the same inputs."""
+    B, H, n = 1, 4, 2000
+    rng = np.random.default_rng(d + causal)
+    q, k, v = (rng.standard_normal((B, H, n, d), dtype=np.float32) for _ in range(3))
+    signs = rng.choice([-1.0, 1.0], d).astype(np.float32)
+    scale = 1.0 / np.sqrt(d)
+    sd = _dev(signs)
+    q8, sq = gpu_lib.fp8_quantize(_dev(q), sd)
+    k8, sk = gpu_lib.fp8_quantize(_dev(k), sd)
+    v8, sv = gpu_lib.fp8_quantize(_dev(v), None)
+    o, lse = gpu_lib.forward(q8, k8, v8, causal=causal, scale=scale, q_scale=sq, k_scale=sk, v_scale=sv)
+    torch.cuda.synchronize()
+    truth, _ = oracle.attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), scale, causal)
+    err = F.rmse(o.double().cpu().numpy(), truth)
+    (rq8, rsq), (rk8, rsk), (rv8, rsv) = F.quantize(q, signs), F.quantize(k, signs), F.quantize(v)
+    emu, _ = F.attention_fp8(rq8, rk8, rv8, rsq, rsk, rsv, scale, causal, block=BLOCK[d])
+    e = F.rmse(emu, truth)
+    print(f"fp8 d{d} causal{causal}: device RMSE {err:.3e}, emulation {e:.3e}")
+    assert err <= 3e-2
+    assert err <= 1.1 * e + 1e-4
