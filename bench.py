@@ -395,14 +395,44 @@ def bench_fp8(attn, steps, warmup, varlen=True):
                             "shape": [w.B, w.H, w.Nq, w.Nk, w.d],
                             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
                                          "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-                                         "kernel": "attn_fwd_fp8_kernel<non-causal, 8 waves, 4 slots>",
+                                         "kernel": "attn_fwd_fp8_kernel<d=128, 128-key tiles, non-causal, 4 waves, 2 slots>",
                                          "mean_launch_ms": round(ms, 4)}},
             "fp8_prep_qkv": {"ms": round(ms_prep, 4), "gbs": round(prep_bytes / (ms_prep / 1e3) / 1e9, 1),
                              "frac_hbm": round(prep_bytes / (ms_prep / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
             # fp32 Q, K, V in HBM -> rotation and block quantisation -> e4m3 attention
             "fp8_end_to_end": {"ms": round(ms + ms_prep, 4),
                                "tflops": round(w.flops() / ((ms + ms_prep) / 1e3) / 1e12, 2)},
+            **bench_fp8_hdim256(attn, steps, warmup),
             **(bench_fp8_varlen(attn, steps, warmup) if varlen else {})}
+
+
+def bench_fp8_hdim256(attn, steps, warmup):
+    """The large-head shape (B=1 H=16 N=8192 d=256, N(0,1), non-causal) in
+    fp8: Q, K rotated and block-quantised, V block-quantised on the device,
+    then the e4m3 attention kernel alone is timed (64-key tiles at d=256)."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+
+    w = W.WORKLOADS["hdim256_bf16"]
+    x = W.make_inputs(w)
+    signs = torch.from_numpy(np.random.default_rng(w.seed).choice([-1.0, 1.0], w.d).astype(np.float32)).cuda()
+    q8, sq = attn.fp8_quantize(torch.from_numpy(x["q"]).cuda(), signs)
+    k8, sk = attn.fp8_quantize(torch.from_numpy(x["k"]).cuda(), signs)
+    v8, sv = attn.fp8_quantize(torch.from_numpy(x["v"]).cuda(), None)
+    o, lse = attn.forward(q8, k8, v8, scale=w.scale, q_scale=sq, k_scale=sk, v_scale=sv)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        attn.forward(q8, k8, v8, scale=w.scale, q_scale=sq, k_scale=sk, v_scale=sv, out=o, lse=lse)
+
+    for _ in range(warmup):
+        run()
+    ms = float(np.mean(timed_launches(run, steps, stream)))
+    tf = w.flops() / (ms / 1e3) / 1e12
+    return {"fp8_hdim256": {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                            "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}}
 
 
 def bench_fp8_varlen(attn, steps, warmup):
