@@ -164,15 +164,6 @@ struct TileLane {
 // has an all-zero operand; its fold ratios are then 0).
 __device__ __forceinline__ float recip_or_zero(float x) { return x > 0.f ? 1.0f / x : 0.f; }
 
-// f(w, r) with an LDS ring slot that direct-to-LDS loads fill (w) and one
-// that the step reads (r) passed as restrict pointers: the caller guarantees
-// they do not overlap, and the compiler then does not wait for the loads
-// before the reads.
-template <typename F>
-__device__ __forceinline__ void with_slots(uint8_t* __restrict__ w, const uint8_t* __restrict__ r, F&& f) {
-  f(w, r);
-}
-
 // Direct-to-LDS load of a 64-row tile (8 KiB) by one wave: rows r0 ..
 // r0 + 63 of the rows at `base` (n_rows of them, r0 < n_rows) go to dst
 // with their chunks permuted (rows8, or tr8 if tr).  The rows come through a

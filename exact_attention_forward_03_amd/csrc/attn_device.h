@@ -129,5 +129,12 @@ __device__ __forceinline__ void with_disjoint(uint8_t* __restrict__ kw, uint8_t*
   f(kw, vw, kr, vr);
 }
 
+// f(w, r) with an LDS buffer that direct-to-LDS loads fill (w) and one that
+// the step reads (r) passed as restrict pointers; the caller guarantees they
+// do not overlap (the two-pointer form of with_disjoint).
+template <typename F>
+__device__ __forceinline__ void with_slots(uint8_t* __restrict__ w, const uint8_t* __restrict__ r, F&& f) {
+  f(w, r);
+}
 
 }  // namespace attn

@@ -152,11 +152,16 @@ __device__ __forceinline__ void dense_tile_load(const uint8_t* base, uint8_t* ri
                                                (uint32_t)(blk * 1024), 0, 0);
     }
   } else {
+    // the lane index through an empty asm: the per-lane rows and chunks of
+    // this rare path are then computed here, not hoisted out of the tile
+    // loop to occupy registers (or scratch) for the whole kernel
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < C::LOADS / NW; ++i) {
       const int blk = i * NW + wv;
-      const int r = blk * RPB + lane / C::CHUNKS;
-      const uint32_t voff = (uint32_t)(min(r, rows - 1) * C::ROWB + chunk(r, lane % C::CHUNKS) * 16);
+      const int r = blk * RPB + ln / C::CHUNKS;
+      const uint32_t voff = (uint32_t)(min(r, rows - 1) * C::ROWB + chunk(r, ln % C::CHUNKS) * 16);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(ring + buf * C::TILEB + blk * 1024), 16, voff,
                                                0, 0, 0);
     }
