@@ -97,8 +97,9 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   p.q_scale = q_scale; p.k_scale = k_scale; p.v_scale = v_scale;
   int64_t heads, tiles;
   if (varlen) {
-    // Sum over sequences of ceil(L_b / BR) <= ceil(Nq / BR) + B; surplus
-    // workgroups exit at once.
+    // Query-tile slots per head: tile j of sequence b is slot
+    // floor(cu_q[b] / BR) + b + j < floor(Nq / BR) + B; workgroups of slots
+    // no tile owns exit at once.
     heads = H;
     tiles = ((int64_t)Nq + br - 1) / br + B;
   } else {

@@ -37,6 +37,7 @@
 // element.
 #include "attn_device.h"
 #include "attn_params.h"
+#include "attn_sched.h"
 
 namespace attn {
 namespace {
@@ -106,27 +107,23 @@ struct SeqView {
   int q_len, k_len;
 };
 
-// Sequence of tile t of a variable-length batch whose sequence s has
-// ceil(len_s / rows) tiles (lengths from the clamped prefix sums); false if
-// t is past the last tile.
-__device__ __forceinline__ bool varlen_tile(const BwdParams& p, int head, int t, int rows, bool by_keys, SeqView& v,
-                                            int& local) {
-  int acc = 0;
-  for (int sq = 0; sq < p.B; ++sq) {
-    const int qa = min(max(p.cu_q[sq], 0), p.Nq), qb = min(max(p.cu_q[sq + 1], qa), p.Nq);
-    const int ka = min(max(p.cu_k[sq], 0), p.Nk), kb = min(max(p.cu_k[sq + 1], ka), p.Nk);
-    const int nt = ((by_keys ? kb - ka : qb - qa) + rows - 1) / rows;
-    if (t < acc + nt) {
-      v.q_row0 = (int64_t)head * p.Nq + qa;
-      v.k_row0 = (int64_t)head * p.Nk + ka;
-      v.q_len = qb - qa;
-      v.k_len = kb - ka;
-      local = t - acc;
-      return true;
-    }
-    acc += nt;
-  }
-  return false;
+// The rows of the tile in slot t of a variable-length batch (R-row tiles of
+// the keys when by_keys, else of the queries; sched::slot_tile), its index
+// within its sequence in `local`; false for a slot no tile owns.
+template <int R, bool BY_KEYS>
+__device__ __forceinline__ bool varlen_tile(const BwdParams& p, int head, int t, SeqView& v, int& local) {
+  sched::SlotTile st;
+  if (!sched::find_tile<R>(BY_KEYS ? p.cu_k : p.cu_q, p.B, BY_KEYS ? p.Nk : p.Nq, BY_KEYS ? p.cu_q : p.cu_k,
+                           BY_KEYS ? p.Nq : p.Nk, t, st))
+    return false;
+  const int qa = BY_KEYS ? st.oa : st.a, qb = BY_KEYS ? st.oe : st.e;
+  const int ka = BY_KEYS ? st.a : st.oa, kb = BY_KEYS ? st.e : st.oe;
+  v.q_row0 = (int64_t)head * p.Nq + qa;
+  v.k_row0 = (int64_t)head * p.Nk + ka;
+  v.q_len = qb - qa;
+  v.k_len = kb - ka;
+  local = st.j;
+  return true;
 }
 
 __device__ __forceinline__ SeqView dense_view(const BwdParams& p, int head) {
@@ -319,8 +316,9 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, const SeqView sv, 
 // and dO).  Causal: key tile kt sees the queries from kt*32*NW on, so the
 // work falls with kt; a workgroup takes tiles j and T-1-j of one head in
 // turn (p.n_work counts the pairs), so that all do the same work.
-// Variable-length batches: a head's key tiles are numbered sequence after
-// sequence (p.tiles_per_head bounds their count; surplus workgroups exit).
+// Variable-length batches: a head's key tiles are numbered by slot
+// (sched::slot_tile; p.tiles_per_head bounds the slots, surplus workgroups
+// exit).
 template <typename TT, int D, int NW, int WPE, int NS, bool CAUSAL, bool VARLEN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 attn_bwd_dkdv_kernel(BwdParams p) {
@@ -329,7 +327,7 @@ attn_bwd_dkdv_kernel(BwdParams p) {
     const int head = w / p.tiles_per_head;
     SeqView sv;
     int kt;
-    if (varlen_tile(p, head, w - head * p.tiles_per_head, 32 * NW, true, sv, kt))
+    if (varlen_tile<32 * NW, true>(p, head, w - head * p.tiles_per_head, sv, kt))
       dkdv_body<TT, D, NW, WPE, NS, CAUSAL>(p, sv, kt);
   } else if constexpr (CAUSAL) {
     const int T = p.tiles_per_head, half = (T + 1) / 2;
@@ -473,7 +471,7 @@ attn_bwd_dq_kernel(BwdParams p) {
     const int head = w / p.tiles_per_head;
     SeqView sv;
     int qt;
-    if (varlen_tile(p, head, w - head * p.tiles_per_head, 32 * NW, false, sv, qt))
+    if (varlen_tile<32 * NW, false>(p, head, w - head * p.tiles_per_head, sv, qt))
       dq_body<TT, D, BC, NW, WPE, NS, CAUSAL>(p, sv, qt);
   } else if constexpr (CAUSAL) {
     const int T = p.tiles_per_head, half = (T + 1) / 2;

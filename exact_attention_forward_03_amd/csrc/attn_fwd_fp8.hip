@@ -30,6 +30,7 @@
 //     per workgroup, as the fp16/bf16 kernel does.
 #include "attn_device.h"
 #include "attn_params.h"
+#include "attn_sched.h"
 
 namespace attn {
 namespace {
@@ -95,8 +96,8 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
 // D head dimension, BC key rows per tile, NW waves per workgroup (32 query
 // rows each), NS LDS ring slots.  VARLEN: a packed batch [H, T, d] with
 // cu_seqlens; the work item is (head, sequence, query tile) and the scales of
-// sequence s start at entry sum_{s' < s} ceil(L_s' / 128) of the head's
-// ceil(T / 128) + B entries.
+// sequence s start at entry floor(cu[s] / 128) + s of the head's
+// ceil(T / 128) + B entries (sched::slot_tile).
 template <int D, int BC, bool CAUSAL, int NW, int NS, bool VARLEN>
 __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   constexpr int SC = kScaleRows;
@@ -116,11 +117,11 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   static_assert(kLoads % NW == 0, "each wave issues the same number of tile loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
 
-  const int head = work / p.tiles_per_head;
-  const int t = work - head * p.tiles_per_head;
-  int qt, q_len, k_len;
+  int head, qt, q_len, k_len;
   int64_t q_row0, k_row0, sq0, sk0;  // first rows of the (sequence,) head; its first scale entries
   if constexpr (!VARLEN) {
+    head = work / p.tiles_per_head;
+    const int t = work - head * p.tiles_per_head;
     qt = CAUSAL ? (p.tiles_per_head - 1 - t) : t;
     q_len = p.Nq;
     k_len = p.Nk;
@@ -129,31 +130,22 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
     sq0 = (int64_t)head * ((q_len + SC - 1) / SC);
     sk0 = (int64_t)head * ((k_len + SC - 1) / SC);
   } else {
-    // sequence of query tile t (tiles of BR rows per sequence), and the
-    // scale tiles (SC = 128 rows) of the sequences before it
-    int acc = 0, seq = -1, qb = 0, qe = 0, kb = 0, ke = 0, nts = 0, tq = 0, tk = 0;
-    for (int s = 0; s < p.B; ++s) {
-      const int a = min(max(p.cu_q[s], 0), p.Nq);
-      const int b = min(max(p.cu_q[s + 1], a), p.Nq);
-      const int ka = min(max(p.cu_k[s], 0), p.Nk);
-      const int kz = min(max(p.cu_k[s + 1], ka), p.Nk);
-      const int nt = (b - a + BR - 1) / BR;
-      if (t < acc + nt) {
-        seq = s; qb = a; qe = b; kb = ka; ke = kz; nts = nt;
-        break;
-      }
-      acc += nt;
-      tq += (b - a + SC - 1) / SC;
-      tk += (kz - ka + SC - 1) / SC;
-    }
-    if (seq < 0) return;  // surplus work item (the grid is an upper bound)
-    qt = CAUSAL ? (nts - 1 - (t - acc)) : (t - acc);
-    q_len = qe - qb;
-    k_len = ke - kb;
-    q_row0 = (int64_t)head * p.Nq + qb;
-    k_row0 = (int64_t)head * p.Nk + kb;
-    sq0 = (int64_t)head * ((p.Nq + SC - 1) / SC + p.B) + tq;
-    sk0 = (int64_t)head * ((p.Nk + SC - 1) / SC + p.B) + tk;
+    // t: a slot of the head's 128-row query tiles (sched::slot_tile); the
+    // scale entries of a packed batch use the same slots, so the sequence's
+    // first q and k scale entries follow from its first rows
+    head = work / p.tiles_per_head;
+    const int t = work - head * p.tiles_per_head;
+    static_assert(BR == SC, "query tiles are the scale tiles");
+    sched::SlotTile st;
+    if (!sched::find_tile<BR>(p.cu_q, p.B, p.Nq, p.cu_k, p.Nk, t, st)) return;  // surplus slot (the grid is an upper bound)
+    const int nts = (st.e - st.a + BR - 1) / BR;
+    qt = CAUSAL ? (nts - 1 - st.j) : st.j;
+    q_len = st.e - st.a;
+    k_len = st.oe - st.oa;
+    q_row0 = (int64_t)head * p.Nq + st.a;
+    k_row0 = (int64_t)head * p.Nk + st.oa;
+    sq0 = (int64_t)head * ((p.Nq + SC - 1) / SC + p.B) + sched::first_slot<SC>(st.a, st.seq);
+    sk0 = (int64_t)head * ((p.Nk + SC - 1) / SC + p.B) + sched::first_slot<SC>(st.oa, st.seq);
   }
   const int q0 = qt * BR;
   const int nks = (k_len + SC - 1) / SC;

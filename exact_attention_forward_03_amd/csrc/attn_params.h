@@ -57,8 +57,8 @@ struct PrepParams {
   const float* signs;    // NULL: no rotation
   int mode;              // 0: block scales; 1: tile amax only; 2: quantise with the tensor amax
   // variable-length batch (cu non-NULL): x is [H, N, d] with sequence s on
-  // tokens [cu[s], cu[s+1]); scale is [H, ceil(N/128) + nseq], sequence s's
-  // tiles from entry sum_{s' < s} ceil(L_s' / 128)
+  // tokens [cu[s], cu[s+1]); scale is [H, ceil(N/128) + nseq], tile j of
+  // sequence s at entry floor(cu[s] / 128) + s + j
   const int32_t* cu;
   int nseq;
 };

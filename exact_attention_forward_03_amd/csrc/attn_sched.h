@@ -1,0 +1,113 @@
+// Work items of a variable-length batch ("Flash Attention 3：让 GPU 跑满的注意力
+// 计算", §5.2: sequences packed along the token axis, described by cu_seqlens
+// prefix sums, no padding).
+//
+// Each sequence's rows are cut into tiles of R rows that restart at the
+// sequence's first row, so no tile mixes two sequences.  Tile j of sequence
+// s gets the slot
+//     slot(s, j) = floor(a_s / R) + s + j,   0 <= j < ceil(L_s / R),
+// with a_s = cu[s] clamped into [0, N] and L_s the sequence's length.  The
+// slot ranges of consecutive sequences do not overlap (floor(a / R) +
+// ceil(L / R) <= floor((a + L) / R) + 1) and all lie below floor(N / R) + B,
+// a bound the host knows without reading cu_seqlens (which is device
+// memory).  A workgroup finds the sequence of its slot with one round of
+// vector loads: lane l reads sequence base + l, and as first slots grow with
+// s, the owner can only be the last lane whose first slot is <= the slot,
+// found by a ballot.  Past 64 sequences a binary search over blocks of 64 (scalar
+// loads) picks `base` first.  A slot no tile owns exits at once (at most
+// B + 1 per head).  The same numbering places the per-tile fp8 scales of a
+// packed batch (R = 128), so a kernel finds the scales of a sequence without
+// summing over the sequences before it.
+#pragma once
+
+#include "attn_device.h"
+
+namespace attn {
+namespace sched {
+
+// First slot of the sequence whose rows start at a (clamped) and whose index
+// is s.
+template <int R>
+__device__ __forceinline__ int first_slot(int a, int s) {
+  return a / R + s;
+}
+
+struct SlotTile {
+  int seq;     // sequence index
+  int j;       // tile index within the sequence
+  int a, e;    // the sequence's rows [a, e) in the tiled array
+  int oa, oe;  // its rows [oa, oe) in the other array (keys of a query tile, ...)
+};
+
+// The tile that owns `slot` of a batch of B sequences over N rows (cu: device
+// array of B + 1 prefix sums), with the same sequence's rows in a second
+// array (cu_o over N_o rows); false if no tile owns the slot.  Prefix sums are
+// clamped as the kernels clamp them: a = cu[s] into [0, N], e = cu[s + 1]
+// into [a, N].  Call with the whole wave active and wave-uniform arguments.
+template <int R>
+__device__ __forceinline__ bool slot_tile(const int32_t* cu, int B, int N, const int32_t* cu_o, int N_o, int slot,
+                                          SlotTile& t) {
+  int base = 0;
+  if (B > 64) {
+    // largest block c with first_slot(a_{64c}, 64c) <= slot
+    int lo = 0, hi = (B + 63) / 64;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (first_slot<R>(min(max(load_uniform(cu, 64 * mid), 0), N), 64 * mid) <= slot)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    base = 64 * lo;
+  }
+  const int s = base + __lane_id();
+  const int i0 = min(s, B), i1 = min(s + 1, B);  // in bounds: cu has B + 1 entries
+  const int x = cu[i0], y = cu[i1], ox = cu_o[i0], oy = cu_o[i1];
+  const int a = min(max(x, 0), N);
+  const uint64_t below = __ballot(s < B && first_slot<R>(a, s) <= slot);
+  if (below == 0) return false;
+  const int l = 63 - __builtin_clzll(below);  // the last such lane
+  t.seq = base + l;
+  t.a = __builtin_amdgcn_readlane(a, l);
+  t.e = min(max(__builtin_amdgcn_readlane(y, l), t.a), N);
+  t.oa = min(max(__builtin_amdgcn_readlane(ox, l), 0), N_o);
+  t.oe = min(max(__builtin_amdgcn_readlane(oy, l), t.oa), N_o);
+  t.j = slot - first_slot<R>(t.a, t.seq);  // >= 0 by the ballot
+  return t.j < (t.e - t.a + R - 1) / R;
+}
+
+// Work index t of a launch over the R-row tiles of a packed batch -> its
+// tile (the rows as in slot_tile); false if t names no tile.  Up to
+// kScanSeqs sequences the tiles are numbered sequence after sequence and
+// found by a scan of the prefix sums (one round of scalar loads per
+// sequence passed; the long first sequences hold most tiles, and this is
+// the shortest start-up path measured for a few sequences); past that, t
+// is a slot (slot_tile: one round of vector loads after an O(log B) search).
+// Both numberings stay below ceil(N / R) + B.
+constexpr int kScanSeqs = 16;
+
+template <int R>
+__device__ __forceinline__ bool find_tile(const int32_t* cu, int B, int N, const int32_t* cu_o, int N_o, int t,
+                                          SlotTile& out) {
+  if (B > kScanSeqs) return slot_tile<R>(cu, B, N, cu_o, N_o, t, out);
+  int acc = 0;
+  for (int s = 0; s < B; ++s) {
+    const int a = min(max(cu[s], 0), N);
+    const int e = min(max(cu[s + 1], a), N);
+    const int nt = (e - a + R - 1) / R;
+    if (t < acc + nt) {
+      out.seq = s;
+      out.j = t - acc;
+      out.a = a;
+      out.e = e;
+      out.oa = min(max(cu_o[s], 0), N_o);
+      out.oe = min(max(cu_o[s + 1], out.oa), N_o);
+      return true;
+    }
+    acc += nt;
+  }
+  return false;
+}
+
+}  // namespace sched
+}  // namespace attn

@@ -7,6 +7,7 @@
 
 #include "attn_device.h"
 #include "attn_params.h"
+#include "attn_sched.h"
 
 namespace attn {
 namespace tile {
@@ -74,6 +75,8 @@ struct WorkItem {
 
 // work index -> item; false for the surplus items of variable-length
 // launches (their grid is an upper bound).  BR: query rows per item.
+// work = head * tiles_per_head + t: t is a query tile (dense), or a slot of
+// the head's query tiles (variable-length batches, sched::slot_tile).
 template <int BR, bool CAUSAL, bool VARLEN, bool SPLIT, bool PAGED>
 __device__ __forceinline__ bool decode_work(const FwdParams& p, const int work, WorkItem& w) {
   const int hs = work / p.tiles_per_head;  // head, or head * n_split + chunk
@@ -100,26 +103,14 @@ __device__ __forceinline__ bool decode_work(const FwdParams& p, const int work, 
     w.k_row0 = PAGED ? 0 : (int64_t)head * p.Nk + w.k_off;
     w.qt = CAUSAL ? (p.tiles_per_head - 1 - t) : t;
   } else {
-    int acc = 0, seq = -1, qb = 0, qe = 0, nts = 0;
-    for (int s = 0; s < p.B; ++s) {
-      const int a = min(max(p.cu_q[s], 0), p.Nq);
-      const int b = min(max(p.cu_q[s + 1], a), p.Nq);
-      const int nt = (b - a + BR - 1) / BR;
-      if (t < acc + nt) {
-        seq = s; qb = a; qe = b; nts = nt;
-        break;
-      }
-      acc += nt;
-    }
-    if (seq < 0) return false;
-    const int lt = t - acc;
-    w.qt = CAUSAL ? (nts - 1 - lt) : lt;
-    const int kb = min(max(p.cu_k[seq], 0), p.Nk);
-    const int ke = min(max(p.cu_k[seq + 1], kb), p.Nk);
-    w.q_len = qe - qb;
-    w.k_len = ke - kb;
-    w.q_row0 = (int64_t)head * p.Nq + qb;
-    w.k_row0 = (int64_t)head * p.Nk + kb;
+    sched::SlotTile st;
+    if (!sched::find_tile<BR>(p.cu_q, p.B, p.Nq, p.cu_k, p.Nk, t, st)) return false;
+    const int nts = (st.e - st.a + BR - 1) / BR;
+    w.qt = CAUSAL ? (nts - 1 - st.j) : st.j;  // causal: a sequence's heaviest tile first
+    w.q_len = st.e - st.a;
+    w.k_len = st.oe - st.oa;
+    w.q_row0 = (int64_t)head * p.Nq + st.a;
+    w.k_row0 = (int64_t)head * p.Nk + st.oa;
   }
   return true;
 }

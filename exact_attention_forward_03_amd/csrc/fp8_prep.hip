@@ -23,6 +23,7 @@
 // quantisation with that s.
 #include "attn_device.h"
 #include "attn_params.h"
+#include "attn_sched.h"
 
 namespace attn {
 namespace {
@@ -134,31 +135,20 @@ __global__ void __launch_bounds__(kTileThreads<D>) fp8_prep_kernel(PrepParams p)
   const int rl = tid / L, cl = tid % L;
   const int64_t base = (int64_t)bh * p.N;
   // rows [row0, row_end) of this tile; a variable-length batch restarts the
-  // tiles at every sequence (entry `tile` = the earlier sequences' tiles +
-  // the tile's index in its sequence; prefix sums clamped into [0, N])
+  // tiles at every sequence, tile j of sequence s at entry
+  // floor(cu[s] / 128) + s + j (sched::slot_tile; prefix sums clamped into
+  // [0, N])
   int row0 = tile * kTileRows, row_end = p.N;
   if (p.cu) {
-    int acc = 0;
-    bool found = false;
-    for (int s = 0; s < p.nseq; ++s) {
-      const int a = min(max(p.cu[s], 0), p.N);
-      const int b = min(max(p.cu[s + 1], a), p.N);
-      const int n = (b - a + kTileRows - 1) / kTileRows;
-      if (tile < acc + n) {
-        row0 = a + (tile - acc) * kTileRows;
-        row_end = b;
-        found = true;
-        break;
-      }
-      acc += n;
-    }
-    if (!found) {
-      // an entry past the last sequence's tiles: 1 (block scales), 0 (tile
-      // amax, so it does not raise the tensor amax); the tensor-scale pass
-      // then overwrites it
+    sched::SlotTile st;
+    if (!sched::slot_tile<kTileRows>(p.cu, p.nseq, p.N, p.cu, p.N, tile, st)) {
+      // an entry no tile owns: 1 (block scales), 0 (tile amax, so it does
+      // not raise the tensor amax); the tensor-scale pass then overwrites it
       if (MODE != 2 && tid == 0) p.scale[bh * nt + tile] = MODE == 1 ? 0.f : 1.f;
       return;
     }
+    row0 = st.a + st.j * kTileRows;
+    row_end = st.e;
   }
 
   float sg[8];

@@ -79,9 +79,9 @@ enum {
  *   fp32 dequantisation multipliers [B, H, ceil(N/128)] (one per 128-row
  *   tile; "FlashAttention-3", "Three techniques" §3: block quantisation).
  *   fp8 varlen: the tiles restart at every sequence, so no tile spans two
- *   sequences; the scales are [H, ceil(N/128) + B] with sequence b's tiles
- *   from entry sum_{b' < b} ceil(L_b' / 128) (the layout
- *   attn_fp8_quantize_varlen writes; later entries are not read).
+ *   sequences; the scales are [H, ceil(N/128) + B] with tile j of sequence b
+ *   at entry floor(cu_seqlens[b] / 128) + b + j (the layout
+ *   attn_fp8_quantize_varlen writes; entries no tile owns are not read).
  *   For fp16/bf16 the three scale pointers are ignored (may be NULL); for
  *   fp8 they may be NULL only where the tensor is empty (Nq or Nk = 0).
  *   Scales must be >= 0 (attn_fp8_quantize writes positive ones).  A V
@@ -147,10 +147,12 @@ int attn_fp8_quantize(const void* x, int x_dtype, void* x_fp8, float* x_scale,
  *     sequences, as the attention kernel reads one scale per (sequence,
  *     128-row tile).
  *   Outputs: x_fp8 uint8 [H, T, d]; x_scale fp32 [H, ceil(T/128) + nseq]
- *     (a size that needs no sequence lengths on the host): sequence b's
- *     tiles from entry sum_{b' < b} ceil(L_b' / 128); the entries after the
- *     last sequence's tiles are written too (1, or the tensor scale with
- *     per_tensor = 1) and never read.
+ *     (a size that needs no sequence lengths on the host): tile j of
+ *     sequence b at entry floor(cu_seqlens[b] / 128) + b + j, so a reader
+ *     finds a sequence's scales from its first token alone (these ranges
+ *     never overlap and end below floor(T/128) + nseq); the entries no tile
+ *     owns are written too (1, or the tensor scale with per_tensor = 1) and
+ *     never read.
  *   H, nseq >= 1; T >= 0 (T = 0 is a no-op).  cu_seqlens must be non-NULL.
  *   Same pointer, stream and error rules as attn_fp8_quantize.
  */

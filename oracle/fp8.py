@@ -353,12 +353,15 @@ def varlen_scale_len(total: int, nseq: int, tile: int = 128) -> int:
 
 
 def varlen_tile_offsets(cu, tile: int = 128) -> np.ndarray:
-    """First scale entry of each sequence: the tiles of the earlier ones,
-    sum_{b' < b} ceil(L_b' / tile) (scale tiles restart at every sequence,
-    so none straddles two sequences)."""
-    lens = np.diff(np.asarray(cu, dtype=np.int64))
-    nt = (lens + tile - 1) // tile
-    return np.concatenate([[0], np.cumsum(nt)[:-1]]).astype(np.int64)
+    """First scale entry of each sequence: floor(cu[b] / tile) + b, tile t of
+    sequence b at that entry + t (scale tiles restart at every sequence, so
+    none straddles two).  The ranges of consecutive sequences do not overlap,
+    as floor(a / tile) + ceil(L / tile) <= floor((a + L) / tile) + 1, and all
+    end below floor(T / tile) + nseq <= `varlen_scale_len`; a reader finds
+    sequence b's entries from cu[b] alone, without the lengths of the
+    sequences before it."""
+    cu = np.asarray(cu, dtype=np.int64)
+    return cu[:-1] // tile + np.arange(len(cu) - 1, dtype=np.int64)
 
 
 def quantize_varlen(x, cu, signs=None, per_tensor: bool = False, tile: int = 128):
@@ -368,7 +371,7 @@ def quantize_varlen(x, cu, signs=None, per_tensor: bool = False, tile: int = 128
     Block mode: each sequence is quantised on its own (`quantize` of its
     [H, L_b, d] slice), its scales stored at entries
     varlen_tile_offsets(cu)[b] + t of a [H, varlen_scale_len] array; entries
-    past the last sequence's tiles are 1.  Per-tensor mode: one scale for the
+    that no tile owns are 1.  Per-tensor mode: one scale for the
     whole tensor (as `quantize` of all of x), in every entry.
     Returns ``(codes uint8 [H, T, d], scales float32 [H, varlen_scale_len])``.
     """

@@ -183,8 +183,15 @@ def test_backward_full_size(gpu_lib, causal):
         check_grads((f(dq), f(dk), f(dv)), ref, bnd, f"full-size bwd head ({b},{h}) causal={causal}")
 
 
+# more sequences than a wave's 64 lanes: the kernels' slot lookup first picks
+# a block of 64 sequences
+MANY_Q = [int(x) for x in np.random.default_rng(11).integers(0, 150, 90)] + [0, 1, 64]
+MANY_K = [int(x) for x in np.random.default_rng(12).integers(0, 150, 90)] + [3, 0, 64]
+
 VARLEN_CASES = [
     # H, q lengths, k lengths, d, dtype, causal
+    (1, MANY_Q, MANY_Q, 64, "bf16", True),
+    (1, MANY_Q, MANY_K, 128, "bf16", False),
     (2, [300, 129, 64, 1], [300, 129, 64, 1], 128, "bf16", True),
     (3, [200, 0, 77], [150, 40, 300], 64, "f16", False),
     (2, [513, 260], [513, 260], 64, "bf16", True),
@@ -211,7 +218,7 @@ def test_backward_varlen_vs_oracle(gpu_lib, H, lq, lk, d, dtype, causal):
     torch.cuda.synchronize()
     f = lambda t: t.double().cpu().numpy()  # noqa: E731
     o, lse, dq, dk, dv = f(o), f(lse), f(dq), f(dk), f(dv)
-    what = f"varlen bwd H{H} lq{lq} lk{lk} d{d} {dtype} causal={causal}"
+    what = f"varlen bwd H{H} lq{lq[:8]} ({len(lq)} sequences) lk{lk[:8]} d{d} {dtype} causal={causal}"
     print(what, flush=True)
     for s in range(len(lq)):
         sq, sk = slice(cu_q[s], cu_q[s + 1]), slice(cu_k[s], cu_k[s + 1])

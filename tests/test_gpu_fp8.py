@@ -503,6 +503,21 @@ def test_prep_varlen_no_rotation_bitwise(gpu_lib, in_dtype, d, per_tensor):
     assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
 
 
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_prep_varlen_many_sequences_bitwise(gpu_lib, per_tensor):
+    """More sequences than a wave's 64 lanes (the slot lookup first picks a
+    block of 64), empty, one-token and tile-aligned ones: codes and every
+    scale entry, owned or not, equal the oracle's bit for bit."""
+    lens = [int(x) for x in np.random.default_rng(19).integers(0, 300, 150)] + [0, 1, 128, 256]
+    cu = W.cu_seqlens(lens)
+    x = np.random.default_rng(20).standard_normal((2, int(cu[-1]), 64), dtype=np.float32)
+    codes, scales = gpu_lib.fp8_quantize_varlen(torch.from_numpy(x).cuda(), _dev(cu), None, per_tensor)
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = F.quantize_varlen(x, cu, None, per_tensor)
+    assert np.array_equal(scales.cpu().numpy(), ref_scales)
+    assert np.array_equal(codes.cpu().numpy(), ref_codes)
+
+
 def _exact_varlen_problem(H, lens_q, lens_k, seed, d=128):
     cq, ck = W.cu_seqlens(lens_q), W.cu_seqlens(lens_k)
     nq, nk, B = int(cq[-1]), int(ck[-1]), len(lens_q)
@@ -515,10 +530,17 @@ def _exact_varlen_problem(H, lens_q, lens_k, seed, d=128):
     return q8, k8, v8, sq, sk, sv, cq, ck
 
 
+# more sequences than one wave's 64 lanes (the kernels' slot lookup then
+# picks a block of 64 first), with empty and one-token ones
+MANY_LENS_Q = [int(x) for x in np.random.default_rng(41).integers(0, 330, 90)] + [0, 1, 129]
+MANY_LENS_K = [int(x) for x in np.random.default_rng(42).integers(0, 330, 90)] + [5, 0, 129]
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("lens_q,lens_k,d", [(VARLEN_LENS, VARLEN_LENS, 128), ([200, 0, 300, 7], [90, 5, 400, 0], 128),
-                                             (VARLEN_LENS, VARLEN_LENS, 64), (VARLEN_LENS, VARLEN_LENS, 256)],
-                         ids=["same", "q_ne_k", "same_d64", "same_d256"])
+                                             (VARLEN_LENS, VARLEN_LENS, 64), (VARLEN_LENS, VARLEN_LENS, 256),
+                                             (MANY_LENS_Q, MANY_LENS_K, 128)],
+                         ids=["same", "q_ne_k", "same_d64", "same_d256", "many"])
 def test_fp8_varlen_kernel_vs_emulation(gpu_lib, causal, lens_q, lens_k, d):
     """Each sequence against the oracle's fp8 emulation of it, with its own
     scale tiles and V-scale normalisation (same bar and allowances as the

@@ -150,6 +150,32 @@ def test_varlen(gpu_lib, dtype, causal, d):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,nseq", [(64, 150), (128, 150), (128, 36)])
+def test_varlen_many_sequences_every_row_written(gpu_lib, causal, d, nseq):
+    """More sequences than the kernels' scalar lookup takes (16) and than one
+    wave's 64 lanes (the lookup then picks a block of 64 first): empty,
+    one-token and ragged sequences, query and key lengths that differ.  O
+    and lse start as NaN, so that a work item the lookup skipped shows up."""
+    lq = [int(x) for x in np.random.default_rng(7).integers(0, 400, nseq)] + [0, 1, 128, 129]
+    lk = [int(x) for x in np.random.default_rng(8).integers(0, 400, nseq)] + [3, 0, 128, 1]
+    cq, ck = W.cu_seqlens(lq), W.cu_seqlens(lk)
+    H = 3
+    rng = np.random.default_rng(d + causal)
+    qd, q64 = to_device(rng.standard_normal((H, int(cq[-1]), d), dtype=np.float32), "bf16")
+    kd, k64 = to_device(rng.standard_normal((H, int(ck[-1]), d), dtype=np.float32), "bf16")
+    vd, v64 = to_device(rng.standard_normal((H, int(ck[-1]), d), dtype=np.float32), "bf16")
+    o = torch.full(qd.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full(qd.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    s = 1.0 / np.sqrt(d)
+    gpu_lib.forward(qd, kd, vd, causal=causal, scale=s, cu_seqlens_q=torch.from_numpy(cq).cuda(),
+                    cu_seqlens_k=torch.from_numpy(ck).cuda(), out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_varlen(q64, k64, v64, cq, ck, s, causal)
+    check(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref, "bf16",
+          f"varlen {len(lq)} sequences d{d} causal{causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_varlen_q_k_lengths_differ(gpu_lib, causal):
     """Per-sequence Nq_b != Nk_b, including an empty key sequence (O = 0, lse = -inf)."""
     lq = [5, 130, 64, 200, 33]

@@ -303,12 +303,33 @@ def _packed(lens, d, seed):
     return x, cu
 
 
+def _owned_entries(lens, tile=128):
+    """Scale entry of every (sequence, tile), brute force from the layout."""
+    offs = F.varlen_tile_offsets(W.cu_seqlens(lens), tile)
+    return [int(offs[b]) + t for b, n in enumerate(lens) for t in range((n + tile - 1) // tile)]
+
+
 def test_varlen_tile_layout():
     cu = W.cu_seqlens(VARLEN_LENS)
-    # tiles per sequence: 2, 1, 0, 2, 3, 1 -> first entries 0, 2, 3, 3, 5, 8
-    assert F.varlen_tile_offsets(cu).tolist() == [0, 2, 3, 3, 5, 8]
+    # cu = 0, 130, 131, 131, 387, 687: floor(cu / 128) + b = 0, 2, 3, 4, 7, 10;
+    # tiles per sequence 2, 1, 0, 2, 3, 1 -> entries 0 1 | 2 | - | 4 5 | 7 8 9 | 10
+    assert F.varlen_tile_offsets(cu).tolist() == [0, 2, 3, 4, 7, 10]
+    assert _owned_entries(VARLEN_LENS) == [0, 1, 2, 4, 5, 7, 8, 9, 10]
     assert F.varlen_scale_len(int(cu[-1]), len(VARLEN_LENS)) == (814 + 127) // 128 + 6
-    assert F.varlen_tile_offsets(cu)[-1] + 1 <= F.varlen_scale_len(int(cu[-1]), len(VARLEN_LENS))
+
+
+def test_varlen_tile_layout_disjoint_and_bounded():
+    """Every (sequence, tile) gets its own entry, below varlen_scale_len, for
+    random length mixes with empty, one-token and tile-aligned sequences."""
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        nseq = int(rng.integers(1, 40))
+        lens = [int(x) for x in rng.choice([0, 1, 127, 128, 129, 256, int(rng.integers(0, 2000))], nseq)]
+        for tile in (64, 128):
+            ent = _owned_entries(lens, tile)
+            assert len(set(ent)) == len(ent)
+            assert all(0 <= e < F.varlen_scale_len(sum(lens), nseq, tile) for e in ent)
+            assert ent == sorted(ent)
 
 
 @pytest.mark.parametrize("rotate", [False, True])
@@ -316,7 +337,7 @@ def test_quantize_varlen_tiles_restart_per_sequence(rotate):
     """Each sequence's tiles start at its first token: the largest magnitude
     of every (head, sequence tile) lands on 448 and the codes round to
     nearest, checked per sequence with the dense property checker; entries
-    past the last tile stay 1."""
+    that no tile owns stay 1."""
     d = 64
     x, cu = _packed(VARLEN_LENS, d, 5)
     s = RNG.choice([-1.0, 1.0], d).astype(np.float32) if rotate else None
@@ -329,8 +350,9 @@ def test_quantize_varlen_tiles_restart_per_sequence(rotate):
         if e > a:
             nt = (e - a + 127) // 128
             _check_quantized(x_rot[:, a:e], codes[:, a:e], scales[:, offs[b]:offs[b] + nt], 128, False)
-    used = int(offs[-1]) + (VARLEN_LENS[-1] + 127) // 128
-    assert np.all(scales[:, used:] == 1.0)
+    free = np.ones(scales.shape[-1], bool)
+    free[_owned_entries(VARLEN_LENS)] = False
+    assert np.all(scales[:, free] == 1.0)
 
 
 def test_quantize_varlen_aligned_equals_dense():
@@ -341,7 +363,8 @@ def test_quantize_varlen_aligned_equals_dense():
     codes, scales = F.quantize_varlen(x, cu)
     ref_c, ref_s = F.quantize(x[None])
     assert np.array_equal(codes, ref_c[0])
-    assert np.array_equal(scales[:, :6], ref_s[0])
+    assert _owned_entries([256, 128, 384]) == [0, 1, 3, 5, 6, 7]
+    assert np.array_equal(scales[:, [0, 1, 3, 5, 6, 7]], ref_s[0])
 
 
 def test_quantize_varlen_per_tensor_equals_dense():
