@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libattn.so")
 PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fwd_fp8.hip", "fp8_prep.hip", "attn_merge.hip", "attn_bwd.hip",
-           "attn_bwd_fp8.hip", "attn_noalloc.hip"]
+           "attn_bwd_fp8.hip", "attn_noalloc.hip", "attn_decode.hip"]
 PROBE_SOURCES = ["mfma_peak.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.

@@ -728,6 +728,7 @@ int fwd_split_tile_keys(int d) {
 
 hipError_t launch_fwd(int dtype, int d, bool causal, bool varlen, bool split, int kv, const FwdParams& p,
                       hipStream_t st) {
+  if (split && decode_shape(p.Nq, kv)) return launch_decode(dtype, d, causal, kv, p, st);
   if (dtype == 0) return launch_dma_t<f16_t>(d, causal, varlen, split, kv, p, st);
   return launch_dma_t<bf16_t>(d, causal, varlen, split, kv, p, st);
 }

@@ -59,6 +59,8 @@ CASES = [
     (1, 8, 130, 128, "bf16", 192, [900], 2),
     (2, 3, 1, 128, "bf16", 64, [63, 65], 1),
     (2, 2, 7, 64, "f16", 128, [5000, 2500], 16),
+    (2, 2, 8, 128, "bf16", 64, [700, 1], 3),
+    (1, 3, 2, 256, "f16", 64, [1111], 7),
 ]
 
 
@@ -76,12 +78,14 @@ def test_paged_decode_full(gpu_lib):
 
 def test_paged_matches_contiguous_splitkv(gpu_lib):
     """One sequence per batch entry whose pages are in order: the paged
-    launch reads the same rows as the contiguous split-KV launch."""
+    launch reads the same rows as the contiguous split-KV launch.  Three
+    query rows, so that both run the prefill kernel's key-chunk launch (with
+    one or two rows the contiguous launch runs the decoding-shaped kernel)."""
     B, H, L, d, P = 2, 4, 1024, 128, 128
     rng = np.random.default_rng(3)
     k = torch.from_numpy(rng.standard_normal((B, L, H, d), dtype=np.float32)).to(torch.bfloat16).cuda()
     v = torch.from_numpy(rng.standard_normal((B, L, H, d), dtype=np.float32)).to(torch.bfloat16).cuda()
-    q = torch.from_numpy(rng.standard_normal((B, H, 1, d), dtype=np.float32)).to(torch.bfloat16).cuda()
+    q = torch.from_numpy(rng.standard_normal((B, H, 3, d), dtype=np.float32)).to(torch.bfloat16).cuda()
     kc = k.reshape(B * L // P, P, H, d)
     vc = v.reshape(B * L // P, P, H, d)
     table = torch.arange(B * L // P, dtype=torch.int32, device="cuda").reshape(B, L // P)
@@ -102,6 +106,9 @@ QCASES = [
     (4, 2, 1, 64, "bf16", 64, [300, 0, 64, 129], 3, "int8"),
     (2, 2, 2, 256, "bf16", 128, [900, 777], 2, "e4m3"),
     (2, 8, 1, 128, "bf16", 256, [8192, 3000], None, "e4m3"),
+    (2, 2, 8, 64, "f16", 64, [1000, 65], 3, "e4m3"),
+    (1, 4, 4, 256, "bf16", 128, [1500], 2, "int8"),
+    (3, 2, 1, 256, "bf16", 64, [64, 0, 2500], 4, "e4m3"),
 ]
 
 
@@ -138,7 +145,8 @@ def test_paged_8bit_vs_oracle(gpu_lib, B, H, Nq, d, dtype, page_size, lens, spli
 def test_paged_8bit_equals_16bit_cache(gpu_lib):
     """int8 codes with scale 1 are small integers: the same values stored as a
     bf16 cache give the same attention (both exact inputs to the kernel; the
-    8-bit path only adds the multiplications by 1)."""
+    8-bit path only adds the multiplications by 1).  Three query rows: both
+    caches on the prefill kernel's key-chunk launch."""
     B, H, d, P = 2, 4, 128, 128
     lens = [1000, 333]
     kc32, _, table = make_cache(B, H, lens, d, P, "bf16", 21)
@@ -146,7 +154,7 @@ def test_paged_8bit_equals_16bit_cache(gpu_lib):
     kcodes = rng.integers(-3, 4, size=kc32.shape).astype(np.int8)
     vcodes = rng.integers(-3, 4, size=kc32.shape).astype(np.int8)
     ones = torch.ones(kc32.shape[:3], dtype=torch.float32, device="cuda")
-    q = torch.from_numpy(rng.standard_normal((B, H, 1, d), dtype=np.float32) * 0.1).to(torch.bfloat16).cuda()
+    q = torch.from_numpy(rng.standard_normal((B, H, 3, d), dtype=np.float32) * 0.1).to(torch.bfloat16).cuda()
     td = torch.from_numpy(table).cuda()
     ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
     k8 = torch.from_numpy(kcodes.view(np.uint8)).cuda()
@@ -155,6 +163,40 @@ def test_paged_8bit_equals_16bit_cache(gpu_lib):
     kb = torch.from_numpy(kcodes.astype(np.float32)).to(torch.bfloat16).cuda()
     vb = torch.from_numpy(vcodes.astype(np.float32)).to(torch.bfloat16).cuda()
     o2, l2 = gpu_lib.forward_paged(q, kb, vb, td, ld, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2) and torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("kind", ["int8", "e4m3"])
+def test_decode_kernel_8bit_cache_equals_dense(gpu_lib, kind):
+    """The decoding-shaped kernel (one query row) on an 8-bit paged cache with
+    unit scales and pages in order equals the same kernel on the dense,
+    contiguous copy of the decoded values: the codes widen to fp32 exactly,
+    the scales multiply by 1, and both launches cut the keys at the same
+    chunk bounds (1024 keys, 4 chunks)."""
+    import workloads as W
+
+    B, H, L, d, P = 2, 4, 1024, 128, 128
+    rng = np.random.default_rng(5)
+    if kind == "int8":
+        kcodes = rng.integers(-100, 101, size=(B, L, H, d)).astype(np.int8).view(np.uint8)
+        vcodes = rng.integers(-100, 101, size=(B, L, H, d)).astype(np.int8).view(np.uint8)
+        dec = lambda c: c.view(np.int8).astype(np.float32)  # noqa: E731
+    else:
+        kcodes = W.random_e4m3_codes((B, L, H, d), 6)
+        vcodes = W.random_e4m3_codes((B, L, H, d), 7)
+        dec = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).float().numpy()  # noqa: E731
+    q = torch.from_numpy(rng.standard_normal((B, H, 1, d), dtype=np.float32) * 0.02).to(torch.bfloat16).cuda()
+    ones = torch.ones((B * L // P, P, H), dtype=torch.float32, device="cuda")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    table = torch.arange(B * L // P, dtype=torch.int32, device="cuda").reshape(B, L // P)
+    lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    o1, l1 = gpu_lib.forward_paged(q, t(kcodes.reshape(B * L // P, P, H, d)), t(vcodes.reshape(B * L // P, P, H, d)),
+                                   table, lens, k_scale=ones, v_scale=ones, kv_dtype=kind, num_splits=4)
+    # the decoded values are exact in bfloat16 (e4m3 and small integers)
+    kd = torch.from_numpy(dec(kcodes).transpose(0, 2, 1, 3).copy()).to(torch.bfloat16).cuda()
+    vd = torch.from_numpy(dec(vcodes).transpose(0, 2, 1, 3).copy()).to(torch.bfloat16).cuda()
+    o2, l2 = gpu_lib.forward_splitkv(q, kd, vd, num_splits=4)
     torch.cuda.synchronize()
     assert torch.equal(l1, l2) and torch.equal(o1, o2)
 

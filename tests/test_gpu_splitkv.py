@@ -5,7 +5,8 @@
   (``oracle.attention``) at the dense tolerances; the per-chunk workspace
   with the oracle's chunk partials (``oracle.splitkv``), which follow the
   same chunk bounds ceil(Nk / S).  Shapes cover decoding (one query per
-  head), prefill with causal masks that make whole chunks invisible to some
+  head, and a few: up to two run the decoding-shaped kernel; causal rows
+  that see only the first keys), prefill with causal masks that make whole chunks invisible to some
   rows, more chunks than keys (empty chunks), and d = 64 / 128 / 256.
 * The merge alone is fed random fp32 partials with -inf parts and all -inf
   rows and compared with ``oracle.splitkv.merge``.
@@ -54,6 +55,15 @@ CASES = [
     (1, 2, 10, 3, 128, "bf16", False, 6),
     (1, 1, 513, 1500, 64, "bf16", True, 3),
     (1, 2, 64, 4096, 256, "f16", True, 9),
+    # at most 8 query rows per head: the decoding-shaped kernel
+    (1, 3, 2, 777, 256, "bf16", True, 3),
+    (2, 2, 4, 1500, 64, "bf16", True, 5),
+    (1, 2, 8, 2049, 128, "f16", False, 4),
+    (1, 2, 5, 600, 128, "bf16", True, 2),
+    (2, 3, 8, 9, 256, "f16", True, 4),
+    (1, 1, 3, 5000, 64, "f16", False, 64),
+    (1, 2, 1, 500, 128, "bf16", True, 4),
+    (1, 1, 2, 5, 64, "f16", False, 16),
 ]
 
 
