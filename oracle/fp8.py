@@ -232,7 +232,7 @@ P_SCALE_LOG2 = 8  # P is rounded as e4m3(2^8 * p), p <= 1, so codes stay <= 256
 
 def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
                   tile: int = 128, quantize_p: bool = True, rows=None, ambiguity=0.0,
-                  parts: bool = False, p_mode: str = "folded", block=None):
+                  parts: bool = False, p_mode: str = "folded", block=None, k_offset: int = 0):
     """fp8 attention of one or more heads: codes [..., N, d], scales [..., nt].
 
     S = scale * (sq q8)(sk k8)^T, softmax statistics in float64, and P
@@ -240,7 +240,9 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     ``quantize_p=False`` P is kept exact (the method without P rounding).
     ``rows`` (query indices) restricts the output to those query rows.
     ``block`` is the key-block length of the running max (default ``tile``;
-    a divisor of it).  Returns float64 ``(O [..., Nq, d], lse [..., Nq])``.
+    a divisor of it).  ``k_offset`` is the absolute index of the first key
+    (a chunk of a longer key range): the causal mask shows key j to query i
+    iff k_offset + j <= i.  Returns float64 ``(O [..., Nq, d], lse [..., Nq])``.
 
     With ``ambiguity = delta > 0`` a third array [..., Nq, d] is returned:
     the largest change of O that re-rounding, to the other neighbouring code,
@@ -275,7 +277,7 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     nk = kd.shape[-2]
     s = float(scale) * np.matmul(qd, np.swapaxes(kd, -1, -2))
     if causal:
-        s = np.where(np.arange(nk)[None, :] <= qrow[:, None], s, -np.inf)
+        s = np.where(int(k_offset) + np.arange(nk)[None, :] <= qrow[:, None], s, -np.inf)
     t = s * LOG2E
     tmax = t.max(axis=-1) if nk else np.full(t.shape[:-1], -np.inf)
     live = np.isfinite(tmax)
@@ -294,7 +296,8 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
     Mj = np.repeat(run, blk, axis=-1)[..., :nk]  # -inf before a row's first visible key (those keys are masked)
     fin = np.isfinite(t)
     shift = np.where(fin, Mj - M[..., None], 0.0)  # <= 0, an integer
-    p_tile = np.where(fin, np.exp2(np.where(fin, t - Mj, 0.0)), 0.0)  # P relative to the running max
+    with np.errstate(invalid="ignore"):  # masked keys: -inf - (-inf), discarded by the where
+        p_tile = np.where(fin, np.exp2(np.where(fin, t - Mj, 0.0)), 0.0)  # P relative to the running max
     if p_mode not in ("folded", "rowmax"):
         raise ValueError("p_mode must be 'folded' or 'rowmax'")
     sv_max = sv.max(axis=-1) if sv.shape[-1] else np.ones(sv.shape[:-1])
@@ -338,6 +341,61 @@ def attention_fp8(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False,
                 "x": pw * 2.0 ** P_SCALE_LOG2, "shift": shift, "t": t, "M": M, "M_tile": run}
     if flip is not None:
         return o, lse, flip
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# Key chunks (FlashDecoding) on fp8 operands
+# --------------------------------------------------------------------------
+
+def split_bounds_fp8(nk: int, num_splits: int, tile: int = 128):
+    """Key ranges [begin, end) of the fp8 key chunks: ceil(nk / num_splits)
+    keys rounded up to whole scale tiles, in order (the last chunks may be
+    short or empty), so that no scale tile is cut between two chunks."""
+    if num_splits < 1:
+        raise ValueError("num_splits must be >= 1")
+    n = -(-nk // num_splits) if nk > 0 else 0
+    n = -(-n // tile) * tile
+    return [(min(s * n, nk), min((s + 1) * n, nk)) for s in range(num_splits)]
+
+
+def attention_fp8_splitkv(q8, k8, v8, sq, sk, sv, scale: float, causal: bool = False, num_splits: int = 1,
+                          tile: int = 128, quantize_p: bool = True, ambiguity=0.0, parts: bool = False,
+                          block=None):
+    """fp8 attention over key chunks, merged ("FlashAttention-3" wiki page:
+    FlashDecoding among the related techniques; the merge of "Flash Attention
+    3：让 GPU 跑满的注意力计算", §2.2, as `oracle.splitkv.merge`).
+
+    Each chunk (`split_bounds_fp8`) is the fp8 attention of its keys alone
+    (`attention_fp8` of the chunk's codes and scale tiles): its own largest V
+    scale for the P weights and a running max that starts at the chunk,
+    with the causal mask on absolute key indices (k_offset).  A chunk with
+    no visible key gives O_s = 0, lse_s = -inf.  Returns float64
+    ``(O, lse)`` merged; ``parts=True`` returns ``(O, lse, chunks)`` with
+    ``chunks`` a list of ``(begin, end, parts dict of attention_fp8 or None
+    for an empty chunk)``.
+    """
+    from .splitkv import merge
+
+    nq, nk = q8.shape[-2], k8.shape[-2]
+    lead = q8.shape[:-2]
+    o_parts, lse_parts, chunks = [], [], []
+    for kb, ke in split_bounds_fp8(nk, num_splits, tile):
+        if ke <= kb:
+            o_parts.append(np.zeros(lead + (nq, q8.shape[-1])))
+            lse_parts.append(np.full(lead + (nq,), -np.inf))
+            chunks.append((kb, ke, None))
+            continue
+        ts = slice(kb // tile, -(-ke // tile))
+        r = attention_fp8(q8, k8[..., kb:ke, :], v8[..., kb:ke, :], sq, sk[..., ts], sv[..., ts], scale, causal,
+                          tile=tile, quantize_p=quantize_p, ambiguity=ambiguity, parts=True, block=block,
+                          k_offset=kb)
+        o_parts.append(r["o"])
+        lse_parts.append(r["lse"])
+        chunks.append((kb, ke, r))
+    o, lse = merge(np.stack(o_parts), np.stack(lse_parts))
+    if parts:
+        return o, lse, chunks
     return o, lse
 
 

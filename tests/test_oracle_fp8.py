@@ -613,3 +613,76 @@ def test_p_rounding_running_max_per_key_block():
     np.testing.assert_allclose(e64[0], e128[0], rtol=1e-14)
     with pytest.raises(ValueError):
         F.attention_fp8(q8, k8, v8, one, one, one, scale, block=48)
+
+
+# ------------------------------------------------------------- key chunks
+
+def _split_problem(lead, nq, nk, d, seed):
+    q8 = W.random_e4m3_codes(lead + (nq, d), seed, max_exp_field=9)
+    k8 = W.random_e4m3_codes(lead + (nk, d), seed + 1, max_exp_field=9)
+    v8 = W.random_e4m3_codes(lead + (nk, d), seed + 2, max_exp_field=9)
+    sq = W.random_scales(lead + ((nq + 127) // 128,), seed + 3)
+    sk = W.random_scales(lead + ((nk + 127) // 128,), seed + 4)
+    sv = W.random_scales(lead + ((nk + 127) // 128,), seed + 5)
+    return q8, k8, v8, sq, sk, sv
+
+
+def test_fp8_split_bounds_whole_scale_tiles():
+    for nk in (0, 1, 127, 128, 129, 700, 1000, 4096):
+        for s in (1, 2, 3, 7, 40):
+            b = F.split_bounds_fp8(nk, s)
+            assert len(b) == s and b[0][0] == 0 and b[-1][1] == nk
+            assert all(e0 == b1 for (_, e0), (b1, _) in zip(b[:-1], b[1:]))
+            assert all(kb % 128 == 0 for kb, ke in b if ke > kb)  # empty chunks sit at nk
+    assert F.split_bounds_fp8(700, 3) == [(0, 256), (256, 512), (512, 700)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def pin_fp8_split_unrounded_equals_exact(causal, split=F.attention_fp8_splitkv):
+    """With P unrounded the merged chunks equal the exact attention of the
+    dequantised operands (a different code path, oracle.attention): chunk
+    bounds, the scale tiles each chunk reads, the absolute causal indices
+    and the merge all have to be right.  Rows whose whole chunk lies above
+    the diagonal contribute nothing."""
+    q8, k8, v8, sq, sk, sv = _split_problem((2,), 300, 700, 32, 41)
+    for S in (1, 3, 6):
+        o, lse = split(q8, k8, v8, sq, sk, sv, 0.25, causal, num_splits=S, quantize_p=False)
+        ref_o, ref_l = oracle.attention(F.dequantize(q8, sq), F.dequantize(k8, sk), F.dequantize(v8, sv), 0.25, causal)
+        np.testing.assert_allclose(o, ref_o, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse, ref_l, rtol=1e-12, atol=1e-12)
+
+
+test_fp8_split_unrounded_equals_exact = pin_fp8_split_unrounded_equals_exact
+
+
+def test_fp8_split_one_chunk_is_the_dense_emulation():
+    q8, k8, v8, sq, sk, sv = _split_problem((2,), 200, 300, 32, 43)
+    for causal in (False, True):
+        o, lse = F.attention_fp8_splitkv(q8, k8, v8, sq, sk, sv, 0.3, causal, num_splits=1)
+        ref_o, ref_l = F.attention_fp8(q8, k8, v8, sq, sk, sv, 0.3, causal)
+        assert np.allclose(o, ref_o, rtol=1e-14, atol=1e-15) and np.array_equal(np.isneginf(lse), np.isneginf(ref_l))
+        np.testing.assert_allclose(lse[np.isfinite(ref_l)], ref_l[np.isfinite(ref_l)], rtol=1e-14)
+
+
+def test_fp8_split_rounded_within_bound():
+    """P rounded per chunk: the merged result stays within what rounding P to
+    three mantissa bits can do against the unrounded split (relative RMSE
+    below 2^-4)."""
+    q8, k8, v8, sq, sk, sv = _split_problem((2,), 128, 1000, 64, 47)
+    a, _ = F.attention_fp8_splitkv(q8, k8, v8, sq, sk, sv, 0.125, False, num_splits=4)
+    b, _ = F.attention_fp8_splitkv(q8, k8, v8, sq, sk, sv, 0.125, False, num_splits=4, quantize_p=False)
+    rel = np.sqrt(np.mean((a - b) ** 2)) / np.sqrt(np.mean(b ** 2))
+    assert 0 < rel < 2.0 ** -4
+
+
+def test_mutation_split_chunk_offset(monkeypatch):
+    """A chunk whose causal mask used local key indices: the pin fails."""
+    orig = F.attention_fp8
+
+    def mutant(*a, **kw):
+        kw["k_offset"] = 0
+        return orig(*a, **kw)
+
+    monkeypatch.setattr(F, "attention_fp8", mutant)
+    with pytest.raises(AssertionError):
+        pin_fp8_split_unrounded_equals_exact(True)
