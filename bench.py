@@ -403,6 +403,7 @@ def bench_fp8(attn, steps, warmup, varlen=True):
             "fp8_end_to_end": {"ms": round(ms + ms_prep, 4),
                                "tflops": round(w.flops() / ((ms + ms_prep) / 1e3) / 1e12, 2)},
             **bench_fp8_hdim256(attn, steps, warmup),
+            **bench_fp8_splitkv(attn, steps, warmup),
             **(bench_fp8_varlen(attn, steps, warmup) if varlen else {})}
 
 
@@ -433,6 +434,45 @@ def bench_fp8_hdim256(attn, steps, warmup):
     tf = w.flops() / (ms / 1e3) / 1e12
     return {"fp8_hdim256": {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_FP8_TFLOPS, 4),
                             "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}}
+
+
+def bench_fp8_splitkv(attn, steps, warmup):
+    """Long keys and few query tiles in fp8 (B=1 H=16 Nq=512 Nk=65536 d=128,
+    N(0,1), non-causal): the e4m3 kernel over 8 key chunks plus the merge
+    (attn_fwd_splitkv_fp8), beside the one-pass kernel on the same codes."""
+    import numpy as np
+    import torch
+
+    B, H, nq, nk, d = 1, 16, 512, 65536, 128
+    g = torch.Generator().manual_seed(11)
+    q8, sq = attn.fp8_quantize(torch.randn(B, H, nq, d, generator=g).cuda())
+    k8, sk = attn.fp8_quantize(torch.randn(B, H, nk, d, generator=g).cuda())
+    v8, sv = attn.fp8_quantize(torch.randn(B, H, nk, d, generator=g).cuda())
+    scale = 1.0 / np.sqrt(d)
+    stream = torch.cuda.current_stream()
+    o = torch.empty(B, H, nq, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, H, nq, dtype=torch.float32, device="cuda")
+    S = 8
+    op = torch.empty(S, B, H, nq, d, dtype=torch.float32, device="cuda")
+    lp = torch.empty(S, B, H, nq, dtype=torch.float32, device="cuda")
+
+    def split():
+        attn.forward_splitkv_fp8(q8, sq, k8, sk, v8, sv, scale=scale, num_splits=S, out=o, lse=lse, o_part=op,
+                                 lse_part=lp)
+
+    def one_pass():
+        attn.forward(q8, k8, v8, scale=scale, q_scale=sq, k_scale=sk, v_scale=sv, out=o, lse=lse)
+
+    flops = 4.0 * B * H * nq * nk * d
+    out = {}
+    for name, fn in (("fp8_splitkv_long_keys", split), ("fp8_one_pass_long_keys", one_pass)):
+        for _ in range(warmup):
+            fn()
+        ms = float(np.mean(timed_launches(fn, steps, stream)))
+        tf = flops / (ms / 1e3) / 1e12
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                     "shape": [B, H, nq, nk, d], "num_splits": S if fn is split else 1}
+    return out
 
 
 def bench_fp8_varlen(attn, steps, warmup):

@@ -3,9 +3,9 @@
 
 The C entry points are exposed under their own names with plain integer
 pointers (argument marshalling only): ``attn_fwd``, ``attn_fwd_stream``,
-``attn_fwd_splitkv``, ``attn_fwd_paged``, ``attn_merge``, ``attn_bwd``,
+``attn_fwd_splitkv``, ``attn_fwd_splitkv_fp8``, ``attn_fwd_paged``, ``attn_merge``, ``attn_bwd``,
 ``attn_bwd_fp8``, ``attn_fp8_quantize``, ``attn_fp8_quantize_varlen``,
-``attn_strerror``.  ``forward``, ``forward_splitkv``, ``forward_paged``,
+``attn_strerror``.  ``forward``, ``forward_splitkv``, ``forward_splitkv_fp8``, ``forward_paged``,
 ``merge``, ``backward``, ``backward_fp8``, ``fp8_quantize`` and
 ``fp8_quantize_varlen`` are the
 torch-facing conveniences: they allocate the
@@ -29,14 +29,15 @@ __all__ = [
     "load", "lib_path", "attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_fp8_quantize",
     "attn_fwd_paged", "attn_bwd", "attn_bwd_fp8", "attn_strerror", "attn_fp8_quantize_varlen", "forward",
     "forward_splitkv", "forward_paged", "merge", "backward", "backward_fp8", "fp8_quantize", "fp8_quantize_varlen",
-    "default_splits", "EXPORTS",
+    "default_splits", "EXPORTS", "attn_fwd_splitkv_fp8", "forward_splitkv_fp8",
 ]
 
 ATTN_DT_F16, ATTN_DT_BF16, ATTN_DT_FP8_E4M3, ATTN_DT_F32, ATTN_DT_INT8 = 0, 1, 2, 3, 4
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_TOO_LARGE = 0, -1, -2, -3, -4
 ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20  # the fixed device scratch of attn_fwd_splitkv_noalloc (include/attn.h)
 
-EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_fwd_paged",
+EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_fwd_splitkv_fp8",
+           "attn_fwd_paged",
            "attn_merge", "attn_bwd", "attn_bwd_fp8", "attn_fp8_quantize", "attn_fp8_quantize_varlen", "attn_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +67,8 @@ def load():
         lib.attn_fwd_stream.restype = _i
         lib.attn_fwd_splitkv.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p, _p, _p]
         lib.attn_fwd_splitkv.restype = _i
+        lib.attn_fwd_splitkv_fp8.argtypes = [_p] * 8 + [_i] * 5 + [_f, _i, _i, _p, _p, _p]
+        lib.attn_fwd_splitkv_fp8.restype = _i
         lib.attn_fwd_splitkv_noalloc.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p]
         lib.attn_fwd_splitkv_noalloc.restype = _i
         lib.attn_merge.argtypes = [_p, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p]
@@ -105,6 +108,12 @@ def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num
                      hip_stream) -> int:
     return load().attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num_splits, o_part,
                                    lse_part, hip_stream)
+
+
+def attn_fwd_splitkv_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o, lse, B, H, Nq, Nk, d, scale, causal,
+                         num_splits, o_part, lse_part, hip_stream) -> int:
+    return load().attn_fwd_splitkv_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o, lse, B, H, Nq, Nk, d, scale,
+                                       causal, num_splits, o_part, lse_part, hip_stream)
 
 
 def attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, num_splits,
@@ -279,6 +288,49 @@ def forward_splitkv(q, k, v, *, causal: bool = False, scale: Optional[float] = N
     rc = attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
                           int(bool(causal)), dt, int(num_splits), _ptr(o_part), _ptr(lse_part),
                           _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def forward_splitkv_fp8(q8, q_scale, k8, k_scale, v8, v_scale, *, causal: bool = False,
+                        scale: Optional[float] = None, num_splits: Optional[int] = None, out=None, lse=None,
+                        o_part=None, lse_part=None):
+    """fp8 attention over key chunks plus the merge, through
+    ``attn_fwd_splitkv_fp8``: e4m3 codes (uint8) q8 [B, H, Nq, d], k8/v8
+    [B, H, Nk, d] with their per-128-row-tile scales (as ``fp8_quantize``
+    writes them) -> (o bfloat16, lse).  Workspace as ``forward_splitkv``."""
+    import torch
+
+    for t in (q8, k8, v8, q_scale, k_scale, v_scale):
+        if not t.is_contiguous():
+            raise ValueError("codes and scales must be contiguous")
+    if any(_dtype_code(t) != ATTN_DT_FP8_E4M3 for t in (q8, k8, v8)):
+        raise TypeError("q8, k8, v8 must be uint8 e4m3 codes")
+    if q8.dim() != 4:
+        raise ValueError("q8 must be [B, H, N, d]")
+    B, H, Nq, d = q8.shape
+    Nk = k8.shape[2]
+    if q_scale.numel() < B * H * ((Nq + 127) // 128) or min(k_scale.numel(), v_scale.numel()) < B * H * (
+            (Nk + 127) // 128):
+        raise ValueError("scales must hold one entry per (b, h, 128-row tile)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        cus = torch.cuda.get_device_properties(q8.device).multi_processor_count
+        num_splits = default_splits(B, H, Nq, Nk, target_workgroups=2 * cus)
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    if o_part is None:
+        o_part = torch.empty((num_splits, B, H, Nq, d), dtype=torch.float32, device=q8.device)
+    if lse_part is None:
+        lse_part = torch.empty((num_splits, B, H, Nq), dtype=torch.float32, device=q8.device)
+    if o_part.numel() < num_splits * B * H * Nq * d or lse_part.numel() < num_splits * B * H * Nq:
+        raise ValueError("o_part / lse_part are smaller than num_splits chunks")
+    rc = attn_fwd_splitkv_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale), _ptr(out),
+                              _ptr(lse), B, H, Nq, Nk, d, float(scale), int(bool(causal)), int(num_splits),
+                              _ptr(o_part), _ptr(lse_part), _stream(q8.device))
     _check(rc)
     return out, lse
 

@@ -114,7 +114,7 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   hipStream_t st = (hipStream_t)hip_stream;
   hipError_t e;
   if (dtype == ATTN_DT_FP8_E4M3)
-    e = attn::launch_fwd_fp8(d, causal != 0, varlen, p, st);
+    e = attn::launch_fwd_fp8(d, causal != 0, varlen, false, p, st);
   else
     e = attn::launch_fwd(dtype, d, causal != 0, varlen, false, 0, p, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -170,6 +170,40 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   hipError_t e = attn::launch_fwd(dtype, d, causal != 0, false, true, 0, p, st);
   if (e != hipSuccess) return ATTN_ERR_HIP;
   return attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, dtype, hip_stream);
+}
+
+int attn_fwd_splitkv_fp8(const void* q8, const float* q_scale, const void* k8, const float* k_scale, const void* v8,
+                         const float* v_scale, void* o, float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                         int causal, int num_splits, float* o_part, float* lse_part, void* hip_stream) {
+  const int rc = validate_fwd(q8, k8, v8, o, lse, B, H, Nq, Nk, d, scale, causal, nullptr, nullptr,
+                              ATTN_DT_FP8_E4M3, q_scale, k_scale, v_scale);
+  if (rc != ATTN_OK) return rc;
+  if (num_splits < 1 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
+  if (Nq > 0 && (!o_part || !lse_part)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned(o_part, 16) || !aligned(lse_part, 4)) return ATTN_ERR_INVALID_ARG;
+  if (Nq == 0) return ATTN_OK;
+  const int br = attn::fwd_fp8_block_rows(causal != 0);
+  const int64_t tiles = ((int64_t)Nq + br - 1) / br;
+  const int64_t n_work = (int64_t)B * H * num_splits * tiles;
+  if (n_work > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  // chunks of whole 128-row scale tiles
+  int64_t split_len = ((int64_t)Nk + num_splits - 1) / num_splits;
+  split_len = (split_len + 127) / 128 * 128;
+  attn::FwdParams p{};
+  p.q = q8; p.k = k8; p.v = v8; p.o = o; p.lse = lse;
+  p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk;
+  p.c = scale * 1.4426950408889634f;
+  p.q_scale = q_scale; p.k_scale = k_scale; p.v_scale = v_scale;
+  p.tiles_per_head = (int)tiles;
+  p.n_work = (int)n_work;
+  p.n_split = num_splits;
+  p.split_len = (int)split_len;
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  hipStream_t st = (hipStream_t)hip_stream;
+  const hipError_t e = attn::launch_fwd_fp8(d, causal != 0, false, true, p, st);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  return attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, ATTN_DT_BF16, hip_stream);
 }
 
 int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,

@@ -98,7 +98,7 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
 // cu_seqlens; the work item is (head, sequence, query tile) and the scales of
 // sequence s start at entry floor(cu[s] / 128) + s of the head's
 // ceil(T / 128) + B entries (sched::slot_tile).
-template <int D, int BC, bool CAUSAL, int NW, int NS, bool VARLEN>
+template <int D, int BC, bool CAUSAL, int NW, int NS, bool VARLEN, bool SPLIT>
 __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   constexpr int SC = kScaleRows;
   constexpr int kRowB = D;               // bytes per K/V row
@@ -117,18 +117,28 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   static_assert(kLoads % NW == 0, "each wave issues the same number of tile loads");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds8[];
 
+  static_assert(!(SPLIT && VARLEN), "key chunks are for dense batches");
   int head, qt, q_len, k_len;
+  int k_off = 0, split = 0;  // key chunks: first key of the chunk, chunk index
   int64_t q_row0, k_row0, sq0, sk0;  // first rows of the (sequence,) head; its first scale entries
   if constexpr (!VARLEN) {
-    head = work / p.tiles_per_head;
-    const int t = work - head * p.tiles_per_head;
+    // work = (head * n_split + chunk) * tiles_per_head + t (n_split = 1 without chunks)
+    const int hs = work / p.tiles_per_head;
+    const int t = work - hs * p.tiles_per_head;
+    head = SPLIT ? hs / p.n_split : hs;
     qt = CAUSAL ? (p.tiles_per_head - 1 - t) : t;
     q_len = p.Nq;
     k_len = p.Nk;
+    if constexpr (SPLIT) {
+      // chunks of whole scale tiles (split_len is a multiple of SC)
+      split = hs - head * p.n_split;
+      k_off = (int)min((int64_t)split * p.split_len, (int64_t)p.Nk);
+      k_len = (int)min((int64_t)p.split_len, (int64_t)p.Nk - k_off);
+    }
     q_row0 = (int64_t)head * p.Nq;
-    k_row0 = (int64_t)head * p.Nk;
+    k_row0 = (int64_t)head * p.Nk + k_off;
     sq0 = (int64_t)head * ((q_len + SC - 1) / SC);
-    sk0 = (int64_t)head * ((k_len + SC - 1) / SC);
+    sk0 = (int64_t)head * ((p.Nk + SC - 1) / SC) + k_off / SC;
   } else {
     // t: a slot of the head's 128-row query tiles (sched::slot_tile); the
     // scale entries of a packed batch use the same slots, so the sequence's
@@ -189,10 +199,18 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   }
 
   int n_kt = (k_len + BC - 1) / BC;
-  if (CAUSAL) n_kt = min(n_kt, (min(q0 + BR, q_len) - 1) / BC + 1);
+  if (CAUSAL) {
+    // last key (within the chunk) that some row of the workgroup sees
+    const int last = min(q0 + BR, q_len) - 1 - k_off;
+    n_kt = last < 0 ? 0 : min(n_kt, last / BC + 1);
+  }
   int wave_kt = n_kt;
-  if (!wave_live) wave_kt = 0;
-  else if (CAUSAL) wave_kt = min(n_kt, (min(qw0 + 31, q_len - 1)) / BC + 1);
+  if (!wave_live) {
+    wave_kt = 0;
+  } else if (CAUSAL) {
+    const int last = min(qw0 + 31, q_len - 1) - k_off;
+    wave_kt = last < 0 ? 0 : min(n_kt, last / BC + 1);
+  }
 
   uint8_t* const ldsK = lds8;
   uint8_t* const ldsV = lds8 + NS * kTileB;
@@ -400,7 +418,7 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
         if (refill) load_tile(kt + NS - 1, kw, vw);
 
         const int key0 = kt * BC;
-        const bool need_mask = (key0 + BC > k_len) || (CAUSAL && key0 + BC - 1 > qw0);
+        const bool need_mask = (key0 + BC > k_len) || (CAUSAL && k_off + key0 + BC - 1 > qw0);
         float t4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         if (need_mask) {
   #pragma unroll
@@ -408,7 +426,7 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int key = key0 + mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-              const bool ok = key < k_len && (!CAUSAL || key <= my_q);
+              const bool ok = key < k_len && (!CAUSAL || k_off + key <= my_q);
               s[mb][i] = ok ? s[mb][i] * cs : -INFINITY;
               t4[i & 3] = fmaxf(t4[i & 3], s[mb][i]);
             }
@@ -475,7 +493,20 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
   }
 
   const float l_tot = sum_halves(l);
-  if (q_ok) {
+  if (SPLIT && q_ok) {
+    // the chunk's normalised O and its lse, fp32, for the merge kernel
+    const float f = l_tot > 0.f ? sv_max * (1.f / 256.f) / l_tot : 0.f;
+    const int64_t prow = (int64_t)split * p.B * p.H * p.Nq + q_row0 + my_q;
+    float* orow = p.o_part + prow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(float4*)(orow + db * 32 + 8 * g + 4 * hh) =
+            make_float4(oacc[db][4 * g + 0] * f, oacc[db][4 * g + 1] * f, oacc[db][4 * g + 2] * f,
+                        oacc[db][4 * g + 3] * f);
+    if (hh == 0) p.lse_part[prow] = l_tot > 0.f ? (M + __log2f(l_tot)) * kLn2 : -INFINITY;
+  } else if (q_ok) {
     const float f = l_tot > 0.f ? sv_max * (1.f / 256.f) / l_tot : 0.f;
     uint16_t* orow = (uint16_t*)p.o + (q_row0 + my_q) * D;
 #pragma unroll
@@ -494,36 +525,36 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
 // tiles of equal total work, one after the other: tile t of head h and tile
 // T-1-t of head h + heads/2 (an even head count), else tiles t and T-1-t of
 // one head; p.n_work counts pairs then.
-template <int D, int BC, bool CAUSAL, int NW, int NS, bool VARLEN>
+template <int D, int BC, bool CAUSAL, int NW, int NS, bool VARLEN, bool SPLIT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(2, 2)))
 attn_fwd_fp8_kernel(FwdParams p) {
   const int w = xcd_remap(blockIdx.x, p.n_work);
-  if constexpr (CAUSAL && !VARLEN) {
+  if constexpr (CAUSAL && !VARLEN && !SPLIT) {
     const int T = p.tiles_per_head, heads = p.B * p.H;
     if (heads % 2 == 0) {
       const int h = w / T, t = w - h * T;
-      fp8_body<D, BC, CAUSAL, NW, NS, VARLEN>(p, h * T + t);
+      fp8_body<D, BC, CAUSAL, NW, NS, VARLEN, SPLIT>(p, h * T + t);
       __syncthreads();
-      fp8_body<D, BC, CAUSAL, NW, NS, VARLEN>(p, (h + heads / 2) * T + (T - 1 - t));
+      fp8_body<D, BC, CAUSAL, NW, NS, VARLEN, SPLIT>(p, (h + heads / 2) * T + (T - 1 - t));
     } else {
       const int half = (T + 1) / 2;
       const int head = w / half, t = w - head * half;
-      fp8_body<D, BC, CAUSAL, NW, NS, VARLEN>(p, head * T + t);
+      fp8_body<D, BC, CAUSAL, NW, NS, VARLEN, SPLIT>(p, head * T + t);
       if (T - 1 - t != t) {
         __syncthreads();
-        fp8_body<D, BC, CAUSAL, NW, NS, VARLEN>(p, head * T + (T - 1 - t));
+        fp8_body<D, BC, CAUSAL, NW, NS, VARLEN, SPLIT>(p, head * T + (T - 1 - t));
       }
     }
   } else {
-    fp8_body<D, BC, CAUSAL, NW, NS, VARLEN>(p, w);
+    fp8_body<D, BC, CAUSAL, NW, NS, VARLEN, SPLIT>(p, w);
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool SPLIT = false>
 hipError_t launch_fp8(const FwdParams& p, hipStream_t st) {
   constexpr int BC = Fp8Tile<D>::BC, NW = Fp8Tile<D>::NW, NS = Fp8Tile<D>::NS;
   constexpr int lds = 2 * NS * BC * D;
-  auto kern = attn_fwd_fp8_kernel<D, BC, CAUSAL, NW, NS, VARLEN>;
+  auto kern = attn_fwd_fp8_kernel<D, BC, CAUSAL, NW, NS, VARLEN, SPLIT>;
   static bool attr_set = false;  // idempotent; a benign race between threads
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -531,7 +562,7 @@ hipError_t launch_fp8(const FwdParams& p, hipStream_t st) {
     attr_set = true;
   }
   FwdParams pp = p;
-  if constexpr (CAUSAL && !VARLEN) {
+  if constexpr (CAUSAL && !VARLEN && !SPLIT) {
     const int64_t heads = p.n_work / p.tiles_per_head;
     pp.n_work = (int)(heads % 2 == 0 ? heads / 2 * p.tiles_per_head : heads * ((p.tiles_per_head + 1) / 2));
   }
@@ -553,17 +584,18 @@ hipError_t launch_fp8(const FwdParams& p, hipStream_t st) {
 int fwd_fp8_block_rows(bool causal) { return 32 * Fp8Tile<128>::NW; }
 
 template <int D>
-hipError_t launch_fp8_d(bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
+hipError_t launch_fp8_d(bool causal, bool varlen, bool split, const FwdParams& p, hipStream_t st) {
   static_assert(32 * Fp8Tile<D>::NW == 32 * Fp8Tile<128>::NW, "one query-tile height for every d");
+  if (split) return causal ? launch_fp8<D, true, false, true>(p, st) : launch_fp8<D, false, false, true>(p, st);
   if (varlen) return causal ? launch_fp8<D, true, true>(p, st) : launch_fp8<D, false, true>(p, st);
   return causal ? launch_fp8<D, true, false>(p, st) : launch_fp8<D, false, false>(p, st);
 }
 
-hipError_t launch_fwd_fp8(int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st) {
+hipError_t launch_fwd_fp8(int d, bool causal, bool varlen, bool split, const FwdParams& p, hipStream_t st) {
   switch (d) {
-    case 64: return launch_fp8_d<64>(causal, varlen, p, st);
-    case 128: return launch_fp8_d<128>(causal, varlen, p, st);
-    case 256: return launch_fp8_d<256>(causal, varlen, p, st);
+    case 64: return launch_fp8_d<64>(causal, varlen, split, p, st);
+    case 128: return launch_fp8_d<128>(causal, varlen, split, p, st);
+    case 256: return launch_fp8_d<256>(causal, varlen, split, p, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -137,7 +137,9 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 constexpr int kDecodeMaxRows = 2;
 bool decode_shape(int Nq, int kv);
 hipError_t launch_decode(int dtype, int d, bool causal, int kv, const FwdParams& p, hipStream_t st);
-hipError_t launch_fwd_fp8(int d, bool causal, bool varlen, const FwdParams& p, hipStream_t st);
+// split: key chunks of p.split_len keys (a multiple of 128), per-chunk results
+// to p.o_part / p.lse_part as the 16-bit key-chunk launch
+hipError_t launch_fwd_fp8(int d, bool causal, bool varlen, bool split, const FwdParams& p, hipStream_t st);
 hipError_t launch_fp8_prep(const PrepParams& p, bool per_tensor, hipStream_t st);
 
 }  // namespace attn

@@ -172,7 +172,8 @@ int attn_fp8_quantize_varlen(const void* x, int x_dtype, void* x_fp8, float* x_s
  * (same top-left convention as attn_fwd); a chunk that a query cannot see
  * contributes nothing.  The result equals attn_fwd's up to rounding.
  *
- *   dtype ATTN_DT_F16 or ATTN_DT_BF16 (fp8: ATTN_ERR_UNSUPPORTED);
+ *   dtype ATTN_DT_F16 or ATTN_DT_BF16 (fp8: ATTN_ERR_UNSUPPORTED; see
+ *     attn_fwd_splitkv_fp8);
  *   1 <= num_splits <= 1024 (more chunks than keys is allowed: the extra
  *     chunks are empty);
  *   o_part: fp32 workspace [num_splits, B, H, Nq, d], lse_part: fp32
@@ -207,6 +208,31 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
 int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
                              int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
                              int num_splits, void* hip_stream);
+
+/*
+ * attn_fwd_splitkv_fp8 — attn_fwd_splitkv on the fp8 operands of attn_fwd
+ * (ATTN_DT_FP8_E4M3: e4m3 codes q8, k8, v8 with their per-128-row-tile fp32
+ * scales [B, H, ceil(N/128)], as attn_fp8_quantize writes them; dense
+ * layout): FlashDecoding ("FlashAttention-3" wiki page, related work) on the
+ * block-quantised fp8 attention ("Three techniques" §3 of that page).  The
+ * keys of every (b, h) are cut into num_splits chunks of ceil(Nk /
+ * num_splits) keys rounded up to whole 128-row scale tiles (the last chunks
+ * may be short or empty); each chunk is the fp8 attention of its keys alone
+ * (its own largest V scale for the P weights, a running max that starts at
+ * the chunk), causal masks with absolute key indices (top-left); the
+ * chunks' normalised O and lse go to the fp32 workspace and attn_merge
+ * combines them into o (bfloat16) and lse.
+ *   q8 [B, H, Nq, d], k8, v8 [B, H, Nk, d] uint8 codes; q_scale [B, H,
+ *   ceil(Nq/128)], k_scale, v_scale [B, H, ceil(Nk/128)] fp32 >= 0;
+ *   o bfloat16 [B, H, Nq, d]; lse fp32 [B, H, Nq]; o_part fp32
+ *   [num_splits, B, H, Nq, d], lse_part fp32 [num_splits, B, H, Nq]
+ *   (caller-owned workspace, as attn_fwd_splitkv).  d ∈ {64, 128, 256};
+ *   1 <= num_splits <= 1024.  Pointer, alignment, NULL (only for empty
+ *   tensors), stream and error rules as attn_fwd_stream with fp8 operands.
+ */
+int attn_fwd_splitkv_fp8(const void* q8, const float* q_scale, const void* k8, const float* k_scale, const void* v8,
+                         const float* v_scale, void* o, float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                         int causal, int num_splits, float* o_part, float* lse_part, void* hip_stream);
 
 /*
  * attn_merge — combine results over disjoint key chunks (the online-softmax

@@ -193,6 +193,34 @@ def test_splitkv_unsupported_and_empty(lib):
     assert split_call(Nq=0, q=None, o=None, lse=None, o_part=None, lse_part=None) == attn.ATTN_OK
 
 
+def split8_call(**over):
+    a = dict(q8=FAKE, q_scale=FAKE, k8=FAKE, k_scale=FAKE, v8=FAKE, v_scale=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=256,
+             Nk=4096, d=128, scale=0.125, causal=0, num_splits=8, o_part=FAKE, lse_part=FAKE)
+    a.update(over)
+    return attn.attn_fwd_splitkv_fp8(a["q8"], a["q_scale"], a["k8"], a["k_scale"], a["v8"], a["v_scale"], a["o"],
+                                     a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                                     a["num_splits"], a["o_part"], a["lse_part"], None)
+
+
+SPLIT8_INVALID = [
+    dict(q8=None), dict(o=None), dict(lse=None), dict(k8=None), dict(v8=None), dict(q_scale=None),
+    dict(k_scale=None), dict(v_scale=None), dict(B=0), dict(Nq=-1), dict(Nk=-1), dict(scale=float("nan")),
+    dict(scale=-1.0), dict(causal=2), dict(num_splits=0), dict(num_splits=1025), dict(o_part=None),
+    dict(lse_part=None), dict(o_part=FAKE + 4), dict(lse_part=FAKE + 2), dict(q8=FAKE + 8), dict(k_scale=FAKE + 2),
+]
+
+
+@pytest.mark.parametrize("over", SPLIT8_INVALID, ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_splitkv_fp8_invalid(lib, over):
+    assert split8_call(**over) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_splitkv_fp8_unsupported_and_empty(lib):
+    assert split8_call(d=96) == attn.ATTN_ERR_UNSUPPORTED
+    assert split8_call(Nq=0) == attn.ATTN_OK
+    assert split8_call(Nq=0, q8=None, q_scale=None, o=None, lse=None, o_part=None, lse_part=None) == attn.ATTN_OK
+
+
 def noalloc_call(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=1, Nk=4096, d=128, scale=0.125, causal=0,
              dtype=attn.ATTN_DT_BF16, num_splits=8)

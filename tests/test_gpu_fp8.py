@@ -679,3 +679,63 @@ def test_fp8_other_head_dims_end_to_end(gpu_lib, d, causal):
     print(f"fp8 d{d} causal{causal}: device RMSE {err:.3e}, emulation {e:.3e}")
     assert err <= 3e-2
     assert err <= 1.1 * e + 1e-4
+
+
+# ---------------------------------------------------------------- key chunks (attn_fwd_splitkv_fp8)
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,nq,nk,S", [(128, 300, 1000, 3), (128, 1, 2000, 8), (64, 129, 700, 4),
+                                       (256, 200, 900, 5), (128, 100, 100, 4), (128, 513, 1500, 16)])
+def test_fp8_splitkv_vs_emulation(gpu_lib, causal, d, nq, nk, S):
+    """Every chunk's workspace rows against the oracle's emulation of that
+    chunk (``attention_fp8_splitkv``: whole 128-key scale tiles, the chunk's
+    own largest V scale, absolute causal indices; same allowances as the
+    dense test), empty and invisible chunks as O = 0, lse = -inf; then the
+    merged bf16 output against the merged emulation, allowing each chunk's
+    allowance at its merge weight."""
+    q8, k8, v8, sq, sk, sv = _exact_problem(2, 2, nq, nk, seed=nq + 5 * nk + d + S, d=d)
+    op = torch.full((S, 2, 2, nq, d), float("nan"), device="cuda")
+    lp = torch.full((S, 2, 2, nq), float("nan"), device="cuda")
+    o, lse = gpu_lib.forward_splitkv_fp8(_dev(q8), _dev(sq), _dev(k8), _dev(sk), _dev(v8), _dev(sv), causal=causal,
+                                         scale=0.0884, num_splits=S, o_part=op, lse_part=lp)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    ref_o, ref_l, chunks = F.attention_fp8_splitkv(q8, k8, v8, sq, sk, sv, 0.0884, causal, num_splits=S,
+                                                   ambiguity=3e-5, parts=True, block=BLOCK[d])
+    op, lp = op.double().cpu().numpy(), lp.double().cpu().numpy()
+    allow_m = np.zeros(ref_o.shape)
+    for s, (kb, ke, r) in enumerate(chunks):
+        what = f"fp8 split d{d} causal{causal} {nq}x{nk} S{S} chunk {s} [{kb}, {ke})"
+        if r is None:
+            assert np.all(np.isneginf(lp[s])) and np.all(op[s] == 0.0), what
+            continue
+        allow = r["flip"] + _pv_bound(r)
+        _check(op[s], lp[s], r["o"], r["lse"], what, allow=allow)
+        with np.errstate(invalid="ignore"):
+            wgt = np.where(np.isfinite(r["lse"]), np.exp(r["lse"] - np.where(np.isfinite(ref_l), ref_l, 0.0)), 0.0)
+        allow_m += wgt[..., None] * allow
+    _check(o.double().cpu().numpy(), lse.double().cpu().numpy(), ref_o, ref_l,
+           f"fp8 split d{d} causal{causal} {nq}x{nk} S{S} merged", allow=allow_m)
+
+
+def test_fp8_splitkv_end_to_end(gpu_lib):
+    """Quantiser codes of N(0,1) inputs (rotation on Q and K), 8192 keys in 8
+    chunks: RMSE against the fp64 attention of the originals within 10 % of
+    the one-pass fp8 kernel's on the same codes, and the two outputs close."""
+    B, H, nq, nk, d = 1, 4, 256, 8192, 128
+    rng = np.random.default_rng(77)
+    q, k, v = (rng.standard_normal((B, H, n, d), dtype=np.float32) for n in (nq, nk, nk))
+    signs = _dev(rng.choice([-1.0, 1.0], d).astype(np.float32))
+    scale = 1.0 / np.sqrt(d)
+    q8, sq = gpu_lib.fp8_quantize(_dev(q), signs)
+    k8, sk = gpu_lib.fp8_quantize(_dev(k), signs)
+    v8, sv = gpu_lib.fp8_quantize(_dev(v), None)
+    o1, l1 = gpu_lib.forward(q8, k8, v8, scale=scale, q_scale=sq, k_scale=sk, v_scale=sv)
+    o2, l2 = gpu_lib.forward_splitkv_fp8(q8, sq, k8, sk, v8, sv, scale=scale, num_splits=8)
+    torch.cuda.synchronize()
+    truth, tl = oracle.attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), scale, False)
+    e1 = F.rmse(o1.double().cpu().numpy(), truth)
+    e2 = F.rmse(o2.double().cpu().numpy(), truth)
+    print(f"fp8 split end to end: RMSE one pass {e1:.3e}, 8 chunks {e2:.3e}")
+    assert e2 <= 1.1 * e1 + 1e-4
+    assert np.abs(l2.double().cpu().numpy() - tl).max() <= 2e-2
