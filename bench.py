@@ -171,9 +171,13 @@ def bench_one(attn, name, steps, warmup):
             "causal": w.causal, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
 
 
+DETAIL_WARMUP = 100  # untimed launches per detail shape, at least (new inputs: ~100 to settle)
+
+
 def bench_detail(attn, steps, warmup):
     """Per-shape throughput of the other workloads (mean and median over
-    `steps` launches)."""
+    `steps` launches, after at least DETAIL_WARMUP untimed ones)."""
+    warmup = max(warmup, DETAIL_WARMUP)
     out = {}
     for name in ("dense_bf16", "dense_bf16_causal", "hdim256_bf16", "varlen_bf16_causal", "tiny_f16"):
         out[name] = bench_one(attn, name, steps, warmup)
@@ -352,7 +356,7 @@ def copy_bandwidth(steps: int = 10) -> float:
     return round(2 * n / (ms / 1e3) / 1e9, 1)
 
 
-def bench_fp8(attn, steps, warmup, varlen=True):
+def bench_fp8(attn, steps, warmup, varlen=True, extras=True):
     """fp8 workload (B=2 H=16 N=8192 d=128, outlier channels): the attention
     kernel alone and the pre-processing of Q, K, V; None if not built."""
     import numpy as np
@@ -402,9 +406,9 @@ def bench_fp8(attn, steps, warmup, varlen=True):
             # fp32 Q, K, V in HBM -> rotation and block quantisation -> e4m3 attention
             "fp8_end_to_end": {"ms": round(ms + ms_prep, 4),
                                "tflops": round(w.flops() / ((ms + ms_prep) / 1e3) / 1e12, 2)},
-            **bench_fp8_hdim256(attn, steps, warmup),
-            **bench_fp8_splitkv(attn, steps, warmup),
-            **(bench_fp8_varlen(attn, steps, warmup) if varlen else {})}
+            **(bench_fp8_hdim256(attn, steps, warmup) if extras else {}),
+            **(bench_fp8_splitkv(attn, steps, warmup) if extras else {}),
+            **(bench_fp8_varlen(attn, steps, warmup) if varlen and extras else {})}
 
 
 def bench_fp8_hdim256(attn, steps, warmup):
@@ -529,7 +533,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)  # the GPU needs ~100 launches to settle
+    # a launch on newly allocated inputs runs up to ~15 % slower for its first
+    # ~100 repetitions; the default warm-up covers that
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
@@ -555,7 +561,7 @@ def main():
     attn.load()
     if args.only:
         if args.only == "fp8_outlier":
-            res = bench_fp8(attn, args.steps, args.warmup, varlen=False)["fp8_outlier"]
+            res = bench_fp8(attn, args.steps, args.warmup, extras=False)["fp8_outlier"]
         else:
             res = bench_one(attn, args.only, args.steps, args.warmup)
         print(json.dumps({"only": args.only, **res}), flush=True)
