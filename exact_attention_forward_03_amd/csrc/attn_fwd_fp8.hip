@@ -92,6 +92,13 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
+// The same with the register of `old` (a value that dies here) as the home of
+// the result.
+__device__ __forceinline__ uint32_t pack4_e4m3_into(float a, float b, float c, float d, float old) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, old), false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
 
 // D head dimension, BC key rows per tile, NW waves per workgroup (32 query
 // rows each), NS LDS ring slots.  VARLEN: a packed batch [H, T, d] with
@@ -481,10 +488,17 @@ __device__ __forceinline__ void fp8_body(const FwdParams& p, const int work) {
         for (int g = 0; g < PG; ++g) {
           const f32x16_t& a = s[2 * g];
           const f32x16_t& bb = s[2 * g + 1];
-          pp[g][0] = make_uint4(pack4_e4m3(a[0], a[1], a[2], a[3]), pack4_e4m3(a[4], a[5], a[6], a[7]),
-                                pack4_e4m3(a[8], a[9], a[10], a[11]), pack4_e4m3(a[12], a[13], a[14], a[15]));
-          pp[g][1] = make_uint4(pack4_e4m3(bb[0], bb[1], bb[2], bb[3]), pack4_e4m3(bb[4], bb[5], bb[6], bb[7]),
-                                pack4_e4m3(bb[8], bb[9], bb[10], bb[11]), pack4_e4m3(bb[12], bb[13], bb[14], bb[15]));
+          // word k of the operand goes to the register of a[k], the first
+          // eight of the block's 16 consecutive registers, each dead by then:
+          // the MFMA operand is then built in place, with no copies
+          pp[g][0] = make_uint4(pack4_e4m3_into(a[0], a[1], a[2], a[3], a[0]),
+                                pack4_e4m3_into(a[4], a[5], a[6], a[7], a[1]),
+                                pack4_e4m3_into(a[8], a[9], a[10], a[11], a[2]),
+                                pack4_e4m3_into(a[12], a[13], a[14], a[15], a[3]));
+          pp[g][1] = make_uint4(pack4_e4m3_into(bb[0], bb[1], bb[2], bb[3], a[4]),
+                                pack4_e4m3_into(bb[4], bb[5], bb[6], bb[7], a[5]),
+                                pack4_e4m3_into(bb[8], bb[9], bb[10], bb[11], a[6]),
+                                pack4_e4m3_into(bb[12], bb[13], bb[14], bb[15], a[7]));
         }
         pv_pass(vr, pp);
       }
