@@ -490,11 +490,14 @@ def test_drifting_row_max_varlen_causal(gpu_lib, shape, d):
 
 
 @pytest.mark.parametrize("shape", DRIFT_SHAPES)
-@pytest.mark.parametrize("d,causal", [(128, False), (128, True), (256, False)])
-def test_drifting_row_max_splitkv(gpu_lib, shape, d, causal):
+@pytest.mark.parametrize("d,causal,nq", [(128, False, 300), (128, True, 300), (256, False, 300), (128, False, 1),
+                                         (256, False, 2), (64, True, 2)])
+def test_drifting_row_max_splitkv(gpu_lib, shape, d, causal, nq):
     """Drifting maxima through the key-chunk launches (3 chunks of 334 keys:
-    the ramp's maximum moves inside every chunk) and the merge."""
-    q, k, v = _drift_problem(300, 1000, d, shape, seed=21 + d)
+    the ramp's maximum moves inside every chunk) and the merge; one or two
+    query rows run the decoding-shaped kernel, whose lanes keep their own
+    lazy reference max."""
+    q, k, v = _drift_problem(nq, 1000, d, shape, seed=21 + d)
     qd, q64 = to_device(q, "bf16")
     kd, k64 = to_device(k, "bf16")
     vd, v64 = to_device(v, "bf16")
@@ -503,11 +506,12 @@ def test_drifting_row_max_splitkv(gpu_lib, shape, d, causal):
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.attention(q64, k64, v64, s, causal)
     check(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref, "bf16",
-          f"drifting max split-KV {shape} d{d} causal{causal}")
+          f"drifting max split-KV {shape} d{d} causal{causal} nq{nq}")
 
 
 @pytest.mark.parametrize("shape", DRIFT_SHAPES)
-def test_drifting_row_max_paged_e4m3(gpu_lib, shape):
+@pytest.mark.parametrize("nq", [7, 1])
+def test_drifting_row_max_paged_e4m3(gpu_lib, shape, nq):
     """Drifting maxima read from a paged e4m3 cache with per-(token, head)
     scales (64-token pages in shuffled order, d = 128, 7 queries).  Key j's
     channel 0 holds the code +-448 and its scale is |ramp_j| / 448, so the
@@ -519,7 +523,7 @@ def test_drifting_row_max_paged_e4m3(gpu_lib, shape):
     from oracle import fp8 as F
     from oracle import paged as PG
 
-    d, nk, H, nq, P = 128, 1000, 2, 7, 64
+    d, nk, H, P = 128, 1000, 2, 64  # one query row: the decoding-shaped kernel
     q, k, _ = _drift_problem(nq, nk, d, shape, seed=31, heads=H)
     rng = np.random.default_rng(33)
     ramp = k[0, :, :, 0].astype(np.float64)  # [H, nk]
@@ -553,7 +557,7 @@ def test_drifting_row_max_paged_e4m3(gpu_lib, shape):
     kd = PG.dequantize(kc, ks, "e4m3")[perm[0], :5, 0, 0]
     assert np.allclose(kd, ramp[0, :5], rtol=1e-6, atol=1e-3)  # channel 0 carries the ramp
     check(o.double().cpu().numpy(), lse.double().cpu().numpy(), ref_o, ref_l, "bf16",
-          f"drifting max paged e4m3 {shape}")
+          f"drifting max paged e4m3 {shape} nq{nq}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
