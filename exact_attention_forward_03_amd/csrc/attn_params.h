@@ -18,7 +18,8 @@ struct FwdParams {
   const int32_t* cu_q;   // varlen only
   const int32_t* cu_k;   // varlen only
   int tiles_per_head;    // query tiles per (b, h) (varlen: upper bound per head)
-  int n_work;            // workgroups launched
+  int n_work;            // work items (workgroups launched, unless persistent)
+  int queue;             // persistent launches: the work-queue slot of this launch
   int pair_tiles;        // dense: each workgroup runs query tiles t and T-1-t (set by the launch)
   const float* q_scale;  // fp8 only: [B, H, ceil(Nq/128)]; varlen [H, ceil(Nq/128) + B]
   const float* k_scale;  // fp8: [B, H, ceil(Nk/128)] (varlen [H, ceil(Nk/128) + B]); 8-bit paged cache: [num_pages, page_size, H]

@@ -150,7 +150,7 @@ def test_varlen(gpu_lib, dtype, causal, d):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d,nseq", [(64, 150), (128, 150), (128, 36)])
+@pytest.mark.parametrize("d,nseq", [(64, 150), (128, 150), (128, 36), (256, 40)])
 def test_varlen_many_sequences_every_row_written(gpu_lib, causal, d, nseq):
     """More sequences than the kernels' scalar lookup takes (16) and than one
     wave's 64 lanes (the lookup then picks a block of 64 first): empty,
@@ -173,6 +173,64 @@ def test_varlen_many_sequences_every_row_written(gpu_lib, causal, d, nseq):
     o_ref, l_ref = oracle.attention_varlen(q64, k64, v64, cq, ck, s, causal)
     check(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, l_ref, "bf16",
           f"varlen {len(lq)} sequences d{d} causal{causal}")
+
+
+def test_varlen_persistent_grid_streams_and_graph(gpu_lib):
+    """Past 16 sequences a packed batch runs on a persistent grid whose work
+    queues are kept per stream and cleared by each launch's last workgroup:
+    repeated launches, launches on two streams at once and the replays of a
+    captured graph (whose launch takes the dispatcher) all give bitwise the
+    O and lse of the first launch, which matches the oracle."""
+    lq = [int(x) for x in np.random.default_rng(11).integers(0, 300, 40)] + [0, 1]
+    cq = W.cu_seqlens(lq)
+    H, d, s = 4, 64, 0.125
+    rng = np.random.default_rng(12)
+    (qd, q64), (kd, k64), (vd, v64) = (to_device(rng.standard_normal((H, int(cq[-1]), d), dtype=np.float32), "bf16")
+                                       for _ in range(3))
+    cu = torch.from_numpy(cq).cuda()
+
+    def run(o, lse):
+        gpu_lib.forward(qd, kd, vd, causal=True, scale=s, cu_seqlens_q=cu, cu_seqlens_k=cu, out=o, lse=lse)
+
+    def fresh():
+        return (torch.full(qd.shape, float("nan"), dtype=torch.bfloat16, device="cuda"),
+                torch.full(qd.shape[:2], float("nan"), dtype=torch.float32, device="cuda"))
+
+    o0, l0 = fresh()
+    run(o0, l0)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_varlen(q64, k64, v64, cq, cq, s, True)
+    check(o0.double().cpu().numpy(), l0.double().cpu().numpy(), o_ref, l_ref, "bf16", "persistent grid")
+    for _ in range(3):
+        o, lse = fresh()
+        run(o, lse)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o0) and torch.equal(lse, l0)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):
+        outs = [fresh() for _ in streams]
+        torch.cuda.synchronize()
+        for st, (o, lse) in zip(streams, outs):
+            with torch.cuda.stream(st):
+                run(o, lse)
+        torch.cuda.synchronize()
+        for o, lse in outs:
+            assert torch.equal(o, o0) and torch.equal(lse, l0)
+    og, lg = fresh()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        run(og, lg)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(og, lg)
+    for _ in range(3):
+        og.fill_(float("nan"))
+        lg.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(og, o0) and torch.equal(lg, l0)
 
 
 @pytest.mark.parametrize("causal", [False, True])
