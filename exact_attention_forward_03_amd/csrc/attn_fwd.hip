@@ -82,30 +82,20 @@ constexpr int kOptPin = 1, kOptPrio = 2;
 // at d = 128 (4-wave workgroups); -10 % for dense d = 128 launches, whose
 // loads need the whole step to land; no change for key-chunk launches.
 constexpr int kOptLateLoad = 16;
-// kOptPersist (variable-length launches): a persistent grid, CUs x the
-// workgroups one CU holds, each taking work items from the queue of its XCD
-// (the XCD's contiguous range of items, the same ranges xcd_remap gives the
-// dispatcher) until it is empty.  One lane claims the next item with a
-// global atomic before running the current one, so the claim's latency
-// overlaps the item.  An item that owns no tile costs a loop turn instead of
-// a workgroup dispatch.  Used for batches of more than sched::kScanSeqs
-// sequences (whose slot numbering leaves up to B + 1 empty items per head),
-// where it measured -17 % (d = 64, causal), -15 % (d = 256, causal) and
-// -6 % (d = 128, non-causal) at 150 sequences of 1..500 rows, 32 heads; not
-// for d = 128 causal launches (+0..5 %) nor for a few long sequences, where
-// every variant tried (padded or packed counters, claims before or after the
-// item, four sub-queues per XCD, a static stride) was 1..10 % slower than the
-// dispatcher.
+// kOptPersist (variable-length launches): a persistent grid
+// (sched::persistent_items).  Used for batches of more than
+// sched::kScanSeqs sequences (whose slot numbering leaves up to B + 1
+// empty items per head), where it measured -17 % (d = 64, causal), -15 %
+// (d = 256, causal) and -6 % (d = 128, non-causal) at 150 sequences of
+// 1..500 rows, 32 heads; not for d = 128 causal launches (+0..5 %) nor for a
+// few long sequences, where every variant tried (padded or packed counters,
+// claims before or after the item, four sub-queues per XCD, a static
+// stride) was 1..10 % slower than the dispatcher.  It gains where one
+// workgroup fills a CU; where two 4-wave workgroups share one (d = 128
+// causal here, the e4m3 kernel) it measured 2..15 % slower.
 constexpr int kOptPersist = 64;
 
-// Work queues of persistent launches: per slot, one counter per XCD and a
-// count of finished workgroups, each on its own 256-byte line (packed
-// counters measured 2 % slower).  Zero when the code object loads; the last
-// workgroup of a persistent launch clears its slot again.  Each stream has
-// a slot of its own (queue_slot), as launches on one stream never overlap.
-constexpr int kQueueSlots = 256;
-constexpr int kQueueStride = 64;  // unsigned ints between counters
-__device__ unsigned int g_queues[kQueueSlots][9 * kQueueStride];
+__device__ unsigned int g_queues[sched::kQueueSlots][sched::kQueueWords];
 
 // SPLIT: the keys of each head are cut into p.n_split chunks of p.split_len
 // rows; a work item is (head, chunk, query tile) and writes the chunk's
@@ -605,35 +595,9 @@ template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAU
 __global__ void __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(WPE, WPE)))
 attn_fwd_dma_kernel(FwdParams p) {
   if constexpr (VARLEN && (OPT & kOptPersist)) {
-    __shared__ int next_item[2];
-    unsigned int* q = g_queues[p.queue];
-    const int x = blockIdx.x & 7;  // the XCD (workgroups are dealt round-robin)
-    const int per = p.n_work >> 3, rem = p.n_work & 7;
-    const int lo = x * per + min(x, rem), cnt = per + (x < rem ? 1 : 0);
-    unsigned int* head = q + x * kQueueStride;
-    if (threadIdx.x == 0) {
-      const unsigned t = atomicAdd(head, 1u);
-      next_item[0] = t < (unsigned)cnt ? lo + (int)t : -1;
-    }
-    int buf = 0;
-    for (;;) {
-      __syncthreads();
-      const int item = next_item[buf];
-      if (item < 0) break;
-      unsigned t_next = 0;
-      if (threadIdx.x == 0) t_next = atomicAdd(head, 1u);  // the next claim, read after the item
+    sched::persistent_items(g_queues[p.queue], p.n_work, [&](int item) __attribute__((always_inline)) {
       attn_fwd_body<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, KV>(p, item);
-      if (threadIdx.x == 0) next_item[buf ^ 1] = t_next < (unsigned)cnt ? lo + (int)t_next : -1;
-      buf ^= 1;
-    }
-    if (threadIdx.x == 0) {
-      // every claim of this workgroup has returned; the last one out clears the slot
-      __threadfence();
-      if (atomicAdd(q + 8 * kQueueStride, 1u) == gridDim.x - 1) {
-        __threadfence();
-        for (int y = 0; y < 9; ++y) atomicExch(q + y * kQueueStride, 0u);
-      }
-    }
+    });
   } else {
     const int w = xcd_remap(blockIdx.x, p.n_work);
     constexpr bool kPairs = !VARLEN && !SPLIT && KV == kKvDense;
@@ -641,37 +605,6 @@ attn_fwd_dma_kernel(FwdParams p) {
       attn_fwd_body<TT, D, BC, NW, WPE, NS, OPT, CAUSAL, VARLEN, SPLIT, KV>(p, item);
     });
   }
-}
-
-// The work-queue slot of the launches on stream st.  Launches on one stream
-// run one after the other, so one slot per stream keeps any two launches
-// that may run together apart (a stream destroyed while its launch still
-// runs and a new stream given the same handle are the exception).  False,
-// and the launch uses the dispatcher: the stream is being captured (the
-// replays of a graph would share the slot recorded at capture), it is the
-// per-thread default stream (one handle for the streams of many threads),
-// or kQueueSlots streams already hold a slot.
-bool queue_slot(hipStream_t st, int* slot) {
-  if (st == hipStreamPerThread) return false;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
-    (void)hipGetLastError();  // the launch reports its own errors
-    return false;
-  }
-  if (cs != hipStreamCaptureStatusNone) return false;
-  static std::mutex mu;
-  static hipStream_t owner[kQueueSlots];
-  static int used = 0;
-  std::lock_guard<std::mutex> lock(mu);
-  for (int i = 0; i < used; ++i)
-    if (owner[i] == st) {
-      *slot = i;
-      return true;
-    }
-  if (used == kQueueSlots) return false;
-  owner[used] = st;
-  *slot = used++;
-  return true;
 }
 
 template <typename TT, int D, int BC, int NW, int WPE, int NS, int OPT, bool CAUSAL, bool VARLEN, bool SPLIT,
@@ -697,18 +630,9 @@ hipError_t launch_dma_one(const FwdParams& p, hipStream_t st) {
   if (pp.n_work == 0) return hipSuccess;
   unsigned grid = (unsigned)pp.n_work;
   if constexpr (VARLEN && (OPT & kOptPersist)) {
-    static std::atomic<int> per_cu_known{0};  // workgroups one CU holds, asked of the runtime once
-    int per_cu = per_cu_known.load(std::memory_order_relaxed);
-    if (per_cu == 0) {
-      const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, NW * 64, lds_bytes);
-      if (e != hipSuccess) return e;
-      per_cu = per_cu < 1 ? 1 : per_cu;
-      per_cu_known.store(per_cu, std::memory_order_relaxed);
-    }
-    int cus = 0;
-    const hipError_t e = device_cu_count(&cus);
+    static std::atomic<int> per_cu{0};
+    const hipError_t e = sched::persistent_grid((const void*)kern, NW * 64, lds_bytes, pp.n_work, per_cu, &grid);
     if (e != hipSuccess) return e;
-    grid = (unsigned)std::min<int64_t>((int64_t)cus * per_cu, pp.n_work);
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds_bytes, st, pp);
   return hipGetLastError();
@@ -751,7 +675,7 @@ hipError_t launch_dma_d(const FwdParams& p, hipStream_t st) {
     return launch_dma_one<TT, D, V::BC, V::NW, V::WPE, V::NS, V::OPT, CAUSAL, VARLEN, SPLIT, KV>(p, st);
   } else if constexpr (VARLEN && !SPLIT) {
     int slot = 0;
-    if (p.B > sched::kScanSeqs && queue_slot(st, &slot)) {
+    if (p.B > sched::kScanSeqs && sched::queue_slot(st, &slot)) {
       FwdParams pp = p;
       pp.queue = slot;
       return launch_dma_one<TT, D, T::BC, T::NW, T::WPE, T::NS, T::OPT | kOptPersist, CAUSAL, VARLEN, SPLIT, KV>(pp,
@@ -795,6 +719,33 @@ hipError_t launch_dma_t(int d, bool causal, bool varlen, bool split, int kv, con
 }
 
 }  // namespace
+
+// One slot per stream: launches on one stream run one after the other, so
+// any two launches that may run together have different slots (a stream
+// destroyed while its launch still runs and a new stream given the same
+// handle are the exception).
+bool sched::queue_slot(hipStream_t st, int* slot) {
+  if (st == hipStreamPerThread) return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();  // the launch reports its own errors
+    return false;
+  }
+  if (cs != hipStreamCaptureStatusNone) return false;
+  static std::mutex mu;
+  static hipStream_t owner[kQueueSlots];
+  static int used = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (owner[i] == st) {
+      *slot = i;
+      return true;
+    }
+  if (used == kQueueSlots) return false;
+  owner[used] = st;
+  *slot = used++;
+  return true;
+}
 
 // Compute units of the current device, asked of the runtime once per device
 // (the launch decides on it for every dense non-causal call).
