@@ -191,32 +191,44 @@ __global__ void __launch_bounds__(kDecWaves * 64) attn_decode_kernel(FwdParams p
       s.vs = 1.f;
     }
   };
-  auto process = [&](int j, const Step& s) {
-    const int key = kb + j * KPL + grp;
-    const bool valid = j < n_steps && key < ke;
-    float kf[8];
-    widen<TT, KV>(s.k, kf);
-    float sc[NQ];
+  // the DEPTH steps of one batch: first every score (independent chains),
+  // then one lazy reference-max check for the batch, then P and O
+  auto process = [&](int j0, const Step (&S)[kDecDepth]) {
+    float sc[kDecDepth][NQ];
 #pragma unroll
-    for (int r = 0; r < NQ; ++r) {
-      float acc = 0.f;
+    for (int u = 0; u < kDecDepth; ++u) {
+      const int j = j0 + u * kDecWaves;
+      const int key = kb + j * KPL + grp;
+      const bool valid = j < n_steps && key < ke;
+      float kf[8];
+      widen<TT, KV>(S[u].k, kf);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(q[r][i], kf[i], acc);
-      acc = group_sum<LPK>(acc);
-      if constexpr (Q8) acc *= s.ks;
-      const bool vis = valid && (!CAUSAL || key <= r);
-      sc[r] = vis ? acc : -INFINITY;
+      for (int r = 0; r < NQ; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(q[r][i], kf[i], acc);
+        acc = group_sum<LPK>(acc);
+        if constexpr (Q8) acc *= S[u].ks;
+        const bool vis = valid && (!CAUSAL || key <= r);
+        sc[u][r] = vis ? acc : -INFINITY;
+      }
     }
     // lazy reference max: a lane moves its reference only when a score
     // passes it by more than kDecLazyBits (p <= 2^kDecLazyBits otherwise)
+    float mb[NQ];
     bool up = false;
 #pragma unroll
-    for (int r = 0; r < NQ; ++r) up |= sc[r] > M[r] + kDecLazyBits;
+    for (int r = 0; r < NQ; ++r) {
+      mb[r] = sc[0][r];
+#pragma unroll
+      for (int u = 1; u < kDecDepth; ++u) mb[r] = fmaxf(mb[r], sc[u][r]);
+      up |= mb[r] > M[r] + kDecLazyBits;
+    }
     if (__any(up)) {
 #pragma unroll
       for (int r = 0; r < NQ; ++r) {
-        if (sc[r] > M[r] + kDecLazyBits) {
-          const float mn = __builtin_ceilf(sc[r]);
+        if (mb[r] > M[r] + kDecLazyBits) {
+          const float mn = __builtin_ceilf(mb[r]);
           const float alpha = M[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[r] - mn);
           l[r] *= alpha;
 #pragma unroll
@@ -225,15 +237,18 @@ __global__ void __launch_bounds__(kDecWaves * 64) attn_decode_kernel(FwdParams p
         }
       }
     }
-    float vf[8];
-    widen<TT, KV>(s.v, vf);
 #pragma unroll
-    for (int r = 0; r < NQ; ++r) {
-      const float pr = __builtin_amdgcn_exp2f(sc[r] - (M[r] == -INFINITY ? 0.f : M[r]));
-      l[r] += pr;
-      const float pv = Q8 ? pr * s.vs : pr;
+    for (int u = 0; u < kDecDepth; ++u) {
+      float vf[8];
+      widen<TT, KV>(S[u].v, vf);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[r][i] = __builtin_fmaf(pv, vf[i], o[r][i]);
+      for (int r = 0; r < NQ; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(sc[u][r] - (M[r] == -INFINITY ? 0.f : M[r]));
+        l[r] += pr;
+        const float pv = Q8 ? pr * S[u].vs : pr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[r][i] = __builtin_fmaf(pv, vf[i], o[r][i]);
+      }
     }
   };
 
@@ -243,22 +258,18 @@ __global__ void __launch_bounds__(kDecWaves * 64) attn_decode_kernel(FwdParams p
 #pragma unroll
     for (int u = 0; u < kDecDepth; ++u) load(wv + u * kDecWaves, A[u]);
     for (int j0 = wv; j0 < n_steps; j0 += 2 * SPAN) {
-      // batch A (steps j0 ..) has been issued; issue batch B, then use A
+      // batch A (steps j0 ..) is in flight; issue batch B, then use A.  The
+      // loads are unconditional (steps past the chunk re-read its last row):
+      // behind a branch, the compiler would wait for every load at the join,
+      // the batch just issued included.
       const int j1 = j0 + SPAN;
-      if (j1 < n_steps) {
 #pragma unroll
-        for (int u = 0; u < kDecDepth; ++u) load(j1 + u * kDecWaves, Bn[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < kDecDepth; ++u) process(j0 + u * kDecWaves, A[u]);
+      for (int u = 0; u < kDecDepth; ++u) load(j1 + u * kDecWaves, Bn[u]);
+      process(j0, A);
       if (j1 >= n_steps) break;
-      const int j2 = j1 + SPAN;
-      if (j2 < n_steps) {
 #pragma unroll
-        for (int u = 0; u < kDecDepth; ++u) load(j2 + u * kDecWaves, A[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < kDecDepth; ++u) process(j1 + u * kDecWaves, Bn[u]);
+      for (int u = 0; u < kDecDepth; ++u) load(j1 + SPAN + u * kDecWaves, A[u]);
+      process(j1, Bn);
     }
   }
 
