@@ -196,7 +196,7 @@ def bench_decode(attn, steps, warmup):
     are the algorithmic traffic); the single-pass kernel on the same shape
     for comparison; the same keys and values read from a paged cache, and a
     paged cache of e4m3 codes with per-(token, head) scales (bytes: codes and
-    scales)."""
+    scales), read by bf16 and by e4m3 queries."""
     import numpy as np
     import torch
 
@@ -273,6 +273,23 @@ def bench_decode(attn, steps, warmup):
     out["decode_e4m3_paged"] = {"ms": round(ms8, 4), "gbs": round(gb8, 1), "frac_hbm": round(gb8 / HBM_PEAK_GBS, 4),
                                 "page_size": P, "num_splits": splits, "vs_bf16_paged": round(ms8 / msp, 4),
                                 "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
+
+    # the same cache with e4m3 queries (one scale per batch and head)
+    q8 = torch.from_numpy(W.random_e4m3_codes(tuple(q.shape), 6)).cuda()
+    qs = torch.from_numpy(W.random_scales((w.B, w.H), 7, 0.5, 2.0)).cuda()
+    o8 = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+
+    def run_paged8q():
+        attn.forward_paged_fp8(q8, qs, k8, v8, table, lens, scale=w.scale, k_scale=ks, v_scale=vs, kv_dtype="e4m3",
+                               num_splits=splits, out=o8, lse=lse, o_part=op, lse_part=lp)
+
+    for _ in range(warmup):
+        run_paged8q()
+    ms8q = float(np.mean(timed_launches(run_paged8q, steps, stream)))
+    gb8q = b8 / (ms8q / 1e3) / 1e9
+    out["decode_e4m3q_e4m3_paged"] = {"ms": round(ms8q, 4), "gbs": round(gb8q, 1),
+                                      "frac_hbm": round(gb8q / HBM_PEAK_GBS, 4), "page_size": P,
+                                      "num_splits": splits, "shape": [w.B, w.H, w.Nq, w.Nk, w.d]}
     return out
 
 

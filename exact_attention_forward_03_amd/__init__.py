@@ -3,9 +3,11 @@
 
 The C entry points are exposed under their own names with plain integer
 pointers (argument marshalling only): ``attn_fwd``, ``attn_fwd_stream``,
-``attn_fwd_splitkv``, ``attn_fwd_splitkv_fp8``, ``attn_fwd_paged``, ``attn_merge``, ``attn_bwd``,
+``attn_fwd_splitkv``, ``attn_fwd_splitkv_fp8``, ``attn_fwd_paged``, ``attn_fwd_paged_fp8``, ``attn_merge``,
+``attn_bwd``,
 ``attn_bwd_fp8``, ``attn_fp8_quantize``, ``attn_fp8_quantize_varlen``,
 ``attn_strerror``.  ``forward``, ``forward_splitkv``, ``forward_splitkv_fp8``, ``forward_paged``,
+``forward_paged_fp8``,
 ``merge``, ``backward``, ``backward_fp8``, ``fp8_quantize`` and
 ``fp8_quantize_varlen`` are the
 torch-facing conveniences: they allocate the
@@ -29,7 +31,8 @@ __all__ = [
     "load", "lib_path", "attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_merge", "attn_fp8_quantize",
     "attn_fwd_paged", "attn_bwd", "attn_bwd_fp8", "attn_strerror", "attn_fp8_quantize_varlen", "forward",
     "forward_splitkv", "forward_paged", "merge", "backward", "backward_fp8", "fp8_quantize", "fp8_quantize_varlen",
-    "default_splits", "EXPORTS", "attn_fwd_splitkv_fp8", "forward_splitkv_fp8",
+    "default_splits", "EXPORTS", "attn_fwd_splitkv_fp8", "forward_splitkv_fp8", "attn_fwd_paged_fp8",
+    "forward_paged_fp8",
 ]
 
 ATTN_DT_F16, ATTN_DT_BF16, ATTN_DT_FP8_E4M3, ATTN_DT_F32, ATTN_DT_INT8 = 0, 1, 2, 3, 4
@@ -37,7 +40,7 @@ ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_TOO_
 ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20  # the fixed device scratch of attn_fwd_splitkv_noalloc (include/attn.h)
 
 EXPORTS = ("attn_fwd", "attn_fwd_stream", "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_fwd_splitkv_fp8",
-           "attn_fwd_paged",
+           "attn_fwd_paged", "attn_fwd_paged_fp8",
            "attn_merge", "attn_bwd", "attn_bwd_fp8", "attn_fp8_quantize", "attn_fp8_quantize_varlen", "attn_strerror")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -76,6 +79,8 @@ def load():
         lib.attn_fwd_paged.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i,
                                         _i, _p, _p, _p]
         lib.attn_fwd_paged.restype = _i
+        lib.attn_fwd_paged_fp8.argtypes = [_p] * 10 + [_i] * 7 + [_f, _i, _i, _p, _p, _p]
+        lib.attn_fwd_paged_fp8.restype = _i
         lib.attn_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _p, _i, _p]
         lib.attn_bwd.restype = _i
         lib.attn_bwd_fp8.argtypes = [_p] * 15 + [_i, _i, _i, _i, _i, _f, _i, _p]
@@ -131,6 +136,14 @@ def attn_fwd_paged(q, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k
     return load().attn_fwd_paged(q, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k, o, lse, B, H, Nq, d,
                                  num_pages, page_size, max_pages, scale, dtype, kv_dtype, num_splits, o_part,
                                  lse_part, hip_stream)
+
+
+def attn_fwd_paged_fp8(q8, q_scale, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k, o, lse, B, H, Nq, d,
+                       num_pages, page_size, max_pages, scale, kv_dtype, num_splits, o_part, lse_part,
+                       hip_stream) -> int:
+    return load().attn_fwd_paged_fp8(q8, q_scale, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k, o, lse,
+                                     B, H, Nq, d, num_pages, page_size, max_pages, scale, kv_dtype, num_splits, o_part,
+                                     lse_part, hip_stream)
 
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, cu_seqlens_q, cu_seqlens_k,
@@ -423,6 +436,59 @@ def forward_paged(q, k_cache, v_cache, block_table, seqlens_k, *, scale: Optiona
     rc = attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
                         _ptr(seqlens_k), _ptr(out), _ptr(lse), B, H, Nq, d, num_pages, page_size, max_pages,
                         float(scale), dt, kvd, int(num_splits), _ptr(o_part), _ptr(lse_part), _stream(q.device))
+    _check(rc)
+    return out, lse
+
+
+def forward_paged_fp8(q8, q_scale, k_cache, v_cache, block_table, seqlens_k, *, k_scale, v_scale, kv_dtype: str,
+                      scale: Optional[float] = None, num_splits: Optional[int] = None, out=None, lse=None,
+                      o_part=None, lse_part=None):
+    """Decoding attention of e4m3 queries q8 (uint8 codes [B, H, Nq, d],
+    Nq <= 2) with q_scale float32 [B, H] over an 8-bit paged cache
+    (``kv_dtype`` "e4m3" or "int8", scales as ``forward_paged``) through
+    ``attn_fwd_paged_fp8`` -> (o bfloat16 [B, H, Nq, d], lse)."""
+    import torch
+
+    for t in (q8, q_scale, k_cache, v_cache, block_table, seqlens_k, k_scale, v_scale):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    if q8.element_size() != 1 or k_cache.element_size() != 1 or v_cache.element_size() != 1:
+        raise TypeError("q8 and the caches must hold 1-byte codes")
+    kvd = {"e4m3": ATTN_DT_FP8_E4M3, "int8": ATTN_DT_INT8}[kv_dtype]
+    if q8.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q8 must be [B, H, Nq, d] and the caches [num_pages, page_size, H, d]")
+    B, H, Nq, d = q8.shape
+    if q_scale.dtype != torch.float32 or tuple(q_scale.shape) != (B, H):
+        raise ValueError("q_scale must be float32 [B, H]")
+    for t in (k_scale, v_scale):
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(k_cache.shape[:3]):
+            raise ValueError("k_scale / v_scale must be float32 [num_pages, page_size, H]")
+    if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
+        raise TypeError("block_table and seqlens_k must be int32")
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    if tuple(k_cache.shape[2:]) != (H, d) or block_table.dim() != 2 or block_table.shape[0] != B or \
+            tuple(seqlens_k.shape) != (B,):
+        raise ValueError("cache / block_table / seqlens_k shapes do not match q8")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        cus = torch.cuda.get_device_properties(q8.device).multi_processor_count
+        num_splits = default_splits(B, H, Nq, max_pages * page_size, target_workgroups=2 * cus)
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    if o_part is None:
+        o_part = torch.empty((num_splits, B, H, Nq, d), dtype=torch.float32, device=q8.device)
+    if lse_part is None:
+        lse_part = torch.empty((num_splits, B, H, Nq), dtype=torch.float32, device=q8.device)
+    if o_part.numel() < num_splits * B * H * Nq * d or lse_part.numel() < num_splits * B * H * Nq:
+        raise ValueError("o_part / lse_part are smaller than num_splits chunks")
+    rc = attn_fwd_paged_fp8(_ptr(q8), _ptr(q_scale), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                            _ptr(block_table), _ptr(seqlens_k), _ptr(out), _ptr(lse), B, H, Nq, d, num_pages,
+                            page_size, max_pages, float(scale), kvd, int(num_splits), _ptr(o_part), _ptr(lse_part),
+                            _stream(q8.device))
     _check(rc)
     return out, lse
 

@@ -206,26 +206,34 @@ int attn_fwd_splitkv_fp8(const void* q8, const float* q_scale, const void* k8, c
   return attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, ATTN_DT_BF16, hip_stream);
 }
 
-int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
-                   const float* v_scale, const int32_t* block_table, const int32_t* seqlens_k, void* o, float* lse,
-                   int B, int H, int Nq, int d, int num_pages, int page_size, int max_pages, float scale, int dtype,
-                   int kv_dtype, int num_splits, float* o_part, float* lse_part, void* hip_stream) {
+namespace {
+
+// attn_fwd_paged (fp8q_entry false: e4m3 queries are UNSUPPORTED there, after
+// the argument checks) and attn_fwd_paged_fp8 (fp8q_entry true).
+int fwd_paged(bool fp8q_entry, const void* q, const float* q_scale, const void* k_cache, const void* v_cache, const float* k_scale,
+              const float* v_scale, const int32_t* block_table, const int32_t* seqlens_k, void* o, float* lse, int B,
+              int H, int Nq, int d, int num_pages, int page_size, int max_pages, float scale, int dtype, int kv_dtype,
+              int num_splits, float* o_part, float* lse_part, void* hip_stream) {
+  const bool fp8q = dtype == ATTN_DT_FP8_E4M3;
   if (B < 1 || H < 1 || Nq < 0) return ATTN_ERR_INVALID_ARG;
   if (num_pages < 1 || max_pages < 1 || page_size < 1) return ATTN_ERR_INVALID_ARG;
   if (Nq > 0 && (!q || !k_cache || !v_cache || !block_table || !seqlens_k || !o || !lse || !o_part || !lse_part))
     return ATTN_ERR_INVALID_ARG;
+  if (fp8q_entry && Nq > 0 && !q_scale) return ATTN_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_DT_F16 && dtype != ATTN_DT_BF16 && dtype != ATTN_DT_FP8_E4M3) return ATTN_ERR_INVALID_ARG;
   const bool quant = kv_dtype == ATTN_DT_FP8_E4M3 || kv_dtype == ATTN_DT_INT8;
-  if (kv_dtype != dtype && !quant) return ATTN_ERR_INVALID_ARG;
+  if (fp8q ? !quant : (kv_dtype != dtype && !quant)) return ATTN_ERR_INVALID_ARG;
   if (quant && Nq > 0 && (!k_scale || !v_scale)) return ATTN_ERR_INVALID_ARG;
   if (num_splits < 1 || num_splits > kMaxSplits) return ATTN_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
       !aligned(block_table, 4) || !aligned(seqlens_k, 4) || !aligned(o_part, 16) || !aligned(lse_part, 4) ||
-      !aligned(k_scale, 4) || !aligned(v_scale, 4))
+      !aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(q_scale, 4))
     return ATTN_ERR_INVALID_ARG;
   if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
-  if (dtype == ATTN_DT_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+  if (fp8q != fp8q_entry) return fp8q ? ATTN_ERR_UNSUPPORTED : ATTN_ERR_INVALID_ARG;
+  // e4m3 queries run on the decoding-shaped kernel only
+  if (fp8q && Nq > attn::kDecodeMaxRows) return ATTN_ERR_UNSUPPORTED;
   const int tile = attn::fwd_split_tile_keys(d);
   if (page_size % tile != 0) return ATTN_ERR_UNSUPPORTED;
   const int64_t max_keys = (int64_t)max_pages * page_size;
@@ -254,13 +262,36 @@ int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, cons
   p.page_size = page_size;
   p.max_pages = max_pages;
   p.num_pages = num_pages;
+  p.q_scale = q_scale;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
   const int kv = kv_dtype == ATTN_DT_FP8_E4M3 ? 2 : kv_dtype == ATTN_DT_INT8 ? 3 : 1;
   hipStream_t st = (hipStream_t)hip_stream;
-  hipError_t e = attn::launch_fwd(dtype, d, false, false, true, kv, p, st);
+  const hipError_t e = fp8q ? attn::launch_decode(2, d, false, kv, p, st)
+                            : attn::launch_fwd(dtype, d, false, false, true, kv, p, st);
   if (e != hipSuccess) return ATTN_ERR_HIP;
-  return attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, dtype, hip_stream);
+  return attn_merge(o_part, lse_part, num_splits, B, H, Nq, d, o, lse, fp8q ? ATTN_DT_BF16 : dtype, hip_stream);
+}
+
+}  // namespace
+
+int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                   const float* v_scale, const int32_t* block_table, const int32_t* seqlens_k, void* o, float* lse,
+                   int B, int H, int Nq, int d, int num_pages, int page_size, int max_pages, float scale, int dtype,
+                   int kv_dtype, int num_splits, float* o_part, float* lse_part, void* hip_stream) {
+  return fwd_paged(false, q, nullptr, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k, o, lse, B, H, Nq,
+                   d, num_pages, page_size, max_pages, scale, dtype, kv_dtype, num_splits, o_part, lse_part,
+                   hip_stream);
+}
+
+int attn_fwd_paged_fp8(const void* q, const float* q_scale, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* block_table,
+                       const int32_t* seqlens_k, void* o, float* lse, int B, int H, int Nq, int d, int num_pages,
+                       int page_size, int max_pages, float scale, int kv_dtype, int num_splits, float* o_part,
+                       float* lse_part, void* hip_stream) {
+  return fwd_paged(true, q, q_scale, k_cache, v_cache, k_scale, v_scale, block_table, seqlens_k, o, lse, B, H, Nq,
+                   d, num_pages, page_size, max_pages, scale, ATTN_DT_FP8_E4M3, kv_dtype, num_splits, o_part,
+                   lse_part, hip_stream);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -24,11 +24,15 @@
 // kDecodeMaxRows).  Dense K/V ([B, H, Nk, d], causal masks with absolute
 // indices, top-left) or an 8-bit paged cache (e4m3 or int8 codes with a
 // per-(token, head) scale multiplying the score and the probability, as in
-// the prefill kernel; the codes widen to fp32 exactly).  A 16-bit paged cache
+// the prefill kernel; the codes widen to fp32 exactly).  Over an 8-bit cache
+// the queries may be e4m3 codes too, with one scale per (batch, head)
+// (widened exactly, the scale applied in fp32).  A 16-bit paged cache
 // stays on the prefill kernel's key-chunk launch, measured faster there
 // (decode_shape).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "attn_device.h"
 #include "attn_params.h"
@@ -57,6 +61,10 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (G >= 32) v += __shfl_xor(v, 16);
   return v;
 }
+
+// Query tag: e4m3 codes with one fp32 scale per (batch, head), the tile
+// scale of the fp8 layout [B, H, ceil(Nq / 128)] for Nq <= kDecodeMaxRows.
+struct e4m3_query_t {};
 
 // One lane's slice of a key or value row as loaded: 16 bytes of a 16-bit row,
 // 8 bytes of codes.
@@ -131,13 +139,24 @@ __global__ void __launch_bounds__(kDecWaves * 64) attn_decode_kernel(FwdParams p
 #pragma unroll
   for (int r = 0; r < NQ; ++r) {
     if (r < p.Nq) {
-      const uint4 raw = *(const uint4*)((const uint16_t*)p.q + ((int64_t)hflat * p.Nq + r) * D + d0);
-      const uint32_t ws[4] = {raw.x, raw.y, raw.z, raw.w};
+      if constexpr (std::is_same_v<TT, e4m3_query_t>) {
+        // codes widen exactly; the scale and c multiply in fp32
+        Raw<kKvE4m3D> raw;
+        raw.w = *(const uint2*)((const uint8_t*)p.q + ((int64_t)hflat * p.Nq + r) * D + d0);
+        float f[8];
+        widen<TT, kKvE4m3D>(raw, f);
+        const float qs = load_uniform(p.q_scale, hflat) * p.c;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x2_t a = unpack2(TT{}, ws[i]);
-        q[r][2 * i] = a[0] * p.c;
-        q[r][2 * i + 1] = a[1] * p.c;
+        for (int i = 0; i < 8; ++i) q[r][i] = f[i] * qs;
+      } else {
+        const uint4 raw = *(const uint4*)((const uint16_t*)p.q + ((int64_t)hflat * p.Nq + r) * D + d0);
+        const uint32_t ws[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x2_t a = unpack2(TT{}, ws[i]);
+          q[r][2 * i] = a[0] * p.c;
+          q[r][2 * i + 1] = a[1] * p.c;
+        }
       }
     } else {
 #pragma unroll
@@ -363,6 +382,14 @@ bool decode_shape(int Nq, int kv) { return Nq <= kDecodeMaxRows && kv != kKvPage
 
 hipError_t launch_decode(int dtype, int d, bool causal, int kv, const FwdParams& p, hipStream_t st) {
   if (!decode_shape(p.Nq, kv) || (causal && kv != kKvDenseD)) return hipErrorInvalidValue;
+  if (dtype == 2) {
+    // e4m3 queries: 8-bit paged caches only
+    switch (kv) {
+      case kKvE4m3D: return launch_decode_kv<e4m3_query_t, kKvE4m3D, false>(d, p, st);
+      case kKvInt8D: return launch_decode_kv<e4m3_query_t, kKvInt8D, false>(d, p, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (dtype == 0) return launch_decode_t<f16_t>(d, causal, kv, p, st);
   return launch_decode_t<bf16_t>(d, causal, kv, p, st);
 }

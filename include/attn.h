@@ -279,13 +279,35 @@ int attn_merge(const float* o_part, const float* lse_part, int num_splits, int B
  *     Nq]: caller-owned workspace, as attn_fwd_splitkv (chunks of
  *     ceil(max_pages * page_size / num_splits) keys rounded up to 64).
  *   All device pointers; tensors 16-byte aligned, int32 and lse arrays
- *   4-byte aligned; NULL allowed only when Nq = 0.  fp8: UNSUPPORTED.  Same
- *   stream and error rules as attn_fwd_stream.
+ *   4-byte aligned; NULL allowed only when Nq = 0.  fp8 queries:
+ *   UNSUPPORTED here (attn_fwd_paged_fp8 takes them).  Same stream and
+ *   error rules as attn_fwd_stream.
  */
 int attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
                    const float* v_scale, const int32_t* block_table, const int32_t* seqlens_k, void* o, float* lse,
                    int B, int H, int Nq, int d, int num_pages, int page_size, int max_pages, float scale, int dtype,
                    int kv_dtype, int num_splits, float* o_part, float* lse_part, void* hip_stream);
+
+/*
+ * attn_fwd_paged_fp8 — attn_fwd_paged with e4m3 queries over an 8-bit
+ * cache, for decoding: one or two query rows per (batch, head) (FP8
+ * attention, "FlashAttention-3" wiki page, "Three techniques" §3, with the
+ * INT8 / FP8 KV caches of "Flash Attention 3：让 GPU 跑满的注意力计算",
+ * §4.1.3).
+ *   q [B, H, Nq, d]: OCP e4m3fn codes; q_scale fp32 [B, H]: query row i of
+ *     (b, h) is q_scale[b][h] * decode(code) (the per-128-row tile scale of
+ *     attn_fwd's fp8 layout [B, H, ceil(Nq / 128)] for Nq <= 128);
+ *   Nq in [0, 2]; more query rows: ATTN_ERR_UNSUPPORTED;
+ *   kv_dtype ATTN_DT_FP8_E4M3 or ATTN_DT_INT8 (else ATTN_ERR_INVALID_ARG),
+ *     with k_scale and v_scale as attn_fwd_paged;
+ *   o bf16 [B, H, Nq, d]; every other argument, the workspace, ownership and
+ *     the error rules as attn_fwd_paged.
+ */
+int attn_fwd_paged_fp8(const void* q, const float* q_scale, const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* block_table,
+                       const int32_t* seqlens_k, void* o, float* lse, int B, int H, int Nq, int d, int num_pages,
+                       int page_size, int max_pages, float scale, int kv_dtype, int num_splits, float* o_part,
+                       float* lse_part, void* hip_stream);
 
 /*
  * attn_bwd — gradients of the attention computed by attn_fwd: given dO =

@@ -380,3 +380,36 @@ def test_paged_unsupported_and_empty(lib):
     assert paged_call(Nq=0) == attn.ATTN_OK
     none = dict(q=None, k=None, v=None, table=None, lens=None, o=None, lse=None, o_part=None, lse_part=None)
     assert paged_call(Nq=0, **none) == attn.ATTN_OK
+
+
+def paged8_call(**over):
+    a = dict(q=FAKE, qs=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, table=FAKE, lens=FAKE, o=FAKE, lse=FAKE, B=2, H=4,
+             Nq=1, d=128, num_pages=64, page_size=128, max_pages=16, scale=0.125, kv_dtype=attn.ATTN_DT_FP8_E4M3,
+             num_splits=4, o_part=FAKE, lse_part=FAKE)
+    a.update(over)
+    return attn.attn_fwd_paged_fp8(a["q"], a["qs"], a["k"], a["v"], a["ks"], a["vs"], a["table"], a["lens"], a["o"],
+                                   a["lse"], a["B"], a["H"], a["Nq"], a["d"], a["num_pages"], a["page_size"],
+                                   a["max_pages"], a["scale"], a["kv_dtype"], a["num_splits"], a["o_part"],
+                                   a["lse_part"], None)
+
+
+PAGED8_INVALID = [
+    dict(q=None), dict(qs=None), dict(k=None), dict(ks=None), dict(vs=None), dict(table=None), dict(o=None),
+    dict(o_part=None), dict(B=0), dict(Nq=-1), dict(scale=-1.0), dict(num_splits=0), dict(qs=FAKE + 2),
+    dict(q=FAKE + 8), dict(kv_dtype=attn.ATTN_DT_BF16), dict(kv_dtype=attn.ATTN_DT_F16), dict(kv_dtype=9),
+]
+
+
+@pytest.mark.parametrize("over", PAGED8_INVALID, ids=lambda o: ",".join(f"{k}={v}" for k, v in o.items()))
+def test_paged_fp8_invalid(lib, over):
+    assert paged8_call(**over) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_paged_fp8_unsupported_and_empty(lib):
+    assert paged8_call(Nq=3) == attn.ATTN_ERR_UNSUPPORTED  # more rows than the decoding-shaped kernel takes
+    assert paged8_call(d=96) == attn.ATTN_ERR_UNSUPPORTED
+    assert paged8_call(page_size=96) == attn.ATTN_ERR_UNSUPPORTED
+    assert paged8_call(Nq=0) == attn.ATTN_OK
+    none = dict(q=None, qs=None, k=None, v=None, ks=None, vs=None, table=None, lens=None, o=None, lse=None,
+                o_part=None, lse_part=None)
+    assert paged8_call(Nq=0, **none) == attn.ATTN_OK

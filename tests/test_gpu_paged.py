@@ -255,3 +255,85 @@ def test_paged_offsets_beyond_2_31(gpu_lib, kind):
     for h in range(H):
         o_ref, l_ref = OX.attention_rows(q[0, h], kb[h], vb[h], np.arange(nq), scale, False)
         check(o_n[0, h], lse_n[0, h], o_ref, l_ref + np.log(m), "bf16", f"paged {kind} offsets beyond 2^31, head {h}")
+
+
+# ---------------------------------------------------------------- e4m3 queries
+
+FP8Q_CASES = [
+    # B, H, Nq, d, page_size, lens, splits, kind
+    (3, 4, 1, 128, 64, [1000, 70, 513], 4, "e4m3"),
+    (2, 2, 2, 128, 128, [2048, 1], 3, "int8"),
+    (4, 2, 1, 64, 64, [300, 0, 64, 129], 3, "e4m3"),
+    (2, 2, 2, 256, 128, [900, 777], 2, "e4m3"),
+    (1, 4, 1, 256, 64, [1500], 5, "int8"),
+    (2, 8, 1, 128, 256, [8192, 3000], None, "e4m3"),
+]
+
+
+def _fp8_query(B, H, Nq, d, seed):
+    """e4m3 query codes and one scale per (batch, head), and the query values
+    they stand for (decoded by the oracle, in fp64)."""
+    import workloads as W
+    from oracle.fp8 import e4m3_decode
+
+    codes = W.random_e4m3_codes((B, H, Nq, d), seed)
+    qs = W.random_scales((B, H), seed + 1, 0.5, 2.0)
+    return codes, qs, e4m3_decode(codes) * qs.astype(np.float64)[:, :, None, None]
+
+
+@pytest.mark.parametrize("B,H,Nq,d,page_size,lens,splits,kind", FP8Q_CASES)
+def test_paged_fp8_queries_vs_oracle(gpu_lib, B, H, Nq, d, page_size, lens, splits, kind):
+    """attn_fwd_paged_fp8: e4m3 queries (one scale per batch and head) on the
+    decoding-shaped kernel over an 8-bit cache, against the oracle's paged
+    attention on the decoded queries; output bf16."""
+    import workloads as W
+
+    seed = sum(lens) + d + 3 * Nq
+    kc32, _, table = make_cache(B, H, lens, d, page_size, "bf16", seed)
+    if kind == "e4m3":
+        kcodes = W.random_e4m3_codes(kc32.shape, seed + 1)
+        vcodes = W.random_e4m3_codes(kc32.shape, seed + 2)
+        ks = W.random_scales(kc32.shape[:3], seed + 3, 0.02, 0.05)
+        vs = W.random_scales(kc32.shape[:3], seed + 4, 0.02, 0.05)
+    else:
+        rng = np.random.default_rng(seed)
+        kcodes = rng.integers(0, 256, size=kc32.shape, dtype=np.uint8)
+        vcodes = rng.integers(0, 256, size=kc32.shape, dtype=np.uint8)
+        ks = W.random_scales(kc32.shape[:3], seed + 3, 0.005, 0.01)
+        vs = W.random_scales(kc32.shape[:3], seed + 4, 0.005, 0.01)
+    qcodes, qs, q64 = _fp8_query(B, H, Nq, d, seed + 5)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    o, lse = gpu_lib.forward_paged_fp8(t(qcodes), t(qs), t(kcodes), t(vcodes), t(table),
+                                       torch.tensor(lens, dtype=torch.int32).cuda(), k_scale=t(ks), v_scale=t(vs),
+                                       kv_dtype=kind, num_splits=splits)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    ref_o, ref_l = PG.attention_paged_quant(q64, kcodes, vcodes, ks, vs, table, np.array(lens), 1.0 / np.sqrt(d), kind)
+    check(o.double().cpu().numpy(), lse.double().cpu().numpy(), ref_o, ref_l, "bf16",
+          f"paged fp8 queries {kind} B{B} H{H} Nq{Nq} d{d} P{page_size} lens{lens} S{splits}")
+
+
+@pytest.mark.parametrize("nq", [1, 2])
+def test_paged_fp8_queries_unit_scale_equal_bf16_queries(gpu_lib, nq):
+    """e4m3 query codes with scale 1 and the same values as bf16 queries (e4m3
+    values are exact in bf16) give bitwise the same result: both run the
+    decoding-shaped kernel, whose query is value * c in fp32 either way."""
+    import workloads as W
+
+    B, H, d, P = 2, 4, 128, 128
+    lens = [1500, 333]
+    kc32, _, table = make_cache(B, H, lens, d, P, "bf16", 31)
+    kcodes = W.random_e4m3_codes(kc32.shape, 32)
+    vcodes = W.random_e4m3_codes(kc32.shape, 33)
+    ks = W.random_scales(kc32.shape[:3], 34, 0.02, 0.05)
+    vs = W.random_scales(kc32.shape[:3], 35, 0.02, 0.05)
+    qcodes = W.random_e4m3_codes((B, H, nq, d), 36)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    td, ld = t(table), torch.tensor(lens, dtype=torch.int32).cuda()
+    o1, l1 = gpu_lib.forward_paged_fp8(t(qcodes), torch.ones((B, H), dtype=torch.float32, device="cuda"), t(kcodes),
+                                       t(vcodes), td, ld, k_scale=t(ks), v_scale=t(vs), kv_dtype="e4m3", num_splits=3)
+    qb = t(qcodes).view(torch.float8_e4m3fn).to(torch.bfloat16)
+    o2, l2 = gpu_lib.forward_paged(qb, t(kcodes), t(vcodes), td, ld, k_scale=t(ks), v_scale=t(vs), kv_dtype="e4m3",
+                                   num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2) and torch.equal(o1, o2)
