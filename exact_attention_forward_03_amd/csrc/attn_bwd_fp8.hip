@@ -597,8 +597,19 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64), 
 bwd8_dkdv_kernel(Bwd8Params p) {
   const int w = xcd_remap(blockIdx.x, p.n_work);
   const int nkt = (p.Nk + kScaleRows - 1) / kScaleRows;
-  const int head = w / nkt;
-  dkdv8_body<CAUSAL>(p, head, w - head * nkt);
+  if constexpr (CAUSAL) {
+    // key tiles j and nkt-1-j: together the same work as any other pair
+    const int half = (nkt + 1) / 2;
+    const int head = w / half, j = w - head * half;
+    dkdv8_body<CAUSAL>(p, head, j);
+    if (nkt - 1 - j != j) {
+      __syncthreads();
+      dkdv8_body<CAUSAL>(p, head, nkt - 1 - j);
+    }
+  } else {
+    const int head = w / nkt;
+    dkdv8_body<CAUSAL>(p, head, w - head * nkt);
+  }
 }
 
 template <bool CAUSAL>
@@ -606,8 +617,19 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(kNW * 64, kNW * 64), 
 bwd8_dq_kernel(Bwd8Params p) {
   const int w = xcd_remap(blockIdx.x, p.n_work);
   const int nqt = (p.Nq + kScaleRows - 1) / kScaleRows;
-  const int head = w / nqt;
-  dq8_body<CAUSAL>(p, head, w - head * nqt);
+  if constexpr (CAUSAL) {
+    // query tiles nqt-1-j (the heavier) and j
+    const int half = (nqt + 1) / 2;
+    const int head = w / half, j = w - head * half;
+    dq8_body<CAUSAL>(p, head, nqt - 1 - j);
+    if (nqt - 1 - j != j) {
+      __syncthreads();
+      dq8_body<CAUSAL>(p, head, j);
+    }
+  } else {
+    const int head = w / nqt;
+    dq8_body<CAUSAL>(p, head, w - head * nqt);
+  }
 }
 
 template <typename K>
@@ -633,13 +655,13 @@ hipError_t launch_bwd8_c(Bwd8Params p, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   if (p.Nk > 0) {
-    p.n_work = (int)(heads * nkt);
+    p.n_work = (int)(heads * (CAUSAL ? (nkt + 1) / 2 : nkt));
     hipLaunchKernelGGL(bwd8_dkdv_kernel<CAUSAL>, dim3(p.n_work), dim3(kNW * 64), 2 * kStage, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (p.Nq > 0) {
-    p.n_work = (int)(heads * nqt);
+    p.n_work = (int)(heads * (CAUSAL ? (nqt + 1) / 2 : nqt));
     hipLaunchKernelGGL(bwd8_dq_kernel<CAUSAL>, dim3(p.n_work), dim3(kNW * 64), 2 * kStageQ, st, p);
     return hipGetLastError();
   }
