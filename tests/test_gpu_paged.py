@@ -337,3 +337,31 @@ def test_paged_fp8_queries_unit_scale_equal_bf16_queries(gpu_lib, nq):
                                    num_splits=3)
     torch.cuda.synchronize()
     assert torch.equal(l1, l2) and torch.equal(o1, o2)
+
+
+def test_paged_fp8_queries_full_decode_shape(gpu_lib):
+    """The benchmark's decoding shape with e4m3 queries over an e4m3 cache (B2
+    H32 d128, 256-token pages in shuffled order, default chunk count), one
+    sequence at the full 32768 tokens and one ragged; four of the 32 heads
+    checked against the oracle (heads are independent, so the oracle reads
+    only their slice of the cache)."""
+    import workloads as W
+
+    B, H, d, P = 2, 32, 128, 256
+    lens = [32768, 20001]
+    kc32, _, table = make_cache(B, 1, lens, d, P, "bf16", 41, spare=3)  # table and page count only
+    shape = (kc32.shape[0], P, H, d)
+    kcodes, vcodes = W.random_e4m3_codes(shape, 42), W.random_e4m3_codes(shape, 43)
+    ks, vs = W.random_scales(shape[:3], 44, 0.02, 0.05), W.random_scales(shape[:3], 45, 0.02, 0.05)
+    qcodes, qs, q64 = _fp8_query(B, H, 1, d, 46)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    o, lse = gpu_lib.forward_paged_fp8(t(qcodes), t(qs), t(kcodes), t(vcodes), t(table),
+                                       torch.tensor(lens, dtype=torch.int32).cuda(), k_scale=t(ks), v_scale=t(vs),
+                                       kv_dtype="e4m3")
+    torch.cuda.synchronize()
+    heads = [0, 7, 20, 31]
+    ref_o, ref_l = PG.attention_paged_quant(q64[:, heads], kcodes[:, :, heads], vcodes[:, :, heads],
+                                            ks[:, :, heads], vs[:, :, heads], table, np.array(lens),
+                                            1.0 / np.sqrt(d), "e4m3")
+    check(o[:, heads].double().cpu().numpy(), lse[:, heads].double().cpu().numpy(), ref_o, ref_l, "bf16",
+          "paged fp8 queries, decoding shape B2 H32 Nk32768")
